@@ -1,0 +1,169 @@
+/*
+ * bakron.h - C ABI of the MI355X (gfx950) BaKron solver.
+ *
+ * BaKron quantises a weight matrix W (m x n) with GPTQ run on vec(W) under a
+ * two-sided Kronecker-factored Hessian A (x) B: A is n x n (input side), B is
+ * m x m (output side), both symmetric positive definite. Source: "BaKron:
+ * Efficient Quantization with Kronecker-Factored Hessians" (arXiv
+ * 2608.06291), §3 (Algorithms 2-6, Theorem 3.2) and Appendix B (recurrence
+ * (2), the order-free definition of the result).
+ *
+ * Conventions for every call:
+ *  - All matrices are row-major with an explicit leading dimension (ld >= the
+ *    number of columns). The column-major vec of §3.1 is an indexing
+ *    convention of the math only; by the symmetry of the dependency order a
+ *    column-major caller can pass (n, m, W^T, B, A) with column scales.
+ *  - Every pointer except `bad_pivot` is a device pointer owned by the
+ *    caller. The library allocates and frees nothing and keeps no global
+ *    state; scratch memory is the caller's `workspace` of at least the
+ *    size the matching *_workspace_bytes query returns (256-byte aligned).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls are
+ *    asynchronous unless stated otherwise; argument errors are reported
+ *    before anything is enqueued. Calls on different streams with distinct
+ *    workspaces may run concurrently.
+ *  - `dtype` selects the element type of every floating-point array of the
+ *    call: BAKRON_F32 (float) or BAKRON_F64 (double). Codes are int32.
+ *  - m = 0 or n = 0 is accepted and does nothing.
+ */
+#ifndef BAKRON_H_
+#define BAKRON_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define BAKRON_OK 0
+#define BAKRON_EINVAL (-1)  /* bad argument: null pointer, size, leading dimension,
+                               mode, alphabet, or workspace too small */
+#define BAKRON_ENOTSPD (-2) /* A or B is not numerically positive definite */
+#define BAKRON_EHIP (-3)    /* a HIP runtime call or kernel launch failed */
+
+/* Element types. */
+#define BAKRON_F32 0
+#define BAKRON_F64 1
+
+/* Scale modes of the quantizer (§3.1: one scale per row and/or column). */
+#define BAKRON_SCALE_NONE 0 /* s = 1 */
+#define BAKRON_SCALE_ROW 1  /* s_i for row i, length m */
+#define BAKRON_SCALE_COL 2  /* s_j for column j, length n */
+
+/* Human-readable text for a status code (static storage). */
+const char *bakron_status_string(int status);
+
+/* ABI revision of this header; bumped on any incompatible change. */
+int bakron_abi_version(void);
+
+/* Tile edge used by the solver for `dtype` (32 for F32, 16 for F64); the
+ * solve works on this tiling of W. Returns 0 for an invalid dtype. */
+int bakron_tile_size(int dtype);
+
+/* ------------------------------------------------------------------------
+ * Factor: the first two steps of Algorithms 2, 3, 5 and 6 (§3.2-§3.5).
+ *
+ * L^A = Cholesky(A^-1) and L^B = Cholesky(B^-1) (§3.1: lower triangular,
+ * L L^T = A^-1, positive diagonal), then every column divided by its
+ * diagonal entry. Computed as L = RevCholesky(A)^-1 (if A = R^T R with R
+ * lower, A^-1 = R^-1 R^-T, so R^-1 is the Cholesky factor of A^-1), in
+ * float64 internally for both dtypes, and rounded once to `dtype`.
+ *
+ * A      n x n (lda >= n), B m x m (ldb >= m); only the lower triangles are
+ *        read.
+ * LA     out, n x n (ldla >= n): unit lower triangular, strict upper part
+ *        written as 0. LB likewise, m x m (ldlb >= m).
+ * dA, dB out (nullable), length n / m: the diagonals of Cholesky(A^-1) and
+ *        Cholesky(B^-1) before normalisation.
+ * bad_pivot  HOST pointer to int64[2] (nullable). On BAKRON_ENOTSPD it
+ *        receives {side, index}: side 0 = A, 1 = B, and the first pivot of
+ *        the reversed Cholesky that was not positive and finite, counted
+ *        from the last row (index k refers to row n-1-k of A). Otherwise
+ *        {-1, -1}.
+ *
+ * SYNCHRONOUS: waits for `stream` to read the pivot check. On
+ * BAKRON_ENOTSPD the outputs are unspecified.
+ * ------------------------------------------------------------------------ */
+size_t bakron_factor_workspace_bytes(int dtype, int64_t m, int64_t n);
+int bakron_factor(int dtype, int64_t m, int64_t n,
+                  const void *A, int64_t lda, const void *B, int64_t ldb,
+                  void *LA, int64_t ldla, void *LB, int64_t ldlb,
+                  void *dA, void *dB,
+                  void *workspace, size_t workspace_bytes,
+                  int64_t *bad_pivot, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Solve: BaKron (Algorithm 6, §3.5) on a tiling of W, which yields the codes
+ * of BaKron-naive (Algorithm 2) by Theorem 3.2 / Appendix B.
+ *
+ * W      m x n (ldw >= n), never modified.
+ * LA, LB the normalised factors (as bakron_factor writes them): only the
+ *        strict lower triangles are read, the diagonal is taken as 1.
+ * alpha_lo, alpha_hi, unbounded
+ *        the alphabet {alpha_lo, ..., alpha_hi} (alpha_lo <= alpha_hi), or
+ *        all integers when unbounded != 0 (§3.1).
+ * scale_mode, scales
+ *        BAKRON_SCALE_NONE (scales must be NULL), ROW (length m) or COL
+ *        (length n). Scales must be finite and > 0; other values give
+ *        unspecified codes.
+ * V      out, m x n int32 codes (ldv >= n): clamp(rint(x / s), lo, hi) at the
+ *        value x each entry has when it is rounded; ties go to even.
+ *        Unbounded codes must fit int32 (|x / s| < 2^31).
+ * Wt     out (nullable), m x n (ldwt >= n): the value x of each entry at the
+ *        moment it was rounded (Appendix B: the workspace keeps it).
+ *
+ * Asynchronous. Deterministic: the same inputs give bit-identical outputs.
+ * Non-finite inputs give unspecified codes.
+ * ------------------------------------------------------------------------ */
+size_t bakron_solve_workspace_bytes(int dtype, int64_t m, int64_t n);
+int bakron_solve(int dtype, int64_t m, int64_t n,
+                 const void *W, int64_t ldw,
+                 const void *LA, int64_t ldla, const void *LB, int64_t ldlb,
+                 int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded,
+                 int scale_mode, const void *scales,
+                 int32_t *V, int64_t ldv,
+                 void *Wt, int64_t ldwt,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* The launch schedule bakron_solve uses for (dtype, m, n), for measurement:
+ * writes up to `max_ops` records of 4 int32 {kind, k, mid, l} to the HOST
+ * array `ops` (nullable) and returns the total number of records, or a
+ * negative status. kind 0 = leaf (tile anti-diagonal k), 1 = small internal
+ * node done in one launch, 2 and 3 = the two band products of a large
+ * internal node (tile anti-diagonals [k, mid) -> [mid, l)). Host only. */
+int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t *ops, int64_t max_ops);
+
+/* ------------------------------------------------------------------------
+ * Loss: tr(B (W - Q) A (W - Q)^T) with Q = s (.) V, the quadratic form of
+ * vec(W - Q) under A (x) B (Proposition 3.1, §3.1). Evaluated in float64 as
+ * sum_ij (B D)_ij (D A)_ij with D = W - Q (A symmetric).
+ *
+ * W (ldw), V (ldv) m x n; A n x n, B m x m, lower triangles read;
+ * scale_mode/scales as for bakron_solve.
+ * loss   out: DEVICE pointer to one double.
+ *
+ * Asynchronous.
+ * ------------------------------------------------------------------------ */
+size_t bakron_loss_workspace_bytes(int dtype, int64_t m, int64_t n);
+int bakron_loss(int dtype, int64_t m, int64_t n,
+                const void *W, int64_t ldw, const int32_t *V, int64_t ldv,
+                int scale_mode, const void *scales,
+                const void *A, int64_t lda, const void *B, int64_t ldb,
+                double *loss, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Per-row scales: s_i = max_j |W_ij| / hi (1 for an all-zero row), the
+ * per-output-feature absmax rule of Appendix D with hi the largest code
+ * (7 for {-8..7}, 3 for {-4..3}). Computed in `dtype`.
+ *
+ * W m x n (ldw); scales out, length m; hi > 0. Asynchronous.
+ * ------------------------------------------------------------------------ */
+int bakron_row_scales(int dtype, int64_t m, int64_t n, const void *W, int64_t ldw,
+                      int32_t hi, void *scales, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BAKRON_H_ */

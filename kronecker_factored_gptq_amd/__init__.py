@@ -1,0 +1,276 @@
+"""MI355X-native BaKron solver.
+
+A thin Python binding over the C ABI of ``libbakron.so`` (include/bakron.h):
+argument marshalling only. PyTorch supplies device memory and streams; every
+step of the computation runs in the library's HIP kernels. The binding fails
+loudly when the library is missing; there is no fallback path.
+
+BaKron ("BaKron: Efficient Quantization with Kronecker-Factored Hessians",
+arXiv 2608.06291) quantises W (m x n) with GPTQ on vec(W) under the Hessian
+A (x) B, A n x n (input side) and B m x m (output side).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+__all__ = ["F32", "F64", "SCALE_NONE", "SCALE_ROW", "SCALE_COL", "BakronError", "lib", "factor",
+           "solve", "loss", "row_scales", "solve_schedule", "tile_size", "workspace_bytes"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libbakron.so")
+
+F32, F64 = 0, 1
+SCALE_NONE, SCALE_ROW, SCALE_COL = 0, 1, 2
+OK, EINVAL, ENOTSPD, EHIP = 0, -1, -2, -3
+
+
+class BakronError(RuntimeError):
+    def __init__(self, status: int, what: str, bad_pivot: Optional[Tuple[int, int]] = None):
+        self.status = status
+        self.bad_pivot = bad_pivot
+        msg = f"{what}: {_status_string(status)} (status {status})"
+        if bad_pivot is not None and bad_pivot[0] >= 0:
+            side = "A" if bad_pivot[0] == 0 else "B"
+            msg += f"; failing pivot {bad_pivot[1]} of the reversed Cholesky of {side}"
+        super().__init__(msg)
+
+
+_lib = None
+_vp, _i64, _i32, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbakron.so (built by __graft_entry__.build() or
+    ``python -m kronecker_factored_gptq_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(f"{LIB_PATH} is not built; run `python -m kronecker_factored_gptq_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.bakron_status_string.argtypes = [_int]
+    L.bakron_status_string.restype = ctypes.c_char_p
+    L.bakron_abi_version.argtypes = []
+    L.bakron_abi_version.restype = _int
+    L.bakron_tile_size.argtypes = [_int]
+    L.bakron_tile_size.restype = _int
+    for name in ("bakron_factor_workspace_bytes", "bakron_solve_workspace_bytes",
+                 "bakron_loss_workspace_bytes"):
+        f = getattr(L, name)
+        f.argtypes = [_int, _i64, _i64]
+        f.restype = _sz
+    L.bakron_factor.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                _vp, _vp, _vp, _sz, ctypes.POINTER(_i64), _vp]
+    L.bakron_factor.restype = _int
+    L.bakron_solve.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
+                               _int, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
+    L.bakron_solve.restype = _int
+    L.bakron_solve_schedule.argtypes = [_int, _i64, _i64, _vp, _i64]
+    L.bakron_solve_schedule.restype = _i64
+    L.bakron_loss.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp, _vp, _i64, _vp,
+                              _i64, _vp, _vp, _sz, _vp]
+    L.bakron_loss.restype = _int
+    L.bakron_row_scales.argtypes = [_int, _i64, _i64, _vp, _i64, _i32, _vp, _vp]
+    L.bakron_row_scales.restype = _int
+    _lib = L
+    return L
+
+
+def _status_string(status: int) -> str:
+    try:
+        return lib().bakron_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "unknown"
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float64:
+        return F64
+    raise TypeError(f"expected float32 or float64, got {t.dtype}")
+
+
+def _tdt(code: int) -> torch.dtype:
+    return torch.float32 if code == F32 else torch.float64
+
+
+def _ld(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.size(1) > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    return max(int(t.stride(0)), int(t.size(1)), 1)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_device(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return ws
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
+def tile_size(dtype: int = F32) -> int:
+    return int(lib().bakron_tile_size(int(dtype)))
+
+
+def workspace_bytes(kind: str, dtype: int, m: int, n: int) -> int:
+    f = {"factor": lib().bakron_factor_workspace_bytes, "solve": lib().bakron_solve_workspace_bytes,
+         "loss": lib().bakron_loss_workspace_bytes}[kind]
+    return int(f(int(dtype), int(m), int(n)))
+
+
+def factor(A: torch.Tensor, B: torch.Tensor, out_dtype: Optional[torch.dtype] = None,
+           workspace: Optional[torch.Tensor] = None):
+    """L^A = Cholesky(A^-1), L^B = Cholesky(B^-1), columns normalised by their
+    diagonals (§3.2 Algorithm 2), plus the diagonals dA, dB. Synchronous.
+    Raises BakronError(ENOTSPD) for a non-positive-definite input."""
+    dev = _check_device(A, B)
+    code = _dt(A)
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same dtype")
+    if out_dtype is not None and out_dtype != A.dtype:
+        raise TypeError("out_dtype must equal the input dtype")
+    n, m = A.size(0), B.size(0)
+    if A.shape != (n, n) or B.shape != (m, m):
+        raise ValueError("A and B must be square")
+    LA = torch.empty((n, n), dtype=A.dtype, device=dev)
+    LB = torch.empty((m, m), dtype=A.dtype, device=dev)
+    dA = torch.empty(n, dtype=A.dtype, device=dev)
+    dB = torch.empty(m, dtype=A.dtype, device=dev)
+    L = lib()
+    nbytes = L.bakron_factor_workspace_bytes(code, m, n)
+    ws = _workspace(nbytes, dev, workspace)
+    bad = (_i64 * 2)(-1, -1)
+    with torch.cuda.device(dev):
+        rc = L.bakron_factor(code, m, n, _p(A), _ld(A, "A"), _p(B), _ld(B, "B"), _p(LA), n,
+                             _p(LB), m, _p(dA), _p(dB), _p(ws), ws.numel(), bad, _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_factor", (int(bad[0]), int(bad[1])))
+    return LA, LB, dA, dB
+
+
+AlphabetLike = Union[Sequence[int], Tuple[int, int, int]]
+
+
+def _scale_mode(scales: Optional[torch.Tensor], m: int, n: int, scale_mode: Optional[int]) -> int:
+    if scales is None:
+        if scale_mode not in (None, SCALE_NONE):
+            raise ValueError("scales required for this scale_mode")
+        return SCALE_NONE
+    if scale_mode is None:
+        if scales.numel() == m:
+            return SCALE_ROW
+        if scales.numel() == n:
+            return SCALE_COL
+        raise ValueError("scales must have length m (rows) or n (columns)")
+    want = m if scale_mode == SCALE_ROW else n
+    if scale_mode not in (SCALE_ROW, SCALE_COL) or scales.numel() != want:
+        raise ValueError("scales do not match scale_mode")
+    return scale_mode
+
+
+def solve(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: AlphabetLike = (0, 0, 1),
+          scales: Optional[torch.Tensor] = None, scale_mode: Optional[int] = None,
+          return_wt: bool = False, workspace: Optional[torch.Tensor] = None,
+          out: Optional[torch.Tensor] = None):
+    """BaKron solve (§3.5 Algorithm 6 on a tiling of W). Returns int32 codes V
+    (m x n), and with ``return_wt`` also the value each entry had when it was
+    rounded. Asynchronous on the current stream."""
+    dev = _check_device(W, LA, LB, scales, workspace, out)
+    code = _dt(W)
+    m, n = W.shape
+    if LA.shape != (n, n) or LB.shape != (m, m) or LA.dtype != W.dtype or LB.dtype != W.dtype:
+        raise ValueError("LA must be n x n and LB m x m, same dtype as W")
+    lo, hi, unb = (int(alphabet[0]), int(alphabet[1]), int(bool(alphabet[2])))
+    mode = _scale_mode(scales, m, n, scale_mode)
+    if scales is not None:
+        if scales.dtype != W.dtype or not scales.is_contiguous():
+            raise ValueError("scales must be contiguous with W's dtype")
+    V = out if out is not None else torch.empty((m, n), dtype=torch.int32, device=dev)
+    Wt = torch.empty((m, n), dtype=W.dtype, device=dev) if return_wt else None
+    L = lib()
+    ws = _workspace(L.bakron_solve_workspace_bytes(code, m, n), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.bakron_solve(code, m, n, _p(W), _ld(W, "W"), _p(LA), _ld(LA, "LA"), _p(LB),
+                            _ld(LB, "LB"), lo, hi, unb, mode, _p(scales), _p(V), _ld(V, "V"),
+                            _p(Wt), _ld(Wt, "Wt") if Wt is not None else 0, _p(ws),
+                            ws.numel() * ws.element_size(), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_solve")
+    return (V, Wt) if return_wt else V
+
+
+def loss(W: torch.Tensor, V: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+         scales: Optional[torch.Tensor] = None, scale_mode: Optional[int] = None,
+         workspace: Optional[torch.Tensor] = None, sync: bool = True):
+    """tr(B (W - s V) A (W - s V)^T) in float64 (Proposition 3.1). Returns a
+    Python float (``sync``) or a 1-element float64 device tensor."""
+    dev = _check_device(W, V, A, B, scales, workspace)
+    code = _dt(W)
+    m, n = W.shape
+    mode = _scale_mode(scales, m, n, scale_mode)
+    if V.dtype != torch.int32:
+        raise TypeError("V must be int32")
+    out = torch.zeros(1, dtype=torch.float64, device=dev)
+    L = lib()
+    ws = _workspace(L.bakron_loss_workspace_bytes(code, m, n), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.bakron_loss(code, m, n, _p(W), _ld(W, "W"), _p(V), _ld(V, "V"), mode, _p(scales),
+                           _p(A), _ld(A, "A"), _p(B), _ld(B, "B"), _p(out), _p(ws),
+                           ws.numel() * ws.element_size(), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_loss")
+    return float(out.item()) if sync else out
+
+
+def row_scales(W: torch.Tensor, hi: int) -> torch.Tensor:
+    """s_i = max_j |W_ij| / hi (1 for an all-zero row), in W's dtype."""
+    dev = _check_device(W)
+    code = _dt(W)
+    m, n = W.shape
+    s = torch.empty(m, dtype=W.dtype, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().bakron_row_scales(code, m, n, _p(W), _ld(W, "W"), int(hi), _p(s), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_row_scales")
+    return s
+
+
+def solve_schedule(dtype: int, m: int, n: int):
+    """The solve's launch schedule: list of (kind, k, mid, l); kind 0 leaf,
+    1 small node, 2/3 the two band products of a large node. Host only."""
+    L = lib()
+    cnt = int(L.bakron_solve_schedule(int(dtype), int(m), int(n), None, 0))
+    if cnt < 0:
+        raise BakronError(cnt, "bakron_solve_schedule")
+    buf = (ctypes.c_int32 * (4 * max(cnt, 1)))()
+    L.bakron_solve_schedule(int(dtype), int(m), int(n), ctypes.cast(buf, ctypes.c_void_p), cnt)
+    return [tuple(buf[4 * i:4 * i + 4]) for i in range(cnt)]

@@ -1,0 +1,396 @@
+// C ABI of the gfx950 BaKron solver (declared in include/bakron.h).
+//
+// Host side only: argument checks, workspace carving, and the launch schedule
+// of the solve, the recursion of "BaKron: Efficient Quantization with
+// Kronecker-Factored Hessians" (arXiv 2608.06291), §3.5 Algorithm 6, over
+// ranges of tile anti-diagonals. Every computation runs in the kernels of the
+// .hip files; nothing here touches matrix data.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "bakron.h"
+#include "launch.hpp"
+
+namespace {
+
+using namespace bk;
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base + used);
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+inline bool dtype_ok(int dtype) { return dtype == BAKRON_F32 || dtype == BAKRON_F64; }
+inline size_t esize(int dtype) { return dtype == BAKRON_F64 ? 8 : 4; }
+inline int64_t tiles(int64_t d) { return (d + kTile - 1) / kTile; }
+
+// ---- solve schedule --------------------------------------------------------
+struct Op {
+  int32_t kind, k, mid, l;
+};
+enum { OP_LEAF = 0, OP_NODE_SMALL = 1, OP_BAND1 = 2, OP_BAND2 = 3 };
+
+void build_schedule(int k, int l, std::vector<Op>& ops) {
+  if (l - k == 1) {
+    ops.push_back({OP_LEAF, k, 0, 0});
+    return;
+  }
+  const int mid = (k + l) / 2;
+  build_schedule(k, mid, ops);
+  if (l - k <= kSmallNodeMaxQ) {
+    ops.push_back({OP_NODE_SMALL, k, mid, l});
+  } else {
+    ops.push_back({OP_BAND1, k, mid, l});
+    ops.push_back({OP_BAND2, k, mid, l});
+  }
+  build_schedule(mid, l, ops);
+}
+
+std::vector<Op> schedule_for(int64_t m, int64_t n) {
+  std::vector<Op> ops;
+  if (m <= 0 || n <= 0) return ops;
+  const int R = (int)(tiles(m) + tiles(n) - 1);
+  ops.reserve(4 * (size_t)R);
+  build_schedule(0, R, ops);
+  return ops;
+}
+
+struct SolveLayout {
+  size_t wk, lb, la, mb, total;
+};
+SolveLayout solve_layout(int dtype, int64_t m, int64_t n) {
+  const size_t es = esize(dtype);
+  const int64_t Mt = tiles(m), Nt = tiles(n);
+  const size_t tt = (size_t)kTile * kTile * es;
+  SolveLayout L;
+  L.wk = align_up((size_t)(Mt * Nt) * tt);
+  L.lb = align_up((size_t)(Mt * (Mt + 1) / 2) * tt);
+  L.la = align_up((size_t)(Nt * (Nt + 1) / 2) * tt);
+  L.mb = L.wk;
+  L.total = L.wk + L.lb + L.la + L.mb + kAlign;
+  return L;
+}
+
+template <typename R>
+int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64_t ldla,
+               const R* LB, int64_t ldlb, int32_t lo, int32_t hi, int32_t unb, int scale_mode,
+               const R* scales, int32_t* V, int64_t ldv, R* Wt, int64_t ldwt, void* ws,
+               hipStream_t s) {
+  SolveGeom g;
+  g.m = m;
+  g.n = n;
+  g.Mt = (int)tiles(m);
+  g.Nt = (int)tiles(n);
+  const SolveLayout lay = solve_layout(sizeof(R) == 8 ? BAKRON_F64 : BAKRON_F32, m, n);
+  char* base = static_cast<char*>(ws);
+  R* Wk = reinterpret_cast<R*>(base);
+  R* LBp = reinterpret_cast<R*>(base + lay.wk);
+  R* LAp = reinterpret_cast<R*>(base + lay.wk + lay.lb);
+  R* Mb = reinterpret_cast<R*>(base + lay.wk + lay.lb + lay.la);
+
+  if (launch_pack_w<R>(g, W, ldw, Wk, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_pack_l<R>(m, g.Mt, LB, ldlb, LBp, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_pack_l<R>(n, g.Nt, LA, ldla, LAp, s) != hipSuccess) return BAKRON_EHIP;
+
+  LeafParams<R> lp;
+  lp.lo = (R)lo;
+  lp.hi = (R)hi;
+  lp.unbounded = unb;
+  lp.scale_mode = scale_mode;
+  lp.scales = scales;
+  lp.V = V;
+  lp.ldv = ldv;
+  lp.Wt = Wt;
+  lp.ldwt = ldwt;
+
+  const std::vector<Op> ops = schedule_for(m, n);
+  for (const Op& op : ops) {
+    hipError_t e = hipSuccess;
+    switch (op.kind) {
+      case OP_LEAF: e = launch_leaf<R>(g, op.k, Wk, LBp, LAp, lp, s); break;
+      case OP_NODE_SMALL: e = launch_node_small<R>(g, op.k, op.mid, op.l, Wk, LBp, LAp, s); break;
+      case OP_BAND1: e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, Wk, LBp, LAp, Mb, s); break;
+      case OP_BAND2: e = launch_node_band<R>(g, op.k, op.mid, op.l, 2, Wk, LBp, LAp, Mb, s); break;
+    }
+    if (e != hipSuccess) return BAKRON_EHIP;
+  }
+  return BAKRON_OK;
+}
+
+// ---- factor ---------------------------------------------------------------
+struct FactorLayout {
+  size_t x, dinv, tmp, info, total;
+};
+FactorLayout factor_layout(int64_t m, int64_t n) {
+  const int64_t D = m > n ? m : n;
+  const int64_t nb = (D + 63) / 64 * 64;
+  FactorLayout L;
+  L.x = align_up((size_t)(D * D) * 8);
+  L.dinv = align_up((size_t)(nb * 64) * 8);
+  L.tmp = align_up((size_t)(D > 0 ? D : 1) * 64 * 8);
+  L.info = align_up(2 * sizeof(int32_t));
+  L.total = L.x + L.dinv + L.tmp + L.info + kAlign;
+  return L;
+}
+
+template <typename R>
+int factor_side(int64_t dim, const R* A, int64_t lda, R* L, int64_t ldl, R* d, double* X,
+                double* Dinv, double* Tmp, int32_t* info, hipStream_t s) {
+  if (dim == 0) return BAKRON_OK;
+  if (launch_load_reversed<R>(dim, A, lda, X, s) != hipSuccess) return BAKRON_EHIP;
+  if (factor_cholesky_inverse(dim, X, Dinv, Tmp, info, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_store_normalized<R>(dim, X, L, ldl, d, s) != hipSuccess) return BAKRON_EHIP;
+  return BAKRON_OK;
+}
+
+template <typename R>
+int factor_impl(int64_t m, int64_t n, const R* A, int64_t lda, const R* B, int64_t ldb, R* LA,
+                int64_t ldla, R* LB, int64_t ldlb, R* dA, R* dB, void* ws, int64_t* bad,
+                hipStream_t s) {
+  const FactorLayout lay = factor_layout(m, n);
+  char* base = static_cast<char*>(ws);
+  double* X = reinterpret_cast<double*>(base);
+  double* Dinv = reinterpret_cast<double*>(base + lay.x);
+  double* Tmp = reinterpret_cast<double*>(base + lay.x + lay.dinv);
+  int32_t* info = reinterpret_cast<int32_t*>(base + lay.x + lay.dinv + lay.tmp);
+  if (launch_fill_i32(info, 2, INT_MAX, s) != hipSuccess) return BAKRON_EHIP;
+  int rc = factor_side<R>(n, A, lda, LA, ldla, dA, X, Dinv, Tmp, info + 0, s);
+  if (rc != BAKRON_OK) return rc;
+  rc = factor_side<R>(m, B, ldb, LB, ldlb, dB, X, Dinv, Tmp, info + 1, s);
+  if (rc != BAKRON_OK) return rc;
+  int32_t hinfo[2] = {INT_MAX, INT_MAX};
+  if (hipMemcpyAsync(hinfo, info, sizeof(hinfo), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return BAKRON_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return BAKRON_EHIP;
+  if (bad) {
+    bad[0] = -1;
+    bad[1] = -1;
+  }
+  for (int side = 0; side < 2; ++side) {
+    if (hinfo[side] != INT_MAX) {
+      if (bad) {
+        bad[0] = side;
+        bad[1] = hinfo[side];
+      }
+      return BAKRON_ENOTSPD;
+    }
+  }
+  return BAKRON_OK;
+}
+
+// ---- loss -----------------------------------------------------------------
+struct LossLayout {
+  size_t a, b, d, be, part, total;
+  int64_t nparts;
+};
+LossLayout loss_layout(int64_t m, int64_t n) {
+  LossLayout L;
+  L.a = align_up((size_t)(n * n) * 8);
+  L.b = align_up((size_t)(m * m) * 8);
+  L.d = align_up((size_t)(m * n) * 8);
+  L.be = L.d;
+  L.nparts = gemm64_num_blocks(m, n);
+  L.part = align_up((size_t)(L.nparts > 0 ? L.nparts : 1) * 8);
+  L.total = L.a + L.b + L.d + L.be + L.part + kAlign;
+  return L;
+}
+
+template <typename R>
+int loss_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V, int64_t ldv,
+              int scale_mode, const R* scales, const R* A, int64_t lda, const R* B, int64_t ldb,
+              double* loss, void* ws, hipStream_t s) {
+  const LossLayout lay = loss_layout(m, n);
+  char* base = static_cast<char*>(ws);
+  double* A64 = reinterpret_cast<double*>(base);
+  double* B64 = reinterpret_cast<double*>(base + lay.a);
+  double* D = reinterpret_cast<double*>(base + lay.a + lay.b);
+  double* BE = reinterpret_cast<double*>(base + lay.a + lay.b + lay.d);
+  double* part = reinterpret_cast<double*>(base + lay.a + lay.b + lay.d + lay.be);
+  if (launch_sym_to_f64<R>(n, A, lda, A64, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_sym_to_f64<R>(m, B, ldb, B64, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_residual_f64<R>(m, n, W, ldw, V, ldv, scale_mode, scales, D, s) != hipSuccess)
+    return BAKRON_EHIP;
+  Gemm64Args g1{};
+  g1.M = m; g1.N = n; g1.K = m;
+  g1.A = B64; g1.lda = m;
+  g1.B = D; g1.ldb = n; g1.transB = 0;
+  g1.C = BE; g1.ldc = n;
+  g1.alpha = 1.0; g1.beta = 0.0;
+  if (launch_gemm64(g1, s) != hipSuccess) return BAKRON_EHIP;
+  Gemm64Args g2{};
+  g2.M = m; g2.N = n; g2.K = n;
+  g2.A = D; g2.lda = n;
+  g2.B = A64; g2.ldb = n; g2.transB = 0;
+  g2.alpha = 1.0;
+  g2.dot = BE; g2.lddot = n; g2.partial = part;
+  if (launch_gemm64(g2, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_sum_partials(part, lay.nparts, loss, s) != hipSuccess) return BAKRON_EHIP;
+  return BAKRON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bakron_status_string(int status) {
+  switch (status) {
+    case BAKRON_OK: return "ok";
+    case BAKRON_EINVAL: return "invalid argument";
+    case BAKRON_ENOTSPD: return "matrix is not numerically positive definite";
+    case BAKRON_EHIP: return "HIP runtime or kernel launch error";
+    default: return "unknown status";
+  }
+}
+
+int bakron_abi_version(void) { return 1; }
+
+int bakron_tile_size(int dtype) { return dtype_ok(dtype) ? kTile : 0; }
+
+size_t bakron_factor_workspace_bytes(int dtype, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0) return 0;
+  return factor_layout(m, n).total;
+}
+
+int bakron_factor(int dtype, int64_t m, int64_t n, const void* A, int64_t lda, const void* B,
+                  int64_t ldb, void* LA, int64_t ldla, void* LB, int64_t ldlb, void* dA, void* dB,
+                  void* workspace, size_t workspace_bytes, int64_t* bad_pivot, void* stream) {
+  if (bad_pivot) {
+    bad_pivot[0] = -1;
+    bad_pivot[1] = -1;
+  }
+  if (!dtype_ok(dtype) || m < 0 || n < 0) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (m == 0 && n == 0) return BAKRON_OK;
+  if (n > 0 && (!A || !LA || lda < n || ldla < n)) return BAKRON_EINVAL;
+  if (m > 0 && (!B || !LB || ldb < m || ldlb < m)) return BAKRON_EINVAL;
+  if (!workspace || workspace_bytes < bakron_factor_workspace_bytes(dtype, m, n))
+    return BAKRON_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == BAKRON_F32)
+    return factor_impl<float>(m, n, (const float*)A, lda, (const float*)B, ldb, (float*)LA, ldla,
+                              (float*)LB, ldlb, (float*)dA, (float*)dB, workspace, bad_pivot, s);
+  return factor_impl<double>(m, n, (const double*)A, lda, (const double*)B, ldb, (double*)LA,
+                             ldla, (double*)LB, ldlb, (double*)dA, (double*)dB, workspace,
+                             bad_pivot, s);
+}
+
+size_t bakron_solve_workspace_bytes(int dtype, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0) return 0;
+  return solve_layout(dtype, m, n).total;
+}
+
+int bakron_solve(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* LA,
+                 int64_t ldla, const void* LB, int64_t ldlb, int32_t alpha_lo, int32_t alpha_hi,
+                 int32_t unbounded, int scale_mode, const void* scales, int32_t* V, int64_t ldv,
+                 void* Wt, int64_t ldwt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (m == 0 || n == 0) return BAKRON_OK;
+  if (!W || !LA || !LB || !V) return BAKRON_EINVAL;
+  if (ldw < n || ldla < n || ldlb < m || ldv < n) return BAKRON_EINVAL;
+  if (Wt && ldwt < n) return BAKRON_EINVAL;
+  if (!unbounded && alpha_lo > alpha_hi) return BAKRON_EINVAL;
+  if (scale_mode == BAKRON_SCALE_NONE) {
+    if (scales) return BAKRON_EINVAL;
+  } else if (scale_mode == BAKRON_SCALE_ROW || scale_mode == BAKRON_SCALE_COL) {
+    if (!scales) return BAKRON_EINVAL;
+  } else {
+    return BAKRON_EINVAL;
+  }
+  if (!workspace || workspace_bytes < bakron_solve_workspace_bytes(dtype, m, n))
+    return BAKRON_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == BAKRON_F32)
+    return solve_impl<float>(m, n, (const float*)W, ldw, (const float*)LA, ldla,
+                             (const float*)LB, ldlb, alpha_lo, alpha_hi, unbounded, scale_mode,
+                             (const float*)scales, V, ldv, (float*)Wt, ldwt, workspace, s);
+  return solve_impl<double>(m, n, (const double*)W, ldw, (const double*)LA, ldla,
+                            (const double*)LB, ldlb, alpha_lo, alpha_hi, unbounded, scale_mode,
+                            (const double*)scales, V, ldv, (double*)Wt, ldwt, workspace, s);
+}
+
+int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t* ops, int64_t max_ops) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0 || max_ops < 0) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  const std::vector<Op> sch = schedule_for(m, n);
+  if (ops) {
+    const int64_t cnt = (int64_t)sch.size() < max_ops ? (int64_t)sch.size() : max_ops;
+    for (int64_t i = 0; i < cnt; ++i) {
+      ops[4 * i + 0] = sch[i].kind;
+      ops[4 * i + 1] = sch[i].k;
+      ops[4 * i + 2] = sch[i].mid;
+      ops[4 * i + 3] = sch[i].l;
+    }
+  }
+  return (int64_t)sch.size();
+}
+
+size_t bakron_loss_workspace_bytes(int dtype, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0) return 0;
+  return loss_layout(m, n).total;
+}
+
+int bakron_loss(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const int32_t* V,
+                int64_t ldv, int scale_mode, const void* scales, const void* A, int64_t lda,
+                const void* B, int64_t ldb, double* loss, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0) return BAKRON_EINVAL;
+  if (!loss) return BAKRON_EINVAL;
+  if (m > 0 && n > 0) {
+    if (!W || !V || !A || !B) return BAKRON_EINVAL;
+    if (ldw < n || ldv < n || lda < n || ldb < m) return BAKRON_EINVAL;
+  }
+  if (scale_mode == BAKRON_SCALE_NONE) {
+    if (scales) return BAKRON_EINVAL;
+  } else if (scale_mode == BAKRON_SCALE_ROW || scale_mode == BAKRON_SCALE_COL) {
+    if (!scales) return BAKRON_EINVAL;
+  } else {
+    return BAKRON_EINVAL;
+  }
+  if (!workspace || workspace_bytes < bakron_loss_workspace_bytes(dtype, m, n))
+    return BAKRON_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m == 0 || n == 0) {
+    // empty problem: loss 0, written by the same reduction kernel over no partials
+    return launch_sum_partials(nullptr, 0, loss, s) == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
+  }
+  if (dtype == BAKRON_F32)
+    return loss_impl<float>(m, n, (const float*)W, ldw, V, ldv, scale_mode, (const float*)scales,
+                            (const float*)A, lda, (const float*)B, ldb, loss, workspace, s);
+  return loss_impl<double>(m, n, (const double*)W, ldw, V, ldv, scale_mode, (const double*)scales,
+                           (const double*)A, lda, (const double*)B, ldb, loss, workspace, s);
+}
+
+int bakron_row_scales(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, int32_t hi,
+                      void* scales, void* stream) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0 || hi <= 0) return BAKRON_EINVAL;
+  if (m == 0) return BAKRON_OK;
+  if (!scales || (n > 0 && (!W || ldw < n))) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == BAKRON_F32)
+    e = launch_row_scales<float>(m, n, (const float*)W, ldw, hi, (float*)scales, s);
+  else
+    e = launch_row_scales<double>(m, n, (const double*)W, ldw, hi, (double*)scales, s);
+  return e == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
+}
+
+}  // extern "C"

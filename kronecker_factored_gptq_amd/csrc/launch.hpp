@@ -1,0 +1,97 @@
+// Host-side launch wrappers of the gfx950 kernels (defined in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bk {
+
+// Solver tile edge (elements). The same tiling serves the anti-diagonal sweep
+// and the masks of the band products.
+constexpr int kTile = 16;
+
+struct SolveGeom {
+  int64_t m, n;
+  int Mt, Nt;  // tiles per column / row direction
+};
+
+// ---- solve (solve_kernels.hip) --------------------------------------------
+template <typename R>
+hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, R* Wk, hipStream_t s);
+template <typename R>
+hipError_t launch_pack_l(int64_t dim, int Dt, const R* L, int64_t ld, R* Lp, hipStream_t s);
+
+template <typename R>
+struct LeafParams {
+  R lo, hi;
+  int unbounded;
+  int scale_mode;
+  const R* scales;
+  int32_t* V;
+  int64_t ldv;
+  R* Wt;
+  int64_t ldwt;
+};
+template <typename R>
+hipError_t launch_leaf(const SolveGeom& g, int K, R* Wk, const R* LBp, const R* LAp,
+                       const LeafParams<R>& lp, hipStream_t s);
+
+// Internal node of the recursion over tile anti-diagonals [k, l) split at mid.
+template <typename R>
+hipError_t launch_node_small(const SolveGeom& g, int k, int mid, int l, R* Wk, const R* LBp,
+                             const R* LAp, hipStream_t s);
+template <typename R>
+hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
+                            const R* LBp, const R* LAp, R* Mb, hipStream_t s);
+// Largest q = l - k handled by the one-launch small-node kernel.
+constexpr int kSmallNodeMaxQ = 4;
+
+// ---- factor (factor_kernels.hip), always float64 inside --------------------
+template <typename R>
+hipError_t launch_load_reversed(int64_t n, const R* A, int64_t lda, double* X, hipStream_t s);
+hipError_t factor_cholesky_inverse(int64_t n, double* X, double* Dinv, double* Tmp,
+                                   int32_t* info, hipStream_t s);
+template <typename R>
+hipError_t launch_store_normalized(int64_t n, const double* Y, R* L, int64_t ldl, R* d,
+                                   hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t v, hipStream_t s);
+
+// ---- float64 GEMM (gemm64.hip) --------------------------------------------
+// C = alpha * A * op(B) + beta * C, op(B) = B (K x N) or B^T (B is N x K).
+// lower_out: only 64x64 output blocks with block_row >= block_col are
+// computed (the others are left untouched). a_lower: A is lower triangular,
+// so row block r only needs k < (r + 1) * 64.
+// dot != nullptr: instead of storing C, the block's sum of (A op(B)) .* dot is
+// written to partial[block] (C unused).
+struct Gemm64Args {
+  int64_t M, N, K;
+  const double* A;
+  int64_t lda;
+  const double* B;
+  int64_t ldb;
+  double* C;
+  int64_t ldc;
+  double alpha, beta;
+  int transB;
+  int lower_out;
+  int a_lower;
+  const double* dot;
+  int64_t lddot;
+  double* partial;
+};
+hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s);
+int64_t gemm64_num_blocks(int64_t M, int64_t N);
+
+// ---- loss and scales (loss_kernels.hip) -----------------------------------
+template <typename R>
+hipError_t launch_sym_to_f64(int64_t n, const R* A, int64_t lda, double* X, hipStream_t s);
+template <typename R>
+hipError_t launch_residual_f64(int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V,
+                               int64_t ldv, int scale_mode, const R* scales, double* D,
+                               hipStream_t s);
+hipError_t launch_sum_partials(const double* partial, int64_t count, double* out, hipStream_t s);
+template <typename R>
+hipError_t launch_row_scales(int64_t m, int64_t n, const R* W, int64_t ldw, int32_t hi, R* s_out,
+                             hipStream_t s);
+
+}  // namespace bk

@@ -1,0 +1,121 @@
+"""Helpers for GPU-vs-oracle parity tests.
+
+Inputs flow one way: the seeded generators and the oracle produce every
+input (W, the normalised factors, the scales), cast once to the solve's
+dtype; the GPU solve and the oracle's solve both consume exactly those
+values (the oracle upcasts them exactly to float64). Nothing computed on the
+GPU is fed to the oracle, except that ``fp32_parity`` re-runs the oracle's
+recurrence with the GPU's codes imposed to check that every GPU decision is
+one the quantizer could take (a validity check, never an expected value).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle as O
+
+DEV = "cuda"
+
+
+def npdt(dtype: str):
+    return np.float32 if dtype == "f32" else np.float64
+
+
+def tdt(dtype: str):
+    return torch.float32 if dtype == "f32" else torch.float64
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+@dataclass
+class Inputs:
+    W: np.ndarray            # in the solve dtype
+    LA: np.ndarray           # oracle factors rounded to the solve dtype
+    LB: np.ndarray
+    dA: np.ndarray           # float64 diagonals from the oracle
+    dB: np.ndarray
+    s: Optional[np.ndarray]  # scales in the solve dtype, or None
+    mode: int
+    alphabet: tuple
+
+
+def prepare(W, A, B, dtype: str, alphabet, scale_rule: Optional[str] = None, hi: int = 7) -> Inputs:
+    dt = npdt(dtype)
+    W = np.asarray(W, dtype=dt)
+    LA, dA = O.factor(A)
+    LB, dB = O.factor(B)
+    s, mode = None, O.SCALE_NONE
+    if scale_rule == "row":
+        s, mode = O.row_scales(W, hi, dt), O.SCALE_ROW
+    elif scale_rule == "col":
+        s, mode = O.row_scales(W.T, hi, dt), O.SCALE_COL
+    return Inputs(W, LA.astype(dt), LB.astype(dt), dA, dB, s, mode, tuple(alphabet))
+
+
+def gpu_solve(bk, inp: Inputs, return_wt=True):
+    W, LA, LB = to_dev(inp.W), to_dev(inp.LA), to_dev(inp.LB)
+    s = None if inp.s is None else to_dev(inp.s)
+    out = bk.solve(W, LA, LB, inp.alphabet, s, scale_mode=inp.mode if s is not None else None,
+                   return_wt=return_wt)
+    torch.cuda.synchronize()
+    if return_wt:
+        V, Wt = out
+        return V.cpu().numpy(), Wt.cpu().numpy()
+    return out.cpu().numpy(), None
+
+
+def oracle_solve(inp: Inputs, naive: bool = False):
+    f = O.solve_naive if naive else O.solve_recursive
+    return f(inp.W, inp.LA, inp.LB, inp.alphabet, inp.mode, inp.s)
+
+
+@dataclass
+class Fp32Report:
+    agreement: float
+    mismatches: int
+    first_mismatch_gap: float     # |frac - 1/2| of the earliest raw mismatch (oracle value)
+    replay_inconsistent: int
+    replay_max_gap: float
+    max_dev: float                # max |Wt_gpu - Wt_replay| / s, in code units
+    loss_rel: float
+
+
+def fp32_parity(inp: Inputs, V_gpu: np.ndarray, Wt_gpu: np.ndarray, ref: O.Result, A, B) -> Fp32Report:
+    m, n = inp.W.shape
+    V_ref = ref.V.astype(np.int64)
+    mism = V_gpu.astype(np.int64) != V_ref
+    S = O.scale_grid(m, n, inp.mode, inp.s)
+    gap_first = 0.0
+    if np.any(mism):
+        ii, jj = np.nonzero(mism)
+        order = np.lexsort((ii, ii + jj))  # earliest anti-diagonal first
+        i0, j0 = ii[order[0]], jj[order[0]]
+        gap_first = float(O.frac_gap(ref.Wt[i0, j0] / S[i0, j0]))
+    rep = O.replay(inp.W, inp.LA, inp.LB, inp.alphabet, inp.mode, inp.s, V_gpu.astype(np.float64))
+    max_dev = float(np.max(np.abs(Wt_gpu.astype(np.float64) - rep.Wt) / S)) if Wt_gpu is not None else float("nan")
+    l_gpu = O.loss(inp.W, V_gpu, A, B, inp.mode, inp.s)
+    l_ref = O.loss(inp.W, ref.V, A, B, inp.mode, inp.s)
+    return Fp32Report(float(np.mean(~mism)), int(np.count_nonzero(mism)), gap_first,
+                      rep.inconsistent, rep.max_inconsistent_gap, max_dev,
+                      abs(l_gpu - l_ref) / abs(l_ref) if l_ref != 0 else abs(l_gpu))
+
+
+def assert_fp32_parity(rep: Fp32Report, min_agreement: float = 0.999, loss_rel: float = 1e-4,
+                       gap_tol: float = 1e-3):
+    """Pass conditions (fp32): raw agreement and loss as stated; every GPU
+    decision the float64 replay disagrees with lies within the measured fp32
+    deviation of a rounding midpoint; the first raw mismatch (the root of any
+    cascade) is itself a near-tie."""
+    assert rep.agreement >= min_agreement, rep
+    assert rep.loss_rel <= loss_rel, rep
+    if rep.replay_inconsistent:
+        assert rep.replay_max_gap <= max(rep.max_dev, 1e-6) + 1e-7, rep
+        assert rep.replay_max_gap <= gap_tol, rep
+    if rep.mismatches:
+        assert rep.first_mismatch_gap <= gap_tol, rep

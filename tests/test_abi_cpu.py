@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kronecker_factored_gptq_amd as bk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bakron.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bakron_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = bk.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version():
+    L = bk.lib()
+    assert L.bakron_abi_version() == 1
+    for st in (0, -1, -2, -3):
+        assert L.bakron_status_string(st)
+    assert bk.tile_size(bk.F32) == bk.tile_size(bk.F64) == 16
+    assert bk.tile_size(7) == 0
+
+
+def test_workspace_queries_scale_with_size():
+    L = bk.lib()
+    for q in (L.bakron_solve_workspace_bytes, L.bakron_factor_workspace_bytes,
+              L.bakron_loss_workspace_bytes):
+        a = q(bk.F32, 64, 64)
+        b = q(bk.F32, 512, 512)
+        assert 0 < a < b
+        assert q(bk.F64, 512, 512) >= b
+        assert q(9, 4, 4) == 0 and q(bk.F32, -1, 4) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def _solve(**kw):
+    a = dict(dtype=bk.F32, m=4, n=4, W=FAKE, ldw=4, LA=FAKE, ldla=4, LB=FAKE, ldlb=4, lo=-8, hi=7,
+             unb=0, mode=0, scales=None, V=FAKE, ldv=4, Wt=None, ldwt=0, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    return bk.lib().bakron_solve(a["dtype"], a["m"], a["n"], a["W"], a["ldw"], a["LA"], a["ldla"],
+                                 a["LB"], a["ldlb"], a["lo"], a["hi"], a["unb"], a["mode"],
+                                 a["scales"], a["V"], a["ldv"], a["Wt"], a["ldwt"], a["ws"],
+                                 a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(dtype=5), dict(m=-1), dict(W=None), dict(LA=None), dict(V=None), dict(ldw=3),
+    dict(ldla=2), dict(ldlb=3), dict(ldv=1), dict(lo=3, hi=2), dict(mode=1, scales=None),
+    dict(mode=0, scales=FAKE), dict(mode=9), dict(ws=None), dict(wsb=16),
+    dict(ws=ctypes.c_void_p(0x1001)), dict(Wt=FAKE, ldwt=2),
+])
+def test_solve_rejects_bad_arguments(bad):
+    assert _solve(**bad) == bk.EINVAL
+
+
+def test_solve_empty_is_noop():
+    assert _solve(m=0, W=None, LA=None, LB=None, V=None, ws=None) == bk.OK
+    assert _solve(n=0, W=None, LA=None, LB=None, V=None, ws=None) == bk.OK
+
+
+def test_factor_and_loss_reject_bad_arguments():
+    L = bk.lib()
+    bad = (ctypes.c_int64 * 2)(7, 7)
+    rc = L.bakron_factor(bk.F32, 4, 4, None, 4, FAKE, 4, FAKE, 4, FAKE, 4, None, None, FAKE,
+                         1 << 40, bad, None)
+    assert rc == bk.EINVAL and tuple(bad) == (-1, -1)
+    rc = L.bakron_factor(bk.F32, 4, 4, FAKE, 3, FAKE, 4, FAKE, 4, FAKE, 4, None, None, FAKE,
+                         1 << 40, None, None)
+    assert rc == bk.EINVAL
+    rc = L.bakron_factor(bk.F32, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, FAKE, 4, None, None, FAKE, 8,
+                         None, None)
+    assert rc == bk.EINVAL
+    rc = L.bakron_loss(bk.F32, 4, 4, FAKE, 4, FAKE, 4, 0, None, FAKE, 4, FAKE, 4, None, FAKE,
+                       1 << 40, None)
+    assert rc == bk.EINVAL
+    rc = L.bakron_loss(bk.F32, 4, 4, FAKE, 4, FAKE, 4, 2, None, FAKE, 4, FAKE, 4, FAKE, FAKE,
+                       1 << 40, None)
+    assert rc == bk.EINVAL
+    assert L.bakron_row_scales(bk.F32, 4, 4, FAKE, 4, 0, FAKE, None) == bk.EINVAL
+    assert L.bakron_row_scales(bk.F32, 4, 4, FAKE, 3, 7, FAKE, None) == bk.EINVAL
+
+
+def _closed_form_leaves(m, n, T=16):
+    return -(-m // T) + -(-n // T) - 1
+
+
+@pytest.mark.parametrize("m,n", [(1, 1), (16, 16), (17, 5), (64, 64), (512, 512), (4096, 4096),
+                                 (14336, 4096), (4096, 14336), (1024, 2048)])
+def test_schedule_is_algorithm_6_over_tile_antidiagonals(m, n):
+    """Table 1 "Steps" for BaKron: one leaf per (tile) anti-diagonal, and every
+    internal node splits [k, l) at floor((k+l)/2). Check the schedule against
+    the closed form: leaves Mt+Nt-1 in increasing order, nodes = leaves - 1,
+    each pair of adjacent diagonals separated by exactly the node whose
+    midpoint lies between them."""
+    ops = bk.solve_schedule(bk.F32, m, n)
+    R = _closed_form_leaves(m, n)
+    leaves = [k for (kind, k, mid, l) in ops if kind == 0]
+    assert leaves == list(range(R))
+    nodes = [(k, mid, l) for (kind, k, mid, l) in ops if kind in (1, 2)]
+    assert len(nodes) == R - 1
+    assert sorted(mid for (_, mid, _) in nodes) == list(range(1, R))
+    for (k, mid, l) in nodes:
+        assert mid == (k + l) // 2 and k < mid < l
+    # band products come in stage pairs
+    kinds = [op[0] for op in ops]
+    for i, kd in enumerate(kinds):
+        if kd == 2:
+            assert kinds[i + 1] == 3 and ops[i][1:] == ops[i + 1][1:]
+    # the node for [k,l) runs after leaf mid-1 and before leaf mid
+    pos = {("leaf", k): i for i, (kind, k, _, _) in enumerate(ops) if kind == 0}
+    for i, (kind, k, mid, l) in enumerate(ops):
+        if kind in (1, 2):
+            assert pos[("leaf", mid - 1)] < i < pos[("leaf", mid)]
