@@ -57,8 +57,8 @@ const char *bakron_status_string(int status);
 /* ABI revision of this header; bumped on any incompatible change. */
 int bakron_abi_version(void);
 
-/* Tile edge used by the solver for `dtype` (32 for F32, 16 for F64); the
- * solve works on this tiling of W. Returns 0 for an invalid dtype. */
+/* Tile edge (16) of the tiling of W the solver works on, for `dtype`.
+ * Returns 0 for an invalid dtype. */
 int bakron_tile_size(int dtype);
 
 /* ------------------------------------------------------------------------
@@ -133,6 +133,24 @@ int bakron_solve(int dtype, int64_t m, int64_t n,
  * node done in one launch, 2 and 3 = the two band products of a large
  * internal node (tile anti-diagonals [k, mid) -> [mid, l)). Host only. */
 int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t *ops, int64_t max_ops);
+
+/* Measurement variant of bakron_solve: same arguments and result, and it
+ * also times its band-product launches. For every record i of
+ * bakron_solve_schedule with kind 2 or 3, op_ms[i] receives the time in
+ * milliseconds between HIP events recorded on `stream` immediately before
+ * and after that launch; every other slot receives -1. `op_ms` is a HOST
+ * array of `n_ops` doubles and n_ops must equal the schedule length.
+ * SYNCHRONOUS (waits for the last event). Creates and destroys its events;
+ * returns BAKRON_EHIP if that fails. */
+int bakron_solve_timed(int dtype, int64_t m, int64_t n,
+                       const void *W, int64_t ldw,
+                       const void *LA, int64_t ldla, const void *LB, int64_t ldlb,
+                       int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded,
+                       int scale_mode, const void *scales,
+                       int32_t *V, int64_t ldv,
+                       void *Wt, int64_t ldwt,
+                       void *workspace, size_t workspace_bytes, void *stream,
+                       double *op_ms, int64_t n_ops);
 
 /* ------------------------------------------------------------------------
  * Loss: tr(B (W - Q) A (W - Q)^T) with Q = s (.) V, the quadratic form of

@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
     L.bakron_solve.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
                                _int, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
     L.bakron_solve.restype = _int
+    L.bakron_solve_timed.argtypes = L.bakron_solve.argtypes + [_vp, _i64]
+    L.bakron_solve_timed.restype = _int
     L.bakron_solve_schedule.argtypes = [_int, _i64, _i64, _vp, _i64]
     L.bakron_solve_schedule.restype = _i64
     L.bakron_loss.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp, _vp, _i64, _vp,
@@ -200,10 +202,12 @@ def _scale_mode(scales: Optional[torch.Tensor], m: int, n: int, scale_mode: Opti
 def solve(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: AlphabetLike = (0, 0, 1),
           scales: Optional[torch.Tensor] = None, scale_mode: Optional[int] = None,
           return_wt: bool = False, workspace: Optional[torch.Tensor] = None,
-          out: Optional[torch.Tensor] = None):
+          out: Optional[torch.Tensor] = None, op_ms: Optional[ctypes.Array] = None):
     """BaKron solve (§3.5 Algorithm 6 on a tiling of W). Returns int32 codes V
     (m x n), and with ``return_wt`` also the value each entry had when it was
-    rounded. Asynchronous on the current stream."""
+    rounded. Asynchronous on the current stream, except with ``op_ms`` (a
+    ctypes double array, one slot per schedule record): then the band-product
+    launches are timed with HIP events and the call waits for them."""
     dev = _check_device(W, LA, LB, scales, workspace, out)
     code = _dt(W)
     m, n = W.shape
@@ -218,11 +222,15 @@ def solve(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: Alphabe
     Wt = torch.empty((m, n), dtype=W.dtype, device=dev) if return_wt else None
     L = lib()
     ws = _workspace(L.bakron_solve_workspace_bytes(code, m, n), dev, workspace)
+    args = (code, m, n, _p(W), _ld(W, "W"), _p(LA), _ld(LA, "LA"), _p(LB), _ld(LB, "LB"), lo, hi,
+            unb, mode, _p(scales), _p(V), _ld(V, "V"), _p(Wt),
+            _ld(Wt, "Wt") if Wt is not None else 0, _p(ws), ws.numel() * ws.element_size(),
+            _stream(dev))
     with torch.cuda.device(dev):
-        rc = L.bakron_solve(code, m, n, _p(W), _ld(W, "W"), _p(LA), _ld(LA, "LA"), _p(LB),
-                            _ld(LB, "LB"), lo, hi, unb, mode, _p(scales), _p(V), _ld(V, "V"),
-                            _p(Wt), _ld(Wt, "Wt") if Wt is not None else 0, _p(ws),
-                            ws.numel() * ws.element_size(), _stream(dev))
+        if op_ms is None:
+            rc = L.bakron_solve(*args)
+        else:
+            rc = L.bakron_solve_timed(*args, ctypes.cast(op_ms, ctypes.c_void_p), len(op_ms))
     if rc != OK:
         raise BakronError(rc, "bakron_solve")
     return (V, Wt) if return_wt else V

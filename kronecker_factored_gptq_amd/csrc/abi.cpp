@@ -23,18 +23,6 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-struct Carver {
-  char* base;
-  size_t used = 0;
-  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
-  template <typename T>
-  T* take(size_t count) {
-    T* p = reinterpret_cast<T*>(base + used);
-    used += align_up(count * sizeof(T));
-    return p;
-  }
-};
-
 inline bool dtype_ok(int dtype) { return dtype == BAKRON_F32 || dtype == BAKRON_F64; }
 inline size_t esize(int dtype) { return dtype == BAKRON_F64 ? 8 : 4; }
 inline int64_t tiles(int64_t d) { return (d + kTile - 1) / kTile; }
@@ -90,7 +78,7 @@ template <typename R>
 int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64_t ldla,
                const R* LB, int64_t ldlb, int32_t lo, int32_t hi, int32_t unb, int scale_mode,
                const R* scales, int32_t* V, int64_t ldv, R* Wt, int64_t ldwt, void* ws,
-               hipStream_t s) {
+               hipStream_t s, double* op_ms = nullptr) {
   SolveGeom g;
   g.m = m;
   g.n = n;
@@ -119,17 +107,53 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   lp.ldwt = ldwt;
 
   const std::vector<Op> ops = schedule_for(m, n);
+  // optional per-launch timing of the band products (measurement entry point)
+  std::vector<hipEvent_t> ev;
+  if (op_ms) {
+    size_t nb = 0;
+    for (const Op& op : ops) nb += (op.kind == OP_BAND1 || op.kind == OP_BAND2) ? 1 : 0;
+    ev.assign(2 * nb, nullptr);
+    for (auto& e : ev)
+      if (hipEventCreate(&e) != hipSuccess) {
+        for (auto& d : ev)
+          if (d) (void)hipEventDestroy(d);
+        return BAKRON_EHIP;
+      }
+  }
+  size_t evi = 0;
+  int rc = BAKRON_OK;
   for (const Op& op : ops) {
     hipError_t e = hipSuccess;
+    const bool timed = op_ms && (op.kind == OP_BAND1 || op.kind == OP_BAND2);
+    if (timed && hipEventRecord(ev[evi], s) != hipSuccess) { rc = BAKRON_EHIP; break; }
     switch (op.kind) {
       case OP_LEAF: e = launch_leaf<R>(g, op.k, Wk, LBp, LAp, lp, s); break;
       case OP_NODE_SMALL: e = launch_node_small<R>(g, op.k, op.mid, op.l, Wk, LBp, LAp, s); break;
       case OP_BAND1: e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, Wk, LBp, LAp, Mb, s); break;
       case OP_BAND2: e = launch_node_band<R>(g, op.k, op.mid, op.l, 2, Wk, LBp, LAp, Mb, s); break;
     }
-    if (e != hipSuccess) return BAKRON_EHIP;
+    if (e != hipSuccess) { rc = BAKRON_EHIP; break; }
+    if (timed) {
+      if (hipEventRecord(ev[evi + 1], s) != hipSuccess) { rc = BAKRON_EHIP; break; }
+      evi += 2;
+    }
   }
-  return BAKRON_OK;
+  if (op_ms) {
+    if (rc == BAKRON_OK && !ev.empty() && hipEventSynchronize(ev.back()) != hipSuccess)
+      rc = BAKRON_EHIP;
+    size_t k = 0;
+    for (size_t i = 0; i < ops.size(); ++i) {
+      op_ms[i] = -1.0;
+      if (rc == BAKRON_OK && (ops[i].kind == OP_BAND1 || ops[i].kind == OP_BAND2)) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) != hipSuccess) rc = BAKRON_EHIP;
+        op_ms[i] = ms;
+        k += 2;
+      }
+    }
+    for (auto& d : ev) (void)hipEventDestroy(d);
+  }
+  return rc;
 }
 
 // ---- factor ---------------------------------------------------------------
@@ -295,10 +319,11 @@ size_t bakron_solve_workspace_bytes(int dtype, int64_t m, int64_t n) {
   return solve_layout(dtype, m, n).total;
 }
 
-int bakron_solve(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* LA,
-                 int64_t ldla, const void* LB, int64_t ldlb, int32_t alpha_lo, int32_t alpha_hi,
-                 int32_t unbounded, int scale_mode, const void* scales, int32_t* V, int64_t ldv,
-                 void* Wt, int64_t ldwt, void* workspace, size_t workspace_bytes, void* stream) {
+static int solve_entry(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* LA,
+                       int64_t ldla, const void* LB, int64_t ldlb, int32_t alpha_lo,
+                       int32_t alpha_hi, int32_t unbounded, int scale_mode, const void* scales,
+                       int32_t* V, int64_t ldv, void* Wt, int64_t ldwt, void* workspace,
+                       size_t workspace_bytes, void* stream, double* op_ms, int64_t n_ops) {
   if (!dtype_ok(dtype) || m < 0 || n < 0) return BAKRON_EINVAL;
   if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
   if (m == 0 || n == 0) return BAKRON_OK;
@@ -316,14 +341,36 @@ int bakron_solve(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, co
   if (!workspace || workspace_bytes < bakron_solve_workspace_bytes(dtype, m, n))
     return BAKRON_EINVAL;
   if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  if (op_ms && n_ops != (int64_t)schedule_for(m, n).size()) return BAKRON_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == BAKRON_F32)
     return solve_impl<float>(m, n, (const float*)W, ldw, (const float*)LA, ldla,
                              (const float*)LB, ldlb, alpha_lo, alpha_hi, unbounded, scale_mode,
-                             (const float*)scales, V, ldv, (float*)Wt, ldwt, workspace, s);
+                             (const float*)scales, V, ldv, (float*)Wt, ldwt, workspace, s, op_ms);
   return solve_impl<double>(m, n, (const double*)W, ldw, (const double*)LA, ldla,
                             (const double*)LB, ldlb, alpha_lo, alpha_hi, unbounded, scale_mode,
-                            (const double*)scales, V, ldv, (double*)Wt, ldwt, workspace, s);
+                            (const double*)scales, V, ldv, (double*)Wt, ldwt, workspace, s, op_ms);
+}
+
+int bakron_solve(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* LA,
+                 int64_t ldla, const void* LB, int64_t ldlb, int32_t alpha_lo, int32_t alpha_hi,
+                 int32_t unbounded, int scale_mode, const void* scales, int32_t* V, int64_t ldv,
+                 void* Wt, int64_t ldwt, void* workspace, size_t workspace_bytes, void* stream) {
+  return solve_entry(dtype, m, n, W, ldw, LA, ldla, LB, ldlb, alpha_lo, alpha_hi, unbounded,
+                     scale_mode, scales, V, ldv, Wt, ldwt, workspace, workspace_bytes, stream,
+                     nullptr, 0);
+}
+
+int bakron_solve_timed(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
+                       const void* LA, int64_t ldla, const void* LB, int64_t ldlb,
+                       int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded, int scale_mode,
+                       const void* scales, int32_t* V, int64_t ldv, void* Wt, int64_t ldwt,
+                       void* workspace, size_t workspace_bytes, void* stream, double* op_ms,
+                       int64_t n_ops) {
+  if (!op_ms) return BAKRON_EINVAL;
+  return solve_entry(dtype, m, n, W, ldw, LA, ldla, LB, ldlb, alpha_lo, alpha_hi, unbounded,
+                     scale_mode, scales, V, ldv, Wt, ldwt, workspace, workspace_bytes, stream,
+                     op_ms, n_ops);
 }
 
 int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t* ops, int64_t max_ops) {

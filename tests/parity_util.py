@@ -84,6 +84,16 @@ class Fp32Report:
     replay_max_gap: float
     max_dev: float                # max |Wt_gpu - Wt_replay| / s, in code units
     loss_rel: float
+    loss_signed: float = 0.0      # (loss(V_gpu) - loss(V_ref)) / loss(V_ref)
+    m: int = 0
+    n: int = 0
+
+    def cascade_loss_bound(self) -> float:
+        """Loss spread expected between two valid solutions that differ on k
+        entries: each differing entry moves its own share of the loss by about
+        the mean share, loss/(mn), in either direction, so the relative
+        difference is ~sqrt(k)/(mn); allow 4 sigma, never below 1e-4."""
+        return max(1e-4, 4.0 * np.sqrt(self.mismatches) / max(self.m * self.n, 1))
 
 
 def fp32_parity(inp: Inputs, V_gpu: np.ndarray, Wt_gpu: np.ndarray, ref: O.Result, A, B) -> Fp32Report:
@@ -101,9 +111,9 @@ def fp32_parity(inp: Inputs, V_gpu: np.ndarray, Wt_gpu: np.ndarray, ref: O.Resul
     max_dev = float(np.max(np.abs(Wt_gpu.astype(np.float64) - rep.Wt) / S)) if Wt_gpu is not None else float("nan")
     l_gpu = O.loss(inp.W, V_gpu, A, B, inp.mode, inp.s)
     l_ref = O.loss(inp.W, ref.V, A, B, inp.mode, inp.s)
+    rel = (l_gpu - l_ref) / abs(l_ref) if l_ref != 0 else l_gpu
     return Fp32Report(float(np.mean(~mism)), int(np.count_nonzero(mism)), gap_first,
-                      rep.inconsistent, rep.max_inconsistent_gap, max_dev,
-                      abs(l_gpu - l_ref) / abs(l_ref) if l_ref != 0 else abs(l_gpu))
+                      rep.inconsistent, rep.max_inconsistent_gap, max_dev, abs(rel), rel, m, n)
 
 
 def assert_fp32_parity(rep: Fp32Report, min_agreement: float = 0.999, loss_rel: float = 1e-4,
@@ -119,3 +129,17 @@ def assert_fp32_parity(rep: Fp32Report, min_agreement: float = 0.999, loss_rel: 
         assert rep.replay_max_gap <= gap_tol, rep
     if rep.mismatches:
         assert rep.first_mismatch_gap <= gap_tol, rep
+
+
+def assert_fp32_validity(rep: Fp32Report, gap_tol: float = 1e-5):
+    """Size-independent conditions (fp32) for sizes where a single near-tie
+    flip cascades: every GPU decision is the quantizer's choice at the float64
+    replayed value except within the measured fp32 deviation of a midpoint;
+    the first raw divergence is itself a near-tie; the loss differs by no more
+    than the spread of two valid solutions that differ on that many entries."""
+    if rep.replay_inconsistent:
+        assert rep.replay_max_gap <= max(rep.max_dev, 1e-6) + 1e-7, rep
+        assert rep.replay_max_gap <= gap_tol, rep
+    if rep.mismatches:
+        assert rep.first_mismatch_gap <= gap_tol, rep
+    assert rep.loss_rel <= rep.cascade_loss_bound(), rep
