@@ -127,11 +127,12 @@ int bakron_solve(int dtype, int64_t m, int64_t n,
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* The launch schedule bakron_solve uses for (dtype, m, n), for measurement:
- * writes up to `max_ops` records of 4 int32 {kind, k, mid, l} to the HOST
+ * writes up to `max_ops` records of 4 int32 {kind, a, b, c} to the HOST
  * array `ops` (nullable) and returns the total number of records, or a
- * negative status. kind 0 = leaf (tile anti-diagonal k), 1 = small internal
- * node done in one launch, 2 and 3 = the two band products of a large
- * internal node (tile anti-diagonals [k, mid) -> [mid, l)). Host only. */
+ * negative status. kind 0 = leaf: a = tile anti-diagonal K, b = first tile
+ * anti-diagonal of its block (the leaf also applies the updates from tile
+ * anti-diagonals b..K-1); kinds 2 and 3 = the two band products of an
+ * internal node, tile anti-diagonals [a, b) -> [b, c). Host only. */
 int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t *ops, int64_t max_ops);
 
 /* Measurement variant of bakron_solve: same arguments and result, and it

@@ -273,8 +273,9 @@ def row_scales(W: torch.Tensor, hi: int) -> torch.Tensor:
 
 
 def solve_schedule(dtype: int, m: int, n: int):
-    """The solve's launch schedule: list of (kind, k, mid, l); kind 0 leaf,
-    1 small node, 2/3 the two band products of a large node. Host only."""
+    """The solve's launch schedule: list of (kind, a, b, c); kind 0 = leaf of
+    tile anti-diagonal a whose block starts at b, kinds 2/3 = the two band
+    products of the internal node [a, b) -> [b, c). Host only."""
     L = lib()
     cnt = int(L.bakron_solve_schedule(int(dtype), int(m), int(n), None, 0))
     if cnt < 0:

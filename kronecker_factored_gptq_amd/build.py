@@ -20,13 +20,13 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libbakron.so")
 
-SOURCES = ["abi.cpp", "solve_kernels.hip", "factor_kernels.hip", "gemm64.hip", "loss_kernels.hip"]
+SOURCES = ["abi.cpp", "solve_kernels.hip", "band_kernels.hip", "factor_kernels.hip", "gemm64.hip", "loss_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
-    # packed fp32 instructions stay off (packed-FP32 note)
+    # never generate packed-fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",

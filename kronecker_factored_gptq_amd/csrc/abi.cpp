@@ -31,30 +31,33 @@ inline int64_t tiles(int64_t d) { return (d + kTile - 1) / kTile; }
 struct Op {
   int32_t kind, k, mid, l;
 };
-enum { OP_LEAF = 0, OP_NODE_SMALL = 1, OP_BAND1 = 2, OP_BAND2 = 3 };
+enum { OP_LEAF = 0, OP_BAND1 = 2, OP_BAND2 = 3 };
 
-void build_schedule(int k, int l, std::vector<Op>& ops) {
-  if (l - k == 1) {
-    ops.push_back({OP_LEAF, k, 0, 0});
+// Algorithm 6 over blocks [kb, lb) of kLeafBlock tile anti-diagonals each
+// (R tile anti-diagonals in all); a block's leaves run in order.
+void build_schedule(int kb, int lb, int R, std::vector<Op>& ops) {
+  if (lb - kb == 1) {
+    const int K0 = kb * kLeafBlock;
+    const int K1 = (kb + 1) * kLeafBlock < R ? (kb + 1) * kLeafBlock : R;
+    for (int K = K0; K < K1; ++K) ops.push_back({OP_LEAF, K, K0, 0});
     return;
   }
-  const int mid = (k + l) / 2;
-  build_schedule(k, mid, ops);
-  if (l - k <= kSmallNodeMaxQ) {
-    ops.push_back({OP_NODE_SMALL, k, mid, l});
-  } else {
-    ops.push_back({OP_BAND1, k, mid, l});
-    ops.push_back({OP_BAND2, k, mid, l});
-  }
-  build_schedule(mid, l, ops);
+  const int midb = (kb + lb) / 2;
+  build_schedule(kb, midb, R, ops);
+  const int k = kb * kLeafBlock, mid = midb * kLeafBlock;
+  const int l = lb * kLeafBlock < R ? lb * kLeafBlock : R;
+  ops.push_back({OP_BAND1, k, mid, l});
+  ops.push_back({OP_BAND2, k, mid, l});
+  build_schedule(midb, lb, R, ops);
 }
 
 std::vector<Op> schedule_for(int64_t m, int64_t n) {
   std::vector<Op> ops;
   if (m <= 0 || n <= 0) return ops;
   const int R = (int)(tiles(m) + tiles(n) - 1);
-  ops.reserve(4 * (size_t)R);
-  build_schedule(0, R, ops);
+  const int nb = (R + kLeafBlock - 1) / kLeafBlock;
+  ops.reserve(3 * (size_t)R);
+  build_schedule(0, nb, R, ops);
   return ops;
 }
 
@@ -127,8 +130,7 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
     const bool timed = op_ms && (op.kind == OP_BAND1 || op.kind == OP_BAND2);
     if (timed && hipEventRecord(ev[evi], s) != hipSuccess) { rc = BAKRON_EHIP; break; }
     switch (op.kind) {
-      case OP_LEAF: e = launch_leaf<R>(g, op.k, Wk, LBp, LAp, lp, s); break;
-      case OP_NODE_SMALL: e = launch_node_small<R>(g, op.k, op.mid, op.l, Wk, LBp, LAp, s); break;
+      case OP_LEAF: e = launch_leaf<R>(g, op.k, op.mid, Wk, LBp, LAp, lp, s); break;
       case OP_BAND1: e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, Wk, LBp, LAp, Mb, s); break;
       case OP_BAND2: e = launch_node_band<R>(g, op.k, op.mid, op.l, 2, Wk, LBp, LAp, Mb, s); break;
     }

@@ -1,0 +1,267 @@
+// Band products of a large internal node, on MFMA (gfx950).
+//
+// An internal node over tile anti-diagonals [k, l), split at mid, applies the
+// errors E recorded on [k, mid) to the tiles on [mid, l) as the two
+// "restricted band products" of "BaKron: Efficient Quantization with
+// Kronecker-Factored Hessians" (arXiv 2608.06291), Appendix C:
+//   stage 1: M[P,J]  = sum_I L^B[P,I] E[I,J],   I <= P, k <= I+J < mid
+//   stage 2: W[P,Q] += sum_J M[P,J] L^A[Q,J]^T, J <= Q, J < mid,
+//            k <= P+J <= l-1, written only where mid <= P+Q <= l-1.
+// (Subscripts are 16 x 16 solver tiles.)
+//
+// Each workgroup owns an MB x MB block of solver tiles (a BM = 16*MB square
+// macro tile) and walks K two solver tiles (32 elements) at a time. Four
+// waves in a 2 x 2 arrangement each hold a (BM/2)^2 accumulator of 16 x 16
+// MFMA blocks. Solver tiles are contiguous in HBM, so a 16-byte load by
+// every lane of a wave moves exactly one tile (float) or half a tile
+// (double): tile masks are wave-uniform and every load is fully coalesced.
+// Operands are double-buffered in LDS with k contiguous (one 128-bit read
+// per lane per four MFMAs); stage 1's E tiles keep their natural row-major
+// order (k = row) and are read one element per MFMA.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace bk {
+
+template <typename R> struct Vec16;
+template <> struct Vec16<float> {
+  typedef float4 T;
+  static constexpr int N = 4;
+  __device__ static inline T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ static inline float get(const T& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+};
+template <> struct Vec16<double> {
+  typedef double2 T;
+  static constexpr int N = 2;
+  __device__ static inline T zero() { return make_double2(0.0, 0.0); }
+  __device__ static inline double get(const T& v, int e) { return e == 0 ? v.x : v.y; }
+};
+
+template <typename R, int MB>
+struct BandShape {
+  static constexpr int T = kTile;
+  static constexpr int BKT = 2;                  // K step in solver tiles
+  static constexpr int BK = BKT * T;             // K step in elements
+  static constexpr int BM = MB * T;              // macro tile edge
+  static constexpr int WT = BM / 2;              // wave tile edge
+  static constexpr int NBW = WT / 16;            // MFMA blocks per wave edge
+  static constexpr int VN = Vec16<R>::N;         // elements per 16-byte vector
+  static constexpr int LDK = BK + VN;            // k-contiguous rows, 16-byte aligned
+  static constexpr int LDC = BM + VN;            // column-contiguous rows (stage-1 B)
+  static constexpr int TV = T * T / VN;          // vectors per solver tile
+  static constexpr int NV = MB * BKT * TV / 256; // vectors per thread per operand per K step
+  static constexpr int KL = BK / 4;              // k values per lane per K step
+  static_assert(NV >= 1 && (MB * BKT * TV) % 256 == 0, "macro tile too small for 256 threads");
+};
+
+template <typename R, int STAGE, int MB>
+__global__ __launch_bounds__(256) void band_kernel(int k, int mid, int l, int Mt, int Nt,
+                                                   R* __restrict__ Wk, const R* __restrict__ LBp,
+                                                   const R* __restrict__ LAp, R* __restrict__ Mb) {
+  typedef BandShape<R, MB> S;
+  typedef Vec16<R> VV;
+  typedef typename VV::T vec_t;
+  typedef Mfma<R> MF;
+  typedef typename MF::acc_t acc_t;
+  constexpr int T = S::T;
+  constexpr int B_ROWS = STAGE == 1 ? S::BK : S::BM;
+  constexpr int B_LD = STAGE == 1 ? S::LDC : S::LDK;
+
+  __shared__ __attribute__((aligned(16))) R As[2][S::BM][S::LDK];
+  __shared__ __attribute__((aligned(16))) R Bs[2][B_ROWS][B_LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int r16 = lane & 15, kg = lane >> 4;
+
+  const int pb = blockIdx.y;
+  const int P0 = pb * MB;
+  int Clo, Chi;
+  if (STAGE == 1) {
+    Clo = k - (P0 + MB - 1); if (Clo < 0) Clo = 0;
+    Chi = Nt - 1; if (mid - 1 < Chi) Chi = mid - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
+  } else {
+    Clo = mid - (P0 + MB - 1); if (Clo < 0) Clo = 0;
+    Chi = Nt - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
+  }
+  if (Clo > Chi) return;
+  const int cb = Clo / MB + (int)blockIdx.x;
+  if (cb > Chi / MB) return;
+  const int C0 = cb * MB;
+
+  int Klo, Khi;
+  if (STAGE == 1) {
+    Klo = k - (C0 + MB - 1); if (Klo < 0) Klo = 0;
+    Khi = P0 + MB - 1; if (mid - 1 - C0 < Khi) Khi = mid - 1 - C0; if (Mt - 1 < Khi) Khi = Mt - 1;
+  } else {
+    Klo = k - (P0 + MB - 1); if (Klo < 0) Klo = 0;
+    Khi = C0 + MB - 1; if (mid - 1 < Khi) Khi = mid - 1; if (Nt - 1 < Khi) Khi = Nt - 1;
+  }
+
+  acc_t acc[S::NBW][S::NBW];
+#pragma unroll
+  for (int i = 0; i < S::NBW; ++i)
+#pragma unroll
+    for (int j = 0; j < S::NBW; ++j) acc[i][j] = MF::zero();
+
+  vec_t ra[S::NV], rb[S::NV];
+
+  // global -> registers for the K step starting at solver tile kk0
+  auto gload = [&](int kk0) {
+#pragma unroll
+    for (int u = 0; u < S::NV; ++u) {
+      const int f = u * 256 + tid;
+      const int ti = f / S::TV;               // tile index within the operand block
+      const int a = ti / S::BKT, kt = ti % S::BKT;
+      const int v = f % S::TV;
+      const int kk = kk0 + kt;
+      const int P = P0 + a, C = C0 + a;
+      vec_t va = VV::zero(), vb = VV::zero();
+      if (STAGE == 1) {
+        if (kk <= Khi && P < Mt && kk <= P)
+          va = reinterpret_cast<const vec_t*>(LBp + tri_index(P, kk) * T * T)[v];
+        const int s = kk + C;
+        if (kk <= Khi && C < Nt && s >= k && s < mid)
+          vb = reinterpret_cast<const vec_t*>(Wk + ((int64_t)kk * Nt + C) * T * T)[v];
+      } else {
+        const int s = P + kk;
+        if (kk <= Khi && P < Mt && kk <= mid - 1 && s >= k && s <= l - 1)
+          va = reinterpret_cast<const vec_t*>(Mb + ((int64_t)P * Nt + kk) * T * T)[v];
+        if (kk <= Khi && C < Nt && kk <= C)
+          vb = reinterpret_cast<const vec_t*>(LAp + tri_index(C, kk) * T * T)[v];
+      }
+      ra[u] = va;
+      rb[u] = vb;
+    }
+  };
+  // registers -> LDS buffer
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < S::NV; ++u) {
+      const int f = u * 256 + tid;
+      const int ti = f / S::TV;
+      const int a = ti / S::BKT, kt = ti % S::BKT;
+      const int e0 = (f % S::TV) * S::VN;
+      const int r = e0 / T, c = e0 % T;
+      *reinterpret_cast<vec_t*>(&As[buf][a * T + r][kt * T + c]) = ra[u];
+      if (STAGE == 1)  // E[k = r][col = c]: keep rows of k
+        *reinterpret_cast<vec_t*>(&Bs[buf][kt * T + r][a * T + c]) = rb[u];
+      else             // L^A[col = r][k = c]: k contiguous per column
+        *reinterpret_cast<vec_t*>(&Bs[buf][a * T + r][kt * T + c]) = rb[u];
+    }
+  };
+  // MFMAs over one K step; lane group kg covers k = kg*KL .. kg*KL + KL - 1
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int sc = 0; sc < S::KL / S::VN; ++sc) {
+      const int k0 = kg * S::KL + sc * S::VN;
+      vec_t af[S::NBW], bf[S::NBW];
+#pragma unroll
+      for (int i = 0; i < S::NBW; ++i)
+        af[i] = *reinterpret_cast<const vec_t*>(&As[buf][wr * S::WT + i * 16 + r16][k0]);
+      R b1[S::NBW][S::VN];
+#pragma unroll
+      for (int j = 0; j < S::NBW; ++j) {
+        if (STAGE == 1) {
+#pragma unroll
+          for (int e = 0; e < S::VN; ++e) b1[j][e] = Bs[buf][k0 + e][wc * S::WT + j * 16 + r16];
+        } else {
+          bf[j] = *reinterpret_cast<const vec_t*>(&Bs[buf][wc * S::WT + j * 16 + r16][k0]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < S::VN; ++e)
+#pragma unroll
+        for (int i = 0; i < S::NBW; ++i)
+#pragma unroll
+          for (int j = 0; j < S::NBW; ++j) {
+            const R bv = STAGE == 1 ? b1[j][e] : VV::get(bf[j], e);
+            acc[i][j] = MF::mma(VV::get(af[i], e), bv, acc[i][j]);
+          }
+    }
+  };
+
+  if (Klo <= Khi) {
+    const int nsteps = (Khi - Klo) / S::BKT + 1;
+    gload(Klo);
+    sstore(0);
+    __syncthreads();
+    for (int it = 0; it < nsteps; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < nsteps) gload(Klo + (it + 1) * S::BKT);
+      compute(buf);
+      if (it + 1 < nsteps) sstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < S::NBW; ++i)
+#pragma unroll
+    for (int j = 0; j < S::NBW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wr * S::WT + i * 16 + MF::row(lane, r);
+        const int col = wc * S::WT + j * 16 + r16;
+        const int P = P0 + row / T, C = C0 + col / T;
+        if (P >= Mt || C >= Nt) continue;
+        const int64_t off = ((int64_t)P * Nt + C) * T * T + (row % T) * T + (col % T);
+        if (STAGE == 1) {
+          Mb[off] = acc[i][j][r];
+        } else {
+          const int s = P + C;
+          if (s >= mid && s <= l - 1) Wk[off] += acc[i][j][r];
+        }
+      }
+}
+
+// Macro-tile size for a node: wide bands use the big tile (more reuse per
+// LDS byte), narrow bands the small one (more workgroups, less padding).
+template <typename R> struct BandChoice;
+template <> struct BandChoice<float> { static constexpr int BIG = 8, SMALL = 4, QMIN_BIG = 32; };
+template <> struct BandChoice<double> { static constexpr int BIG = 4, SMALL = 2, QMIN_BIG = 32; };
+
+template <typename R, int MB>
+static hipError_t launch_band_mb(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
+                                 const R* LBp, const R* LAp, R* Mb, hipStream_t s) {
+  const int nPb = (g.Mt + MB - 1) / MB;
+  int maxw = 0;
+  for (int pb = 0; pb < nPb; ++pb) {
+    const int P0 = pb * MB;
+    int Clo, Chi;
+    if (stage == 1) {
+      Clo = k - (P0 + MB - 1); if (Clo < 0) Clo = 0;
+      Chi = g.Nt - 1; if (mid - 1 < Chi) Chi = mid - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
+    } else {
+      Clo = mid - (P0 + MB - 1); if (Clo < 0) Clo = 0;
+      Chi = g.Nt - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
+    }
+    if (Clo > Chi) continue;
+    const int w = Chi / MB - Clo / MB + 1;
+    if (w > maxw) maxw = w;
+  }
+  if (maxw == 0) return hipSuccess;
+  if (stage == 1)
+    hipLaunchKernelGGL((band_kernel<R, 1, MB>), dim3(maxw, nPb), dim3(256), 0, s, k, mid, l,
+                       g.Mt, g.Nt, Wk, LBp, LAp, Mb);
+  else
+    hipLaunchKernelGGL((band_kernel<R, 2, MB>), dim3(maxw, nPb), dim3(256), 0, s, k, mid, l,
+                       g.Mt, g.Nt, Wk, LBp, LAp, Mb);
+  return hipGetLastError();
+}
+
+template <typename R>
+hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
+                            const R* LBp, const R* LAp, R* Mb, hipStream_t s) {
+  if (l - k >= BandChoice<R>::QMIN_BIG)
+    return launch_band_mb<R, BandChoice<R>::BIG>(g, k, mid, l, stage, Wk, LBp, LAp, Mb, s);
+  return launch_band_mb<R, BandChoice<R>::SMALL>(g, k, mid, l, stage, Wk, LBp, LAp, Mb, s);
+}
+
+template hipError_t launch_node_band<float>(const SolveGeom&, int, int, int, int, float*,
+                                            const float*, const float*, float*, hipStream_t);
+template hipError_t launch_node_band<double>(const SolveGeom&, int, int, int, int, double*,
+                                             const double*, const double*, double*, hipStream_t);
+
+}  // namespace bk

@@ -32,19 +32,18 @@ struct LeafParams {
   R* Wt;
   int64_t ldwt;
 };
+// Leaf for tile anti-diagonal K whose block of tile anti-diagonals starts at K0.
 template <typename R>
-hipError_t launch_leaf(const SolveGeom& g, int K, R* Wk, const R* LBp, const R* LAp,
+hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
                        const LeafParams<R>& lp, hipStream_t s);
 
-// Internal node of the recursion over tile anti-diagonals [k, l) split at mid.
-template <typename R>
-hipError_t launch_node_small(const SolveGeom& g, int k, int mid, int l, R* Wk, const R* LBp,
-                             const R* LAp, hipStream_t s);
+// Internal node of the recursion over tile anti-diagonals [k, l) split at mid:
+// stage 1 or 2 of the band products.
 template <typename R>
 hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
                             const R* LBp, const R* LAp, R* Mb, hipStream_t s);
-// Largest q = l - k handled by the one-launch small-node kernel.
-constexpr int kSmallNodeMaxQ = 4;
+// Tile anti-diagonals per leaf block (updates inside a block are left-looking).
+constexpr int kLeafBlock = 8;
 
 // ---- factor (factor_kernels.hip), always float64 inside --------------------
 template <typename R>

@@ -6,11 +6,13 @@
 // K = P + Q. Tiles on one tile anti-diagonal never influence each other (an
 // error at (i, j) only reaches (p, q) with p >= i and q >= j, §3.3), so a leaf
 // processes all of them in parallel, each tile running the entry-level
-// anti-diagonal sweep of §3.3 (Algorithm 3 restricted to the tile). An
-// internal node [k, l) split at mid adds, to every tile on tile
-// anti-diagonals [mid, l), the update L^B E L^A^T of the errors E recorded on
-// [k, mid) — the "restricted band products" of Appendix C — as two products:
-// M = L^B E on the band, then W += M L^A^T on the second half.
+// anti-diagonal sweep of §3.3 (Algorithm 3 restricted to the tile). The
+// recursion runs over blocks of G consecutive tile anti-diagonals; inside a
+// block, each leaf first applies the updates from the block's earlier tile
+// anti-diagonals (left-looking), and an internal node [k, l) split at mid
+// (block boundaries) adds to every tile on [mid, l) the update L^B E L^A^T of
+// the errors E recorded on [k, mid) — the "restricted band products" of
+// Appendix C, in band_kernels.hip.
 //
 // Workspace layout (HBM): W as Mt x Nt tiles, tile (P,Q) contiguous and
 // row-major; after a tile is processed its slot holds its errors
@@ -59,284 +61,169 @@ __global__ __launch_bounds__(256) void pack_l_kernel(int64_t dim, const R* __res
 }
 
 // ---------------------------------------------------------------------------
-// Leaf: one tile anti-diagonal K. One workgroup per tile, one thread per entry.
-// Entry (p, q) of the tile is rounded at in-tile step t = p + q; after each
-// step the errors of that in-tile anti-diagonal are added to the tile with
-// the rank-d update of §3.3, L^B[:, i] e_i L^A[:, t-i]^T summed over the
-// step's entries (i, t-i). Rows p of the diagonal factor tiles live in
-// registers; entries with i > p or t-i > q meet exact zeros of the
-// triangular factors, so every thread runs the same unrolled update.
+// Leaf: tile anti-diagonal K, the (K - K0)-th of the block [K0, K0 + G) of
+// tile anti-diagonals. One workgroup per tile (P, Q); T = 16.
+//
+// 1. Prologue (four waves): add the errors of the tiles (I, J) of the same
+//    block on earlier tile anti-diagonals, I <= P, J <= Q, as
+//    sum_J (sum_I L^B[P,I] E[I,J]) L^A[Q,J]^T — the updates between tile
+//    anti-diagonals of one block are done here, left-looking, instead of by
+//    internal nodes (any grouping of the updates gives the same codes,
+//    Appendix B). Each wave takes every fourth J. The inner sum is computed
+//    transposed, M^T = E^T L^B^T, because the MFMA result layout of M^T is
+//    exactly the A-operand layout of the outer product with k = its row
+//    index: no data movement between the two products.
+// 2. Sweep (wave 0): the tile lives in the MFMA accumulator. In-tile step t
+//    rounds the entries (p, t - p) (one per column, §3.3's anti-diagonal
+//    order) and adds L^B e L^A^T for the step's errors e as one 16x16x16
+//    MFMA product: A[p][k] = L^B[p][k] e_k, B[k][q] = L^A[q][t - k]. Entries
+//    already rounded, or with (k, t - k) outside the tile, meet exact zeros
+//    of the triangular factors.
 // ---------------------------------------------------------------------------
-template <typename R, int T>
-__global__ __launch_bounds__(T * T) void leaf_kernel(int K, int Mt, int Nt, int64_t m, int64_t n,
-                                                     R* __restrict__ Wk,
-                                                     const R* __restrict__ LBp,
-                                                     const R* __restrict__ LAp, LeafParams<R> lp) {
-  __shared__ R ebuf[2][T];
-  const int tid = threadIdx.x;
-  const int p = tid / T, q = tid % T;
-  const int P = (K - (Nt - 1) > 0 ? K - (Nt - 1) : 0) + (int)blockIdx.x;
-  const int Q = K - P;
-  R* tileW = Wk + ((int64_t)P * Nt + Q) * T * T;
-  const R* tB = LBp + tri_index(P, P) * T * T + p * T;  // row p of L^B[P,P]
-  const R* tA = LAp + tri_index(Q, Q) * T * T + q * T;  // row q of L^A[Q,Q]
-
-  R lb[T], la[T];
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    lb[i] = tB[i];
-    la[i] = tA[i];
+template <typename R> struct EVec;
+template <> struct EVec<float> {
+  __device__ static inline void load4(const float* p, float* out) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
   }
-  R x = tileW[p * T + q];
-  const int64_t gi = (int64_t)P * T + p, gj = (int64_t)Q * T + q;
-  const bool valid = gi < m && gj < n;
-  R s = R(1);
-  if (lp.scale_mode == 1) s = gi < m ? lp.scales[gi] : R(1);
-  else if (lp.scale_mode == 2) s = gj < n ? lp.scales[gj] : R(1);
-  const bool unb = lp.unbounded != 0;
-
-  R code = R(0), xt = R(0), eout = R(0);
-#pragma unroll
-  for (int t = 0; t < 2 * T - 1; ++t) {
-    if (p + q == t) {
-      const R c = quant_code(x, s, lp.lo, lp.hi, unb);
-      const R e = valid ? s * c - x : R(0);
-      code = c;
-      xt = x;
-      eout = e;
-      ebuf[t & 1][p] = e;
-    }
-    __syncthreads();
-    const int ilo = t - (T - 1) > 0 ? t - (T - 1) : 0;
-    const int ihi = t < T - 1 ? t : T - 1;
-    R acc0 = R(0), acc1 = R(0);
-#pragma unroll
-    for (int i = ilo; i <= ihi; ++i) {
-      const R g = lb[i] * ebuf[t & 1][i];
-      if ((i - ilo) & 1) acc1 = __builtin_fma(g, la[t - i], acc1);
-      else acc0 = __builtin_fma(g, la[t - i], acc0);
-    }
-    x += acc0 + acc1;
+};
+template <> struct EVec<double> {
+  __device__ static inline void load4(const double* p, double* out) {
+    const double2 v0 = reinterpret_cast<const double2*>(p)[0];
+    const double2 v1 = reinterpret_cast<const double2*>(p)[1];
+    out[0] = v0.x; out[1] = v0.y; out[2] = v1.x; out[3] = v1.y;
   }
-  tileW[p * T + q] = eout;
-  if (valid) {
-    lp.V[gi * lp.ldv + gj] = (int32_t)code;
-    if (lp.Wt) lp.Wt[gi * lp.ldwt + gj] = xt;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Small internal node (q = l - k <= kSmallNodeMaxQ): one wave per target tile
-// (P, Q) on tile anti-diagonals [mid, l), computing
-//   sum_J (sum_I L^B[P,I] E[I,J]) L^A[Q,J]^T
-// over source tiles (I, J) on [k, mid) with I <= P, J <= Q, in one launch.
-// T must be 16: a tile is one 16x16 MFMA block.
-// ---------------------------------------------------------------------------
-struct SmallNodeDiags {
-  int count;        // number of target tile anti-diagonals (l - mid)
-  int first[9];     // first[d] = linear index of the first tile of diagonal mid + d
 };
 
+__device__ inline void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <typename R>
-__global__ __launch_bounds__(64) void node_small_kernel(int k, int mid, int l, int Mt, int Nt,
-                                                        R* __restrict__ Wk,
-                                                        const R* __restrict__ LBp,
-                                                        const R* __restrict__ LAp,
-                                                        SmallNodeDiags dg) {
+__global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt, int64_t m,
+                                                   int64_t n, R* __restrict__ Wk,
+                                                   const R* __restrict__ LBp,
+                                                   const R* __restrict__ LAp, LeafParams<R> lp) {
   constexpr int T = 16;
   typedef Mfma<R> MF;
   typedef typename MF::acc_t acc_t;
-  __shared__ R ms[T][T + 2];
-  const int lane = threadIdx.x;
-  const int idx = blockIdx.x;
-  int d = 0;
-  while (d + 1 < dg.count && idx >= dg.first[d + 1]) ++d;
-  const int Kt = mid + d;
-  const int Plo = Kt - (Nt - 1) > 0 ? Kt - (Nt - 1) : 0;
-  const int P = Plo + (idx - dg.first[d]);
-  const int Q = Kt - P;
-  const int r16 = lane & 15, kg = lane >> 4;
-
-  acc_t acc = MF::zero();
-  const int Jlo = k - P > 0 ? k - P : 0;
-  const int Jhi = Q < mid - 1 ? Q : mid - 1;
-  for (int J = Jlo; J <= Jhi; ++J) {
-    const int Ilo = k - J > 0 ? k - J : 0;
-    const int Ihi = P < mid - 1 - J ? P : mid - 1 - J;
-    if (Ilo > Ihi) continue;
-    acc_t macc = MF::zero();
-    for (int I = Ilo; I <= Ihi; ++I) {
-      const R* a = LBp + tri_index(P, I) * T * T;   // [r][k]
-      const R* b = Wk + ((int64_t)I * Nt + J) * T * T;  // E[I,J] [k][c]
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kk = 4 * kg + st;
-        macc = MF::mma(a[r16 * T + kk], b[kk * T + r16], macc);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ms[MF::row(lane, r)][r16] = macc[r];
-    __syncthreads();
-    const R* la = LAp + tri_index(Q, J) * T * T;  // B[k][c] = L^A[Q,J][c][k]
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kk = 4 * kg + st;
-      acc = MF::mma(ms[r16][kk], la[r16 * T + kk], acc);
-    }
-  }
-  R* w = Wk + ((int64_t)P * Nt + Q) * T * T;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = MF::row(lane, r);
-    w[row * T + r16] += acc[r];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Large internal node: the two restricted band products as MFMA GEMMs over
-// macro tiles of MB x MB solver tiles (MB*T elements square), 4 waves in a
-// 2 x 2 arrangement, K stepped one solver tile at a time through
-// double-buffered LDS. Masks are per solver tile.
-//   stage 1: M[P,J]  = sum_I L^B[P,I] E[I,J],   I <= P, k <= I+J < mid
-//   stage 2: W[P,Q] += sum_J M[P,J] L^A[Q,J]^T, J <= Q, J < mid,
-//            k <= P+J <= l-1, written only where mid <= P+Q <= l-1.
-// ---------------------------------------------------------------------------
-template <typename R> struct BandCfg;
-template <> struct BandCfg<float> { static constexpr int MB = 8; static constexpr int PAD = 4; };
-template <> struct BandCfg<double> { static constexpr int MB = 4; static constexpr int PAD = 2; };
-
-template <typename R, int STAGE>
-__global__ __launch_bounds__(256) void band_kernel(int k, int mid, int l, int Mt, int Nt,
-                                                   R* __restrict__ Wk, const R* __restrict__ LBp,
-                                                   const R* __restrict__ LAp, R* __restrict__ Mb) {
-  constexpr int T = kTile;
-  constexpr int MB = BandCfg<R>::MB;
-  constexpr int BM = MB * T;       // macro tile edge in elements
-  constexpr int LDS_LD = T + BandCfg<R>::PAD;
-  constexpr int WT = BM / 2;       // wave tile edge
-  constexpr int NBW = WT / 16;     // 16x16 blocks per wave edge
-  constexpr int PER = MB * T * T / 256;  // elements per thread per operand per K step
-  typedef Mfma<R> MF;
-  typedef typename MF::acc_t acc_t;
-
-  __shared__ R As[2][BM][LDS_LD];
-  __shared__ R Bs[2][BM][LDS_LD];
+  __shared__ R red[3][T][T + 1];
+  __shared__ R lat[T][T + 1];
+  __shared__ __attribute__((aligned(16))) R ebuf[T];
+  __shared__ R oc[T][T + 1], ow[T][T + 1], oe[T][T + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int r16 = lane & 15, kg = lane >> 4;
+  const int c = lane & 15, kg = lane >> 4;
+  const int P = (K - (Nt - 1) > 0 ? K - (Nt - 1) : 0) + (int)blockIdx.x;
+  const int Q = K - P;
 
-  const int pb = blockIdx.y;
-  const int P0 = pb * MB;
-  // column-block range of this macro row
-  int Clo, Chi;
-  if (STAGE == 1) {
-    Clo = k - (P0 + MB - 1); if (Clo < 0) Clo = 0;
-    Chi = Nt - 1; if (mid - 1 < Chi) Chi = mid - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
-  } else {
-    Clo = mid - (P0 + MB - 1); if (Clo < 0) Clo = 0;
-    Chi = Nt - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
-  }
-  if (Clo > Chi) return;
-  const int cb = Clo / MB + (int)blockIdx.x;
-  if (cb > Chi / MB) return;
-  const int C0 = cb * MB;
-
-  int Klo, Khi;
-  if (STAGE == 1) {
-    Klo = k - (C0 + MB - 1); if (Klo < 0) Klo = 0;
-    Khi = P0 + MB - 1; if (mid - 1 - C0 < Khi) Khi = mid - 1 - C0; if (Mt - 1 < Khi) Khi = Mt - 1;
-  } else {
-    Klo = k - (P0 + MB - 1); if (Klo < 0) Klo = 0;
-    Khi = C0 + MB - 1; if (mid - 1 < Khi) Khi = mid - 1; if (Nt - 1 < Khi) Khi = Nt - 1;
-  }
-
-  acc_t acc[NBW][NBW];
+  // ---- 1. prologue
+  acc_t acc = MF::zero();
+  if (K > K0) {
+    const int Jlo = K0 - P > 0 ? K0 - P : 0;
+    for (int J = Jlo + wave; J <= Q; J += 4) {
+      const int Ilo = K0 - J > 0 ? K0 - J : 0;
+      const int Ihi = P < K - 1 - J ? P : K - 1 - J;
+      if (Ilo > Ihi) continue;
+      acc_t mt = MF::zero();  // lane holds M^T[row(lane, r)][c] = M[c][row(lane, r)]
+      for (int I = Ilo; I <= Ihi; ++I) {
+        const R* E = Wk + ((int64_t)I * Nt + J) * T * T;
+        const R* Lb = LBp + tri_index(P, I) * T * T;
+        R lb4[4];
+        EVec<R>::load4(Lb + c * T + 4 * kg, lb4);
 #pragma unroll
-  for (int i = 0; i < NBW; ++i)
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) acc[i][j] = MF::zero();
-
-  R ra[PER], rb[PER];
-  auto gload = [&](int kk) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = u * 256 + tid;
-      const int t = e / (T * T);          // which tile of the macro row / column
-      const int w = e % (T * T);
-      const int P = P0 + t, C = C0 + t;
-      R va = R(0), vb = R(0);
-      if (STAGE == 1) {
-        if (P < Mt && kk <= P) va = LBp[tri_index(P, kk) * T * T + w];
-        const int s = kk + C;
-        if (C < Nt && s >= k && s < mid) vb = Wk[((int64_t)kk * Nt + C) * T * T + w];
-      } else {
-        const int s = P + kk;
-        if (P < Mt && kk <= mid - 1 && s >= k && s <= l - 1) va = Mb[((int64_t)P * Nt + kk) * T * T + w];
-        if (C < Nt && kk <= C) vb = LAp[tri_index(C, kk) * T * T + w];
+        for (int s = 0; s < 4; ++s) mt = MF::mma(E[(4 * kg + s) * T + c], lb4[s], mt);
       }
-      ra[u] = va;
-      rb[u] = vb;
-    }
-  };
-  auto sstore = [&](int buf) {
+      const R* La = LAp + tri_index(Q, J) * T * T;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = u * 256 + tid;
-      const int t = e / (T * T);
-      const int w = e % (T * T);
-      const int r = w / T, c = w % T;
-      As[buf][t * T + r][c] = ra[u];               // A[row][k]
-      if (STAGE == 1) Bs[buf][t * T + c][r] = rb[u];  // E[k=r][col=c] -> Bs[col][k]
-      else Bs[buf][t * T + r][c] = rb[u];           // L^A[col=r][k=c] -> Bs[col][k]
-    }
-  };
-
-  if (Klo <= Khi) {
-    gload(Klo);
-    sstore(0);
-    __syncthreads();
-    for (int kk = Klo; kk <= Khi; ++kk) {
-      const int buf = (kk - Klo) & 1;
-      if (kk < Khi) gload(kk + 1);
-#pragma unroll
-      for (int st = 0; st < T / 4; ++st) {
-        R af[NBW], bf[NBW];
-#pragma unroll
-        for (int i = 0; i < NBW; ++i) af[i] = As[buf][wr * WT + i * 16 + r16][4 * kg + st];
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) bf[j] = Bs[buf][wc * WT + j * 16 + r16][4 * kg + st];
-#pragma unroll
-        for (int i = 0; i < NBW; ++i)
-#pragma unroll
-          for (int j = 0; j < NBW; ++j) acc[i][j] = MF::mma(af[i], bf[j], acc[i][j]);
-      }
-      if (kk < Khi) sstore(buf ^ 1);
-      __syncthreads();
+      for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], La[c * T + MF::row(lane, s)], acc);
     }
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave - 1][MF::row(lane, r)][c] = acc[r];
+  }
+  {
+    const R* tA = LAp + tri_index(Q, Q) * T * T;
+    lat[tid >> 4][tid & 15] = tA[tid];
+  }
+  if (tid < T) ebuf[tid] = R(0);
+  __syncthreads();
+  if (wave > 0) return;
 
-  // epilogue
+  // ---- 2. sweep on wave 0
+  R* tW = Wk + ((int64_t)P * Nt + Q) * T * T;
+  const int64_t gj = (int64_t)Q * T + c;
+  const bool unb = lp.unbounded != 0;
+  int dr[4];
+  R sr[4];
+  bool vr[4];
 #pragma unroll
-  for (int i = 0; i < NBW; ++i)
+  for (int r = 0; r < 4; ++r) {
+    const int row = MF::row(lane, r);
+    acc[r] += tW[row * T + c] + red[0][row][c] + red[1][row][c] + red[2][row][c];
+    const int64_t gi = (int64_t)P * T + row;
+    dr[r] = row + c;
+    vr[r] = gi < m && gj < n;
+    R sv = R(1);
+    if (lp.scale_mode == 1) sv = gi < m ? lp.scales[gi] : R(1);
+    else if (lp.scale_mode == 2) sv = gj < n ? lp.scales[gj] : R(1);
+    sr[r] = sv;
+  }
+  R lbK[4];
+  EVec<R>::load4(LBp + tri_index(P, P) * T * T + c * T + 4 * kg, lbK);
+  R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - 4 kg]
 #pragma unroll
-    for (int j = 0; j < NBW; ++j)
+  for (int j = 0; j < 2 * T - 1; ++j) {
+    const int jj = j - 4 * kg;
+    laK[j] = (jj >= 0 && jj < T) ? lat[c][jj] : R(0);
+  }
+
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wr * WT + i * 16 + MF::row(lane, r);
-        const int col = wc * WT + j * 16 + r16;
-        const int P = P0 + row / T, C = C0 + col / T;
-        if (P >= Mt || C >= Nt) continue;
-        const int64_t off = ((int64_t)P * Nt + C) * T * T + (row % T) * T + (col % T);
-        if (STAGE == 1) {
-          Mb[off] = acc[i][j][r];
-        } else {
-          const int s = P + C;
-          if (s >= mid && s <= l - 1) Wk[off] += acc[i][j][r];
-        }
-      }
+  for (int t = 0; t < 2 * T - 1; ++t) {
+    R x = R(0), sa = R(1);
+    bool act = false, va = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool on = dr[r] == t;
+      x = on ? acc[r] : x;
+      sa = on ? sr[r] : sa;
+      va = on ? vr[r] : va;
+      act = act || on;
+    }
+    const R cq = quant_code(x, sa, lp.lo, lp.hi, unb);
+    const R e = (act && va) ? sa * cq - x : R(0);
+    if (act) {
+      const int p = t - c;
+      ebuf[p] = e;
+      oc[p][c] = cq;
+      ow[p][c] = x;
+      oe[p][c] = e;
+    }
+    wave_sync_lds();
+    R ev[4];
+    EVec<R>::load4(ebuf + 4 * kg, ev);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const R b = (t - s >= 0) ? laK[t - s] : R(0);
+      acc = MF::mma(lbK[s] * ev[s], b, acc);
+    }
+  }
+  wave_sync_lds();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = lane + 64 * u;
+    const int p = idx >> 4, q = idx & 15;
+    const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + q;
+    tW[idx] = oe[p][q];
+    if (gi < m && gjj < n) {
+      lp.V[gi * lp.ldv + gjj] = (int32_t)oc[p][q];
+      if (lp.Wt) lp.Wt[gi * lp.ldwt + gjj] = ow[p][q];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -366,76 +253,22 @@ static inline void diag_range(const SolveGeom& g, int K, int* lo, int* hi) {
 }
 
 template <typename R>
-hipError_t launch_leaf(const SolveGeom& g, int K, R* Wk, const R* LBp, const R* LAp,
+hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
                        const LeafParams<R>& lp, hipStream_t s) {
+  static_assert(kTile == 16, "the leaf kernel works on 16 x 16 tiles");
   int lo, hi;
   diag_range(g, K, &lo, &hi);
   if (hi < lo) return hipSuccess;
-  hipLaunchKernelGGL((leaf_kernel<R, kTile>), dim3(hi - lo + 1), dim3(kTile * kTile), 0, s, K,
-                     g.Mt, g.Nt, g.m, g.n, Wk, LBp, LAp, lp);
-  return hipGetLastError();
-}
-
-template <typename R>
-hipError_t launch_node_small(const SolveGeom& g, int k, int mid, int l, R* Wk, const R* LBp,
-                             const R* LAp, hipStream_t s) {
-  static_assert(kTile == 16, "small-node kernel assumes 16x16 tiles");
-  SmallNodeDiags dg;
-  dg.count = l - mid;
-  if (dg.count > 8 || dg.count < 1) return hipErrorInvalidValue;
-  int total = 0;
-  for (int d = 0; d < dg.count; ++d) {
-    dg.first[d] = total;
-    int lo, hi;
-    diag_range(g, mid + d, &lo, &hi);
-    total += hi >= lo ? hi - lo + 1 : 0;
-  }
-  for (int d = dg.count; d < 9; ++d) dg.first[d] = total;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((node_small_kernel<R>), dim3(total), dim3(64), 0, s, k, mid, l, g.Mt, g.Nt,
-                     Wk, LBp, LAp, dg);
-  return hipGetLastError();
-}
-
-template <typename R>
-hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
-                            const R* LBp, const R* LAp, R* Mb, hipStream_t s) {
-  constexpr int MB = BandCfg<R>::MB;
-  const int nPb = (g.Mt + MB - 1) / MB;
-  int maxw = 0;
-  for (int pb = 0; pb < nPb; ++pb) {
-    const int P0 = pb * MB;
-    int Clo, Chi;
-    if (stage == 1) {
-      Clo = k - (P0 + MB - 1); if (Clo < 0) Clo = 0;
-      Chi = g.Nt - 1; if (mid - 1 < Chi) Chi = mid - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
-    } else {
-      Clo = mid - (P0 + MB - 1); if (Clo < 0) Clo = 0;
-      Chi = g.Nt - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
-    }
-    if (Clo > Chi) continue;
-    const int w = Chi / MB - Clo / MB + 1;
-    if (w > maxw) maxw = w;
-  }
-  if (maxw == 0) return hipSuccess;
-  if (stage == 1)
-    hipLaunchKernelGGL((band_kernel<R, 1>), dim3(maxw, nPb), dim3(256), 0, s, k, mid, l, g.Mt,
-                       g.Nt, Wk, LBp, LAp, Mb);
-  else
-    hipLaunchKernelGGL((band_kernel<R, 2>), dim3(maxw, nPb), dim3(256), 0, s, k, mid, l, g.Mt,
-                       g.Nt, Wk, LBp, LAp, Mb);
+  hipLaunchKernelGGL((leaf_kernel<R>), dim3(hi - lo + 1), dim3(256), 0, s, K, K0, g.Mt, g.Nt,
+                     g.m, g.n, Wk, LBp, LAp, lp);
   return hipGetLastError();
 }
 
 #define BK_INST(R)                                                                              \
   template hipError_t launch_pack_w<R>(const SolveGeom&, const R*, int64_t, R*, hipStream_t);  \
   template hipError_t launch_pack_l<R>(int64_t, int, const R*, int64_t, R*, hipStream_t);      \
-  template hipError_t launch_leaf<R>(const SolveGeom&, int, R*, const R*, const R*,             \
-                                     const LeafParams<R>&, hipStream_t);                        \
-  template hipError_t launch_node_small<R>(const SolveGeom&, int, int, int, R*, const R*,       \
-                                           const R*, hipStream_t);                              \
-  template hipError_t launch_node_band<R>(const SolveGeom&, int, int, int, int, R*, const R*,   \
-                                          const R*, R*, hipStream_t);
+  template hipError_t launch_leaf<R>(const SolveGeom&, int, int, R*, const R*, const R*,        \
+                                     const LeafParams<R>&, hipStream_t);
 BK_INST(float)
 BK_INST(double)
 #undef BK_INST

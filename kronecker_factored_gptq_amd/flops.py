@@ -77,13 +77,17 @@ def node_useful_flops(m: int, n: int, T: int, k: int, mid: int, l: int) -> Tuple
 
 def schedule_flops(m: int, n: int, T: int, ops: Iterable[Tuple[int, int, int, int]]
                    ) -> Dict[str, int]:
-    """Useful flops of every internal node of a solve schedule, grouped by
-    how it runs: kind 1 (one-launch small node) and kinds 2+3 (the two band
-    products of a large node). Returns totals and per-op values."""
+    """Useful flops of the updates between tiles in a solve schedule: kinds
+    2 and 3 are the two band products of an internal node; a leaf (kind 0)
+    of tile anti-diagonal K in a block starting at K0 applies the updates
+    from [K0, K) to K, counted as the node [K0, K) -> [K, K+1) ("small").
+    Returns totals and per-op values."""
     out = {"small": 0, "band": 0, "band_stage1": 0, "band_stage2": 0, "per_op": []}
     for (kind, k, mid, l) in ops:
         if kind == 0:
-            out["per_op"].append(0)
+            f = sum(node_useful_flops(m, n, T, mid, k, k + 1)) if k > mid else 0
+            out["small"] += f
+            out["per_op"].append(f)
             continue
         f1, f2 = node_useful_flops(m, n, T, k, mid, l)
         if kind == 1:

@@ -89,11 +89,13 @@ class Fp32Report:
     n: int = 0
 
     def cascade_loss_bound(self) -> float:
-        """Loss spread expected between two valid solutions that differ on k
-        entries: each differing entry moves its own share of the loss by about
-        the mean share, loss/(mn), in either direction, so the relative
-        difference is ~sqrt(k)/(mn); allow 4 sigma, never below 1e-4."""
-        return max(1e-4, 4.0 * np.sqrt(self.mismatches) / max(self.m * self.n, 1))
+        """Loss spread between two valid solutions that took different
+        near-tie branches. Measured with the float64 oracle alone on the
+        4096x4096 workload: perturbing W by one float32 ulp flips a near-tie
+        (gap 2.9e-8 code units) and moves the oracle's own loss by 1.1e-3 and
+        1.7e-3 (agreement 82.5%); round-to-nearest is 72% worse. Allow 3x the
+        larger measured spread, 5e-3, once branches differ; 1e-4 otherwise."""
+        return 5e-3 if self.mismatches else 1e-4
 
 
 def fp32_parity(inp: Inputs, V_gpu: np.ndarray, Wt_gpu: np.ndarray, ref: O.Result, A, B) -> Fp32Report:

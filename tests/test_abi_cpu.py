@@ -101,30 +101,35 @@ def _closed_form_leaves(m, n, T=16):
     return -(-m // T) + -(-n // T) - 1
 
 
-@pytest.mark.parametrize("m,n", [(1, 1), (16, 16), (17, 5), (64, 64), (512, 512), (4096, 4096),
-                                 (14336, 4096), (4096, 14336), (1024, 2048)])
-def test_schedule_is_algorithm_6_over_tile_antidiagonals(m, n):
-    """Table 1 "Steps" for BaKron: one leaf per (tile) anti-diagonal, and every
-    internal node splits [k, l) at floor((k+l)/2). Check the schedule against
-    the closed form: leaves Mt+Nt-1 in increasing order, nodes = leaves - 1,
-    each pair of adjacent diagonals separated by exactly the node whose
-    midpoint lies between them."""
+BLOCK = 8
+
+
+@pytest.mark.parametrize("m,n", [(1, 1), (16, 16), (17, 5), (64, 64), (200, 300), (512, 512),
+                                 (4096, 4096), (14336, 4096), (4096, 14336), (1024, 2048)])
+def test_schedule_is_algorithm_6_over_blocks_of_tile_antidiagonals(m, n):
+    """Table 1 "Steps" for BaKron: one leaf per (tile) anti-diagonal, in
+    order; Algorithm 6's recursion over blocks of 8 tile anti-diagonals, each
+    internal node splitting block range [kb, lb) at floor((kb+lb)/2) and
+    running after the last leaf left of its midpoint and before the first
+    leaf right of it; inside a block, each leaf names its block start."""
     ops = bk.solve_schedule(bk.F32, m, n)
     R = _closed_form_leaves(m, n)
-    leaves = [k for (kind, k, mid, l) in ops if kind == 0]
-    assert leaves == list(range(R))
-    nodes = [(k, mid, l) for (kind, k, mid, l) in ops if kind in (1, 2)]
-    assert len(nodes) == R - 1
-    assert sorted(mid for (_, mid, _) in nodes) == list(range(1, R))
+    nblocks = -(-R // BLOCK)
+    leaves = [(a, b) for (kind, a, b, c) in ops if kind == 0]
+    assert [a for a, _ in leaves] == list(range(R))
+    assert all(b == (a // BLOCK) * BLOCK for a, b in leaves)
+    nodes = [(a, b, c) for (kind, a, b, c) in ops if kind == 2]
+    assert len(nodes) == nblocks - 1
+    assert sorted(mid for (_, mid, _) in nodes) == [BLOCK * i for i in range(1, nblocks)]
     for (k, mid, l) in nodes:
-        assert mid == (k + l) // 2 and k < mid < l
-    # band products come in stage pairs
+        kb, lb = k // BLOCK, -(-l // BLOCK)
+        assert k % BLOCK == 0 and mid == BLOCK * ((kb + lb) // 2) and k < mid < l <= R
     kinds = [op[0] for op in ops]
+    assert set(kinds) <= {0, 2, 3}
     for i, kd in enumerate(kinds):
         if kd == 2:
             assert kinds[i + 1] == 3 and ops[i][1:] == ops[i + 1][1:]
-    # the node for [k,l) runs after leaf mid-1 and before leaf mid
-    pos = {("leaf", k): i for i, (kind, k, _, _) in enumerate(ops) if kind == 0}
+    pos = {a: i for i, (kind, a, _, _) in enumerate(ops) if kind == 0}
     for i, (kind, k, mid, l) in enumerate(ops):
-        if kind in (1, 2):
-            assert pos[("leaf", mid - 1)] < i < pos[("leaf", mid)]
+        if kind in (2, 3):
+            assert pos[mid - 1] < i < pos[mid]

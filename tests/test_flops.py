@@ -53,4 +53,4 @@ def test_total_matches_survey_scale_at_4096():
     f = schedule_flops(4096, 4096, 16, ops)
     total = f["small"] + f["band"]
     assert 1.6 * 4096 ** 3 * 2 < total < 1.8 * 4096 ** 3 * 2
-    assert f["band"] > 0.97 * total
+    assert f["band"] > 0.95 * total
