@@ -159,29 +159,32 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
 }
 
 // ---- factor ---------------------------------------------------------------
+// Per side of order D: X (D^2), Y (D^2), Tmp ((D/2 + 64)^2) doubles; one info
+// word per side. When m == n both sides run in the same launches.
+size_t side_bytes(int64_t D) {
+  const int64_t h = D / 2 + 64;
+  return 2 * align_up((size_t)(D * D) * 8) + align_up((size_t)(h * h) * 8);
+}
+
 struct FactorLayout {
-  size_t x, dinv, tmp, info, total;
+  size_t a, b, info, total;
 };
 FactorLayout factor_layout(int64_t m, int64_t n) {
-  const int64_t D = m > n ? m : n;
-  const int64_t nb = (D + 63) / 64 * 64;
   FactorLayout L;
-  L.x = align_up((size_t)(D * D) * 8);
-  L.dinv = align_up((size_t)(nb * 64) * 8);
-  L.tmp = align_up((size_t)(D > 0 ? D : 1) * 64 * 8);
+  L.a = side_bytes(n);
+  L.b = side_bytes(m);
   L.info = align_up(2 * sizeof(int32_t));
-  L.total = L.x + L.dinv + L.tmp + L.info + kAlign;
+  L.total = L.a + L.b + L.info + kAlign;
   return L;
 }
 
-template <typename R>
-int factor_side(int64_t dim, const R* A, int64_t lda, R* L, int64_t ldl, R* d, double* X,
-                double* Dinv, double* Tmp, int32_t* info, hipStream_t s) {
-  if (dim == 0) return BAKRON_OK;
-  if (launch_load_reversed<R>(dim, A, lda, X, s) != hipSuccess) return BAKRON_EHIP;
-  if (factor_cholesky_inverse(dim, X, Dinv, Tmp, info, s) != hipSuccess) return BAKRON_EHIP;
-  if (launch_store_normalized<R>(dim, X, L, ldl, d, s) != hipSuccess) return BAKRON_EHIP;
-  return BAKRON_OK;
+FactorSide carve_side(char* base, int64_t D, int32_t* info) {
+  FactorSide f;
+  f.X = reinterpret_cast<double*>(base);
+  f.Y = reinterpret_cast<double*>(base + align_up((size_t)(D * D) * 8));
+  f.Tmp = reinterpret_cast<double*>(base + 2 * align_up((size_t)(D * D) * 8));
+  f.info = info;
+  return f;
 }
 
 template <typename R>
@@ -190,15 +193,21 @@ int factor_impl(int64_t m, int64_t n, const R* A, int64_t lda, const R* B, int64
                 hipStream_t s) {
   const FactorLayout lay = factor_layout(m, n);
   char* base = static_cast<char*>(ws);
-  double* X = reinterpret_cast<double*>(base);
-  double* Dinv = reinterpret_cast<double*>(base + lay.x);
-  double* Tmp = reinterpret_cast<double*>(base + lay.x + lay.dinv);
-  int32_t* info = reinterpret_cast<int32_t*>(base + lay.x + lay.dinv + lay.tmp);
+  int32_t* info = reinterpret_cast<int32_t*>(base + lay.a + lay.b);
+  const FactorSide sa = carve_side(base, n, info + 0);
+  const FactorSide sb = carve_side(base + lay.a, m, info + 1);
   if (launch_fill_i32(info, 2, INT_MAX, s) != hipSuccess) return BAKRON_EHIP;
-  int rc = factor_side<R>(n, A, lda, LA, ldla, dA, X, Dinv, Tmp, info + 0, s);
-  if (rc != BAKRON_OK) return rc;
-  rc = factor_side<R>(m, B, ldb, LB, ldlb, dB, X, Dinv, Tmp, info + 1, s);
-  if (rc != BAKRON_OK) return rc;
+  if (n > 0 && launch_load_reversed<R>(n, A, lda, sa.X, s) != hipSuccess) return BAKRON_EHIP;
+  if (m > 0 && launch_load_reversed<R>(m, B, ldb, sb.X, s) != hipSuccess) return BAKRON_EHIP;
+  if (m == n) {
+    const FactorSide both[2] = {sa, sb};
+    if (factor_cholesky_inverse(n, both, 2, s) != hipSuccess) return BAKRON_EHIP;
+  } else {
+    if (factor_cholesky_inverse(n, &sa, 1, s) != hipSuccess) return BAKRON_EHIP;
+    if (factor_cholesky_inverse(m, &sb, 1, s) != hipSuccess) return BAKRON_EHIP;
+  }
+  if (n > 0 && launch_store_normalized<R>(n, sa.Y, LA, ldla, dA, s) != hipSuccess) return BAKRON_EHIP;
+  if (m > 0 && launch_store_normalized<R>(m, sb.Y, LB, ldlb, dB, s) != hipSuccess) return BAKRON_EHIP;
   int32_t hinfo[2] = {INT_MAX, INT_MAX};
   if (hipMemcpyAsync(hinfo, info, sizeof(hinfo), hipMemcpyDeviceToHost, s) != hipSuccess)
     return BAKRON_EHIP;
@@ -252,18 +261,18 @@ int loss_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V, i
   if (launch_residual_f64<R>(m, n, W, ldw, V, ldv, scale_mode, scales, D, s) != hipSuccess)
     return BAKRON_EHIP;
   Gemm64Args g1{};
-  g1.M = m; g1.N = n; g1.K = m;
-  g1.A = B64; g1.lda = m;
-  g1.B = D; g1.ldb = n; g1.transB = 0;
-  g1.C = BE; g1.ldc = n;
+  g1.M = m; g1.N = n; g1.K = m; g1.batch = 1;
+  g1.A[0] = B64; g1.lda = m;
+  g1.B[0] = D; g1.ldb = n; g1.transB = 0;
+  g1.C[0] = BE; g1.ldc = n;
   g1.alpha = 1.0; g1.beta = 0.0;
   if (launch_gemm64(g1, s) != hipSuccess) return BAKRON_EHIP;
   Gemm64Args g2{};
-  g2.M = m; g2.N = n; g2.K = n;
-  g2.A = D; g2.lda = n;
-  g2.B = A64; g2.ldb = n; g2.transB = 0;
+  g2.M = m; g2.N = n; g2.K = n; g2.batch = 1;
+  g2.A[0] = D; g2.lda = n;
+  g2.B[0] = A64; g2.ldb = n; g2.transB = 0;
   g2.alpha = 1.0;
-  g2.dot = BE; g2.lddot = n; g2.partial = part;
+  g2.dot[0] = BE; g2.lddot = n; g2.partial[0] = part;
   if (launch_gemm64(g2, s) != hipSuccess) return BAKRON_EHIP;
   if (launch_sum_partials(part, lay.nparts, loss, s) != hipSuccess) return BAKRON_EHIP;
   return BAKRON_OK;

@@ -7,13 +7,15 @@
 // reversal permutation and C = Cholesky(J A J), A = (J C J)(J C J)^T, so
 // A^-1 = (J C^-T J)(J C^-T J)^T and J C^-T J is lower triangular with a
 // positive diagonal, i.e. it IS Cholesky(A^-1). Steps:
-//   X = J A J (lower triangle)      load_reversed_kernel
-//   X = Cholesky(X) in place        blocked, right-looking, 64-wide panels:
-//                                   diag block in LDS (+ its inverse),
-//                                   panel = A21 * inv(L11)^T, trailing
-//                                   rank-64 update on MFMA (gemm64)
-//   X = X^-1 in place               blocked from the bottom block up:
-//                                   X21 = -X22^-1 X21 inv(X11) (gemm64)
+//   X = J A J (lower triangle)        load_reversed_kernel
+//   Y = Cholesky(X)^-1                recursive: for X = [X11 .; X21 X22],
+//       (Y11 from X11)                  C11 and Y11 = C11^-1 recursively,
+//       C21 = X21 Y11^T                 the panel of the Cholesky factor,
+//       X22 -= C21 C21^T                the Schur complement,
+//       (Y22 from X22)                  recursively,
+//       Y21 = -Y22 (C21 Y11)            the off-diagonal block of the inverse;
+//                                     64 x 64 leaves in LDS, everything else
+//                                     float64 MFMA GEMMs (gemm64)
 //   L[i][j] = Y[n-1-j][n-1-i], normalised by its diagonal  store_normalized
 #include <climits>
 
@@ -51,73 +53,51 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* 
   }
 }
 
-// Cholesky of the bs x bs diagonal block at (kb, kb) in LDS, plus its
-// lower-triangular inverse. A pivot that is not positive and finite records
-// kb + j in *info (smallest wins) and the factorisation continues with NaN.
-__global__ __launch_bounds__(256) void potrf_diag_kernel(int64_t n, int64_t kb, int bs,
-                                                         double* __restrict__ X,
-                                                         double* __restrict__ Dinv,
-                                                         int32_t* __restrict__ info) {
-  __shared__ double L[NB][NB + 1];
-  __shared__ double Y[NB][NB + 1];
+// Leaf of the recursion: the Cholesky factor C of the bs x bs diagonal block
+// X[off.., off..] (bs <= 64) and its inverse, in LDS; Y[off.., off..]
+// receives C^-1 (zeros above the diagonal). Right-looking, two barriers per
+// column: phase A scales column j of C and row j of the inverse by C[j][j],
+// phase B updates the trailing block and the rows of the inverse below j. A
+// pivot that is not positive and finite records off + j in *info (smallest
+// wins) and the factorisation continues with NaN. blockIdx.x selects the side.
+__global__ __launch_bounds__(256) void chol_inv_leaf_kernel(FactorSide s0, FactorSide s1,
+                                                            int64_t n, int64_t off, int bs) {
+  constexpr int NBL = 64;
+  __shared__ double L[NBL][NBL + 1];
+  __shared__ double Y[NBL][NBL + 1];
+  const FactorSide S = blockIdx.x == 0 ? s0 : s1;
   const int tid = threadIdx.x;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    double v = 0.0;
-    if (r < bs && c <= r) v = X[(kb + r) * n + kb + c];
-    L[r][c] = v;
-    Y[r][c] = 0.0;
+  for (int e = tid; e < NBL * NBL; e += 256) {
+    const int r = e / NBL, c = e % NBL;
+    L[r][c] = (r < bs && c <= r) ? S.X[(off + r) * n + off + c] : 0.0;
+    Y[r][c] = r == c ? 1.0 : 0.0;
   }
   __syncthreads();
   for (int j = 0; j < bs; ++j) {
-    if (tid == 0) {
-      const double piv = L[j][j];
-      if (!(piv > 0.0) || !(piv < INFINITY)) {
-        atomicMin(info, (int32_t)(kb + j));
-        L[j][j] = __builtin_nan("");
-      } else {
-        L[j][j] = __builtin_sqrt(piv);
-      }
-    }
+    const double piv = L[j][j];
+    const bool ok = piv > 0.0 && piv < INFINITY;
+    const double d = ok ? __builtin_sqrt(piv) : __builtin_nan("");
+    if (tid == 0 && !ok) atomicMin(S.info, (int32_t)(off + j));
+    // phase A: column j of C below the diagonal, row j of the inverse
+    for (int i = j + 1 + tid; i < bs; i += 256) L[i][j] /= d;
+    for (int c = tid; c <= j; c += 256) Y[j][c] /= d;
     __syncthreads();
-    const double djj = L[j][j];
-    for (int i = j + 1 + tid; i < bs; i += 256) L[i][j] /= djj;
-    __syncthreads();
-    // trailing update of the block: L[i][c] -= L[i][j] L[c][j], j < c <= i
+    if (tid == 0) L[j][j] = d;
+    // phase B: trailing update of C, and rows i > j of the inverse
     const int rem = bs - j - 1;
     for (int e = tid; e < rem * rem; e += 256) {
       const int i = j + 1 + e / rem, c = j + 1 + e % rem;
       if (c <= i) L[i][c] -= L[i][j] * L[c][j];
     }
+    for (int e = tid; e < rem * (j + 1); e += 256) {
+      const int i = j + 1 + e / (j + 1), c = e % (j + 1);
+      Y[i][c] -= L[i][j] * Y[j][c];
+    }
     __syncthreads();
   }
-  // inverse of the lower-triangular L: column c by thread c
-  if (tid < bs) {
-    const int c = tid;
-    Y[c][c] = 1.0 / L[c][c];
-    for (int r = c + 1; r < bs; ++r) {
-      double sum = 0.0;
-      for (int k = c; k < r; ++k) sum += L[r][k] * Y[k][c];
-      Y[r][c] = -sum / L[r][r];
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    if (r < bs && c < bs) {
-      if (c <= r) X[(kb + r) * n + kb + c] = L[r][c];
-      Dinv[kb * NB + r * NB + c] = c <= r ? Y[r][c] : 0.0;
-    }
-  }
-}
-
-// Copy the stored inverse of diagonal block (kb, kb) into X (upper part 0).
-__global__ __launch_bounds__(256) void put_diag_inverse_kernel(int64_t n, int64_t kb, int bs,
-                                                               double* __restrict__ X,
-                                                               const double* __restrict__ Dinv) {
-  for (int e = threadIdx.x; e < bs * bs; e += 256) {
-    const int r = e / bs, c = e % bs;
-    X[(kb + r) * n + kb + c] = c <= r ? Dinv[kb * NB + r * NB + c] : 0.0;
+  for (int e = tid; e < NBL * NBL; e += 256) {
+    const int r = e / NBL, c = e % NBL;
+    if (r < bs && c < bs) S.Y[(off + r) * n + off + c] = c <= r ? Y[r][c] : 0.0;
   }
 }
 
@@ -195,65 +175,57 @@ hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t v, hipStream_t s) 
   return hipGetLastError();
 }
 
-// Cholesky then triangular inverse of the n x n lower triangle of X, in place.
-// Dinv: (ceil(n/64) * 64) x 64 scratch for the diagonal-block inverses;
-// Tmp: n x 64 scratch. info must hold INT_MAX on entry.
-hipError_t factor_cholesky_inverse(int64_t n, double* X, double* Dinv, double* Tmp,
-                                   int32_t* info, hipStream_t s) {
+// Recursive split point: about half, a multiple of 64, strictly inside.
+static inline int64_t split_point(int64_t n) {
+  int64_t n1 = (n / 2 + 63) / 64 * 64;
+  if (n1 >= n) n1 = n - 64;
+  return n1;
+}
+
+static hipError_t chol_inv_rec(int64_t n, const FactorSide* sd, int ns, int64_t off, int64_t len,
+                               hipStream_t s) {
   hipError_t err;
-  for (int64_t kb = 0; kb < n; kb += NB) {
-    const int bs = (int)((n - kb) < NB ? (n - kb) : NB);
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, s, n, kb, bs, X, Dinv, info);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    const int64_t r0 = kb + bs, nr = n - r0;
-    if (nr <= 0) break;
-    // panel: X[r0:, kb:kb+bs] = X[r0:, kb:kb+bs] * inv(L11)^T. In place is
-    // safe: one 64-wide output column block, and each block reads its rows of
-    // A completely (K = bs <= 64) before it writes them.
-    Gemm64Args p{};
-    p.M = nr; p.N = bs; p.K = bs;
-    p.A = X + r0 * n + kb; p.lda = n;
-    p.B = Dinv + kb * NB; p.ldb = NB; p.transB = 1;
-    p.C = X + r0 * n + kb; p.ldc = n;
-    p.alpha = 1.0; p.beta = 0.0;
-    if ((err = launch_gemm64(p, s)) != hipSuccess) return err;
-    // trailing: X[r0:, r0:] -= P P^T, lower 64-blocks only
-    Gemm64Args t{};
-    t.M = nr; t.N = nr; t.K = bs;
-    t.A = X + r0 * n + kb; t.lda = n;
-    t.B = X + r0 * n + kb; t.ldb = n; t.transB = 1;
-    t.C = X + r0 * n + r0; t.ldc = n;
-    t.alpha = -1.0; t.beta = 1.0; t.lower_out = 1;
-    if ((err = launch_gemm64(t, s)) != hipSuccess) return err;
+  if (len <= NB) {
+    hipLaunchKernelGGL(chol_inv_leaf_kernel, dim3(ns), dim3(256), 0, s, sd[0],
+                       sd[ns > 1 ? 1 : 0], n, off, (int)len);
+    return hipGetLastError();
   }
-  // triangular inverse, bottom block first
-  const int64_t nblk = (n + NB - 1) / NB;
-  for (int64_t jb = nblk - 1; jb >= 0; --jb) {
-    const int64_t kb = jb * NB;
-    const int bs = (int)((n - kb) < NB ? (n - kb) : NB);
-    const int64_t r0 = kb + bs, nr = n - r0;
-    if (nr > 0) {
-      // Tmp = X22^-1 (already in place, lower) * X21
-      Gemm64Args g1{};
-      g1.M = nr; g1.N = bs; g1.K = nr;
-      g1.A = X + r0 * n + r0; g1.lda = n; g1.a_lower = 1;
-      g1.B = X + r0 * n + kb; g1.ldb = n; g1.transB = 0;
-      g1.C = Tmp; g1.ldc = NB;
-      g1.alpha = 1.0; g1.beta = 0.0;
-      if ((err = launch_gemm64(g1, s)) != hipSuccess) return err;
-      // X21 = -Tmp * inv(X11)
-      Gemm64Args g2{};
-      g2.M = nr; g2.N = bs; g2.K = bs;
-      g2.A = Tmp; g2.lda = NB;
-      g2.B = Dinv + kb * NB; g2.ldb = NB; g2.transB = 0;
-      g2.C = X + r0 * n + kb; g2.ldc = n;
-      g2.alpha = -1.0; g2.beta = 0.0;
-      if ((err = launch_gemm64(g2, s)) != hipSuccess) return err;
-    }
-    hipLaunchKernelGGL(put_diag_inverse_kernel, dim3(1), dim3(256), 0, s, n, kb, bs, X, Dinv);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  return hipSuccess;
+  const int64_t n1 = split_point(len), n2 = len - n1;
+  if ((err = chol_inv_rec(n, sd, ns, off, n1, s)) != hipSuccess) return err;
+  const int64_t o11 = off * n + off;            // (off, off)
+  const int64_t o21 = (off + n1) * n + off;     // (off + n1, off)
+  const int64_t o22 = (off + n1) * n + off + n1;
+  // C21 = X21 Y11^T, written where Y21 will go (that block of Y is free until then)
+  Gemm64Args g{};
+  g.M = n2; g.N = n1; g.K = n1; g.batch = ns;
+  for (int z = 0; z < ns; ++z) { g.A[z] = sd[z].X + o21; g.B[z] = sd[z].Y + o11; g.C[z] = sd[z].Y + o21; }
+  g.lda = n; g.ldb = n; g.ldc = n; g.transB = 1; g.b_lower = 1; g.alpha = 1.0; g.beta = 0.0;
+  if ((err = launch_gemm64(g, s)) != hipSuccess) return err;
+  // X22 -= C21 C21^T (lower blocks)
+  Gemm64Args h{};
+  h.M = n2; h.N = n2; h.K = n1; h.batch = ns;
+  for (int z = 0; z < ns; ++z) { h.A[z] = sd[z].Y + o21; h.B[z] = sd[z].Y + o21; h.C[z] = sd[z].X + o22; }
+  h.lda = n; h.ldb = n; h.ldc = n; h.transB = 1; h.lower_out = 1; h.alpha = -1.0; h.beta = 1.0;
+  if ((err = launch_gemm64(h, s)) != hipSuccess) return err;
+  if ((err = chol_inv_rec(n, sd, ns, off + n1, n2, s)) != hipSuccess) return err;
+  // Tmp = C21 Y11 (Y11 lower: column block c needs k >= c * 64)
+  Gemm64Args t{};
+  t.M = n2; t.N = n1; t.K = n1; t.batch = ns;
+  for (int z = 0; z < ns; ++z) { t.A[z] = sd[z].Y + o21; t.B[z] = sd[z].Y + o11; t.C[z] = sd[z].Tmp; }
+  t.lda = n; t.ldb = n; t.ldc = n1; t.transB = 0; t.b_lower = 1; t.alpha = 1.0; t.beta = 0.0;
+  if ((err = launch_gemm64(t, s)) != hipSuccess) return err;
+  // Y21 = -Y22 Tmp (Y22 lower)
+  Gemm64Args u{};
+  u.M = n2; u.N = n1; u.K = n2; u.batch = ns;
+  for (int z = 0; z < ns; ++z) { u.A[z] = sd[z].Y + o22; u.B[z] = sd[z].Tmp; u.C[z] = sd[z].Y + o21; }
+  u.lda = n; u.ldb = n1; u.ldc = n; u.transB = 0; u.a_lower = 1; u.alpha = -1.0; u.beta = 0.0;
+  return launch_gemm64(u, s);
+}
+
+hipError_t factor_cholesky_inverse(int64_t n, const FactorSide* sides, int nsides, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (nsides < 1 || nsides > 2) return hipErrorInvalidValue;
+  return chol_inv_rec(n, sides, nsides, 0, n, s);
 }
 
 template hipError_t launch_load_reversed<float>(int64_t, const float*, int64_t, double*, hipStream_t);

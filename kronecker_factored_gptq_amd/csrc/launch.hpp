@@ -48,35 +48,52 @@ constexpr int kLeafBlock = 8;
 // ---- factor (factor_kernels.hip), always float64 inside --------------------
 template <typename R>
 hipError_t launch_load_reversed(int64_t n, const R* A, int64_t lda, double* X, hipStream_t s);
-hipError_t factor_cholesky_inverse(int64_t n, double* X, double* Dinv, double* Tmp,
-                                   int32_t* info, hipStream_t s);
+// One matrix being factored: X (n x n, ld n) holds the lower triangle of the
+// (reversed) input and is overwritten with Schur complements; Y (n x n, ld n)
+// receives the inverse of its Cholesky factor (lower, zeros above the
+// diagonal inside 64 x 64 diagonal blocks); Tmp holds >= (n/2 + 64)^2
+// doubles; *info receives the smallest failing pivot index (starts INT_MAX).
+struct FactorSide {
+  double* X;
+  double* Y;
+  double* Tmp;
+  int32_t* info;
+};
+// Y = Cholesky(X)^-1 for `nsides` (1 or 2) matrices of the same order n, in
+// one sequence of launches (the two sides share every launch).
+hipError_t factor_cholesky_inverse(int64_t n, const FactorSide* sides, int nsides, hipStream_t s);
 template <typename R>
 hipError_t launch_store_normalized(int64_t n, const double* Y, R* L, int64_t ldl, R* d,
                                    hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t v, hipStream_t s);
 
 // ---- float64 GEMM (gemm64.hip) --------------------------------------------
-// C = alpha * A * op(B) + beta * C, op(B) = B (K x N) or B^T (B is N x K).
+// C = alpha * A * op(B) + beta * C, op(B) = B (K x N) or B^T (B is N x K), for
+// `batch` (1 or 2) problems of one shape (pointers [z]).
 // lower_out: only 64x64 output blocks with block_row >= block_col are
 // computed (the others are left untouched). a_lower: A is lower triangular,
-// so row block r only needs k < (r + 1) * 64.
-// dot != nullptr: instead of storing C, the block's sum of (A op(B)) .* dot is
-// written to partial[block] (C unused).
+// so row block r only needs k < (r + 1) * 64. b_lower: B as stored is lower
+// triangular: with transB the column block c only needs k < (c + 1) * 64,
+// without it only k >= c * 64.
+// dot[0] != nullptr: instead of storing C, the block's sum of
+// alpha (A op(B)) .* dot is written to partial[z][block] (C unused).
 struct Gemm64Args {
   int64_t M, N, K;
-  const double* A;
+  const double* A[2];
   int64_t lda;
-  const double* B;
+  const double* B[2];
   int64_t ldb;
-  double* C;
+  double* C[2];
   int64_t ldc;
   double alpha, beta;
   int transB;
   int lower_out;
   int a_lower;
-  const double* dot;
+  int b_lower;
+  const double* dot[2];
   int64_t lddot;
-  double* partial;
+  double* partial[2];
+  int batch;
 };
 hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s);
 int64_t gemm64_num_blocks(int64_t M, int64_t N);
