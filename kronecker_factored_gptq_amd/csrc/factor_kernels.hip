@@ -54,51 +54,94 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* 
 }
 
 // Leaf of the recursion: the Cholesky factor C of the bs x bs diagonal block
-// X[off.., off..] (bs <= 64) and its inverse, in LDS; Y[off.., off..]
-// receives C^-1 (zeros above the diagonal). Right-looking, two barriers per
-// column: phase A scales column j of C and row j of the inverse by C[j][j],
-// phase B updates the trailing block and the rows of the inverse below j. A
-// pivot that is not positive and finite records off + j in *info (smallest
-// wins) and the factorisation continues with NaN. blockIdx.x selects the side.
+// X[off.., off..] (bs <= 64) and its inverse Y = C^-1; Y[off.., off..]
+// receives C^-1 (zeros above the diagonal). Thread (ty, tx) of a 16 x 16
+// grid keeps the 4 x 4 patch rows 4ty.., columns 4tx.. of both C and Y in
+// registers. Right-looking, one barrier per column j: the owners publish the
+// raw pivot C[j][j], the raw column j of C below it and the raw row j of Y;
+// after the barrier every thread forms d = sqrt(pivot) and scales what it
+// read by 1/d, then updates its patch: C[i][c] -= C[i][j] C[c][j]
+// (j < c <= i) and Y[i][c] -= C[i][j] Y[j][c] (i > j). Published values are
+// double-buffered by the parity of j. A pivot that is not positive and
+// finite records off + j in *info (smallest wins) and the factorisation
+// continues with NaN. blockIdx.x selects the side.
 __global__ __launch_bounds__(256) void chol_inv_leaf_kernel(FactorSide s0, FactorSide s1,
                                                             int64_t n, int64_t off, int bs) {
-  constexpr int NBL = 64;
-  __shared__ double L[NBL][NBL + 1];
-  __shared__ double Y[NBL][NBL + 1];
+  __shared__ double piv_s[2];
+  __shared__ double colj[2][64];
+  __shared__ double rowj[2][64];
   const FactorSide S = blockIdx.x == 0 ? s0 : s1;
   const int tid = threadIdx.x;
-  for (int e = tid; e < NBL * NBL; e += 256) {
-    const int r = e / NBL, c = e % NBL;
-    L[r][c] = (r < bs && c <= r) ? S.X[(off + r) * n + off + c] : 0.0;
-    Y[r][c] = r == c ? 1.0 : 0.0;
-  }
-  __syncthreads();
+  const int ty = tid >> 4, tx = tid & 15;
+  double Lr[4][4], Yr[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = 4 * ty + a, c = 4 * tx + b;
+      Lr[a][b] = (i < bs && c <= i) ? S.X[(off + i) * n + off + c] : 0.0;
+      Yr[a][b] = (i == c) ? 1.0 : 0.0;
+    }
   for (int j = 0; j < bs; ++j) {
-    const double piv = L[j][j];
+    const int jq = j >> 2, jr = j & 3, pb = j & 1;
+    // publish raw values of step j
+    if (ty == jq && tx == jq) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a == jr) piv_s[pb] = Lr[a][a];
+    }
+    if (tx == jq) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (b == jr) colj[pb][4 * ty + a] = Lr[a][b];
+    }
+    if (ty == jq) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a == jr) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) rowj[pb][4 * tx + b] = Yr[a][b];
+        }
+    }
+    __syncthreads();
+    const double piv = piv_s[pb];
     const bool ok = piv > 0.0 && piv < INFINITY;
-    const double d = ok ? __builtin_sqrt(piv) : __builtin_nan("");
     if (tid == 0 && !ok) atomicMin(S.info, (int32_t)(off + j));
-    // phase A: column j of C below the diagonal, row j of the inverse
-    for (int i = j + 1 + tid; i < bs; i += 256) L[i][j] /= d;
-    for (int c = tid; c <= j; c += 256) Y[j][c] /= d;
-    __syncthreads();
-    if (tid == 0) L[j][j] = d;
-    // phase B: trailing update of C, and rows i > j of the inverse
-    const int rem = bs - j - 1;
-    for (int e = tid; e < rem * rem; e += 256) {
-      const int i = j + 1 + e / rem, c = j + 1 + e % rem;
-      if (c <= i) L[i][c] -= L[i][j] * L[c][j];
+    const double inv = ok ? 1.0 / __builtin_sqrt(piv) : __builtin_nan("");
+    double ci[4], cc[4], yr[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int i = 4 * ty + a, c = 4 * tx + a;
+      ci[a] = (i > j && i < bs) ? colj[pb][i] * inv : 0.0;
+      cc[a] = (c > j && c < bs) ? colj[pb][c] * inv : 0.0;
+      yr[a] = c <= j ? rowj[pb][c] * inv : 0.0;
     }
-    for (int e = tid; e < rem * (j + 1); e += 256) {
-      const int i = j + 1 + e / (j + 1), c = e % (j + 1);
-      Y[i][c] -= L[i][j] * Y[j][c];
+    if (ty == jq) {  // row j of Y is final now
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a == jr) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) Yr[a][b] = yr[b];
+        }
     }
-    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i = 4 * ty + a, c = 4 * tx + b;
+        if (c <= i) Lr[a][b] -= ci[a] * cc[b];  // zero unless j < c <= i < bs
+        Yr[a][b] -= ci[a] * yr[b];              // zero unless i > j and c <= j
+      }
   }
-  for (int e = tid; e < NBL * NBL; e += 256) {
-    const int r = e / NBL, c = e % NBL;
-    if (r < bs && c < bs) S.Y[(off + r) * n + off + c] = c <= r ? Y[r][c] : 0.0;
-  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = 4 * ty + a, c = 4 * tx + b;
+      if (i < bs && c < bs) S.Y[(off + i) * n + off + c] = c <= i ? Yr[a][b] : 0.0;
+    }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {

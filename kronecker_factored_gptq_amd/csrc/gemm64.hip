@@ -1,9 +1,11 @@
 // Float64 MFMA GEMM for the factorisation and the loss (gfx950).
 //
-// C = alpha * A * op(B) + beta * C over 64 x 64 output blocks, 256 threads in
-// four waves (2 x 2), each wave a 32 x 32 sub-block of 2 x 2
+// C = alpha * A * op(B) + beta * C over BM x BM output blocks (BM = 64 or
+// 128), 256 threads in four waves (2 x 2), each wave a (BM/2)^2 sub-block of
 // v_mfma_f64_16x16x4 blocks; K advances 16 at a time through double-buffered
-// LDS. Options: only lower output blocks (symmetric rank-k update), A lower
+// LDS; operands move as 16-byte vectors when their rows are 16-byte aligned.
+// The large blocks serve the big products (more MFMA work per LDS byte), the
+// small ones the small products (more workgroups). Options: only lower output blocks (symmetric rank-k update), A lower
 // triangular (K ends with the row block), B lower triangular (K ends with the
 // column block when op(B) = B^T, starts with it when op(B) = B), a batch of
 // two independent problems of one shape (grid z), and a dot epilogue that
@@ -14,14 +16,17 @@
 namespace bk {
 
 namespace {
-constexpr int GB = 64;  // block edge
-constexpr int GK = 16;  // K step
+constexpr int GTRI = 64;  // granularity of the triangular options
+constexpr int GK = 16;    // K step
 constexpr int GLD = GK + 2;
 }  // namespace
 
+template <int GB, bool VEC, bool TRI>
 __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
   typedef Mfma<double> MF;
   typedef MF::acc_t acc_t;
+  constexpr int WT = GB / 2, NBW = WT / 16;
+  constexpr int PER = GB * GK / 256;  // elements per thread per operand per K step
   __shared__ double As[2][GB][GLD];
   __shared__ double Bs[2][GB][GLD];
   __shared__ double red[4];
@@ -36,13 +41,15 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
   const double* __restrict__ Bp = a.B[z];
   double* Cp = a.C[z];
   const int64_t row0 = bm * GB, col0 = bn * GB;
-  const bool skip = a.lower_out && bn > bm;
+  // lower_out is decided on the 64-granular triangle: a block is computed if
+  // any of its 64 x 64 sub-blocks is on or below the diagonal
+  const bool skip = a.lower_out && col0 >= row0 + GB;
 
-  acc_t acc[2][2];
+  acc_t acc[NBW][NBW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = MF::zero();
+    for (int j = 0; j < NBW; ++j) acc[i][j] = MF::zero();
 
   int64_t kend = a.K, kbeg = 0;
   if (a.a_lower && row0 + GB < kend) kend = row0 + GB;
@@ -54,31 +61,83 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
     }
   }
 
-  double ra[4], rb[4];
+  double ra[PER], rb[PER];
+  auto kin = [&](int64_t gk) { return gk < kend && gk >= kbeg; };
+  // exact 64-granular triangular structure of A (row gr) and B (column gn)
+  auto ain = [&](int64_t gr, int64_t gk) {
+    return gr < a.M && kin(gk) && (!TRI || !a.a_lower || gk < (gr / GTRI + 1) * GTRI);
+  };
+  auto bin = [&](int64_t gn, int64_t gk) {
+    if (gn >= a.N || !kin(gk)) return false;
+    if (!TRI || !a.b_lower) return true;
+    return a.transB ? gk < (gn / GTRI + 1) * GTRI : gk >= (gn / GTRI) * GTRI;
+  };
   auto gload = [&](int64_t k0) {
+    if (VEC) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = u * 256 + tid;
-      {  // A tile: 64 rows x 16 k
-        const int r = e / GK, c = e % GK;
-        const int64_t gr = row0 + r, gk = k0 + c;
-        ra[u] = (gr < a.M && gk < kend && gk >= kbeg) ? Ap[gr * a.lda + gk] : 0.0;
+      for (int u = 0; u < PER / 2; ++u) {
+        const int e = 2 * (u * 256 + tid);
+        {
+          const int r = e / GK, c = e % GK;
+          const int64_t gr = row0 + r, gk = k0 + c;
+          double2 v = make_double2(0.0, 0.0);
+          const bool i0 = ain(gr, gk), i1 = ain(gr, gk + 1);
+          if (i0 && i1) v = *reinterpret_cast<const double2*>(Ap + gr * a.lda + gk);
+          else {
+            if (i0) v.x = Ap[gr * a.lda + gk];
+            if (i1) v.y = Ap[gr * a.lda + gk + 1];
+          }
+          ra[2 * u] = v.x; ra[2 * u + 1] = v.y;
+        }
+        if (a.transB) {
+          const int r = e / GK, c = e % GK;
+          const int64_t gn = col0 + r, gk = k0 + c;
+          double2 v = make_double2(0.0, 0.0);
+          const bool i0 = bin(gn, gk), i1 = bin(gn, gk + 1);
+          if (i0 && i1) v = *reinterpret_cast<const double2*>(Bp + gn * a.ldb + gk);
+          else {
+            if (i0) v.x = Bp[gn * a.ldb + gk];
+            if (i1) v.y = Bp[gn * a.ldb + gk + 1];
+          }
+          rb[2 * u] = v.x; rb[2 * u + 1] = v.y;
+        } else {
+          const int kr = e / GB, cc = e % GB;
+          const int64_t gk = k0 + kr, gn = col0 + cc;
+          double2 v = make_double2(0.0, 0.0);
+          const bool i0 = bin(gn, gk), i1 = bin(gn + 1, gk);
+          if (i0 && i1) v = *reinterpret_cast<const double2*>(Bp + gk * a.ldb + gn);
+          else {
+            if (i0) v.x = Bp[gk * a.ldb + gn];
+            if (i1) v.y = Bp[gk * a.ldb + gn + 1];
+          }
+          rb[2 * u] = v.x; rb[2 * u + 1] = v.y;
+        }
       }
-      if (a.transB) {  // B is N x K
-        const int r = e / GK, c = e % GK;
-        const int64_t gn = col0 + r, gk = k0 + c;
-        rb[u] = (gn < a.N && gk < kend && gk >= kbeg) ? Bp[gn * a.ldb + gk] : 0.0;
-      } else {  // B is K x N
-        const int kr = e / GB, cc = e % GB;
-        const int64_t gk = k0 + kr, gn = col0 + cc;
-        rb[u] = (gn < a.N && gk < kend && gk >= kbeg) ? Bp[gk * a.ldb + gn] : 0.0;
+    } else {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int e = u * 256 + tid;
+        {
+          const int r = e / GK, c = e % GK;
+          const int64_t gr = row0 + r, gk = k0 + c;
+          ra[u] = ain(gr, gk) ? Ap[gr * a.lda + gk] : 0.0;
+        }
+        if (a.transB) {
+          const int r = e / GK, c = e % GK;
+          const int64_t gn = col0 + r, gk = k0 + c;
+          rb[u] = bin(gn, gk) ? Bp[gn * a.ldb + gk] : 0.0;
+        } else {
+          const int kr = e / GB, cc = e % GB;
+          const int64_t gk = k0 + kr, gn = col0 + cc;
+          rb[u] = bin(gn, gk) ? Bp[gk * a.ldb + gn] : 0.0;
+        }
       }
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = u * 256 + tid;
+    for (int u = 0; u < PER; ++u) {
+      const int e = VEC ? 2 * ((u >> 1) * 256 + tid) + (u & 1) : u * 256 + tid;
       As[buf][e / GK][e % GK] = ra[u];
       if (a.transB) Bs[buf][e / GK][e % GK] = rb[u];
       else Bs[buf][e % GB][e / GB] = rb[u];
@@ -96,15 +155,15 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
       if (it + 1 < nk) gload(k00 + (it + 1) * GK);
 #pragma unroll
       for (int st = 0; st < GK / 4; ++st) {
-        double af[2], bf[2];
+        double af[NBW], bf[NBW];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = As[buf][wr * 32 + i * 16 + r16][4 * kg + st];
+        for (int i = 0; i < NBW; ++i) af[i] = As[buf][wr * WT + i * 16 + r16][4 * kg + st];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = Bs[buf][wc * 32 + j * 16 + r16][4 * kg + st];
+        for (int j = 0; j < NBW; ++j) bf[j] = Bs[buf][wc * WT + j * 16 + r16][4 * kg + st];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NBW; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = MF::mma(af[i], bf[j], acc[i][j]);
+          for (int j = 0; j < NBW; ++j) acc[i][j] = MF::mma(af[i], bf[j], acc[i][j]);
       }
       if (it + 1 < nk) sstore(buf ^ 1);
       __syncthreads();
@@ -115,13 +174,13 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
     double part = 0.0;
     if (!skip) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NBW; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NBW; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int64_t gr = row0 + wr * 32 + i * 16 + MF::row(lane, r);
-            const int64_t gc = col0 + wc * 32 + j * 16 + r16;
+            const int64_t gr = row0 + wr * WT + i * 16 + MF::row(lane, r);
+            const int64_t gc = col0 + wc * WT + j * 16 + r16;
             if (gr < a.M && gc < a.N) part += a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
           }
     }
@@ -135,13 +194,15 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
   }
   if (skip) return;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NBW; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t gr = row0 + wr * 32 + i * 16 + MF::row(lane, r);
-        const int64_t gc = col0 + wc * 32 + j * 16 + r16;
+        const int64_t gr = row0 + wr * WT + i * 16 + MF::row(lane, r);
+        const int64_t gc = col0 + wc * WT + j * 16 + r16;
+        // lower_out: leave 64 x 64 sub-blocks strictly above the diagonal untouched
+        if (a.lower_out && gc / GTRI > gr / GTRI) continue;
         if (gr < a.M && gc < a.N) {
           double v = a.alpha * acc[i][j][r];
           if (a.beta != 0.0) v += a.beta * Cp[gr * a.ldc + gc];
@@ -150,16 +211,42 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
       }
 }
 
+// Block edge for a product. The 128 variant runs at one wave per SIMD
+// (register-bound) and measured slower than 64 on the 2048^3 and 4096^3
+// products, so 64 is used throughout; the variant stays compiled for tuning.
+static int gemm64_block(int64_t, int64_t, int) { return 64; }
+
 int64_t gemm64_num_blocks(int64_t M, int64_t N) {
-  return ((M + GB - 1) / GB) * ((N + GB - 1) / GB);
+  const int gb = gemm64_block(M, N, 1);
+  return ((M + gb - 1) / gb) * ((N + gb - 1) / gb);
+}
+
+template <int GB>
+static hipError_t launch_gb(const Gemm64Args& a, bool vec, hipStream_t s) {
+  dim3 grid((unsigned)((a.N + GB - 1) / GB), (unsigned)((a.M + GB - 1) / GB), (unsigned)a.batch);
+  const bool tri = a.a_lower || a.b_lower;
+  if (vec) {
+    if (tri) hipLaunchKernelGGL((gemm64_kernel<GB, true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm64_kernel<GB, true, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (tri) hipLaunchKernelGGL((gemm64_kernel<GB, false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm64_kernel<GB, false, false>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.batch < 1 || a.batch > 2) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((a.N + GB - 1) / GB), (unsigned)((a.M + GB - 1) / GB), (unsigned)a.batch);
-  hipLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  // 16-byte vectors need every row start of A and B 16-byte aligned; they
+  // measured slower than element loads here (more registers, lower
+  // occupancy), so they are off
+  bool vec = false && (a.lda % 2 == 0) && (a.ldb % 2 == 0);
+  for (int z = 0; z < a.batch; ++z)
+    vec = vec && (reinterpret_cast<uintptr_t>(a.A[z]) % 16 == 0) &&
+          (reinterpret_cast<uintptr_t>(a.B[z]) % 16 == 0);
+  if (gemm64_block(a.M, a.N, a.batch) == 128) return launch_gb<128>(a, vec, s);
+  return launch_gb<64>(a, vec, s);
 }
 
 }  // namespace bk
