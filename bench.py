@@ -28,6 +28,14 @@ if ROOT not in sys.path:
 
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix
 PEAK_FP64_MFMA_TFLOPS = 78.6    # MI355X dense FP64 matrix
+
+# HBM bytes per band launch from the FETCH_SIZE / WRITE_SIZE counter passes
+# over one step of this workload, scaled by a plain 512 MiB copy (FETCH_SIZE
+# x2.0, WRITE_SIZE x1.0), valid for the band-kernel source with this hash
+# only: after any change to that file the figure is reported as null.
+BAND_TRAFFIC = {"sha256": "012b270df02b353d22f4e3c09c1d60dbf1a0070e7c56687becd8a46fd043d5a5",
+                "bytes_per_launch": 5.7622e7, "launches": 126,
+                "summary": "profiles/band_kernel_attn4096_f32_counters.md"}
 METRIC = "weights quantized/s (m·n/solve-time) + % FP32 MFMA peak, 4096×4096"
 
 
@@ -40,7 +48,31 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--untimed-solve", action="store_true",
                     help="time steps with the plain solve (no per-launch events); roofline omitted")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 512 MiB three times (HBM counter scale)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy kernel of known size: 512 MiB read + 512 MiB written per
+    launch. Its FETCH_SIZE / WRITE_SIZE readings scale the counters of the
+    solve kernels to bytes."""
+    import torch
+    n = 512 * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+
+
+def band_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "kronecker_factored_gptq_amd", "csrc", "band_kernels.hip")
+    with open(src, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()
+    return BAND_TRAFFIC["bytes_per_launch"] if h == BAND_TRAFFIC["sha256"] else None
 
 
 def cpu_baseline(p, hi: int):
@@ -68,6 +100,9 @@ def cpu_baseline(p, hi: int):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -181,7 +216,9 @@ def main():
         achieved = fl["band"] / (band_ms / 1e3) / 1e12
         result["roofline"] = {
             "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+            "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+            "traffic": band_traffic() if args.workload == "attn4096" else None,
+            "traffic_unit": "HBM bytes per launch (counters)",
             "kernel": "band_kernel (both stages)", "launches_per_step": nb,
             "useful_flop_per_step": fl["band"], "ms_per_step": band_ms,
             "avg_launch_us": band_ms * 1e3 / nb,

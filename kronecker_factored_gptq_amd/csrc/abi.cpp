@@ -128,17 +128,18 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   for (const Op& op : ops) {
     hipError_t e = hipSuccess;
     const bool timed = op_ms && (op.kind == OP_BAND1 || op.kind == OP_BAND2);
-    if (timed && hipEventRecord(ev[evi], s) != hipSuccess) { rc = BAKRON_EHIP; break; }
+    hipEvent_t e0 = timed ? ev[evi] : nullptr, e1 = timed ? ev[evi + 1] : nullptr;
     switch (op.kind) {
       case OP_LEAF: e = launch_leaf<R>(g, op.k, op.mid, Wk, LBp, LAp, lp, s); break;
-      case OP_BAND1: e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, Wk, LBp, LAp, Mb, s); break;
-      case OP_BAND2: e = launch_node_band<R>(g, op.k, op.mid, op.l, 2, Wk, LBp, LAp, Mb, s); break;
+      case OP_BAND1:
+        e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, Wk, LBp, LAp, Mb, s, e0, e1);
+        break;
+      case OP_BAND2:
+        e = launch_node_band<R>(g, op.k, op.mid, op.l, 2, Wk, LBp, LAp, Mb, s, e0, e1);
+        break;
     }
     if (e != hipSuccess) { rc = BAKRON_EHIP; break; }
-    if (timed) {
-      if (hipEventRecord(ev[evi + 1], s) != hipSuccess) { rc = BAKRON_EHIP; break; }
-      evi += 2;
-    }
+    if (timed) evi += 2;
   }
   if (op_ms) {
     if (rc == BAKRON_OK && !ev.empty() && hipEventSynchronize(ev.back()) != hipSuccess)

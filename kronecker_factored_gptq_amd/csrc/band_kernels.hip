@@ -18,6 +18,8 @@
 // Operands are double-buffered in LDS with k contiguous (one 128-bit read
 // per lane per four MFMAs); stage 1's E tiles keep their natural row-major
 // order (k = row) and are read one element per MFMA.
+#include <hip/hip_ext.h>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -224,7 +226,8 @@ template <> struct BandChoice<double> { static constexpr int BIG = 4, SMALL = 2,
 
 template <typename R, int MB>
 static hipError_t launch_band_mb(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
-                                 const R* LBp, const R* LAp, R* Mb, hipStream_t s) {
+                                 const R* LBp, const R* LAp, R* Mb, hipStream_t s,
+                                 hipEvent_t ev0, hipEvent_t ev1) {
   const int nPb = (g.Mt + MB - 1) / MB;
   int maxw = 0;
   for (int pb = 0; pb < nPb; ++pb) {
@@ -241,27 +244,47 @@ static hipError_t launch_band_mb(const SolveGeom& g, int k, int mid, int l, int 
     const int w = Chi / MB - Clo / MB + 1;
     if (w > maxw) maxw = w;
   }
-  if (maxw == 0) return hipSuccess;
-  if (stage == 1)
-    hipLaunchKernelGGL((band_kernel<R, 1, MB>), dim3(maxw, nPb), dim3(256), 0, s, k, mid, l,
-                       g.Mt, g.Nt, Wk, LBp, LAp, Mb);
-  else
-    hipLaunchKernelGGL((band_kernel<R, 2, MB>), dim3(maxw, nPb), dim3(256), 0, s, k, mid, l,
-                       g.Mt, g.Nt, Wk, LBp, LAp, Mb);
+  if (maxw == 0) {
+    // nothing to do; keep the timing events valid (zero duration)
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return hipErrorUnknown;
+    if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return hipErrorUnknown;
+    return hipSuccess;
+  }
+  const dim3 grid(maxw, nPb), block(256);
+  if (ev0 || ev1) {
+    // the events are stamped by the dispatch packet itself: exact kernel time
+    if (stage == 1)
+      hipExtLaunchKernelGGL((band_kernel<R, 1, MB>), grid, block, 0, s, ev0, ev1, 0, k, mid, l,
+                            g.Mt, g.Nt, Wk, LBp, LAp, Mb);
+    else
+      hipExtLaunchKernelGGL((band_kernel<R, 2, MB>), grid, block, 0, s, ev0, ev1, 0, k, mid, l,
+                            g.Mt, g.Nt, Wk, LBp, LAp, Mb);
+  } else if (stage == 1) {
+    hipLaunchKernelGGL((band_kernel<R, 1, MB>), grid, block, 0, s, k, mid, l, g.Mt, g.Nt, Wk,
+                       LBp, LAp, Mb);
+  } else {
+    hipLaunchKernelGGL((band_kernel<R, 2, MB>), grid, block, 0, s, k, mid, l, g.Mt, g.Nt, Wk,
+                       LBp, LAp, Mb);
+  }
   return hipGetLastError();
 }
 
 template <typename R>
 hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
-                            const R* LBp, const R* LAp, R* Mb, hipStream_t s) {
+                            const R* LBp, const R* LAp, R* Mb, hipStream_t s, hipEvent_t ev0,
+                            hipEvent_t ev1) {
   if (l - k >= BandChoice<R>::QMIN_BIG)
-    return launch_band_mb<R, BandChoice<R>::BIG>(g, k, mid, l, stage, Wk, LBp, LAp, Mb, s);
-  return launch_band_mb<R, BandChoice<R>::SMALL>(g, k, mid, l, stage, Wk, LBp, LAp, Mb, s);
+    return launch_band_mb<R, BandChoice<R>::BIG>(g, k, mid, l, stage, Wk, LBp, LAp, Mb, s, ev0,
+                                                 ev1);
+  return launch_band_mb<R, BandChoice<R>::SMALL>(g, k, mid, l, stage, Wk, LBp, LAp, Mb, s, ev0,
+                                                 ev1);
 }
 
 template hipError_t launch_node_band<float>(const SolveGeom&, int, int, int, int, float*,
-                                            const float*, const float*, float*, hipStream_t);
+                                            const float*, const float*, float*, hipStream_t,
+                                            hipEvent_t, hipEvent_t);
 template hipError_t launch_node_band<double>(const SolveGeom&, int, int, int, int, double*,
-                                             const double*, const double*, double*, hipStream_t);
+                                             const double*, const double*, double*, hipStream_t,
+                                             hipEvent_t, hipEvent_t);
 
 }  // namespace bk
