@@ -61,6 +61,8 @@ std::vector<Op> schedule_for(int64_t m, int64_t n) {
   return ops;
 }
 
+// Solve workspace: W tiles, packed L^B and L^A tiles, and the stage-1
+// product M of the band products.
 struct SolveLayout {
   size_t wk, lb, la, mb, total;
 };
@@ -93,6 +95,11 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   R* LBp = reinterpret_cast<R*>(base + lay.wk);
   R* LAp = reinterpret_cast<R*>(base + lay.wk + lay.lb);
   R* Mb = reinterpret_cast<R*>(base + lay.wk + lay.lb + lay.la);
+  BandBuffers<R> bb;
+  bb.Wk = Wk;
+  bb.LBp = LBp;
+  bb.LAp = LAp;
+  bb.Mb = Mb;
 
   if (launch_pack_w<R>(g, W, ldw, Wk, s) != hipSuccess) return BAKRON_EHIP;
   if (launch_pack_l<R>(m, g.Mt, LB, ldlb, LBp, s) != hipSuccess) return BAKRON_EHIP;
@@ -132,10 +139,10 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
     switch (op.kind) {
       case OP_LEAF: e = launch_leaf<R>(g, op.k, op.mid, Wk, LBp, LAp, lp, s); break;
       case OP_BAND1:
-        e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, Wk, LBp, LAp, Mb, s, e0, e1);
+        e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, bb, s, e0, e1);
         break;
       case OP_BAND2:
-        e = launch_node_band<R>(g, op.k, op.mid, op.l, 2, Wk, LBp, LAp, Mb, s, e0, e1);
+        e = launch_node_band<R>(g, op.k, op.mid, op.l, 2, bb, s, e0, e1);
         break;
     }
     if (e != hipSuccess) { rc = BAKRON_EHIP; break; }

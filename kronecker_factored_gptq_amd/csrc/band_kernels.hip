@@ -56,10 +56,72 @@ struct BandShape {
   static_assert(NV >= 1 && (MB * BKT * TV) % 256 == 0, "macro tile too small for 256 threads");
 };
 
+// Geometry of the output macro tile (row block pb, column block number bx of
+// that row) of one stage: first column tile C0 and the K range [Klo, Khi] in
+// solver tiles. Shared by the kernels and the host-side launch planning.
+struct BandTile {
+  int P0, C0, Klo, Khi;
+};
+// Column tiles [Clo, Chi] that row block pb of a stage writes; false if none.
+__host__ __device__ inline bool band_cols(int stage, int k, int mid, int l, int Nt, int MB, int pb,
+                                          int* Clo, int* Chi) {
+  const int P0 = pb * MB;
+  int lo, hi;
+  if (stage == 1) {  // M[P, J] is needed where stage 2 reads it: J < mid, P + J <= l - 1
+    lo = k - (P0 + MB - 1); if (lo < 0) lo = 0;
+    hi = Nt - 1; if (mid - 1 < hi) hi = mid - 1; if (l - 1 - P0 < hi) hi = l - 1 - P0;
+  } else {           // W[P, Q] on mid <= P + Q <= l - 1
+    lo = mid - (P0 + MB - 1); if (lo < 0) lo = 0;
+    hi = Nt - 1; if (l - 1 - P0 < hi) hi = l - 1 - P0;
+  }
+  *Clo = lo;
+  *Chi = hi;
+  return lo <= hi;
+}
+__host__ __device__ inline bool band_tile(int stage, int k, int mid, int l, int Mt, int Nt, int MB,
+                                          int pb, int bx, BandTile* t) {
+  const int P0 = pb * MB;
+  int Clo, Chi;
+  if (!band_cols(stage, k, mid, l, Nt, MB, pb, &Clo, &Chi)) return false;
+  const int cb = Clo / MB + bx;
+  if (cb > Chi / MB) return false;
+  const int C0 = cb * MB;
+  int Klo, Khi;
+  if (stage == 1) {  // I <= P, k <= I + J < mid
+    Klo = k - (C0 + MB - 1); if (Klo < 0) Klo = 0;
+    Khi = P0 + MB - 1; if (mid - 1 - C0 < Khi) Khi = mid - 1 - C0; if (Mt - 1 < Khi) Khi = Mt - 1;
+  } else {           // J <= Q, J < mid, k <= P + J <= l - 1
+    Klo = k - (P0 + MB - 1); if (Klo < 0) Klo = 0;
+    Khi = C0 + MB - 1; if (mid - 1 < Khi) Khi = mid - 1; if (Nt - 1 < Khi) Khi = Nt - 1;
+    if (l - 1 - P0 < Khi) Khi = l - 1 - P0;
+  }
+  t->P0 = P0;
+  t->C0 = C0;
+  t->Klo = Klo;
+  t->Khi = Khi;
+  return Klo <= Khi;
+}
+
+template <typename R>
+struct BandArgs {
+  int k, mid, l, Mt, Nt;
+  int maxw;  // column blocks per row block (workgroups per row block)
+  R* Wk;
+  const R* LBp;
+  const R* LAp;
+  R* Mb;
+};
+
+// One-dimensional grid of nPb8 * maxw workgroups, nPb8 = row blocks rounded up
+// to a multiple of the 8 XCDs. Workgroup w runs on XCD w % 8 (round-robin
+// dispatch), and all workgroups of one row block go to the same XCD, so a row
+// panel of the left operand is fetched into one L2 only. Within an XCD the
+// row blocks are taken so that the macro tiles with the longest K ranges
+// start first (stage 1: the last row blocks; stage 2: the last column blocks
+// of a row).
+constexpr int kXcds = 8;
 template <typename R, int STAGE, int MB>
-__global__ __launch_bounds__(256) void band_kernel(int k, int mid, int l, int Mt, int Nt,
-                                                   R* __restrict__ Wk, const R* __restrict__ LBp,
-                                                   const R* __restrict__ LAp, R* __restrict__ Mb) {
+__global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
   typedef BandShape<R, MB> S;
   typedef Vec16<R> VV;
   typedef typename VV::T vec_t;
@@ -69,37 +131,44 @@ __global__ __launch_bounds__(256) void band_kernel(int k, int mid, int l, int Mt
   constexpr int B_ROWS = STAGE == 1 ? S::BK : S::BM;
   constexpr int B_LD = STAGE == 1 ? S::LDC : S::LDK;
 
-  __shared__ __attribute__((aligned(16))) R As[2][S::BM][S::LDK];
-  __shared__ __attribute__((aligned(16))) R Bs[2][B_ROWS][B_LD];
+  // one LDS block: the double-buffered operands, reused by the epilogue
+  typedef R AsT[2][S::BM][S::LDK];
+  typedef R BsT[2][B_ROWS][B_LD];
+  constexpr size_t kOps = sizeof(AsT) + sizeof(BsT);
+  constexpr size_t kOut = sizeof(R) * S::BM * S::BM;
+  __shared__ __attribute__((aligned(16))) char smem[kOps > kOut ? kOps : kOut];
+  AsT& As = *reinterpret_cast<AsT*>(smem);
+  BsT& Bs = *reinterpret_cast<BsT*>(smem + sizeof(AsT));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int r16 = lane & 15, kg = lane >> 4;
+  const int k = a.k, mid = a.mid, l = a.l, Mt = a.Mt, Nt = a.Nt;
 
-  const int pb = blockIdx.y;
-  const int P0 = pb * MB;
-  int Clo, Chi;
-  if (STAGE == 1) {
-    Clo = k - (P0 + MB - 1); if (Clo < 0) Clo = 0;
-    Chi = Nt - 1; if (mid - 1 < Chi) Chi = mid - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
-  } else {
-    Clo = mid - (P0 + MB - 1); if (Clo < 0) Clo = 0;
-    Chi = Nt - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
+  const int w = blockIdx.x;
+  const int xcd = w % kXcds, idx = w / kXcds;
+  const int rowj = idx / a.maxw;
+  int bx = idx % a.maxw;
+  const int nPb8 = (int)gridDim.x / a.maxw;
+  const int pl = xcd + kXcds * rowj;  // row block in dispatch order
+  const int pb = STAGE == 1 ? nPb8 - 1 - pl : pl;
+  if (pb >= (Mt + MB - 1) / MB) return;
+  if (STAGE == 2) {
+    int Clo, Chi;
+    if (!band_cols(STAGE, k, mid, l, Nt, MB, pb, &Clo, &Chi)) return;
+    bx = Chi / MB - Clo / MB - bx;
+    if (bx < 0) return;
   }
-  if (Clo > Chi) return;
-  const int cb = Clo / MB + (int)blockIdx.x;
-  if (cb > Chi / MB) return;
-  const int C0 = cb * MB;
+  BandTile bt;
+  if (!band_tile(STAGE, k, mid, l, Mt, Nt, MB, pb, bx, &bt)) return;
+  const int P0 = bt.P0, C0 = bt.C0;
+  const int Klo = bt.Klo, Khi = bt.Khi;
 
-  int Klo, Khi;
-  if (STAGE == 1) {
-    Klo = k - (C0 + MB - 1); if (Klo < 0) Klo = 0;
-    Khi = P0 + MB - 1; if (mid - 1 - C0 < Khi) Khi = mid - 1 - C0; if (Mt - 1 < Khi) Khi = Mt - 1;
-  } else {
-    Klo = k - (P0 + MB - 1); if (Klo < 0) Klo = 0;
-    Khi = C0 + MB - 1; if (mid - 1 < Khi) Khi = mid - 1; if (Nt - 1 < Khi) Khi = Nt - 1;
-  }
+  R* __restrict__ Wk = a.Wk;
+  const R* __restrict__ LBp = a.LBp;
+  const R* __restrict__ LAp = a.LAp;
+  R* __restrict__ Mb = a.Mb;
 
   acc_t acc[S::NBW][S::NBW];
 #pragma unroll
@@ -115,20 +184,20 @@ __global__ __launch_bounds__(256) void band_kernel(int k, int mid, int l, int Mt
     for (int u = 0; u < S::NV; ++u) {
       const int f = u * 256 + tid;
       const int ti = f / S::TV;               // tile index within the operand block
-      const int a = ti / S::BKT, kt = ti % S::BKT;
+      const int at = ti / S::BKT, kt = ti % S::BKT;
       const int v = f % S::TV;
       const int kk = kk0 + kt;
-      const int P = P0 + a, C = C0 + a;
+      const int P = P0 + at, C = C0 + at;
       vec_t va = VV::zero(), vb = VV::zero();
       if (STAGE == 1) {
         if (kk <= Khi && P < Mt && kk <= P)
           va = reinterpret_cast<const vec_t*>(LBp + tri_index(P, kk) * T * T)[v];
-        const int s = kk + C;
-        if (kk <= Khi && C < Nt && s >= k && s < mid)
+        const int sd = kk + C;
+        if (kk <= Khi && C < Nt && sd >= k && sd < mid)
           vb = reinterpret_cast<const vec_t*>(Wk + ((int64_t)kk * Nt + C) * T * T)[v];
       } else {
-        const int s = P + kk;
-        if (kk <= Khi && P < Mt && kk <= mid - 1 && s >= k && s <= l - 1)
+        const int sd = P + kk;
+        if (kk <= Khi && P < Mt && kk <= mid - 1 && sd >= k && sd <= l - 1)
           va = reinterpret_cast<const vec_t*>(Mb + ((int64_t)P * Nt + kk) * T * T)[v];
         if (kk <= Khi && C < Nt && kk <= C)
           vb = reinterpret_cast<const vec_t*>(LAp + tri_index(C, kk) * T * T)[v];
@@ -143,21 +212,23 @@ __global__ __launch_bounds__(256) void band_kernel(int k, int mid, int l, int Mt
     for (int u = 0; u < S::NV; ++u) {
       const int f = u * 256 + tid;
       const int ti = f / S::TV;
-      const int a = ti / S::BKT, kt = ti % S::BKT;
+      const int at = ti / S::BKT, kt = ti % S::BKT;
       const int e0 = (f % S::TV) * S::VN;
       const int r = e0 / T, c = e0 % T;
-      *reinterpret_cast<vec_t*>(&As[buf][a * T + r][kt * T + c]) = ra[u];
+      *reinterpret_cast<vec_t*>(&As[buf][at * T + r][kt * T + c]) = ra[u];
       if (STAGE == 1)  // E[k = r][col = c]: keep rows of k
-        *reinterpret_cast<vec_t*>(&Bs[buf][kt * T + r][a * T + c]) = rb[u];
+        *reinterpret_cast<vec_t*>(&Bs[buf][kt * T + r][at * T + c]) = rb[u];
       else             // L^A[col = r][k = c]: k contiguous per column
-        *reinterpret_cast<vec_t*>(&Bs[buf][a * T + r][kt * T + c]) = rb[u];
+        *reinterpret_cast<vec_t*>(&Bs[buf][at * T + r][kt * T + c]) = rb[u];
     }
   };
-  // MFMAs over one K step; lane group kg covers k = kg*KL .. kg*KL + KL - 1
+  // MFMAs over one K step. Lane group kg takes k = (sc * 4 + kg) * VN + e:
+  // the four groups of one sub-step sit VN apart, which keeps stage 1's
+  // row-wise B reads of lane groups 0 and 1 (and 2 and 3) on disjoint banks.
   auto compute = [&](int buf) {
 #pragma unroll
     for (int sc = 0; sc < S::KL / S::VN; ++sc) {
-      const int k0 = kg * S::KL + sc * S::VN;
+      const int k0 = (sc * 4 + kg) * S::VN;
       vec_t af[S::NBW], bf[S::NBW];
 #pragma unroll
       for (int i = 0; i < S::NBW; ++i)
@@ -184,7 +255,7 @@ __global__ __launch_bounds__(256) void band_kernel(int k, int mid, int l, int Mt
     }
   };
 
-  if (Klo <= Khi) {
+  {
     const int nsteps = (Khi - Klo) / S::BKT + 1;
     gload(Klo);
     sstore(0);
@@ -198,6 +269,10 @@ __global__ __launch_bounds__(256) void band_kernel(int k, int mid, int l, int Mt
     }
   }
 
+  // Epilogue through LDS: the macro tile is laid out as its MB x MB solver
+  // tiles (each 16 x 16 contiguous, as in HBM), then every wave moves whole
+  // tiles with one 16-byte access per lane.
+  R* Cs = reinterpret_cast<R*>(smem);
 #pragma unroll
   for (int i = 0; i < S::NBW; ++i)
 #pragma unroll
@@ -206,41 +281,48 @@ __global__ __launch_bounds__(256) void band_kernel(int k, int mid, int l, int Mt
       for (int r = 0; r < 4; ++r) {
         const int row = wr * S::WT + i * 16 + MF::row(lane, r);
         const int col = wc * S::WT + j * 16 + r16;
-        const int P = P0 + row / T, C = C0 + col / T;
-        if (P >= Mt || C >= Nt) continue;
-        const int64_t off = ((int64_t)P * Nt + C) * T * T + (row % T) * T + (col % T);
-        if (STAGE == 1) {
-          Mb[off] = acc[i][j][r];
-        } else {
-          const int s = P + C;
-          if (s >= mid && s <= l - 1) Wk[off] += acc[i][j][r];
-        }
+        Cs[((row / T) * MB + col / T) * T * T + (row % T) * T + (col % T)] = acc[i][j][r];
       }
+  __syncthreads();
+  R* out = STAGE == 1 ? Mb : Wk;
+  constexpr int VPT = S::TV / 64;  // 16-byte vectors per lane per tile
+  for (int t = wave; t < MB * MB; t += 4) {
+    const int P = P0 + t / MB, C = C0 + t % MB;
+    if (P >= Mt || C >= Nt) continue;
+    if (STAGE == 2 && (P + C < mid || P + C > l - 1)) continue;
+    vec_t* dst = reinterpret_cast<vec_t*>(out + ((int64_t)P * Nt + C) * T * T);
+    const vec_t* src = reinterpret_cast<const vec_t*>(Cs + t * T * T);
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+      const int v = q * 64 + lane;
+      vec_t x = src[v];
+      if (STAGE == 2) {
+        const vec_t w = dst[v];
+        x = x + w;
+      }
+      dst[v] = x;
+    }
+  }
 }
 
-// Macro-tile size for a node: wide bands use the big tile (more reuse per
-// LDS byte), narrow bands the small one (more workgroups, less padding).
+// Macro-tile size: 4 x 4 solver tiles (64 x 64) for float and 2 x 2 (32 x 32)
+// for double, with a wide-band option kept for tuning. Measured on the
+// 4096 x 4096 float32 solve: 64 x 64 tiles everywhere (four workgroups per
+// CU) beat 128 x 128 tiles on the wide bands (two per CU): 5.2 ms against
+// 7.6 ms for all band products.
 template <typename R> struct BandChoice;
-template <> struct BandChoice<float> { static constexpr int BIG = 8, SMALL = 4, QMIN_BIG = 32; };
+template <> struct BandChoice<float> { static constexpr int BIG = 4, SMALL = 4, QMIN_BIG = 1 << 30; };
 template <> struct BandChoice<double> { static constexpr int BIG = 4, SMALL = 2, QMIN_BIG = 32; };
 
 template <typename R, int MB>
-static hipError_t launch_band_mb(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
-                                 const R* LBp, const R* LAp, R* Mb, hipStream_t s,
-                                 hipEvent_t ev0, hipEvent_t ev1) {
+static hipError_t launch_band_mb(const SolveGeom& g, int k, int mid, int l, int stage,
+                                 const BandBuffers<R>& bb, hipStream_t s, hipEvent_t ev0,
+                                 hipEvent_t ev1) {
   const int nPb = (g.Mt + MB - 1) / MB;
   int maxw = 0;
   for (int pb = 0; pb < nPb; ++pb) {
-    const int P0 = pb * MB;
     int Clo, Chi;
-    if (stage == 1) {
-      Clo = k - (P0 + MB - 1); if (Clo < 0) Clo = 0;
-      Chi = g.Nt - 1; if (mid - 1 < Chi) Chi = mid - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
-    } else {
-      Clo = mid - (P0 + MB - 1); if (Clo < 0) Clo = 0;
-      Chi = g.Nt - 1; if (l - 1 - P0 < Chi) Chi = l - 1 - P0;
-    }
-    if (Clo > Chi) continue;
+    if (!band_cols(stage, k, mid, l, g.Nt, MB, pb, &Clo, &Chi)) continue;
     const int w = Chi / MB - Clo / MB + 1;
     if (w > maxw) maxw = w;
   }
@@ -250,41 +332,40 @@ static hipError_t launch_band_mb(const SolveGeom& g, int k, int mid, int l, int 
     if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return hipErrorUnknown;
     return hipSuccess;
   }
-  const dim3 grid(maxw, nPb), block(256);
+  BandArgs<R> a;
+  a.k = k; a.mid = mid; a.l = l; a.Mt = g.Mt; a.Nt = g.Nt;
+  a.maxw = maxw;
+  a.Wk = bb.Wk; a.LBp = bb.LBp; a.LAp = bb.LAp; a.Mb = bb.Mb;
+  const int nPb8 = (nPb + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid((unsigned)(nPb8 * maxw)), block(256);
   if (ev0 || ev1) {
     // the events are stamped by the dispatch packet itself: exact kernel time
     if (stage == 1)
-      hipExtLaunchKernelGGL((band_kernel<R, 1, MB>), grid, block, 0, s, ev0, ev1, 0, k, mid, l,
-                            g.Mt, g.Nt, Wk, LBp, LAp, Mb);
+      hipExtLaunchKernelGGL((band_kernel<R, 1, MB>), grid, block, 0, s, ev0, ev1, 0, a);
     else
-      hipExtLaunchKernelGGL((band_kernel<R, 2, MB>), grid, block, 0, s, ev0, ev1, 0, k, mid, l,
-                            g.Mt, g.Nt, Wk, LBp, LAp, Mb);
+      hipExtLaunchKernelGGL((band_kernel<R, 2, MB>), grid, block, 0, s, ev0, ev1, 0, a);
   } else if (stage == 1) {
-    hipLaunchKernelGGL((band_kernel<R, 1, MB>), grid, block, 0, s, k, mid, l, g.Mt, g.Nt, Wk,
-                       LBp, LAp, Mb);
+    hipLaunchKernelGGL((band_kernel<R, 1, MB>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((band_kernel<R, 2, MB>), grid, block, 0, s, k, mid, l, g.Mt, g.Nt, Wk,
-                       LBp, LAp, Mb);
+    hipLaunchKernelGGL((band_kernel<R, 2, MB>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <typename R>
-hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
-                            const R* LBp, const R* LAp, R* Mb, hipStream_t s, hipEvent_t ev0,
+hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage,
+                            const BandBuffers<R>& bb, hipStream_t s, hipEvent_t ev0,
                             hipEvent_t ev1) {
   if (l - k >= BandChoice<R>::QMIN_BIG)
-    return launch_band_mb<R, BandChoice<R>::BIG>(g, k, mid, l, stage, Wk, LBp, LAp, Mb, s, ev0,
-                                                 ev1);
-  return launch_band_mb<R, BandChoice<R>::SMALL>(g, k, mid, l, stage, Wk, LBp, LAp, Mb, s, ev0,
-                                                 ev1);
+    return launch_band_mb<R, BandChoice<R>::BIG>(g, k, mid, l, stage, bb, s, ev0, ev1);
+  return launch_band_mb<R, BandChoice<R>::SMALL>(g, k, mid, l, stage, bb, s, ev0, ev1);
 }
 
-template hipError_t launch_node_band<float>(const SolveGeom&, int, int, int, int, float*,
-                                            const float*, const float*, float*, hipStream_t,
-                                            hipEvent_t, hipEvent_t);
-template hipError_t launch_node_band<double>(const SolveGeom&, int, int, int, int, double*,
-                                             const double*, const double*, double*, hipStream_t,
-                                             hipEvent_t, hipEvent_t);
+template hipError_t launch_node_band<float>(const SolveGeom&, int, int, int, int,
+                                            const BandBuffers<float>&, hipStream_t, hipEvent_t,
+                                            hipEvent_t);
+template hipError_t launch_node_band<double>(const SolveGeom&, int, int, int, int,
+                                             const BandBuffers<double>&, hipStream_t, hipEvent_t,
+                                             hipEvent_t);
 
 }  // namespace bk

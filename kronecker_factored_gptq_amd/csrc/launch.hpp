@@ -37,13 +37,22 @@ template <typename R>
 hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
                        const LeafParams<R>& lp, hipStream_t s);
 
+// Buffers of the band products: W tiles (errors on finished tiles), packed
+// L^B and L^A tiles, and the stage-1 product M.
+template <typename R>
+struct BandBuffers {
+  R* Wk;
+  const R* LBp;
+  const R* LAp;
+  R* Mb;
+};
 // Internal node of the recursion over tile anti-diagonals [k, l) split at mid:
 // stage 1 or 2 of the band products. ev0 / ev1 (nullable): events stamped
 // with the kernel's start and end by its dispatch (for measurement).
 template <typename R>
-hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage, R* Wk,
-                            const R* LBp, const R* LAp, R* Mb, hipStream_t s,
-                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage,
+                            const BandBuffers<R>& bb, hipStream_t s, hipEvent_t ev0 = nullptr,
+                            hipEvent_t ev1 = nullptr);
 // Tile anti-diagonals per leaf block (updates inside a block are left-looking).
 constexpr int kLeafBlock = 8;
 
