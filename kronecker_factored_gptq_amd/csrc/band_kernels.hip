@@ -186,35 +186,38 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
       const int ti = f / S::TV;               // tile index within the operand block
       const int at = ti / S::BKT, kt = ti % S::BKT;
       const int v = f % S::TV;
+      const int vo = (v % T) * (T / S::VN) + v / T;  // 16-byte vector of row v % 16
       const int kk = kk0 + kt;
       const int P = P0 + at, C = C0 + at;
       vec_t va = VV::zero(), vb = VV::zero();
       if (STAGE == 1) {
         if (kk <= Khi && P < Mt && kk <= P)
-          va = reinterpret_cast<const vec_t*>(LBp + tri_index(P, kk) * T * T)[v];
+          va = reinterpret_cast<const vec_t*>(LBp + tri_index(P, kk) * T * T)[vo];
         const int sd = kk + C;
         if (kk <= Khi && C < Nt && sd >= k && sd < mid)
-          vb = reinterpret_cast<const vec_t*>(Wk + ((int64_t)kk * Nt + C) * T * T)[v];
+          vb = reinterpret_cast<const vec_t*>(Wk + ((int64_t)kk * Nt + C) * T * T)[vo];
       } else {
         const int sd = P + kk;
         if (kk <= Khi && P < Mt && kk <= mid - 1 && sd >= k && sd <= l - 1)
-          va = reinterpret_cast<const vec_t*>(Mb + ((int64_t)P * Nt + kk) * T * T)[v];
+          va = reinterpret_cast<const vec_t*>(Mb + ((int64_t)P * Nt + kk) * T * T)[vo];
         if (kk <= Khi && C < Nt && kk <= C)
-          vb = reinterpret_cast<const vec_t*>(LAp + tri_index(C, kk) * T * T)[v];
+          vb = reinterpret_cast<const vec_t*>(LAp + tri_index(C, kk) * T * T)[vo];
       }
       ra[u] = va;
       rb[u] = vb;
     }
   };
-  // registers -> LDS buffer
+  // registers -> LDS buffer. Vector v of a tile holds row v % 16, columns
+  // VN * (v / 16) ..: eight consecutive lanes then write eight different rows,
+  // which the padded row strides place on eight different bank groups.
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < S::NV; ++u) {
       const int f = u * 256 + tid;
       const int ti = f / S::TV;
       const int at = ti / S::BKT, kt = ti % S::BKT;
-      const int e0 = (f % S::TV) * S::VN;
-      const int r = e0 / T, c = e0 % T;
+      const int v = f % S::TV;
+      const int r = v % T, c = (v / T) * S::VN;
       *reinterpret_cast<vec_t*>(&As[buf][at * T + r][kt * T + c]) = ra[u];
       if (STAGE == 1)  // E[k = r][col = c]: keep rows of k
         *reinterpret_cast<vec_t*>(&Bs[buf][kt * T + r][at * T + c]) = rb[u];
