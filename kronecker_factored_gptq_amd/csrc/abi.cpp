@@ -282,7 +282,7 @@ int loss_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V, i
   g2.alpha = 1.0;
   g2.dot[0] = BE; g2.lddot = n; g2.partial[0] = part;
   if (launch_gemm64(g2, s) != hipSuccess) return BAKRON_EHIP;
-  if (launch_sum_partials(part, lay.nparts, loss, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_sum_partials(part, gemm64_partials(g2), loss, s) != hipSuccess) return BAKRON_EHIP;
   return BAKRON_OK;
 }
 

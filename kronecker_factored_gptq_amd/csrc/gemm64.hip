@@ -1,15 +1,16 @@
 // Float64 MFMA GEMM for the factorisation and the loss (gfx950).
 //
-// C = alpha * A * op(B) + beta * C over BM x BM output blocks (BM = 64 or
-// 128), 256 threads in four waves (2 x 2), each wave a (BM/2)^2 sub-block of
-// v_mfma_f64_16x16x4 blocks; K advances 16 at a time through double-buffered
-// LDS; operands move as 16-byte vectors when their rows are 16-byte aligned.
-// The large blocks serve the big products (more MFMA work per LDS byte), the
-// small ones the small products (more workgroups). Options: only lower output blocks (symmetric rank-k update), A lower
-// triangular (K ends with the row block), B lower triangular (K ends with the
-// column block when op(B) = B^T, starts with it when op(B) = B), a batch of
-// two independent problems of one shape (grid z), and a dot epilogue that
-// reduces sum(C_block .* D_block) per block instead of storing C (loss).
+// C = alpha * A * op(B) + beta * C with v_mfma_f64_16x16x4 blocks; K advances
+// 16 at a time through double-buffered LDS. Two kernels: 64 x 64 output
+// blocks on four waves (2 x 2), and 128 x 128 blocks on eight waves (2 x 4,
+// twice the MFMA work per loaded byte) for the products that still give at
+// least 256 such blocks. Options: only lower output blocks (symmetric rank-k
+// update), A lower triangular (K ends with the row block), B lower
+// triangular (K ends with the column block when op(B) = B^T, starts with it
+// when op(B) = B), a batch of two independent problems of one shape (grid
+// z), and a dot epilogue that reduces sum(C_block .* D_block) per block
+// instead of storing C (loss). With a triangular operand the blocks with the
+// longest K ranges are dispatched first.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -35,7 +36,9 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int64_t bm = blockIdx.y, bn = blockIdx.x;
+  // with a triangular operand the longest K ranges are dispatched first
+  const int64_t bm = a.a_lower ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
+  const int64_t bn = (a.b_lower && a.transB) ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
   const int z = blockIdx.z;
   const double* __restrict__ Ap = a.A[z];
   const double* __restrict__ Bp = a.B[z];
@@ -211,14 +214,180 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
       }
 }
 
-// Block edge for a product. The 128 variant runs at one wave per SIMD
-// (register-bound) and measured slower than 64 on the 2048^3 and 4096^3
-// products, so 64 is used throughout; the variant stays compiled for tuning.
-static int gemm64_block(int64_t, int64_t, int) { return 64; }
+// Large-tile variant: BM x BN output blocks, WM x WN waves (64 * WM * WN
+// threads), each wave a (BM / WM) x (BN / WN) sub-block of 16 x 16 MFMA
+// blocks; otherwise the same options and the same K loop as gemm64_kernel.
+// Twice the MFMA work per loaded byte of the 64 x 64 kernel.
+template <int BM, int BN, int WM, int WN, bool TRI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
+  typedef Mfma<double> MF;
+  typedef MF::acc_t acc_t;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN, NBM = TM / 16, NBN = TN / 16;
+  constexpr int PA = BM * GK / NT, PB = BN * GK / NT;
+  static_assert(PA >= 1 && PB >= 1 && BM % GTRI == 0 && BN % GTRI == 0, "tile shape");
+  __shared__ double As[2][BM][GLD];
+  __shared__ double Bs[2][BN][GLD];
+  __shared__ double red[WM * WN];
 
-int64_t gemm64_num_blocks(int64_t M, int64_t N) {
-  const int gb = gemm64_block(M, N, 1);
-  return ((M + gb - 1) / gb) * ((N + gb - 1) / gb);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int r16 = lane & 15, kg = lane >> 4;
+  // with a triangular operand the longest K ranges are dispatched first
+  const int64_t bm = a.a_lower ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
+  const int64_t bn = (a.b_lower && a.transB) ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
+  const int z = blockIdx.z;
+  const double* __restrict__ Ap = a.A[z];
+  const double* __restrict__ Bp = a.B[z];
+  double* Cp = a.C[z];
+  const int64_t row0 = bm * BM, col0 = bn * BN;
+  const bool skip = a.lower_out && col0 >= row0 + BM;
+
+  acc_t acc[NBM][NBN];
+#pragma unroll
+  for (int i = 0; i < NBM; ++i)
+#pragma unroll
+    for (int j = 0; j < NBN; ++j) acc[i][j] = MF::zero();
+
+  int64_t kend = a.K, kbeg = 0;
+  if (a.a_lower && row0 + BM < kend) kend = row0 + BM;
+  if (a.b_lower) {
+    if (a.transB) {
+      if (col0 + BN < kend) kend = col0 + BN;
+    } else {
+      kbeg = col0;
+    }
+  }
+  auto kin = [&](int64_t gk) { return gk < kend && gk >= kbeg; };
+  auto ain = [&](int64_t gr, int64_t gk) {
+    return gr < a.M && kin(gk) && (!TRI || !a.a_lower || gk < (gr / GTRI + 1) * GTRI);
+  };
+  auto bin = [&](int64_t gn, int64_t gk) {
+    if (gn >= a.N || !kin(gk)) return false;
+    if (!TRI || !a.b_lower) return true;
+    return a.transB ? gk < (gn / GTRI + 1) * GTRI : gk >= (gn / GTRI) * GTRI;
+  };
+  double ra[PA], rb[PB];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int u = 0; u < PA; ++u) {
+      const int e = u * NT + tid;
+      const int r = e / GK, c = e % GK;
+      const int64_t gr = row0 + r, gk = k0 + c;
+      ra[u] = ain(gr, gk) ? Ap[gr * a.lda + gk] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int e = u * NT + tid;
+      if (a.transB) {
+        const int r = e / GK, c = e % GK;
+        const int64_t gn = col0 + r, gk = k0 + c;
+        rb[u] = bin(gn, gk) ? Bp[gn * a.ldb + gk] : 0.0;
+      } else {
+        const int kr = e / BN, cc = e % BN;
+        const int64_t gk = k0 + kr, gn = col0 + cc;
+        rb[u] = bin(gn, gk) ? Bp[gk * a.ldb + gn] : 0.0;
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PA; ++u) {
+      const int e = u * NT + tid;
+      As[buf][e / GK][e % GK] = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int e = u * NT + tid;
+      if (a.transB) Bs[buf][e / GK][e % GK] = rb[u];
+      else Bs[buf][e % BN][e / BN] = rb[u];
+    }
+  };
+
+  if (!skip && kend > kbeg) {
+    const int64_t k00 = kbeg / GK * GK;
+    gload(k00);
+    sstore(0);
+    __syncthreads();
+    const int64_t nk = (kend - k00 + GK - 1) / GK;
+    for (int64_t it = 0; it < nk; ++it) {
+      const int buf = (int)(it & 1);
+      if (it + 1 < nk) gload(k00 + (it + 1) * GK);
+#pragma unroll
+      for (int st = 0; st < GK / 4; ++st) {
+        double af[NBM], bf[NBN];
+#pragma unroll
+        for (int i = 0; i < NBM; ++i) af[i] = As[buf][wm * TM + i * 16 + r16][4 * kg + st];
+#pragma unroll
+        for (int j = 0; j < NBN; ++j) bf[j] = Bs[buf][wn * TN + j * 16 + r16][4 * kg + st];
+#pragma unroll
+        for (int i = 0; i < NBM; ++i)
+#pragma unroll
+          for (int j = 0; j < NBN; ++j) acc[i][j] = MF::mma(af[i], bf[j], acc[i][j]);
+      }
+      if (it + 1 < nk) sstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (a.dot[0]) {
+    double part = 0.0;
+    if (!skip) {
+#pragma unroll
+      for (int i = 0; i < NBM; ++i)
+#pragma unroll
+        for (int j = 0; j < NBN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t gr = row0 + wm * TM + i * 16 + MF::row(lane, r);
+            const int64_t gc = col0 + wn * TN + j * 16 + r16;
+            if (gr < a.M && gc < a.N) part += a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
+          }
+    }
+    // fixed-order reduction: wave butterfly, then the waves in order
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (lane == 0) red[wave] = part;
+    __syncthreads();
+    if (tid == 0) {
+      double t = red[0];
+      for (int q = 1; q < WM * WN; ++q) t += red[q];
+      a.partial[z][bm * gridDim.x + bn] = t;
+    }
+    return;
+  }
+  if (skip) return;
+#pragma unroll
+  for (int i = 0; i < NBM; ++i)
+#pragma unroll
+    for (int j = 0; j < NBN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t gr = row0 + wm * TM + i * 16 + MF::row(lane, r);
+        const int64_t gc = col0 + wn * TN + j * 16 + r16;
+        if (a.lower_out && gc / GTRI > gr / GTRI) continue;
+        if (gr < a.M && gc < a.N) {
+          double v = a.alpha * acc[i][j][r];
+          if (a.beta != 0.0) v += a.beta * Cp[gr * a.ldc + gc];
+          Cp[gr * a.ldc + gc] = v;
+        }
+      }
+}
+
+// Kernel choice: the 128 x 128 eight-wave kernel when it still gives at
+// least 256 workgroups, else the 64 x 64 kernel (more workgroups for the
+// smaller products).
+static bool use_big(const Gemm64Args& a) {
+  const int64_t t = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.batch;
+  return t >= 256;
+}
+
+int64_t gemm64_num_blocks(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 63) / 64); }
+
+int64_t gemm64_partials(const Gemm64Args& a) {
+  if (use_big(a)) return ((a.M + 127) / 128) * ((a.N + 127) / 128);
+  return gemm64_num_blocks(a.M, a.N);
 }
 
 template <int GB>
@@ -245,7 +414,14 @@ hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
   for (int z = 0; z < a.batch; ++z)
     vec = vec && (reinterpret_cast<uintptr_t>(a.A[z]) % 16 == 0) &&
           (reinterpret_cast<uintptr_t>(a.B[z]) % 16 == 0);
-  if (gemm64_block(a.M, a.N, a.batch) == 128) return launch_gb<128>(a, vec, s);
+  if (use_big(a)) {
+    dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)((a.M + 127) / 128), (unsigned)a.batch);
+    if (a.a_lower || a.b_lower)
+      hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, 4, true>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, 4, false>), grid, dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
   return launch_gb<64>(a, vec, s);
 }
 
