@@ -20,6 +20,8 @@
 // order (k = row) and are read one element per MFMA.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -53,6 +55,9 @@ struct BandShape {
   static constexpr int TV = T * T / VN;          // vectors per solver tile
   static constexpr int NV = MB * BKT * TV / 256; // vectors per thread per operand per K step
   static constexpr int KL = BK / 4;              // k values per lane per K step
+  // global loads run PD K steps ahead (register ring): the small float tiles
+  // do little MFMA work per step, so one step does not cover the latency
+  static constexpr int PD = (sizeof(R) == 4 && MB <= 4) ? 2 : 1;
   static_assert(NV >= 1 && (MB * BKT * TV) % 256 == 0, "macro tile too small for 256 threads");
 };
 
@@ -176,10 +181,11 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
 #pragma unroll
     for (int j = 0; j < S::NBW; ++j) acc[i][j] = MF::zero();
 
-  vec_t ra[S::NV], rb[S::NV];
+  vec_t ra[S::PD][S::NV], rb[S::PD][S::NV];
 
-  // global -> registers for the K step starting at solver tile kk0
-  auto gload = [&](int kk0) {
+  // global -> register set SET for the K step starting at solver tile kk0
+  auto gload = [&](int kk0, auto SETC) {
+    constexpr int set = decltype(SETC)::value;
 #pragma unroll
     for (int u = 0; u < S::NV; ++u) {
       const int f = u * 256 + tid;
@@ -203,14 +209,15 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
         if (kk <= Khi && C < Nt && kk <= C)
           vb = reinterpret_cast<const vec_t*>(LAp + tri_index(C, kk) * T * T)[vo];
       }
-      ra[u] = va;
-      rb[u] = vb;
+      ra[set][u] = va;
+      rb[set][u] = vb;
     }
   };
   // registers -> LDS buffer. Vector v of a tile holds row v % 16, columns
   // VN * (v / 16) ..: eight consecutive lanes then write eight different rows,
   // which the padded row strides place on eight different bank groups.
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, auto SETC) {
+    constexpr int set = decltype(SETC)::value;
 #pragma unroll
     for (int u = 0; u < S::NV; ++u) {
       const int f = u * 256 + tid;
@@ -218,11 +225,11 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
       const int at = ti / S::BKT, kt = ti % S::BKT;
       const int v = f % S::TV;
       const int r = v % T, c = (v / T) * S::VN;
-      *reinterpret_cast<vec_t*>(&As[buf][at * T + r][kt * T + c]) = ra[u];
+      *reinterpret_cast<vec_t*>(&As[buf][at * T + r][kt * T + c]) = ra[set][u];
       if (STAGE == 1)  // E[k = r][col = c]: keep rows of k
-        *reinterpret_cast<vec_t*>(&Bs[buf][kt * T + r][at * T + c]) = rb[u];
+        *reinterpret_cast<vec_t*>(&Bs[buf][kt * T + r][at * T + c]) = rb[set][u];
       else             // L^A[col = r][k = c]: k contiguous per column
-        *reinterpret_cast<vec_t*>(&Bs[buf][at * T + r][kt * T + c]) = rb[u];
+        *reinterpret_cast<vec_t*>(&Bs[buf][at * T + r][kt * T + c]) = rb[set][u];
     }
   };
   // MFMAs over one K step. Lane group kg takes k = (sc * 4 + kg) * VN + e:
@@ -259,16 +266,27 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
   };
 
   {
+    // register set it % PD holds K step it; LDS buffer it % 2 is computed
+    typedef std::integral_constant<int, 0> I0;
+    typedef std::integral_constant<int, (S::PD > 1 ? 1 : 0)> I1;
+    typedef std::integral_constant<int, (S::PD > 2 ? 2 : 0)> I2;
     const int nsteps = (Khi - Klo) / S::BKT + 1;
-    gload(Klo);
-    sstore(0);
+    gload(Klo, I0());
+    if (S::PD > 1 && 1 < nsteps) gload(Klo + S::BKT, I1());
+    if (S::PD > 2 && 2 < nsteps) gload(Klo + 2 * S::BKT, I2());
+    sstore(0, I0());
     __syncthreads();
-    for (int it = 0; it < nsteps; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < nsteps) gload(Klo + (it + 1) * S::BKT);
-      compute(buf);
-      if (it + 1 < nsteps) sstore(buf ^ 1);
+    auto step = [&](auto PH, int it) {
+      constexpr int ph = decltype(PH)::value;
+      if (it + S::PD < nsteps) gload(Klo + (it + S::PD) * S::BKT, PH);
+      compute(it & 1);
+      if (it + 1 < nsteps) sstore((it + 1) & 1, std::integral_constant<int, (ph + 1) % S::PD>());
       __syncthreads();
+    };
+    for (int it0 = 0; it0 < nsteps; it0 += S::PD) {
+      step(I0(), it0);
+      if (S::PD > 1 && it0 + 1 < nsteps) step(I1(), it0 + 1);
+      if (S::PD > 2 && it0 + 2 < nsteps) step(I2(), it0 + 2);
     }
   }
 
