@@ -33,8 +33,8 @@ PEAK_FP64_MFMA_TFLOPS = 78.6    # MI355X dense FP64 matrix
 # over one step of this workload, scaled by a plain 512 MiB copy (FETCH_SIZE
 # x2.0, WRITE_SIZE x1.0), valid for the band-kernel source with this hash
 # only: after any change to that file the figure is reported as null.
-BAND_TRAFFIC = {"sha256": "012b270df02b353d22f4e3c09c1d60dbf1a0070e7c56687becd8a46fd043d5a5",
-                "bytes_per_launch": 5.7622e7, "launches": 126,
+BAND_TRAFFIC = {"sha256": "18d74fc48c9d67529b86108fe925b33e08d0d4be18c356ecfd395f2b0c463430",
+                "bytes_per_launch": 6.5805e7, "launches": 126,
                 "summary": "profiles/band_kernel_attn4096_f32_counters.md"}
 METRIC = "weights quantized/s (m·n/solve-time) + % FP32 MFMA peak, 4096×4096"
 
