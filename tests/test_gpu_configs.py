@@ -1,0 +1,158 @@
+"""The other benchmark workloads at their full sizes, through the C ABI.
+
+* MLP shapes (14336 x 4096 and 4096 x 14336, float32, 3-bit {-4..3}, per-row
+  absmax/3 scales): the whole GPU path runs at full size. Entry (i, j) of the
+  solve depends only on entries (i', j') with i' <= i and j' <= j (errors flow
+  down and to the right, §3.3), so the leading a x b block of the full-size
+  result must equal the oracle's solve of the leading block on the same
+  inputs: that block is checked against the float64 oracle. Every output is
+  checked through a property that holds at any size: the loss of the GPU's
+  codes (float64 loss kernel, from A and B) equals the sum of the recorded
+  errors E_ij^2 / (d^B_i d^A_j)^2 (the identity behind Theorem 3.3, pinned on
+  the CPU against the brute-force quadratic form).
+* 28 small k/v projections (1024 x 2048, float32, Wishart Hessians) solved
+  back to back on four streams, then the same 28 with B = I (one-sided GPTQ):
+  every matrix is checked through the loss identity, three of each set against
+  the float64 oracle on the whole matrix (replay validity: a float32 near-tie
+  flip may cascade, as at 4096 x 4096), and the stream results are compared
+  with a one-stream rerun (bit-identical).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import config4, config5
+
+from parity_util import (Inputs, assert_fp32_parity, assert_fp32_validity, fp32_parity,
+                         oracle_solve, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_path(bk, p, hi):
+    """factor + row scales + solve (with pre-rounding values) + loss on the GPU."""
+    W, A, B = to_dev(p.W), to_dev(p.A), to_dev(p.B)
+    LA, LB, dA, dB = bk.factor(A, B)
+    s = bk.row_scales(W, hi)
+    V, Wt = bk.solve(W, LA, LB, p.alphabet, s, return_wt=True)
+    loss = bk.loss(W, V, A, B, s)
+    torch.cuda.synchronize()
+    host = lambda x: x.cpu().numpy()
+    return dict(LA=host(LA), LB=host(LB), dA=host(dA).astype(np.float64),
+                dB=host(dB).astype(np.float64), s=host(s), V=host(V), Wt=host(Wt), loss=loss)
+
+
+def _loss_identity_rel(out):
+    E = out["s"].astype(np.float64)[:, None] * out["V"].astype(np.float64) - out["Wt"].astype(np.float64)
+    ident = O.loss_from_errors(E, out["dA"], out["dB"])
+    return abs(ident - out["loss"]) / abs(out["loss"])
+
+
+def _block_hessian(Lhat, d, b):
+    """Hessian side whose normalised factor is the leading b x b block of
+    Lhat: L = Lhat diag(d) = Cholesky(H^-1), and the leading block of a
+    Cholesky factor is the Cholesky factor of the leading block, so the block
+    problem's side is ((L L^T)[:b, :b])^-1 = (L_b L_b^T)^-1."""
+    Lb = Lhat[:b, :b].astype(np.float64) * np.asarray(d[:b], dtype=np.float64)[None, :]
+    H = np.linalg.inv(Lb @ Lb.T)
+    return 0.5 * (H + H.T)
+
+
+def _block_inputs(p, out, a, b):
+    W = np.ascontiguousarray(p.W[:a, :b])
+    LA = np.ascontiguousarray(out["LA"][:b, :b])
+    LB = np.ascontiguousarray(out["LB"][:a, :a])
+    s = np.ascontiguousarray(out["s"][:a])
+    inp = Inputs(W, LA, LB, out["dA"][:b], out["dB"][:a], s, O.SCALE_ROW, tuple(p.alphabet))
+    return inp
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_mlp_full_size(gpu_lib, which):
+    p = config4(which)
+    m, n = p.W.shape
+    out = _gpu_path(gpu_lib, p, p.scale_hi)
+    print(p.name, "loss", out["loss"])
+    # scales: the GPU rule equals the oracle's bit for bit
+    np.testing.assert_array_equal(out["s"], O.row_scales(p.W, p.scale_hi, np.float32))
+    lo, hi_, _ = p.alphabet
+    assert out["V"].min() >= lo and out["V"].max() <= hi_
+    # factors: unit diagonal, zero upper triangle
+    for L in (out["LA"], out["LB"]):
+        assert np.all(np.diag(L) == 1.0)
+        assert not np.any(np.triu(L, 1))
+    # every output: loss identity (float32 recorded errors, float64 loss)
+    rel = _loss_identity_rel(out)
+    print("loss identity rel", rel)
+    assert rel <= 1e-3
+    # leading block against the float64 oracle on the same inputs
+    a = b = 512
+    inp = _block_inputs(p, out, a, b)
+    ref = oracle_solve(inp)
+    Vb, Wtb = out["V"][:a, :b], out["Wt"][:a, :b]
+    rep = fp32_parity(inp, Vb, Wtb, ref, _block_hessian(out["LA"], out["dA"], b),
+                      _block_hessian(out["LB"], out["dB"], a))
+    print(rep)
+    assert_fp32_parity(rep)
+    assert rep.max_dev <= 1e-4, rep
+
+
+def _kv_batch(bk, b_identity, streams):
+    """The 28 projections: factor + scales + solve + loss, round-robin on the
+    given streams (None: the current stream)."""
+    probs = [config5(i, b_identity=b_identity) for i in range(28)]
+    outs = [None] * 28
+    for i, p in enumerate(probs):
+        st = streams[i % len(streams)] if streams else torch.cuda.current_stream()
+        with torch.cuda.stream(st):
+            W, A, B = to_dev(p.W), to_dev(p.A), to_dev(p.B)
+            LA, LB, dA, dB = bk.factor(A, B)
+            s = bk.row_scales(W, p.scale_hi)
+            V, Wt = bk.solve(W, LA, LB, p.alphabet, s, return_wt=True)
+            outs[i] = (W, A, B, LA, LB, dA, dB, s, V, Wt)
+    torch.cuda.synchronize()
+    res = []
+    for p, (W, A, B, LA, LB, dA, dB, s, V, Wt) in zip(probs, outs):
+        loss = bk.loss(W, V, A, B, s)
+        host = lambda x: x.cpu().numpy()
+        res.append(dict(LA=host(LA), LB=host(LB), dA=host(dA).astype(np.float64),
+                        dB=host(dB).astype(np.float64), s=host(s), V=host(V), Wt=host(Wt),
+                        loss=loss))
+    return probs, res
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("b_identity", [False, True])
+def test_kv_batch_on_streams(gpu_lib, b_identity):
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    probs, res = _kv_batch(gpu_lib, b_identity, streams)
+    for p, out in zip(probs, res):
+        lo, hi_, _ = p.alphabet
+        assert out["V"].min() >= lo and out["V"].max() <= hi_, p.name
+        rel = _loss_identity_rel(out)
+        assert rel <= 1e-3, (p.name, rel)
+        if b_identity:
+            # B = I: the output-side factor is exactly the identity
+            assert np.array_equal(out["LB"], np.eye(p.W.shape[0], dtype=np.float32)), p.name
+            assert np.all(out["dB"] == 1.0), p.name
+    # three matrices of the set against the float64 oracle on the whole matrix
+    for i in (0, 13, 27):
+        p, out = probs[i], res[i]
+        m, n = p.W.shape
+        inp = _block_inputs(p, out, m, n)
+        ref = oracle_solve(inp)
+        rep = fp32_parity(inp, out["V"], out["Wt"], ref, p.A.astype(np.float64),
+                          p.B.astype(np.float64))
+        print(p.name, rep)
+        # a float32 near-tie flip cascades into its downstream quadrant (the
+        # 4096 x 4096 test explains it): raw agreement is reported, validity
+        # is asserted
+        assert_fp32_validity(rep)
+        assert rep.max_dev <= 1e-4, rep
+    # the stream run equals a one-stream rerun, bit for bit
+    _, seq = _kv_batch(gpu_lib, b_identity, None)
+    for a_, b_ in zip(res, seq):
+        assert np.array_equal(a_["V"], b_["V"]) and np.array_equal(a_["Wt"], b_["Wt"])
+        assert a_["loss"] == b_["loss"]
