@@ -26,6 +26,7 @@ namespace bk {
 
 namespace {
 constexpr int NB = 64;  // Cholesky panel width
+constexpr int kLeafCols = 4;  // columns per barrier step of the leaf (8 measured no faster)
 }
 
 // X[i][j] = A[n-1-j][n-1-i] for i >= j (the lower triangle of J A J read from
@@ -57,19 +58,27 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* 
 // X[off.., off..] (bs <= 64) and its inverse Y = C^-1; Y[off.., off..]
 // receives C^-1 (zeros above the diagonal). Thread (ty, tx) of a 16 x 16
 // grid keeps the 4 x 4 patch rows 4ty.., columns 4tx.. of both C and Y in
-// registers. Right-looking, one barrier per column j: the owners publish the
-// raw pivot C[j][j], the raw column j of C below it and the raw row j of Y;
-// after the barrier every thread forms d = sqrt(pivot) and scales what it
-// read by 1/d, then updates its patch: C[i][c] -= C[i][j] C[c][j]
-// (j < c <= i) and Y[i][c] -= C[i][j] Y[j][c] (i > j). Published values are
-// double-buffered by the parity of j. A pivot that is not positive and
-// finite records off + j in *info (smallest wins) and the factorisation
-// continues with NaN. blockIdx.x selects the side.
+// registers; rows and columns past bs are padded with the identity.
+// Right-looking, NC columns j .. j+NC-1 per step (whole patch columns) and
+// one barrier per step: the owners publish the raw NC x NC pivot block, the
+// raw columns j.. and the raw rows j.. of Y; after the barrier every thread
+// forms the pivot block's Cholesky factor l (NC x NC lower) and, by forward
+// substitution,
+//   C[i][j+q] = (X[i][j+q] - sum_{p<q} C[i][j+p] l[q][p]) / l[q][q],
+//   Y[j+q]    = (Y[j+q]    - sum_{p<q} l[q][p] Y[j+p]) / l[q][q]   (rows),
+// then updates its patch with the rank-NC terms
+//   C[i][c] -= sum_q C[i][j+q] C[c][j+q]   (j + NC <= c <= i),
+//   Y[i][c] -= sum_q C[i][j+q] Y[j+q][c]   (i >= j + NC).
+// Published values are double-buffered by the parity of the step. A pivot
+// that is not positive and finite records off + j + q in *info (smallest
+// wins) and the factorisation continues with NaN.
+template <int NC>
 __global__ __launch_bounds__(256) void chol_inv_leaf_kernel(FactorSide s0, FactorSide s1,
                                                             int64_t n, int64_t off, int bs) {
-  __shared__ double piv_s[2];
-  __shared__ double colj[2][64];
-  __shared__ double rowj[2][64];
+  constexpr int PC = NC / 4;  // patch columns per step
+  __shared__ double pblk[2][NC][NC];
+  __shared__ double colp[2][NC][64];
+  __shared__ double rowp[2][NC][64];
   const FactorSide S = blockIdx.x == 0 ? s0 : s1;
   const int tid = threadIdx.x;
   const int ty = tid >> 4, tx = tid & 15;
@@ -79,60 +88,112 @@ __global__ __launch_bounds__(256) void chol_inv_leaf_kernel(FactorSide s0, Facto
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int i = 4 * ty + a, c = 4 * tx + b;
-      Lr[a][b] = (i < bs && c <= i) ? S.X[(off + i) * n + off + c] : 0.0;
+      double v = 0.0;
+      if (i < bs && c < bs) v = c <= i ? S.X[(off + i) * n + off + c] : 0.0;
+      else if (i == c) v = 1.0;
+      Lr[a][b] = v;
       Yr[a][b] = (i == c) ? 1.0 : 0.0;
     }
-  for (int j = 0; j < bs; ++j) {
-    const int jq = j >> 2, jr = j & 3, pb = j & 1;
-    // publish raw values of step j
-    if (ty == jq && tx == jq) {
+  const int steps = (bs + NC - 1) / NC;
+  for (int st = 0; st < steps; ++st) {
+    const int j = NC * st, pb = st & 1;
+    const int q0 = PC * st;            // first patch row / column of the step
+    const bool ownc = tx >= q0 && tx < q0 + PC, ownr = ty >= q0 && ty < q0 + PC;
+    // publish the raw pivot block, columns j..j+NC-1 and rows j..j+NC-1 of Y
+    if (ownc && ownr) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
-        if (a == jr) piv_s[pb] = Lr[a][a];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) pblk[pb][4 * (ty - q0) + a][4 * (tx - q0) + b] = Lr[a][b];
     }
-    if (tx == jq) {
+    if (ownc) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) colp[pb][4 * (tx - q0) + b][4 * ty + a] = Lr[a][b];
+    }
+    if (ownr) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) rowp[pb][4 * (ty - q0) + a][4 * tx + b] = Yr[a][b];
+    }
+    __syncthreads();
+    // Cholesky factor of the NC x NC pivot block (every thread, same values)
+    double l[NC][NC], dinv[NC];
+    int bad = -1;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+#pragma unroll
+      for (int p = 0; p < NC; ++p) {
+        if (p > q) continue;
+        double v = pblk[pb][q][p];
+#pragma unroll
+        for (int r = 0; r < NC; ++r)
+          if (r < p) v -= l[q][r] * l[p][r];
+        if (p < q) {
+          l[q][p] = v * dinv[p];
+        } else {
+          const bool ok = v > 0.0 && v < INFINITY;
+          if (!ok && bad < 0) bad = q;
+          const double sq = __builtin_sqrt(v);
+          l[q][q] = sq;
+          dinv[q] = ok ? 1.0 / sq : __builtin_nan("");
+        }
+      }
+    }
+    if (tid == 0 && bad >= 0 && j + bad < bs) atomicMin(S.info, (int32_t)(off + j + bad));
+    // columns j.. of C at rows i and at rows c (zero on and above the pivot
+    // block), and rows j.. of Y at columns c (final after this step)
+    double ci[4][NC], cc[4][NC], yq[NC][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int i = 4 * ty + a, c = 4 * tx + a;
+#pragma unroll
+      for (int q = 0; q < NC; ++q) {
+        double vi = colp[pb][q][i], vc = colp[pb][q][c];
+#pragma unroll
+        for (int p = 0; p < NC; ++p)
+          if (p < q) { vi -= ci[a][p] * l[q][p]; vc -= cc[a][p] * l[q][p]; }
+        ci[a][q] = vi * dinv[q];
+        cc[a][q] = vc * dinv[q];
+      }
+#pragma unroll
+      for (int q = 0; q < NC; ++q) {
+        if (i < j + NC) ci[a][q] = 0.0;
+        if (c < j + NC) cc[a][q] = 0.0;
+      }
+#pragma unroll
+      for (int q = 0; q < NC; ++q) {
+        double v = rowp[pb][q][c];
+#pragma unroll
+        for (int p = 0; p < NC; ++p)
+          if (p < q) v -= l[q][p] * yq[p][a];
+        yq[q][a] = c < j + NC ? v * dinv[q] : 0.0;
+      }
+    }
+    if (ownr) {  // rows j.. of Y are final now
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          if (b == jr) colj[pb][4 * ty + a] = Lr[a][b];
-    }
-    if (ty == jq) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        if (a == jr) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) rowj[pb][4 * tx + b] = Yr[a][b];
-        }
-    }
-    __syncthreads();
-    const double piv = piv_s[pb];
-    const bool ok = piv > 0.0 && piv < INFINITY;
-    if (tid == 0 && !ok) atomicMin(S.info, (int32_t)(off + j));
-    const double inv = ok ? 1.0 / __builtin_sqrt(piv) : __builtin_nan("");
-    double ci[4], cc[4], yr[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int i = 4 * ty + a, c = 4 * tx + a;
-      ci[a] = (i > j && i < bs) ? colj[pb][i] * inv : 0.0;
-      cc[a] = (c > j && c < bs) ? colj[pb][c] * inv : 0.0;
-      yr[a] = c <= j ? rowj[pb][c] * inv : 0.0;
-    }
-    if (ty == jq) {  // row j of Y is final now
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        if (a == jr) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) Yr[a][b] = yr[b];
-        }
+          for (int pr = 0; pr < PC; ++pr)
+            if (ty - q0 == pr) Yr[a][b] = yq[4 * pr + a][b];
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int i = 4 * ty + a, c = 4 * tx + b;
-        if (c <= i) Lr[a][b] -= ci[a] * cc[b];  // zero unless j < c <= i < bs
-        Yr[a][b] -= ci[a] * yr[b];              // zero unless i > j and c <= j
+        double dl = 0.0, dy = 0.0;
+#pragma unroll
+        for (int q = 0; q < NC; ++q) {
+          dl += ci[a][q] * cc[b][q];
+          dy += ci[a][q] * yq[q][b];
+        }
+        if (c <= i) Lr[a][b] -= dl;  // zero unless j + NC <= c <= i
+        Yr[a][b] -= dy;              // zero unless i >= j + NC
       }
   }
 #pragma unroll
@@ -229,7 +290,7 @@ static hipError_t chol_inv_rec(int64_t n, const FactorSide* sd, int ns, int64_t 
                                hipStream_t s) {
   hipError_t err;
   if (len <= NB) {
-    hipLaunchKernelGGL(chol_inv_leaf_kernel, dim3(ns), dim3(256), 0, s, sd[0],
+    hipLaunchKernelGGL(chol_inv_leaf_kernel<kLeafCols>, dim3(ns), dim3(256), 0, s, sd[0],
                        sd[ns > 1 ? 1 : 0], n, off, (int)len);
     return hipGetLastError();
   }
