@@ -184,7 +184,11 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
           for (int r = 0; r < 4; ++r) {
             const int64_t gr = row0 + wr * WT + i * 16 + MF::row(lane, r);
             const int64_t gc = col0 + wc * WT + j * 16 + r16;
-            if (gr < a.M && gc < a.N) part += a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
+            if (gr < a.M && gc < a.N) {
+              double wgt = 1.0;
+              if (a.sym_dot) wgt = gr > gc ? 2.0 : (gr == gc ? 1.0 : 0.0);
+              part += wgt * a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
+            }
           }
     }
     // fixed-order reduction: wave butterfly, then the four waves in order
@@ -342,7 +346,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
           for (int r = 0; r < 4; ++r) {
             const int64_t gr = row0 + wm * TM + i * 16 + MF::row(lane, r);
             const int64_t gc = col0 + wn * TN + j * 16 + r16;
-            if (gr < a.M && gc < a.N) part += a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
+            if (gr < a.M && gc < a.N) {
+              double wgt = 1.0;
+              if (a.sym_dot) wgt = gr > gc ? 2.0 : (gr == gc ? 1.0 : 0.0);
+              part += wgt * a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
+            }
           }
     }
     // fixed-order reduction: wave butterfly, then the waves in order
@@ -377,8 +385,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
 
 // Kernel choice: the 128 x 128 eight-wave kernel when it still gives at
 // least 256 workgroups, else the 64 x 64 kernel (more workgroups for the
-// smaller products).
+// smaller products and the lower-block ones).
 static bool use_big(const Gemm64Args& a) {
+  // lower-block products (half of the blocks idle) balance better on the
+  // finer 64 x 64 grid
+  if (a.lower_out) return false;
   const int64_t t = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.batch;
   return t >= 256;
 }

@@ -87,7 +87,8 @@ hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t v, hipStream_t s);
 // triangular: with transB the column block c only needs k < (c + 1) * 64,
 // without it only k >= c * 64.
 // dot[0] != nullptr: instead of storing C, the block's sum of
-// alpha (A op(B)) .* dot is written to partial[z][block] (C unused).
+// alpha (A op(B)) .* dot is written to partial[z][block] (C unused); with
+// sym_dot the elements are weighted 2 below the diagonal, 1 on it, 0 above.
 struct Gemm64Args {
   int64_t M, N, K;
   const double* A[2];
@@ -105,6 +106,9 @@ struct Gemm64Args {
   int64_t lddot;
   double* partial[2];
   int batch;
+  // dot epilogue of a symmetric product computed on its lower blocks only:
+  // element (r, c) counts twice below the diagonal, once on it, not above
+  int sym_dot;
 };
 hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s);
 // Upper bound of the per-block partials of a dot-epilogue product of this
