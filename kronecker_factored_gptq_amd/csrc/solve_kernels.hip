@@ -128,18 +128,34 @@ __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt
       const int Ilo = K0 - J > 0 ? K0 - J : 0;
       const int Ihi = P < K - 1 - J ? P : K - 1 - J;
       if (Ilo > Ihi) continue;
-      acc_t mt = MF::zero();  // lane holds M^T[row(lane, r)][c] = M[c][row(lane, r)]
-      for (int I = Ilo; I <= Ihi; ++I) {
-        const R* E = Wk + ((int64_t)I * Nt + J) * T * T;
-        const R* Lb = LBp + tri_index(P, I) * T * T;
-        R lb4[4];
-        EVec<R>::load4(Lb + c * T + 4 * kg, lb4);
+      // at most kLeafBlock - 1 earlier tiles (I, J) of the block: all their
+      // loads are issued before the first MFMA
+      R ev[kLeafBlock][4], lv[kLeafBlock][4], la[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) mt = MF::mma(E[(4 * kg + s) * T + c], lb4[s], mt);
+      for (int u = 0; u < kLeafBlock; ++u) {
+        const int I = Ilo + u;
+        if (I <= Ihi) {
+          const R* E = Wk + ((int64_t)I * Nt + J) * T * T;
+          EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lv[u]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) ev[u][s] = E[(4 * kg + s) * T + c];
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) { ev[u][s] = R(0); lv[u][s] = R(0); }
+        }
       }
       const R* La = LAp + tri_index(Q, J) * T * T;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], La[c * T + MF::row(lane, s)], acc);
+      for (int s = 0; s < 4; ++s) la[s] = La[c * T + MF::row(lane, s)];
+      acc_t mt = MF::zero();  // lane holds M^T[row(lane, r)][c] = M[c][row(lane, r)]
+#pragma unroll
+      for (int u = 0; u < kLeafBlock; ++u) {
+        if (Ilo + u > Ihi) break;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mt = MF::mma(ev[u][s], lv[u][s], mt);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], la[s], acc);
     }
   }
   if (wave > 0) {
