@@ -10,6 +10,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <limits>
 #include <vector>
 
 #include "bakron.h"
@@ -101,13 +102,17 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   bb.LAp = LAp;
   bb.Mb = Mb;
 
-  if (launch_pack_w<R>(g, W, ldw, Wk, s) != hipSuccess) return BAKRON_EHIP;
-  if (launch_pack_l<R>(m, g.Mt, LB, ldlb, LBp, s) != hipSuccess) return BAKRON_EHIP;
-  if (launch_pack_l<R>(n, g.Nt, LA, ldla, LAp, s) != hipSuccess) return BAKRON_EHIP;
+  // the solve runs in code units: U = W / s, the factor on the scaled side
+  // conjugated by the scales
+  const R* scB = scale_mode == 1 ? scales : nullptr;
+  const R* scA = scale_mode == 2 ? scales : nullptr;
+  if (launch_pack_w<R>(g, W, ldw, scales, scale_mode, Wk, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_pack_l<R>(m, g.Mt, LB, ldlb, scB, LBp, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_pack_l<R>(n, g.Nt, LA, ldla, scA, LAp, s) != hipSuccess) return BAKRON_EHIP;
 
   LeafParams<R> lp;
-  lp.lo = (R)lo;
-  lp.hi = (R)hi;
+  lp.lo = unb ? -std::numeric_limits<R>::infinity() : (R)lo;
+  lp.hi = unb ? std::numeric_limits<R>::infinity() : (R)hi;
   lp.unbounded = unb;
   lp.scale_mode = scale_mode;
   lp.scales = scales;

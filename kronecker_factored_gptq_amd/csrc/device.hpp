@@ -37,18 +37,20 @@ template <> struct Mfma<double> {
 };
 
 // ---------------------------------------------------------------------------
-// Quantizer (§3.1 of the BaKron paper: closest alphabet element after scaling).
-// c = clamp(rint(x / s), lo, hi); rint rounds half to even. True division.
+// Quantizer (§3.1 of the BaKron paper: closest alphabet element after
+// scaling), applied in code units, i.e. to u = x / s, which the solve keeps
+// directly: c = clamp(rint(u), lo, hi), rint rounding half to even, with
+// lo = -inf, hi = +inf for the unbounded alphabet.
 // ---------------------------------------------------------------------------
-__device__ inline float quant_code(float x, float s, float lo, float hi, bool unbounded) {
-  float c = __builtin_rintf(x / s);
-  if (!unbounded) c = fminf(fmaxf(c, lo), hi);
-  return c;
+__device__ inline float fmin_(float a, float b) { return fminf(a, b); }
+__device__ inline float fmax_(float a, float b) { return fmaxf(a, b); }
+__device__ inline double fmin_(double a, double b) { return fmin(a, b); }
+__device__ inline double fmax_(double a, double b) { return fmax(a, b); }
+__device__ inline float quant_unit(float u, float lo, float hi) {
+  return fminf(fmaxf(__builtin_rintf(u), lo), hi);
 }
-__device__ inline double quant_code(double x, double s, double lo, double hi, bool unbounded) {
-  double c = __builtin_rint(x / s);
-  if (!unbounded) c = fmin(fmax(c, lo), hi);
-  return c;
+__device__ inline double quant_unit(double u, double lo, double hi) {
+  return fmin(fmax(__builtin_rint(u), lo), hi);
 }
 
 // ---------------------------------------------------------------------------

@@ -17,9 +17,11 @@ struct SolveGeom {
 
 // ---- solve (solve_kernels.hip) --------------------------------------------
 template <typename R>
-hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, R* Wk, hipStream_t s);
+hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, const R* scales,
+                         int scale_mode, R* Wk, hipStream_t s);
 template <typename R>
-hipError_t launch_pack_l(int64_t dim, int Dt, const R* L, int64_t ld, R* Lp, hipStream_t s);
+hipError_t launch_pack_l(int64_t dim, int Dt, const R* L, int64_t ld, const R* scales, R* Lp,
+                         hipStream_t s);
 
 template <typename R>
 struct LeafParams {

@@ -14,37 +14,56 @@
 // the errors E recorded on [k, mid) — the "restricted band products" of
 // Appendix C, in band_kernels.hip.
 //
-// Workspace layout (HBM): W as Mt x Nt tiles, tile (P,Q) contiguous and
-// row-major; after a tile is processed its slot holds its errors
-// E = s*code - (value at rounding), which is what the band products read.
-// L^A, L^B as packed lower-triangular tile arrays (tile (P,I), I <= P, at
-// P(P+1)/2 + I), unit diagonal, zero above it and on padding.
+// Code units. With per-row scales s (S = diag(s)) the solve runs on
+// U = S^-1 W, whose entries are rounded by a plain rint: the update
+// W += e (L^B e_i)(L^A e_j)^T of §3.3 with e = s_i (c - u) is, divided by the
+// row scales, U += (c - u) (S^-1 L^B S e_i)(L^A e_j)^T. So the packed L^B is
+// S^-1 L^B S (still unit lower triangular) and every error is c - u, in units
+// of its row's scale; per-column scales scale L^A the same way; without
+// scales nothing changes. Exact arithmetic gives the same codes (the
+// quotient x / s at rounding time equals u), with no division in the sweep.
+//
+// Workspace layout (HBM): U as Mt x Nt tiles, tile (P,Q) contiguous and
+// row-major; after a tile is processed its slot holds its errors c - u
+// (code units), which is what the band products read. The scaled L^A, L^B as
+// packed lower-triangular tile arrays (tile (P,I), I <= P, at P(P+1)/2 + I),
+// unit diagonal, zero above it and on padding.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace bk {
 
 // ---------------------------------------------------------------------------
-// Pack W (row-major, ldw) into tiles; padding is zero.
+// Pack U = W / s (row-major W, ldw) into tiles; padding is zero. mode: 0 no
+// scales, 1 per-row, 2 per-column.
 // ---------------------------------------------------------------------------
 template <typename R, int T>
 __global__ __launch_bounds__(256) void pack_w_kernel(int64_t m, int64_t n, int Nt,
                                                      const R* __restrict__ W, int64_t ldw,
+                                                     const R* __restrict__ sc, int mode,
                                                      R* __restrict__ Wk) {
   const int64_t tile = blockIdx.x;
   const int64_t P = tile / Nt, Q = tile % Nt;
   R* dst = Wk + tile * T * T;
   for (int e = threadIdx.x; e < T * T; e += blockDim.x) {
     const int64_t i = P * T + e / T, j = Q * T + e % T;
-    dst[e] = (i < m && j < n) ? W[i * ldw + j] : R(0);
+    R v = R(0);
+    if (i < m && j < n) {
+      v = W[i * ldw + j];
+      if (mode == 1) v = v / sc[i];
+      else if (mode == 2) v = v / sc[j];
+    }
+    dst[e] = v;
   }
 }
 
-// Pack the strict lower triangle of a normalised factor into lower tiles;
-// the diagonal is 1 (normalised factor), everything above it and on padding 0.
+// Pack the strict lower triangle of a normalised factor into lower tiles,
+// scaled to code units when sc is given (entry (i, j) times s_j / s_i); the
+// diagonal is 1, everything above it and on padding 0.
 template <typename R, int T>
 __global__ __launch_bounds__(256) void pack_l_kernel(int64_t dim, const R* __restrict__ L,
-                                                     int64_t ld, R* __restrict__ Lp) {
+                                                     int64_t ld, const R* __restrict__ sc,
+                                                     R* __restrict__ Lp) {
   const int64_t t = blockIdx.x;
   int64_t P = (int64_t)((__builtin_sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
   while (P * (P + 1) / 2 > t) --P;
@@ -55,7 +74,10 @@ __global__ __launch_bounds__(256) void pack_l_kernel(int64_t dim, const R* __res
     const int64_t i = P * T + e / T, j = I * T + e % T;
     R v = R(0);
     if (i == j) v = R(1);
-    else if (j < i && i < dim) v = L[i * ld + j];
+    else if (j < i && i < dim) {
+      v = L[i * ld + j];
+      if (sc) v = v * sc[j] / sc[i];
+    }
     dst[e] = v;
   }
 }
@@ -75,10 +97,12 @@ __global__ __launch_bounds__(256) void pack_l_kernel(int64_t dim, const R* __res
 //    index: no data movement between the two products.
 // 2. Sweep (wave 0): the tile lives in the MFMA accumulator. In-tile step t
 //    rounds the entries (p, t - p) (one per column, §3.3's anti-diagonal
-//    order) and adds L^B e L^A^T for the step's errors e as one 16x16x16
-//    MFMA product: A[p][k] = L^B[p][k] e_k, B[k][q] = L^A[q][t - k]. Entries
-//    already rounded, or with (k, t - k) outside the tile, meet exact zeros
-//    of the triangular factors.
+//    order) to c = clamp(rint(u)) and adds L^B e L^A^T for the step's errors
+//    e = c - u as one 16x16x16 MFMA product: A[p][k] = L^B[p][k] e_k,
+//    B[k][q] = L^A[q][t - k]. Entries already rounded, or with (k, t - k)
+//    outside the tile, meet exact zeros of the triangular factors. Each step
+//    records the value at rounding in LDS; codes and errors are formed from
+//    it again (same operations) when the tile is written back.
 // ---------------------------------------------------------------------------
 template <typename R> struct EVec;
 template <> struct EVec<float> {
@@ -94,6 +118,53 @@ template <> struct EVec<double> {
     out[0] = v0.x; out[1] = v0.y; out[2] = v1.x; out[3] = v1.y;
   }
 };
+
+// Sweep error exchange. MFMA s of a sweep step takes, in lane row kg
+// (lanes 16 kg .. 16 kg + 15), the in-tile row k = KA kg + KB s. The choice
+// makes the error e_k come from the same lane row that consumes it: the float
+// accumulator holds tile row 4 kg + r in lane row kg, the double one row
+// kg + 4 r. The producing lane sits at column t - k; skewing lane row kg by
+// KA kg columns (two masked row rotations) moves every producer of MFMA s to
+// column (t - KB s) mod 16, and one row broadcast hands e_k to the row.
+template <typename R> struct SweepK;
+template <> struct SweepK<float> { static constexpr int KA = 4, KB = 1; };
+template <> struct SweepK<double> { static constexpr int KA = 1, KB = 4; };
+
+// gfx9 DPP controls: rotate right inside each row of 16 lanes (lane c reads
+// lane c - n), and broadcast lane n of each row to that row (gfx90a on).
+constexpr int kDppRowRor = 0x120;
+constexpr int kDppRowNewBcast = 0x150;
+
+template <int CTRL, int ROWS>
+__device__ inline float dpp_mov(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS>
+__device__ inline double dpp_mov(double old, double v) {
+  const int2 o = __builtin_bit_cast(int2, old), x = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __builtin_amdgcn_update_dpp(o.x, x.x, CTRL, ROWS, 0xF, false);
+  r.y = __builtin_amdgcn_update_dpp(o.y, x.y, CTRL, ROWS, 0xF, false);
+  return __builtin_bit_cast(double, r);
+}
+
+// lane row kg: result column c holds the input's column (c - KA kg) mod 16
+template <typename R>
+__device__ inline R row_skew(R e) {
+  constexpr int A = SweepK<R>::KA;
+  const R a = dpp_mov<kDppRowRor + A, 0xA>(e, e);      // rows 1 and 3
+  return dpp_mov<kDppRowRor + 2 * A, 0xC>(a, a);       // rows 2 and 3
+}
+
+template <int I, int N, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -111,14 +182,29 @@ __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt
   typedef typename MF::acc_t acc_t;
   __shared__ R red[3][T][T + 1];
   __shared__ R lat[T][T + 1];
-  __shared__ __attribute__((aligned(16))) R ebuf[T];
-  __shared__ R oc[T][T + 1], ow[T][T + 1], oe[T][T + 1];
+  __shared__ R ow[T][T + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, kg = lane >> 4;
   const int P = (K - (Nt - 1) > 0 ? K - (Nt - 1) : 0) + (int)blockIdx.x;
   const int Q = K - P;
+  R* tW = Wk + ((int64_t)P * Nt + Q) * T * T;
+
+  // sweep inputs, requested before the prologue so that their latency
+  // overlaps it: this thread's element of L^A[Q,Q] and, on wave 0, the tile
+  // and its lbK operands (lbK[s] = L^B[P,P][c][KA kg + KB s])
+  constexpr int KA = SweepK<R>::KA, KB = SweepK<R>::KB;
+  const R lat_v = LAp[tri_index(Q, Q) * T * T + tid];
+  R w0[4], lbK[4];
+  if (wave == 0) {
+    const R* lb = LBp + tri_index(P, P) * T * T + c * T + KA * kg;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      w0[r] = tW[MF::row(lane, r) * T + c];
+      lbK[r] = lb[KB * r];
+    }
+  }
 
   // ---- 1. prologue
   acc_t acc = MF::zero();
@@ -162,82 +248,74 @@ __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave - 1][MF::row(lane, r)][c] = acc[r];
   }
-  {
-    const R* tA = LAp + tri_index(Q, Q) * T * T;
-    lat[tid >> 4][tid & 15] = tA[tid];
-  }
-  if (tid < T) ebuf[tid] = R(0);
+  lat[tid >> 4][tid & 15] = lat_v;
   __syncthreads();
   if (wave > 0) return;
 
   // ---- 2. sweep on wave 0
-  R* tW = Wk + ((int64_t)P * Nt + Q) * T * T;
   const int64_t gj = (int64_t)Q * T + c;
-  const bool unb = lp.unbounded != 0;
+  // an entry outside the matrix is never selected: it keeps its exact zero
+  // and contributes no error
   int dr[4];
-  R sr[4];
-  bool vr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = MF::row(lane, r);
-    acc[r] += tW[row * T + c] + red[0][row][c] + red[1][row][c] + red[2][row][c];
-    const int64_t gi = (int64_t)P * T + row;
-    dr[r] = row + c;
-    vr[r] = gi < m && gj < n;
-    R sv = R(1);
-    if (lp.scale_mode == 1) sv = gi < m ? lp.scales[gi] : R(1);
-    else if (lp.scale_mode == 2) sv = gj < n ? lp.scales[gj] : R(1);
-    sr[r] = sv;
+    acc[r] += w0[r] + red[0][row][c] + red[1][row][c] + red[2][row][c];
+    const bool valid = (int64_t)P * T + row < m && gj < n;
+    dr[r] = valid ? row + c : -1;
   }
-  R lbK[4];
-  EVec<R>::load4(LBp + tri_index(P, P) * T * T + c * T + 4 * kg, lbK);
-  R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - 4 kg]
+  R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - KA kg]
 #pragma unroll
   for (int j = 0; j < 2 * T - 1; ++j) {
-    const int jj = j - 4 * kg;
+    const int jj = j - KA * kg;
     laK[j] = (jj >= 0 && jj < T) ? lat[c][jj] : R(0);
   }
+  const R lo = lp.lo, hi = lp.hi;  // +-infinity for the unbounded alphabet
+  // lanes without an entry on the step see the code of 0, so their error is
+  // an exact zero
+  const R c0 = fmin_(fmax_(R(0), lo), hi);
 
-#pragma unroll
-  for (int t = 0; t < 2 * T - 1; ++t) {
-    R x = R(0), sa = R(1);
-    bool act = false, va = false;
+  static_for<0, 2 * T - 1>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    R x = c0;
+    bool act = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool on = dr[r] == t;
       x = on ? acc[r] : x;
-      sa = on ? sr[r] : sa;
-      va = on ? vr[r] : va;
       act = act || on;
     }
-    const R cq = quant_code(x, sa, lp.lo, lp.hi, unb);
-    const R e = (act && va) ? sa * cq - x : R(0);
-    if (act) {
-      const int p = t - c;
-      ebuf[p] = e;
-      oc[p][c] = cq;
-      ow[p][c] = x;
-      oe[p][c] = e;
-    }
-    wave_sync_lds();
-    R ev[4];
-    EVec<R>::load4(ebuf + 4 * kg, ev);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const R b = (t - s >= 0) ? laK[t - s] : R(0);
-      acc = MF::mma(lbK[s] * ev[s], b, acc);
-    }
-  }
+    const R e = quant_unit(x, lo, hi) - x;
+    if (act) ow[t - c][c] = x;
+    const R es = row_skew(e);
+    static_for<0, 4>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (t - KB * s >= 0) {
+        const R ev = dpp_mov<kDppRowNewBcast + ((t - KB * s) & 15), 0xF>(R(0), es);
+        acc = MF::mma(lbK[s] * ev, laK[t - KB * s], acc);
+      }
+    });
+  });
   wave_sync_lds();
+  // write back: errors (code units) into the workspace, codes and the values
+  // at rounding (back in the units of W) to the outputs
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int idx = lane + 64 * u;
     const int p = idx >> 4, q = idx & 15;
     const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + q;
-    tW[idx] = oe[p][q];
-    if (gi < m && gjj < n) {
-      lp.V[gi * lp.ldv + gjj] = (int32_t)oc[p][q];
-      if (lp.Wt) lp.Wt[gi * lp.ldwt + gjj] = ow[p][q];
+    const bool valid = gi < m && gjj < n;
+    const R x = ow[p][q];
+    const R cq = quant_unit(x, lo, hi);
+    tW[idx] = valid ? cq - x : R(0);
+    if (valid) {
+      lp.V[gi * lp.ldv + gjj] = (int32_t)cq;
+      if (lp.Wt) {
+        R sv = R(1);
+        if (lp.scale_mode == 1) sv = lp.scales[gi];
+        else if (lp.scale_mode == 2) sv = lp.scales[gjj];
+        lp.Wt[gi * lp.ldwt + gjj] = lp.scale_mode ? sv * x : x;
+      }
     }
   }
 }
@@ -246,20 +324,22 @@ __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt
 // Host wrappers
 // ---------------------------------------------------------------------------
 template <typename R>
-hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, R* Wk, hipStream_t s) {
+hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, const R* scales,
+                         int scale_mode, R* Wk, hipStream_t s) {
   const int64_t nt = (int64_t)g.Mt * g.Nt;
   if (nt == 0) return hipSuccess;
   hipLaunchKernelGGL((pack_w_kernel<R, kTile>), dim3((unsigned)nt), dim3(256), 0, s, g.m, g.n,
-                     g.Nt, W, ldw, Wk);
+                     g.Nt, W, ldw, scales, scale_mode, Wk);
   return hipGetLastError();
 }
 
 template <typename R>
-hipError_t launch_pack_l(int64_t dim, int Dt, const R* L, int64_t ld, R* Lp, hipStream_t s) {
+hipError_t launch_pack_l(int64_t dim, int Dt, const R* L, int64_t ld, const R* scales, R* Lp,
+                         hipStream_t s) {
   const int64_t nt = (int64_t)Dt * (Dt + 1) / 2;
   if (nt == 0) return hipSuccess;
   hipLaunchKernelGGL((pack_l_kernel<R, kTile>), dim3((unsigned)nt), dim3(256), 0, s, dim, L, ld,
-                     Lp);
+                     scales, Lp);
   return hipGetLastError();
 }
 
@@ -281,8 +361,10 @@ hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, c
 }
 
 #define BK_INST(R)                                                                              \
-  template hipError_t launch_pack_w<R>(const SolveGeom&, const R*, int64_t, R*, hipStream_t);  \
-  template hipError_t launch_pack_l<R>(int64_t, int, const R*, int64_t, R*, hipStream_t);      \
+  template hipError_t launch_pack_w<R>(const SolveGeom&, const R*, int64_t, const R*, int, R*,  \
+                                       hipStream_t);                                            \
+  template hipError_t launch_pack_l<R>(int64_t, int, const R*, int64_t, const R*, R*,          \
+                                       hipStream_t);                                            \
   template hipError_t launch_leaf<R>(const SolveGeom&, int, int, R*, const R*, const R*,        \
                                      const LeafParams<R>&, hipStream_t);
 BK_INST(float)

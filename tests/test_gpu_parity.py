@@ -65,6 +65,23 @@ def test_factor_rejects_non_spd(gpu_lib, side):
     assert ei.value.bad_pivot[0] == (0 if side == "A" else 1)
 
 
+@pytest.mark.parametrize("n,i", [(100, 80), (100, 20), (128, 0), (250, 3), (250, 120)])
+def test_factor_reports_first_failing_pivot(gpu_lib, n, i):
+    """A negative diagonal entry at i of an otherwise SPD matrix: every
+    leading principal block of the reversed matrix J A J that excludes i is
+    SPD, and the Schur complement at i is A_ii minus a non-negative number,
+    so the reversed Cholesky fails first at pivot n-1-i (covers the fused
+    order-128 nodes and the levels above them)."""
+    bk = gpu_lib
+    p = random_problem(30, n, "f64", seed=n + i)
+    A = p.A.copy()
+    A[i, i] = -5.0
+    with pytest.raises(bk.BakronError) as ei:
+        bk.factor(to_dev(A), to_dev(p.B))
+    assert ei.value.status == bk.ENOTSPD
+    assert tuple(ei.value.bad_pivot) == (0, n - 1 - i)
+
+
 # ------------------------------------------------------------------- solve ---
 
 def test_config1_fp64_bit_exact(gpu_lib):
