@@ -221,48 +221,36 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
 // Large-tile variant: BM x BN output blocks, WM x WN waves (64 * WM * WN
 // threads), each wave a (BM / WM) x (BN / WN) sub-block of 16 x 16 MFMA
 // blocks; otherwise the same options and the same K loop as gemm64_kernel.
-// Twice the MFMA work per loaded byte of the 64 x 64 kernel.
-template <int BM, int BN, int WM, int WN, bool TRI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
-  typedef Mfma<double> MF;
-  typedef MF::acc_t acc_t;
-  constexpr int NT = 64 * WM * WN;
-  constexpr int TM = BM / WM, TN = BN / WN, NBM = TM / 16, NBN = TN / 16;
-  constexpr int PA = BM * GK / NT, PB = BN * GK / NT;
+// Twice the MFMA work per loaded byte of the 64 x 64 kernel. The main loop
+// and the dot epilogue are shared with the stream-K kernel below.
+template <int BM, int BN, int WM, int WN>
+struct BigCfg {
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN, NBM = TM / 16, NBN = TN / 16;
+  static constexpr int PA = BM * GK / NT, PB = BN * GK / NT;
   static_assert(PA >= 1 && PB >= 1 && BM % GTRI == 0 && BN % GTRI == 0, "tile shape");
-  __shared__ double As[2][BM][GLD];
-  __shared__ double Bs[2][BN][GLD];
-  __shared__ double red[WM * WN];
+  typedef Mfma<double>::acc_t acc_t;
+};
 
+// acc += A[row0.., kbeg..kend) op(B)[kbeg..kend), col0..) for the block at
+// (row0, col0); ends with a barrier (the LDS buffers are free again).
+template <int BM, int BN, int WM, int WN, bool TRI>
+__device__ __forceinline__ void big_mainloop(const Gemm64Args& a, int z, int64_t row0,
+                                             int64_t col0, int64_t kbeg, int64_t kend,
+                                             typename BigCfg<BM, BN, WM, WN>::acc_t (
+                                                 &acc)[BigCfg<BM, BN, WM, WN>::NBM]
+                                                      [BigCfg<BM, BN, WM, WN>::NBN],
+                                             double (*As)[BM][GLD], double (*Bs)[BN][GLD]) {
+  typedef BigCfg<BM, BN, WM, WN> C;
+  typedef Mfma<double> MF;
+  constexpr int NT = C::NT, TM = C::TM, TN = C::TN, NBM = C::NBM, NBN = C::NBN;
+  constexpr int PA = C::PA, PB = C::PB;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, kg = lane >> 4;
-  // with a triangular operand the longest K ranges are dispatched first
-  const int64_t bm = a.a_lower ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
-  const int64_t bn = (a.b_lower && a.transB) ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
-  const int z = blockIdx.z;
   const double* __restrict__ Ap = a.A[z];
   const double* __restrict__ Bp = a.B[z];
-  double* Cp = a.C[z];
-  const int64_t row0 = bm * BM, col0 = bn * BN;
-  const bool skip = a.lower_out && col0 >= row0 + BM;
-
-  acc_t acc[NBM][NBN];
-#pragma unroll
-  for (int i = 0; i < NBM; ++i)
-#pragma unroll
-    for (int j = 0; j < NBN; ++j) acc[i][j] = MF::zero();
-
-  int64_t kend = a.K, kbeg = 0;
-  if (a.a_lower && row0 + BM < kend) kend = row0 + BM;
-  if (a.b_lower) {
-    if (a.transB) {
-      if (col0 + BN < kend) kend = col0 + BN;
-    } else {
-      kbeg = col0;
-    }
-  }
   auto kin = [&](int64_t gk) { return gk < kend && gk >= kbeg; };
   auto ain = [&](int64_t gr, int64_t gk) {
     return gr < a.M && kin(gk) && (!TRI || !a.a_lower || gk < (gr / GTRI + 1) * GTRI);
@@ -308,72 +296,125 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
       else Bs[buf][e % BN][e / BN] = rb[u];
     }
   };
-
-  if (!skip && kend > kbeg) {
-    const int64_t k00 = kbeg / GK * GK;
-    gload(k00);
-    sstore(0);
-    __syncthreads();
-    const int64_t nk = (kend - k00 + GK - 1) / GK;
-    for (int64_t it = 0; it < nk; ++it) {
-      const int buf = (int)(it & 1);
-      if (it + 1 < nk) gload(k00 + (it + 1) * GK);
+  if (kend <= kbeg) return;
+  const int64_t k00 = kbeg / GK * GK;
+  gload(k00);
+  sstore(0);
+  __syncthreads();
+  const int64_t nk = (kend - k00 + GK - 1) / GK;
+  for (int64_t it = 0; it < nk; ++it) {
+    const int buf = (int)(it & 1);
+    if (it + 1 < nk) gload(k00 + (it + 1) * GK);
 #pragma unroll
-      for (int st = 0; st < GK / 4; ++st) {
-        double af[NBM], bf[NBN];
+    for (int st = 0; st < GK / 4; ++st) {
+      double af[NBM], bf[NBN];
 #pragma unroll
-        for (int i = 0; i < NBM; ++i) af[i] = As[buf][wm * TM + i * 16 + r16][4 * kg + st];
+      for (int i = 0; i < NBM; ++i) af[i] = As[buf][wm * TM + i * 16 + r16][4 * kg + st];
 #pragma unroll
-        for (int j = 0; j < NBN; ++j) bf[j] = Bs[buf][wn * TN + j * 16 + r16][4 * kg + st];
-#pragma unroll
-        for (int i = 0; i < NBM; ++i)
-#pragma unroll
-          for (int j = 0; j < NBN; ++j) acc[i][j] = MF::mma(af[i], bf[j], acc[i][j]);
-      }
-      if (it + 1 < nk) sstore(buf ^ 1);
-      __syncthreads();
-    }
-  }
-
-  if (a.dot[0]) {
-    double part = 0.0;
-    if (!skip) {
+      for (int j = 0; j < NBN; ++j) bf[j] = Bs[buf][wn * TN + j * 16 + r16][4 * kg + st];
 #pragma unroll
       for (int i = 0; i < NBM; ++i)
 #pragma unroll
-        for (int j = 0; j < NBN; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int64_t gr = row0 + wm * TM + i * 16 + MF::row(lane, r);
-            const int64_t gc = col0 + wn * TN + j * 16 + r16;
-            if (gr < a.M && gc < a.N) {
-              double wgt = 1.0;
-              if (a.sym_dot) wgt = gr > gc ? 2.0 : (gr == gc ? 1.0 : 0.0);
-              part += wgt * a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
-            }
-          }
+        for (int j = 0; j < NBN; ++j) acc[i][j] = MF::mma(af[i], bf[j], acc[i][j]);
     }
-    // fixed-order reduction: wave butterfly, then the waves in order
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-    if (lane == 0) red[wave] = part;
+    if (it + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
-    if (tid == 0) {
-      double t = red[0];
-      for (int q = 1; q < WM * WN; ++q) t += red[q];
-      a.partial[z][bm * gridDim.x + bn] = t;
+  }
+}
+
+// This thread's share of sum(alpha C_block .* dot_block) (sym_dot weights).
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ double big_dot(const Gemm64Args& a, int z, int64_t row0, int64_t col0,
+                                          const typename BigCfg<BM, BN, WM, WN>::acc_t (
+                                              &acc)[BigCfg<BM, BN, WM, WN>::NBM]
+                                                   [BigCfg<BM, BN, WM, WN>::NBN]) {
+  typedef BigCfg<BM, BN, WM, WN> C;
+  typedef Mfma<double> MF;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN, r16 = lane & 15;
+  double part = 0.0;
+#pragma unroll
+  for (int i = 0; i < C::NBM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NBN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t gr = row0 + wm * C::TM + i * 16 + MF::row(lane, r);
+        const int64_t gc = col0 + wn * C::TN + j * 16 + r16;
+        if (gr < a.M && gc < a.N) {
+          double wgt = 1.0;
+          if (a.sym_dot) wgt = gr > gc ? 2.0 : (gr == gc ? 1.0 : 0.0);
+          part += wgt * a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
+        }
+      }
+  return part;
+}
+
+// Fixed-order workgroup sum of one value per thread (result on thread 0).
+template <int NW>
+__device__ __forceinline__ double wg_sum(double part, double* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+  if (lane == 0) red[wave] = part;
+  __syncthreads();
+  double t = red[0];
+  for (int q = 1; q < NW; ++q) t += red[q];
+  return t;
+}
+
+template <int BM, int BN, int WM, int WN, bool TRI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
+  typedef BigCfg<BM, BN, WM, WN> C;
+  typedef Mfma<double> MF;
+  __shared__ double As[2][BM][GLD];
+  __shared__ double Bs[2][BN][GLD];
+  __shared__ double red[WM * WN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int r16 = lane & 15;
+  // with a triangular operand the longest K ranges are dispatched first
+  const int64_t bm = a.a_lower ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
+  const int64_t bn = (a.b_lower && a.transB) ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
+  const int z = blockIdx.z;
+  double* Cp = a.C[z];
+  const int64_t row0 = bm * BM, col0 = bn * BN;
+  const bool skip = a.lower_out && col0 >= row0 + BM;
+
+  typename C::acc_t acc[C::NBM][C::NBN];
+#pragma unroll
+  for (int i = 0; i < C::NBM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NBN; ++j) acc[i][j] = MF::zero();
+
+  int64_t kend = a.K, kbeg = 0;
+  if (a.a_lower && row0 + BM < kend) kend = row0 + BM;
+  if (a.b_lower) {
+    if (a.transB) {
+      if (col0 + BN < kend) kend = col0 + BN;
+    } else {
+      kbeg = col0;
     }
+  }
+  if (!skip) big_mainloop<BM, BN, WM, WN, TRI>(a, z, row0, col0, kbeg, kend, acc, As, Bs);
+
+  if (a.dot[0]) {
+    const double part = skip ? 0.0 : big_dot<BM, BN, WM, WN>(a, z, row0, col0, acc);
+    const double t = wg_sum<WM * WN>(part, red);
+    if (tid == 0) a.partial[z][bm * gridDim.x + bn] = t;
     return;
   }
   if (skip) return;
 #pragma unroll
-  for (int i = 0; i < NBM; ++i)
+  for (int i = 0; i < C::NBM; ++i)
 #pragma unroll
-    for (int j = 0; j < NBN; ++j)
+    for (int j = 0; j < C::NBN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t gr = row0 + wm * TM + i * 16 + MF::row(lane, r);
-        const int64_t gc = col0 + wn * TN + j * 16 + r16;
+        const int64_t gr = row0 + wm * C::TM + i * 16 + MF::row(lane, r);
+        const int64_t gc = col0 + wn * C::TN + j * 16 + r16;
         if (a.lower_out && gc / GTRI > gr / GTRI) continue;
         if (gr < a.M && gc < a.N) {
           double v = a.alpha * acc[i][j][r];
@@ -383,9 +424,62 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
       }
 }
 
+// Stream-K dot product over the lower blocks of a square product (the
+// loss): the nblk = nb (nb + 1) / 2 blocks (bm >= bn) times nk K steps form
+// one list of block-steps, cut into gridDim.x equal contiguous ranges, one
+// per workgroup. The dot epilogue is linear in the block's product, so a
+// workgroup adds the epilogue of each partial K range it holds and writes
+// one partial; every workgroup has the same amount of MFMA work whatever
+// the number of blocks.
+template <int BM, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_sk_lower_dot_kernel(Gemm64Args a,
+                                                                         int64_t nk,
+                                                                         int64_t total) {
+  typedef BigCfg<BM, BM, WM, WN> C;
+  typedef Mfma<double> MF;
+  __shared__ double As[2][BM][GLD];
+  __shared__ double Bs[2][BM][GLD];
+  __shared__ double red[WM * WN];
+  const int64_t g = blockIdx.x, G = gridDim.x;
+  const int64_t it1 = total * (g + 1) / G;
+  double part = 0.0;
+  for (int64_t it = total * g / G; it < it1;) {
+    const int64_t b = it / nk, kb = it % nk;
+    const int64_t cnt = (nk - kb) < (it1 - it) ? (nk - kb) : (it1 - it);
+    int64_t bm = (int64_t)((__builtin_sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
+    while (bm * (bm + 1) / 2 > b) --bm;
+    while ((bm + 1) * (bm + 2) / 2 <= b) ++bm;
+    const int64_t bn = b - bm * (bm + 1) / 2;
+    typename C::acc_t acc[C::NBM][C::NBN];
+#pragma unroll
+    for (int i = 0; i < C::NBM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NBN; ++j) acc[i][j] = MF::zero();
+    const int64_t kbeg = kb * GK, kend = (kb + cnt) * GK < a.K ? (kb + cnt) * GK : a.K;
+    big_mainloop<BM, BM, WM, WN, false>(a, 0, bm * BM, bn * BM, kbeg, kend, acc, As, Bs);
+    part += big_dot<BM, BM, WM, WN>(a, 0, bm * BM, bn * BM, acc);
+    it += cnt;
+  }
+  const double t = wg_sum<WM * WN>(part, red);
+  if (threadIdx.x == 0) a.partial[0][g] = t;
+}
+
 // Kernel choice: the 128 x 128 eight-wave kernel when it still gives at
 // least 256 workgroups, else the 64 x 64 kernel (more workgroups for the
 // smaller products and the lower-block ones).
+// Stream-K: the dot product of a square lower-block product (one problem,
+// no triangular operand), on one workgroup per compute unit.
+constexpr int kSkGrid = 256;
+static bool use_sk(const Gemm64Args& a) {
+  return a.lower_out && a.dot[0] && a.sym_dot && a.batch == 1 && !a.a_lower && !a.b_lower &&
+         a.M == a.N;
+}
+static int64_t sk_total(const Gemm64Args& a, int64_t* nk) {
+  const int64_t nb = (a.M + 127) / 128;
+  *nk = (a.K + GK - 1) / GK;
+  return nb * (nb + 1) / 2 * *nk;
+}
+
 static bool use_big(const Gemm64Args& a) {
   // lower-block products (half of the blocks idle) balance better on the
   // finer 64 x 64 grid
@@ -394,11 +488,19 @@ static bool use_big(const Gemm64Args& a) {
   return t >= 256;
 }
 
-int64_t gemm64_num_blocks(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 63) / 64); }
+int64_t gemm64_num_blocks(int64_t M, int64_t N) {
+  const int64_t b = ((M + 63) / 64) * ((N + 63) / 64);
+  return b > kSkGrid ? b : kSkGrid;
+}
 
 int64_t gemm64_partials(const Gemm64Args& a) {
+  if (use_sk(a)) {
+    int64_t nk;
+    const int64_t t = sk_total(a, &nk);
+    return t < kSkGrid ? t : kSkGrid;
+  }
   if (use_big(a)) return ((a.M + 127) / 128) * ((a.N + 127) / 128);
-  return gemm64_num_blocks(a.M, a.N);
+  return ((a.M + 63) / 64) * ((a.N + 63) / 64);
 }
 
 template <int GB>
@@ -425,6 +527,15 @@ hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
   for (int z = 0; z < a.batch; ++z)
     vec = vec && (reinterpret_cast<uintptr_t>(a.A[z]) % 16 == 0) &&
           (reinterpret_cast<uintptr_t>(a.B[z]) % 16 == 0);
+  if (use_sk(a)) {
+    int64_t nk;
+    const int64_t t = sk_total(a, &nk);
+    if (t == 0) return hipSuccess;
+    const int64_t G = t < kSkGrid ? t : kSkGrid;
+    hipLaunchKernelGGL((gemm_sk_lower_dot_kernel<128, 2, 4>), dim3((unsigned)G), dim3(512), 0, s,
+                       a, nk, t);
+    return hipGetLastError();
+  }
   if (use_big(a)) {
     dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)((a.M + 127) / 128), (unsigned)a.batch);
     if (a.a_lower || a.b_lower)

@@ -113,8 +113,9 @@ struct Gemm64Args {
   int sym_dot;
 };
 hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s);
-// Upper bound of the per-block partials of a dot-epilogue product of this
-// shape (for workspace sizing), and the exact count a given product writes.
+// Upper bound of the partials a dot-epilogue product of this shape writes
+// (per-block or per-workgroup; for workspace sizing), and the exact count a
+// given product writes.
 int64_t gemm64_num_blocks(int64_t M, int64_t N);
 int64_t gemm64_partials(const Gemm64Args& a);
 

@@ -183,7 +183,7 @@ def test_already_quantised_is_fixed_point(gpu_lib):
 
 @pytest.mark.parametrize("dtype", ["f64", "f32"])
 @pytest.mark.parametrize("m,n,mode", [(1, 1, "row"), (37, 50, "row"), (64, 33, "col"),
-                                      (130, 97, None)])
+                                      (130, 97, None), (300, 170, None), (700, 1000, "row")])
 def test_loss_matches_oracle(gpu_lib, dtype, m, n, mode):
     p = random_problem(m, n, dtype, seed=m * n, w_std=0.3)
     g = np.random.default_rng(m + n)
