@@ -425,20 +425,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
 }
 
 // Stream-K dot product over the lower blocks of a square product (the
-// loss): the nblk = nb (nb + 1) / 2 blocks (bm >= bn) times nk K steps form
-// one list of block-steps, cut into gridDim.x equal contiguous ranges, one
-// per workgroup. The dot epilogue is linear in the block's product, so a
+// loss). Blocks are BM x BN with BM = RB BN (RB = 1 or 2); row block bm
+// holds the column blocks bn < RB (bm + 1), which cover its part of the
+// lower triangle. The nblk blocks times nk K steps form one list of
+// block-steps, cut into gridDim.x equal contiguous ranges, one per
+// workgroup. The dot epilogue is linear in the block's product, so a
 // workgroup adds the epilogue of each partial K range it holds and writes
 // one partial; every workgroup has the same amount of MFMA work whatever
 // the number of blocks.
-template <int BM, int WM, int WN>
+template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_sk_lower_dot_kernel(Gemm64Args a,
                                                                          int64_t nk,
                                                                          int64_t total) {
-  typedef BigCfg<BM, BM, WM, WN> C;
+  typedef BigCfg<BM, BN, WM, WN> C;
   typedef Mfma<double> MF;
+  constexpr int RB = BM / BN;
+  static_assert(RB * BN == BM && (RB == 1 || RB == 2), "block shape");
   __shared__ double As[2][BM][GLD];
-  __shared__ double Bs[2][BM][GLD];
+  __shared__ double Bs[2][BN][GLD];
   __shared__ double red[WM * WN];
   const int64_t g = blockIdx.x, G = gridDim.x;
   const int64_t it1 = total * (g + 1) / G;
@@ -446,18 +450,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sk_lower_dot_kernel(Gemm64A
   for (int64_t it = total * g / G; it < it1;) {
     const int64_t b = it / nk, kb = it % nk;
     const int64_t cnt = (nk - kb) < (it1 - it) ? (nk - kb) : (it1 - it);
-    int64_t bm = (int64_t)((__builtin_sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
-    while (bm * (bm + 1) / 2 > b) --bm;
-    while ((bm + 1) * (bm + 2) / 2 <= b) ++bm;
-    const int64_t bn = b - bm * (bm + 1) / 2;
+    // blocks before row bm: RB bm (bm + 1) / 2
+    int64_t bm = (int64_t)((__builtin_sqrt(8.0 * (double)b / RB + 1.0) - 1.0) * 0.5);
+    while (RB * bm * (bm + 1) / 2 > b) --bm;
+    while (RB * (bm + 1) * (bm + 2) / 2 <= b) ++bm;
+    const int64_t bn = b - RB * bm * (bm + 1) / 2;
     typename C::acc_t acc[C::NBM][C::NBN];
 #pragma unroll
     for (int i = 0; i < C::NBM; ++i)
 #pragma unroll
       for (int j = 0; j < C::NBN; ++j) acc[i][j] = MF::zero();
     const int64_t kbeg = kb * GK, kend = (kb + cnt) * GK < a.K ? (kb + cnt) * GK : a.K;
-    big_mainloop<BM, BM, WM, WN, false>(a, 0, bm * BM, bn * BM, kbeg, kend, acc, As, Bs);
-    part += big_dot<BM, BM, WM, WN>(a, 0, bm * BM, bn * BM, acc);
+    big_mainloop<BM, BN, WM, WN, false>(a, 0, bm * BM, bn * BN, kbeg, kend, acc, As, Bs);
+    part += big_dot<BM, BN, WM, WN>(a, 0, bm * BM, bn * BN, acc);
     it += cnt;
   }
   const double t = wg_sum<WM * WN>(part, red);
@@ -474,6 +479,8 @@ static bool use_sk(const Gemm64Args& a) {
   return a.lower_out && a.dot[0] && a.sym_dot && a.batch == 1 && !a.a_lower && !a.b_lower &&
          a.M == a.N;
 }
+// blocks of 128 x 128 (256 x 128 blocks measured slower here: the stream-K
+// loop state makes that kernel spill)
 static int64_t sk_total(const Gemm64Args& a, int64_t* nk) {
   const int64_t nb = (a.M + 127) / 128;
   *nk = (a.K + GK - 1) / GK;
@@ -532,8 +539,16 @@ hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
     const int64_t t = sk_total(a, &nk);
     if (t == 0) return hipSuccess;
     const int64_t G = t < kSkGrid ? t : kSkGrid;
-    hipLaunchKernelGGL((gemm_sk_lower_dot_kernel<128, 2, 4>), dim3((unsigned)G), dim3(512), 0, s,
-                       a, nk, t);
+    hipLaunchKernelGGL((gemm_sk_lower_dot_kernel<128, 128, 2, 4>), dim3((unsigned)G), dim3(512),
+                       0, s, a, nk, t);
+    return hipGetLastError();
+  }
+  // full products with at least 256 blocks of 256 x 128 (the loss's D A):
+  // 4 x 2 waves of 64 x 64, a third more MFMA work per loaded byte again
+  if (!a.lower_out && !a.a_lower && !a.b_lower && !a.dot[0] &&
+      ((a.M + 255) / 256) * ((a.N + 127) / 128) * a.batch >= 256) {
+    dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)((a.M + 255) / 256), (unsigned)a.batch);
+    hipLaunchKernelGGL((gemm_big_kernel<256, 128, 4, 2, false>), grid, dim3(512), 0, s, a);
     return hipGetLastError();
   }
   if (use_big(a)) {
