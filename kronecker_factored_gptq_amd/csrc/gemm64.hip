@@ -11,6 +11,8 @@
 // z), and a dot epilogue that reduces sum(C_block .* D_block) per block
 // instead of storing C (loss). With a triangular operand the blocks with the
 // longest K ranges are dispatched first.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -64,7 +66,11 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
     }
   }
 
-  double ra[PER], rb[PER];
+  // global loads run PD K steps ahead in a register ring: the small
+  // products of the factor's lower levels have few K steps, each too short to
+  // cover a load's latency
+  constexpr int PD = 4;
+  double ra[PD][PER], rb[PD][PER];
   auto kin = [&](int64_t gk) { return gk < kend && gk >= kbeg; };
   // exact 64-granular triangular structure of A (row gr) and B (column gn)
   auto ain = [&](int64_t gr, int64_t gk) {
@@ -75,7 +81,8 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
     if (!TRI || !a.b_lower) return true;
     return a.transB ? gk < (gn / GTRI + 1) * GTRI : gk >= (gn / GTRI) * GTRI;
   };
-  auto gload = [&](int64_t k0) {
+  auto gload = [&](int64_t k0, auto SETC) {
+    constexpr int set = decltype(SETC)::value;
     if (VEC) {
 #pragma unroll
       for (int u = 0; u < PER / 2; ++u) {
@@ -90,7 +97,7 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
             if (i0) v.x = Ap[gr * a.lda + gk];
             if (i1) v.y = Ap[gr * a.lda + gk + 1];
           }
-          ra[2 * u] = v.x; ra[2 * u + 1] = v.y;
+          ra[set][2 * u] = v.x; ra[set][2 * u + 1] = v.y;
         }
         if (a.transB) {
           const int r = e / GK, c = e % GK;
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
             if (i0) v.x = Bp[gn * a.ldb + gk];
             if (i1) v.y = Bp[gn * a.ldb + gk + 1];
           }
-          rb[2 * u] = v.x; rb[2 * u + 1] = v.y;
+          rb[set][2 * u] = v.x; rb[set][2 * u + 1] = v.y;
         } else {
           const int kr = e / GB, cc = e % GB;
           const int64_t gk = k0 + kr, gn = col0 + cc;
@@ -113,7 +120,7 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
             if (i0) v.x = Bp[gk * a.ldb + gn];
             if (i1) v.y = Bp[gk * a.ldb + gn + 1];
           }
-          rb[2 * u] = v.x; rb[2 * u + 1] = v.y;
+          rb[set][2 * u] = v.x; rb[set][2 * u + 1] = v.y;
         }
       }
     } else {
@@ -123,39 +130,49 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
         {
           const int r = e / GK, c = e % GK;
           const int64_t gr = row0 + r, gk = k0 + c;
-          ra[u] = ain(gr, gk) ? Ap[gr * a.lda + gk] : 0.0;
+          ra[set][u] = ain(gr, gk) ? Ap[gr * a.lda + gk] : 0.0;
         }
         if (a.transB) {
           const int r = e / GK, c = e % GK;
           const int64_t gn = col0 + r, gk = k0 + c;
-          rb[u] = bin(gn, gk) ? Bp[gn * a.ldb + gk] : 0.0;
+          rb[set][u] = bin(gn, gk) ? Bp[gn * a.ldb + gk] : 0.0;
         } else {
           const int kr = e / GB, cc = e % GB;
           const int64_t gk = k0 + kr, gn = col0 + cc;
-          rb[u] = bin(gn, gk) ? Bp[gk * a.ldb + gn] : 0.0;
+          rb[set][u] = bin(gn, gk) ? Bp[gk * a.ldb + gn] : 0.0;
         }
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, auto SETC) {
+    constexpr int set = decltype(SETC)::value;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = VEC ? 2 * ((u >> 1) * 256 + tid) + (u & 1) : u * 256 + tid;
-      As[buf][e / GK][e % GK] = ra[u];
-      if (a.transB) Bs[buf][e / GK][e % GK] = rb[u];
-      else Bs[buf][e % GB][e / GB] = rb[u];
+      As[buf][e / GK][e % GK] = ra[set][u];
+      if (a.transB) Bs[buf][e / GK][e % GK] = rb[set][u];
+      else Bs[buf][e % GB][e / GB] = rb[set][u];
     }
   };
 
   if (!skip && kend > kbeg) {
+    typedef std::integral_constant<int, 0> I0;
+    typedef std::integral_constant<int, 1> I1;
+    typedef std::integral_constant<int, 2> I2;
+    typedef std::integral_constant<int, 3> I3;
+    static_assert(PD == 4, "ring of four register sets");
     const int64_t k00 = kbeg / GK * GK;
-    gload(k00);
-    sstore(0);
-    __syncthreads();
     const int64_t nk = (kend - k00 + GK - 1) / GK;
-    for (int64_t it = 0; it < nk; ++it) {
+    // register set it % PD holds K step it; LDS buffer it % 2 is computed
+    gload(k00, I0());
+    if (1 < nk) gload(k00 + GK, I1());
+    if (2 < nk) gload(k00 + 2 * GK, I2());
+    if (3 < nk) gload(k00 + 3 * GK, I3());
+    sstore(0, I0());
+    __syncthreads();
+    auto step = [&](auto PH, int64_t it) {
+      constexpr int ph = decltype(PH)::value;
       const int buf = (int)(it & 1);
-      if (it + 1 < nk) gload(k00 + (it + 1) * GK);
 #pragma unroll
       for (int st = 0; st < GK / 4; ++st) {
         double af[NBW], bf[NBW];
@@ -168,8 +185,16 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
 #pragma unroll
           for (int j = 0; j < NBW; ++j) acc[i][j] = MF::mma(af[i], bf[j], acc[i][j]);
       }
-      if (it + 1 < nk) sstore(buf ^ 1);
+      if (it + 1 < nk) sstore(buf ^ 1, std::integral_constant<int, (ph + 1) % PD>());
+      // set ph is free once step it is in LDS: refill it with step it + PD
+      if (it + PD < nk) gload(k00 + (it + PD) * GK, PH);
       __syncthreads();
+    };
+    for (int64_t it0 = 0; it0 < nk; it0 += PD) {
+      step(I0(), it0);
+      if (it0 + 1 < nk) step(I1(), it0 + 1);
+      if (it0 + 2 < nk) step(I2(), it0 + 2);
+      if (it0 + 3 < nk) step(I3(), it0 + 3);
     }
   }
 
