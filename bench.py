@@ -34,10 +34,10 @@ PEAK_FP64_MFMA_TFLOPS = 78.6    # MI355X dense FP64 matrix
 
 # HBM bytes per band launch from the FETCH_SIZE / WRITE_SIZE counter passes
 # over one step of this workload, scaled by a plain 512 MiB copy (FETCH_SIZE
-# x2.0, WRITE_SIZE x1.0), valid for the band-kernel source with this hash
-# only: after any change to that file the figure is reported as null.
-BAND_TRAFFIC = {"sha256": "18d74fc48c9d67529b86108fe925b33e08d0d4be18c356ecfd395f2b0c463430",
-                "bytes_per_launch": 6.5805e7, "launches": 126,
+# x2.0, WRITE_SIZE x1.0), valid only for the band-kernel source and build
+# options with this hash: after any change to either the figure is null.
+BAND_TRAFFIC = {"sha256": "a065479d072b3edbcdcbacf9ddcbb22b9d3a955da1ad68902d598d43c274718d",
+                "bytes_per_launch": 6.6080e7, "launches": 126,
                 "summary": "profiles/band_kernel_attn4096_f32_counters.md"}
 METRIC = "weights quantized/s (m·n/solve-time) + % FP32 MFMA peak, 4096×4096"
 
@@ -70,12 +70,21 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
-def band_traffic():
+def band_kernel_hash() -> str:
+    """SHA-256 of the band-kernel source followed by its build options."""
     import hashlib
+    from kronecker_factored_gptq_amd import build as B
     src = os.path.join(ROOT, "kronecker_factored_gptq_amd", "csrc", "band_kernels.hip")
     with open(src, "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()
-    return BAND_TRAFFIC["bytes_per_launch"] if h == BAND_TRAFFIC["sha256"] else None
+        data = f.read()
+    opts = " ".join(o for o in B.COMMON + B.EXTRA.get("band_kernels.hip", [])
+                    if not o.startswith("-I"))  # include paths differ between machines
+    return hashlib.sha256(data + b"\n" + opts.encode()).hexdigest()
+
+
+def band_traffic():
+    ok = band_kernel_hash() == BAND_TRAFFIC["sha256"]
+    return BAND_TRAFFIC["bytes_per_launch"] if ok else None
 
 
 def cpu_baseline(p, hi: int):

@@ -33,10 +33,17 @@ COMMON = [
 ]
 
 
+# per-source options: MFMA accumulators in ordinary VGPRs (the leaf sweep
+# reads its accumulator every in-tile step, and accumulation registers would
+# need a copy per read; measured slightly faster for the band products too)
+EXTRA = {"solve_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "band_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", path, "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-x", "hip", "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)
