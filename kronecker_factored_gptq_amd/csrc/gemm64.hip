@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
   const int64_t row0 = bm * GB, col0 = bn * GB;
   // lower_out is decided on the 64-granular triangle: a block is computed if
   // any of its 64 x 64 sub-blocks is on or below the diagonal
-  const bool skip = a.lower_out && col0 >= row0 + GB;
+  const bool skip = a.lower_out && col0 / GTRI > (row0 + GB - 1) / GTRI;
 
   acc_t acc[NBW][NBW];
 #pragma unroll
@@ -584,6 +584,10 @@ hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
       hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, 4, false>), grid, dim3(512), 0, s, a);
     return hipGetLastError();
   }
+  // small products (the factor's lower levels): 32 x 32 blocks give four
+  // times the workgroups, each with a quarter of the dependent MFMA chain
+  const int64_t b64 = ((a.M + 63) / 64) * ((a.N + 63) / 64) * a.batch;
+  if (!a.dot[0] && b64 <= 128) return launch_gb<32>(a, vec, s);
   return launch_gb<64>(a, vec, s);
 }
 
