@@ -24,6 +24,40 @@ constexpr int GK = 16;    // K step
 constexpr int GLD = GK + 2;
 }  // namespace
 
+// Output block and problem of this workgroup. With a triangular operand the
+// K range of a block grows with its row (A lower) or column (B lower, op(B)
+// = B^T) or shrinks with its column (B lower, op(B) = B): the linear
+// workgroup number is mapped so that blocks are dispatched longest K range
+// first across both problems of a batch, which keeps the greedy placement
+// of blocks on compute units balanced.
+struct BlockMap {
+  int64_t bm, bn;
+  int z;
+};
+template <bool TRI>
+__device__ inline BlockMap map_block(const Gemm64Args& a) {
+  if constexpr (!TRI) return BlockMap{(int64_t)blockIdx.y, (int64_t)blockIdx.x, (int)blockIdx.z};
+  const int64_t X = gridDim.x, Y = gridDim.y, Z = gridDim.z;
+  const int64_t lin = blockIdx.x + X * (blockIdx.y + Y * (int64_t)blockIdx.z);
+  BlockMap m;
+  if (a.a_lower) {
+    const int64_t q = lin / (X * Z), r = lin % (X * Z);
+    m.bm = Y - 1 - q;
+    m.bn = r % X;
+    m.z = (int)(r / X);
+  } else if (a.b_lower) {
+    const int64_t q = lin / (Y * Z), r = lin % (Y * Z);
+    m.bn = a.transB ? X - 1 - q : q;
+    m.bm = r % Y;
+    m.z = (int)(r / Y);
+  } else {
+    m.bm = blockIdx.y;
+    m.bn = blockIdx.x;
+    m.z = blockIdx.z;
+  }
+  return m;
+}
+
 template <int GB, bool VEC, bool TRI>
 __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
   typedef Mfma<double> MF;
@@ -38,10 +72,9 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int r16 = lane & 15, kg = lane >> 4;
-  // with a triangular operand the longest K ranges are dispatched first
-  const int64_t bm = a.a_lower ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
-  const int64_t bn = (a.b_lower && a.transB) ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
-  const int z = blockIdx.z;
+  const BlockMap bmap = map_block<TRI>(a);
+  const int64_t bm = bmap.bm, bn = bmap.bn;
+  const int z = bmap.z;
   const double* __restrict__ Ap = a.A[z];
   const double* __restrict__ Bp = a.B[z];
   double* Cp = a.C[z];
@@ -400,10 +433,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15;
-  // with a triangular operand the longest K ranges are dispatched first
-  const int64_t bm = a.a_lower ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
-  const int64_t bn = (a.b_lower && a.transB) ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
-  const int z = blockIdx.z;
+  const BlockMap bmap = map_block<TRI>(a);
+  const int64_t bm = bmap.bm, bn = bmap.bn;
+  const int z = bmap.z;
   double* Cp = a.C[z];
   const int64_t row0 = bm * BM, col0 = bn * BN;
   const bool skip = a.lower_out && col0 >= row0 + BM;
@@ -568,9 +600,10 @@ hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
                        0, s, a, nk, t);
     return hipGetLastError();
   }
-  // full products with at least 256 blocks of 256 x 128 (the loss's D A):
-  // 4 x 2 waves of 64 x 64, a third more MFMA work per loaded byte again
-  if (!a.lower_out && !a.a_lower && !a.b_lower && !a.dot[0] &&
+  // products with at least 256 blocks of 256 x 128 (the loss's D A, the
+  // factor's top Schur complement on its lower blocks): 4 x 2 waves of
+  // 64 x 64, a third more MFMA work per loaded byte again
+  if (!a.a_lower && !a.b_lower && !a.dot[0] &&
       ((a.M + 255) / 256) * ((a.N + 127) / 128) * a.batch >= 256) {
     dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)((a.M + 255) / 256), (unsigned)a.batch);
     hipLaunchKernelGGL((gemm_big_kernel<256, 128, 4, 2, false>), grid, dim3(512), 0, s, a);
