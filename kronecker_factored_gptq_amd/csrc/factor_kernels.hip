@@ -27,6 +27,7 @@ namespace bk {
 namespace {
 constexpr int NB = 64;  // Cholesky panel width
 constexpr int kLeafCols = 4;  // columns per barrier step of the leaf (8 measured no faster)
+constexpr int kLeafPatchCols = 2;  // columns of a thread's patch: 4 x 2 patches, 512 threads
 }
 
 // X[i][j] = A[n-1-j][n-1-i] for i >= j (the lower triangle of J A J read from
@@ -72,22 +73,24 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* 
 // Published values are double-buffered by the parity of the step. A pivot
 // that is not positive and finite records off + j + q in *info (smallest
 // wins) and the factorisation continues with NaN.
-template <int NC>
-__global__ __launch_bounds__(256) void chol_inv_leaf_kernel(FactorSide s0, FactorSide s1,
-                                                            int64_t n, int64_t off, int bs) {
-  constexpr int PC = NC / 4;  // patch columns per step
+template <int NC, int PCW>
+__global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSide s0,
+                                                                       FactorSide s1, int64_t n,
+                                                                       int64_t off, int bs) {
+  static_assert(NC == 4, "one patch row per step");
+  constexpr int TX = 64 / PCW;  // thread columns; 16 thread rows of 4 rows each
   __shared__ double pblk[2][NC][NC];
   __shared__ double colp[2][NC][64];
   __shared__ double rowp[2][NC][64];
   const FactorSide S = blockIdx.x == 0 ? s0 : s1;
   const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
-  double Lr[4][4], Yr[4][4];
+  const int ty = tid / TX, tx = tid % TX;
+  double Lr[4][PCW], Yr[4][PCW];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = 4 * ty + a, c = 4 * tx + b;
+    for (int b = 0; b < PCW; ++b) {
+      const int i = 4 * ty + a, c = PCW * tx + b;
       double v = 0.0;
       if (i < bs && c < bs) v = c <= i ? S.X[(off + i) * n + off + c] : 0.0;
       else if (i == c) v = 1.0;
@@ -97,26 +100,26 @@ __global__ __launch_bounds__(256) void chol_inv_leaf_kernel(FactorSide s0, Facto
   const int steps = (bs + NC - 1) / NC;
   for (int st = 0; st < steps; ++st) {
     const int j = NC * st, pb = st & 1;
-    const int q0 = PC * st;            // first patch row / column of the step
-    const bool ownc = tx >= q0 && tx < q0 + PC, ownr = ty >= q0 && ty < q0 + PC;
+    // owners of columns j..j+NC-1 and of rows j..j+NC-1
+    const bool ownc = tx >= j / PCW && tx < (j + NC) / PCW, ownr = ty == st;
     // publish the raw pivot block, columns j..j+NC-1 and rows j..j+NC-1 of Y
     if (ownc && ownr) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) pblk[pb][4 * (ty - q0) + a][4 * (tx - q0) + b] = Lr[a][b];
+        for (int b = 0; b < PCW; ++b) pblk[pb][a][PCW * tx + b - j] = Lr[a][b];
     }
     if (ownc) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) colp[pb][4 * (tx - q0) + b][4 * ty + a] = Lr[a][b];
+        for (int b = 0; b < PCW; ++b) colp[pb][PCW * tx + b - j][4 * ty + a] = Lr[a][b];
     }
     if (ownr) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) rowp[pb][4 * (ty - q0) + a][4 * tx + b] = Yr[a][b];
+        for (int b = 0; b < PCW; ++b) rowp[pb][a][PCW * tx + b] = Yr[a][b];
     }
     __syncthreads();
     // Cholesky factor of the NC x NC pivot block (every thread, same values)
@@ -143,49 +146,56 @@ __global__ __launch_bounds__(256) void chol_inv_leaf_kernel(FactorSide s0, Facto
       }
     }
     if (tid == 0 && bad >= 0 && j + bad < bs) atomicMin(S.info, (int32_t)(off + j + bad));
-    // columns j.. of C at rows i and at rows c (zero on and above the pivot
-    // block), and rows j.. of Y at columns c (final after this step)
-    double ci[4][NC], cc[4][NC], yq[NC][4];
+    // columns j.. of C at this thread's rows i and at its columns c taken as
+    // rows (zero on and above the pivot block), and rows j.. of Y at its
+    // columns c (final after this step)
+    double ci[4][NC], cc[PCW][NC], yq[NC][PCW];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int i = 4 * ty + a, c = 4 * tx + a;
+      const int i = 4 * ty + a;
 #pragma unroll
       for (int q = 0; q < NC; ++q) {
-        double vi = colp[pb][q][i], vc = colp[pb][q][c];
+        double vi = colp[pb][q][i];
 #pragma unroll
         for (int p = 0; p < NC; ++p)
-          if (p < q) { vi -= ci[a][p] * l[q][p]; vc -= cc[a][p] * l[q][p]; }
-        ci[a][q] = vi * dinv[q];
-        cc[a][q] = vc * dinv[q];
+          if (p < q) vi -= ci[a][p] * l[q][p];
+        ci[a][q] = i < j + NC ? 0.0 : vi * dinv[q];
       }
+    }
+#pragma unroll
+    for (int b = 0; b < PCW; ++b) {
+      const int c = PCW * tx + b;
 #pragma unroll
       for (int q = 0; q < NC; ++q) {
-        if (i < j + NC) ci[a][q] = 0.0;
-        if (c < j + NC) cc[a][q] = 0.0;
+        double vc = colp[pb][q][c];
+#pragma unroll
+        for (int p = 0; p < NC; ++p)
+          if (p < q) vc -= cc[b][p] * l[q][p];
+        cc[b][q] = vc * dinv[q];
       }
+#pragma unroll
+      for (int q = 0; q < NC; ++q)
+        if (c < j + NC) cc[b][q] = 0.0;
 #pragma unroll
       for (int q = 0; q < NC; ++q) {
         double v = rowp[pb][q][c];
 #pragma unroll
         for (int p = 0; p < NC; ++p)
-          if (p < q) v -= l[q][p] * yq[p][a];
-        yq[q][a] = c < j + NC ? v * dinv[q] : 0.0;
+          if (p < q) v -= l[q][p] * yq[p][b];
+        yq[q][b] = c < j + NC ? v * dinv[q] : 0.0;
       }
     }
     if (ownr) {  // rows j.. of Y are final now
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int pr = 0; pr < PC; ++pr)
-            if (ty - q0 == pr) Yr[a][b] = yq[4 * pr + a][b];
+        for (int b = 0; b < PCW; ++b) Yr[a][b] = yq[a][b];
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int i = 4 * ty + a, c = 4 * tx + b;
+      for (int b = 0; b < PCW; ++b) {
+        const int i = 4 * ty + a, c = PCW * tx + b;
         double dl = 0.0, dy = 0.0;
 #pragma unroll
         for (int q = 0; q < NC; ++q) {
@@ -199,8 +209,8 @@ __global__ __launch_bounds__(256) void chol_inv_leaf_kernel(FactorSide s0, Facto
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = 4 * ty + a, c = 4 * tx + b;
+    for (int b = 0; b < PCW; ++b) {
+      const int i = 4 * ty + a, c = PCW * tx + b;
       if (i < bs && c < bs) S.Y[(off + i) * n + off + c] = c <= i ? Yr[a][b] : 0.0;
     }
 }
@@ -290,8 +300,9 @@ static hipError_t chol_inv_rec(int64_t n, const FactorSide* sd, int ns, int64_t 
                                hipStream_t s) {
   hipError_t err;
   if (len <= NB) {
-    hipLaunchKernelGGL(chol_inv_leaf_kernel<kLeafCols>, dim3(ns), dim3(256), 0, s, sd[0],
-                       sd[ns > 1 ? 1 : 0], n, off, (int)len);
+    hipLaunchKernelGGL((chol_inv_leaf_kernel<kLeafCols, kLeafPatchCols>), dim3(ns),
+                       dim3(16 * (64 / kLeafPatchCols)), 0, s, sd[0], sd[ns > 1 ? 1 : 0], n, off,
+                       (int)len);
     return hipGetLastError();
   }
   const int64_t n1 = split_point(len), n2 = len - n1;
