@@ -63,7 +63,8 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* 
 // Right-looking, NC columns j .. j+NC-1 per step (whole patch columns) and
 // one barrier per step: the owners publish the raw NC x NC pivot block, the
 // raw columns j.. and the raw rows j.. of Y; after the barrier every thread
-// forms the pivot block's Cholesky factor l (NC x NC lower) and, by forward
+// forms the pivot block's Cholesky factor l (NC x NC lower; reciprocal
+// square roots by one Newton step from the hardware estimate) and, by forward
 // substitution,
 //   C[i][j+q] = (X[i][j+q] - sum_{p<q} C[i][j+p] l[q][p]) / l[q][q],
 //   Y[j+q]    = (Y[j+q]    - sum_{p<q} l[q][p] Y[j+p]) / l[q][q]   (rows),
@@ -139,9 +140,14 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSi
         } else {
           const bool ok = v > 0.0 && v < INFINITY;
           if (!ok && bad < 0) bad = q;
-          const double sq = __builtin_sqrt(v);
-          l[q][q] = sq;
-          dinv[q] = ok ? 1.0 / sq : __builtin_nan("");
+          // 1/sqrt(v) from the hardware estimate and one Newton step
+          // (y += y (1 - v y^2) / 2), then sqrt(v) = v / sqrt(v): a short
+          // dependent chain instead of a rounded square root and a division
+          const double y0 = __builtin_amdgcn_rsq(v);
+          const double r = __builtin_fma(-v * y0, y0, 1.0);
+          const double y = __builtin_fma(0.5 * y0, r, y0);
+          dinv[q] = ok ? y : __builtin_nan("");
+          l[q][q] = v * dinv[q];
         }
       }
     }
