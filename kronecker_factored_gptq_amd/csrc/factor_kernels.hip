@@ -26,7 +26,7 @@ namespace bk {
 
 namespace {
 constexpr int NB = 64;  // Cholesky panel width
-constexpr int kLeafCols = 4;  // columns per barrier step of the leaf (8 measured no faster)
+constexpr int kLeafCols = 4;  // columns per barrier step of the leaf (8: spills, 6.90 ms factor against 6.69)
 constexpr int kLeafPatchCols = 2;  // columns of a thread's patch: 4 x 2 patches, 512 threads
 }
 
@@ -78,7 +78,8 @@ template <int NC, int PCW>
 __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSide s0,
                                                                        FactorSide s1, int64_t n,
                                                                        int64_t off, int bs) {
-  static_assert(NC == 4, "one patch row per step");
+  static_assert(NC % 4 == 0 && NC % PCW == 0, "whole patch rows and columns per step");
+  constexpr int PRS = NC / 4;  // patch rows per step
   constexpr int TX = 64 / PCW;  // thread columns; 16 thread rows of 4 rows each
   __shared__ double pblk[2][NC][NC];
   __shared__ double colp[2][NC][64];
@@ -102,13 +103,15 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSi
   for (int st = 0; st < steps; ++st) {
     const int j = NC * st, pb = st & 1;
     // owners of columns j..j+NC-1 and of rows j..j+NC-1
-    const bool ownc = tx >= j / PCW && tx < (j + NC) / PCW, ownr = ty == st;
+    const bool ownc = tx >= j / PCW && tx < (j + NC) / PCW;
+    const bool ownr = ty >= PRS * st && ty < PRS * (st + 1);
+    const int rq = 4 * (ty - PRS * st);  // first pivot row of this thread row
     // publish the raw pivot block, columns j..j+NC-1 and rows j..j+NC-1 of Y
     if (ownc && ownr) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < PCW; ++b) pblk[pb][a][PCW * tx + b - j] = Lr[a][b];
+        for (int b = 0; b < PCW; ++b) pblk[pb][rq + a][PCW * tx + b - j] = Lr[a][b];
     }
     if (ownc) {
 #pragma unroll
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSi
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < PCW; ++b) rowp[pb][a][PCW * tx + b] = Yr[a][b];
+        for (int b = 0; b < PCW; ++b) rowp[pb][rq + a][PCW * tx + b] = Yr[a][b];
     }
     __syncthreads();
     // Cholesky factor of the NC x NC pivot block (every thread, same values)
@@ -193,9 +196,13 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSi
     }
     if (ownr) {  // rows j.. of Y are final now
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int pr = 0; pr < PRS; ++pr)
+        if (rq == 4 * pr) {
 #pragma unroll
-        for (int b = 0; b < PCW; ++b) Yr[a][b] = yq[a][b];
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < PCW; ++b) Yr[a][b] = yq[4 * pr + a][b];
+        }
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
