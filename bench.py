@@ -37,7 +37,7 @@ PEAK_FP64_MFMA_TFLOPS = 78.6    # MI355X dense FP64 matrix
 # x2.0, WRITE_SIZE x1.0), valid only for the band-kernel source and build
 # options with this hash: after any change to either the figure is null.
 BAND_TRAFFIC = {"sha256": "a065479d072b3edbcdcbacf9ddcbb22b9d3a955da1ad68902d598d43c274718d",
-                "bytes_per_launch": 6.6080e7, "launches": 126,
+                "bytes_per_launch": 9.4458e+07, "launches": 84,
                 "summary": "profiles/band_kernel_attn4096_f32_counters.md"}
 METRIC = "weights quantized/s (m·n/solve-time) + % FP32 MFMA peak, 4096×4096"
 
@@ -82,8 +82,11 @@ def band_kernel_hash() -> str:
     return hashlib.sha256(data + b"\n" + opts.encode()).hexdigest()
 
 
-def band_traffic():
-    ok = band_kernel_hash() == BAND_TRAFFIC["sha256"]
+def band_traffic(launches: int):
+    """Counter-measured HBM bytes per band launch, or None when the kernel,
+    its build options or the number of band launches per step (the solve
+    schedule) differ from those the counters were taken with."""
+    ok = band_kernel_hash() == BAND_TRAFFIC["sha256"] and launches == BAND_TRAFFIC["launches"]
     return BAND_TRAFFIC["bytes_per_launch"] if ok else None
 
 
@@ -237,7 +240,7 @@ def main():
         result["roofline"] = {
             "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
-            "traffic": band_traffic() if args.workload == "attn4096" else None,
+            "traffic": band_traffic(nb) if args.workload == "attn4096" else None,
             "traffic_unit": "HBM bytes per launch (counters)",
             "kernel": "band_kernel (both stages)", "launches_per_step": nb,
             "useful_flop_per_step": fl["band"], "ms_per_step": band_ms,

@@ -56,7 +56,7 @@ hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage
                             const BandBuffers<R>& bb, hipStream_t s, hipEvent_t ev0 = nullptr,
                             hipEvent_t ev1 = nullptr);
 // Tile anti-diagonals per leaf block (updates inside a block are left-looking).
-constexpr int kLeafBlock = 8;
+constexpr int kLeafBlock = 12;
 
 // ---- factor (factor_kernels.hip), always float64 inside --------------------
 template <typename R>

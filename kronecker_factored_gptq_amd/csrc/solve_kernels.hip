@@ -214,31 +214,40 @@ __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt
       const int Ilo = K0 - J > 0 ? K0 - J : 0;
       const int Ihi = P < K - 1 - J ? P : K - 1 - J;
       if (Ilo > Ihi) continue;
-      // at most kLeafBlock - 1 earlier tiles (I, J) of the block: all their
-      // loads are issued before the first MFMA
-      R ev[kLeafBlock][4], lv[kLeafBlock][4], la[4];
-#pragma unroll
-      for (int u = 0; u < kLeafBlock; ++u) {
-        const int I = Ilo + u;
-        if (I <= Ihi) {
-          const R* E = Wk + ((int64_t)I * Nt + J) * T * T;
-          EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lv[u]);
-#pragma unroll
-          for (int s = 0; s < 4; ++s) ev[u][s] = E[(4 * kg + s) * T + c];
-        } else {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) { ev[u][s] = R(0); lv[u][s] = R(0); }
-        }
-      }
+      // the block's earlier tiles (I, J), Ilo <= I <= Ihi (at most
+      // kLeafBlock - 1), in kChunks chunks of up to kPro: all loads of a
+      // chunk are issued before its first MFMA
+      constexpr int kChunks = (kLeafBlock - 1 + 7) / 8;
+      constexpr int kPro = (kLeafBlock - 1 + kChunks - 1) / kChunks;
+      R la[4];
       const R* La = LAp + tri_index(Q, J) * T * T;
 #pragma unroll
       for (int s = 0; s < 4; ++s) la[s] = La[c * T + MF::row(lane, s)];
       acc_t mt = MF::zero();  // lane holds M^T[row(lane, r)][c] = M[c][row(lane, r)]
 #pragma unroll
-      for (int u = 0; u < kLeafBlock; ++u) {
-        if (Ilo + u > Ihi) break;
+      for (int ch = 0; ch < kChunks; ++ch) {
+        const int I0 = Ilo + ch * kPro;
+        if (I0 > Ihi) break;
+        R ev[kPro][4], lv[kPro][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) mt = MF::mma(ev[u][s], lv[u][s], mt);
+        for (int u = 0; u < kPro; ++u) {
+          const int I = I0 + u;
+          if (I <= Ihi) {
+            const R* E = Wk + ((int64_t)I * Nt + J) * T * T;
+            EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lv[u]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ev[u][s] = E[(4 * kg + s) * T + c];
+          } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) { ev[u][s] = R(0); lv[u][s] = R(0); }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kPro; ++u) {
+          if (I0 + u > Ihi) break;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) mt = MF::mma(ev[u][s], lv[u][s], mt);
+        }
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], la[s], acc);

@@ -101,22 +101,22 @@ def _closed_form_leaves(m, n, T=16):
     return -(-m // T) + -(-n // T) - 1
 
 
-BLOCK = 8
-
-
 @pytest.mark.parametrize("m,n", [(1, 1), (16, 16), (17, 5), (64, 64), (200, 300), (512, 512),
                                  (4096, 4096), (14336, 4096), (4096, 14336), (1024, 2048)])
 def test_schedule_is_algorithm_6_over_blocks_of_tile_antidiagonals(m, n):
     """Table 1 "Steps" for BaKron: one leaf per (tile) anti-diagonal, in
-    order; Algorithm 6's recursion over blocks of 8 tile anti-diagonals, each
-    internal node splitting block range [kb, lb) at floor((kb+lb)/2) and
-    running after the last leaf left of its midpoint and before the first
-    leaf right of it; inside a block, each leaf names its block start."""
+    order; Algorithm 6's recursion over blocks of G tile anti-diagonals (G
+    read from the second block's start), each internal node splitting block
+    range [kb, lb) at floor((kb+lb)/2) and running after the last leaf left
+    of its midpoint and before the first leaf right of it; inside a block,
+    each leaf names its block start."""
     ops = bk.solve_schedule(bk.F32, m, n)
     R = _closed_form_leaves(m, n)
-    nblocks = -(-R // BLOCK)
     leaves = [(a, b) for (kind, a, b, c) in ops if kind == 0]
     assert [a for a, _ in leaves] == list(range(R))
+    starts = sorted({b for _, b in leaves})
+    BLOCK = starts[1] if len(starts) > 1 else R + 1  # one block: any G > R
+    nblocks = -(-R // BLOCK)
     assert all(b == (a // BLOCK) * BLOCK for a, b in leaves)
     nodes = [(a, b, c) for (kind, a, b, c) in ops if kind == 2]
     assert len(nodes) == nblocks - 1

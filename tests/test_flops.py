@@ -47,10 +47,12 @@ def test_closed_form_matches_brute_force(m, n, T):
 
 
 def test_total_matches_survey_scale_at_4096():
-    """Sum over all nodes at 4096^2 with 16-wide tiles: ~1.75 mn(m+n) flop in
-    total (Appendix C's O(mn(m+n))), the bulk of it in the large nodes."""
+    """Sum over all nodes at 4096^2 with 16-wide tiles: ~1.8 mn(m+n) flop in
+    total (Appendix C's O(mn(m+n))), the bulk of it in the band products (the
+    leaves' in-block updates take the rest: 7 % with 12 tile anti-diagonals
+    per leaf block)."""
     ops = bk.solve_schedule(bk.F32, 4096, 4096)
     f = schedule_flops(4096, 4096, 16, ops)
     total = f["small"] + f["band"]
-    assert 1.6 * 4096 ** 3 * 2 < total < 1.8 * 4096 ** 3 * 2
-    assert f["band"] > 0.95 * total
+    assert 1.6 * 4096 ** 3 * 2 < total < 1.85 * 4096 ** 3 * 2
+    assert f["band"] > 0.9 * total
