@@ -172,11 +172,14 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
 }
 
 // ---- factor ---------------------------------------------------------------
-// Per side of order D: X (D^2), Y (D^2), Tmp ((D/2 + 64)^2) doubles; one info
-// word per side. When m == n both sides run in the same launches.
+// Per side of order D: X (D^2), Y (D^2), Tmp ((D/2 + 64)^2) doubles, and
+// the small nodes' Tmp buffers (64^2 + 128^2 + 256^2 + 512^2 doubles); one
+// info word per side. When m == n both sides run in the same launches.
+constexpr int64_t kTmpSmall = 64 * 64 + 128 * 128 + 256 * 256 + 512 * 512;
 size_t side_bytes(int64_t D) {
   const int64_t h = D / 2 + 64;
-  return 2 * align_up((size_t)(D * D) * 8) + align_up((size_t)(h * h) * 8);
+  return 2 * align_up((size_t)(D * D) * 8) + align_up((size_t)(h * h) * 8) +
+         align_up((size_t)kTmpSmall * 8);
 }
 
 struct FactorLayout {
@@ -196,6 +199,9 @@ FactorSide carve_side(char* base, int64_t D, int32_t* info) {
   f.X = reinterpret_cast<double*>(base);
   f.Y = reinterpret_cast<double*>(base + align_up((size_t)(D * D) * 8));
   f.Tmp = reinterpret_cast<double*>(base + 2 * align_up((size_t)(D * D) * 8));
+  const int64_t h = D / 2 + 64;
+  f.TmpS = reinterpret_cast<double*>(base + 2 * align_up((size_t)(D * D) * 8) +
+                                     align_up((size_t)(h * h) * 8));
   f.info = info;
   return f;
 }

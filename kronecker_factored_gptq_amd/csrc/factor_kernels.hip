@@ -334,18 +334,38 @@ static hipError_t chol_inv_rec(int64_t n, const FactorSide* sd, int ns, int64_t 
   h.M = n2; h.N = n2; h.K = n1; h.batch = ns;
   for (int z = 0; z < ns; ++z) { h.A[z] = sd[z].Y + o21; h.B[z] = sd[z].Y + o21; h.C[z] = sd[z].X + o22; }
   h.lda = n; h.ldb = n; h.ldc = n; h.transB = 1; h.lower_out = 1; h.alpha = -1.0; h.beta = 1.0;
-  if ((err = launch_gemm64(h, s)) != hipSuccess) return err;
-  if ((err = chol_inv_rec(n, sd, ns, off + n1, n2, s)) != hipSuccess) return err;
-  // Tmp = C21 Y11 (Y11 lower: column block c needs k >= c * 64)
+  // Tmp = C21 Y11 (Y11 lower: column block c needs k >= c * 64). A node of
+  // order up to 1024 forms it together with the Schur update, in one
+  // launch, into the buffer of its size class (the nodes inside the X22
+  // recursion are of smaller classes); larger nodes form it after the
+  // recursion, in the shared buffer.
+  int cls = -1;
+  for (int c = 0; c < 4; ++c)
+    if (len <= (int64_t)128 << c) { cls = c; break; }
   Gemm64Args t{};
   t.M = n2; t.N = n1; t.K = n1; t.batch = ns;
-  for (int z = 0; z < ns; ++z) { t.A[z] = sd[z].Y + o21; t.B[z] = sd[z].Y + o11; t.C[z] = sd[z].Tmp; }
   t.lda = n; t.ldb = n; t.ldc = n1; t.transB = 0; t.b_lower = 1; t.alpha = 1.0; t.beta = 0.0;
-  if ((err = launch_gemm64(t, s)) != hipSuccess) return err;
+  for (int z = 0; z < ns; ++z) {
+    double* tmp = sd[z].Tmp;
+    if (cls >= 0) {
+      int64_t o = 0;
+      for (int c = 0; c < cls; ++c) o += ((int64_t)64 << c) * ((int64_t)64 << c);
+      tmp = sd[z].TmpS + o;
+    }
+    t.A[z] = sd[z].Y + o21; t.B[z] = sd[z].Y + o11; t.C[z] = tmp;
+  }
+  if (cls >= 0) {
+    if ((err = launch_gemm64_pair(h, t, s)) != hipSuccess) return err;
+    if ((err = chol_inv_rec(n, sd, ns, off + n1, n2, s)) != hipSuccess) return err;
+  } else {
+    if ((err = launch_gemm64(h, s)) != hipSuccess) return err;
+    if ((err = chol_inv_rec(n, sd, ns, off + n1, n2, s)) != hipSuccess) return err;
+    if ((err = launch_gemm64(t, s)) != hipSuccess) return err;
+  }
   // Y21 = -Y22 Tmp (Y22 lower)
   Gemm64Args u{};
   u.M = n2; u.N = n1; u.K = n2; u.batch = ns;
-  for (int z = 0; z < ns; ++z) { u.A[z] = sd[z].Y + o22; u.B[z] = sd[z].Tmp; u.C[z] = sd[z].Y + o21; }
+  for (int z = 0; z < ns; ++z) { u.A[z] = sd[z].Y + o22; u.B[z] = t.C[z]; u.C[z] = sd[z].Y + o21; }
   u.lda = n; u.ldb = n1; u.ldc = n; u.transB = 0; u.a_lower = 1; u.alpha = -1.0; u.beta = 0.0;
   return launch_gemm64(u, s);
 }

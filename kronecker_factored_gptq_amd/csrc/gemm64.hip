@@ -34,11 +34,10 @@ struct BlockMap {
   int64_t bm, bn;
   int z;
 };
-template <bool TRI>
-__device__ inline BlockMap map_block(const Gemm64Args& a) {
-  if constexpr (!TRI) return BlockMap{(int64_t)blockIdx.y, (int64_t)blockIdx.x, (int)blockIdx.z};
-  const int64_t X = gridDim.x, Y = gridDim.y, Z = gridDim.z;
-  const int64_t lin = blockIdx.x + X * (blockIdx.y + Y * (int64_t)blockIdx.z);
+// block of linear workgroup number lin in a grid of X column blocks, Y row
+// blocks and Z problems
+__device__ inline BlockMap map_block_lin(const Gemm64Args& a, int64_t lin, int64_t X, int64_t Y,
+                                         int64_t Z) {
   BlockMap m;
   if (a.a_lower) {
     const int64_t q = lin / (X * Z), r = lin % (X * Z);
@@ -51,15 +50,24 @@ __device__ inline BlockMap map_block(const Gemm64Args& a) {
     m.bm = r % Y;
     m.z = (int)(r / Y);
   } else {
-    m.bm = blockIdx.y;
-    m.bn = blockIdx.x;
-    m.z = blockIdx.z;
+    m.bn = lin % X;
+    m.bm = (lin / X) % Y;
+    m.z = (int)(lin / (X * Y));
   }
   return m;
 }
+template <bool TRI>
+__device__ inline BlockMap map_block(const Gemm64Args& a) {
+  if constexpr (!TRI) return BlockMap{(int64_t)blockIdx.y, (int64_t)blockIdx.x, (int)blockIdx.z};
+  const int64_t X = gridDim.x, Y = gridDim.y, Z = gridDim.z;
+  return map_block_lin(a, blockIdx.x + X * (blockIdx.y + Y * (int64_t)blockIdx.z), X, Y, Z);
+}
 
+// One output block (bmap) of one problem; nbx = column blocks of the grid
+// (indexes the dot epilogue's per-block partials).
 template <int GB, bool VEC, bool TRI>
-__global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
+__device__ __forceinline__ void gemm64_block(const Gemm64Args& a, const BlockMap bmap,
+                                             int64_t nbx) {
   typedef Mfma<double> MF;
   typedef MF::acc_t acc_t;
   constexpr int WT = GB / 2, NBW = WT / 16;
@@ -72,7 +80,6 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int r16 = lane & 15, kg = lane >> 4;
-  const BlockMap bmap = map_block<TRI>(a);
   const int64_t bm = bmap.bm, bn = bmap.bn;
   const int z = bmap.z;
   const double* __restrict__ Ap = a.A[z];
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
     for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
     if (lane == 0) red[wave] = part;
     __syncthreads();
-    if (tid == 0) a.partial[z][bm * gridDim.x + bn] = ((red[0] + red[1]) + red[2]) + red[3];
+    if (tid == 0) a.partial[z][bm * nbx + bn] = ((red[0] + red[1]) + red[2]) + red[3];
     return;
   }
   if (skip) return;
@@ -274,6 +281,22 @@ __global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
           Cp[gr * a.ldc + gc] = v;
         }
       }
+}
+
+template <int GB, bool VEC, bool TRI>
+__global__ __launch_bounds__(256) void gemm64_kernel(Gemm64Args a) {
+  gemm64_block<GB, VEC, TRI>(a, map_block<TRI>(a), gridDim.x);
+}
+
+// Two independent products of one launch (one-dimensional grid: the blocks
+// of a0, then those of a1, each mapped as in gemm64_kernel).
+template <int GB, bool TRI>
+__global__ __launch_bounds__(256) void gemm64_pair_kernel(Gemm64Args a0, Gemm64Args a1,
+                                                          int64_t X0, int64_t Y0, int64_t X1,
+                                                          int64_t Y1) {
+  const int64_t w = blockIdx.x, n0 = X0 * Y0 * a0.batch;
+  if (w < n0) gemm64_block<GB, false, TRI>(a0, map_block_lin(a0, w, X0, Y0, a0.batch), X0);
+  else gemm64_block<GB, false, TRI>(a1, map_block_lin(a1, w - n0, X1, Y1, a1.batch), X1);
 }
 
 // Large-tile variant: BM x BN output blocks, WM x WN waves (64 * WM * WN
@@ -578,6 +601,39 @@ static hipError_t launch_gb(const Gemm64Args& a, bool vec, hipStream_t s) {
     if (tri) hipLaunchKernelGGL((gemm64_kernel<GB, false, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((gemm64_kernel<GB, false, false>), grid, dim3(256), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+// Block size of the 64 x 64 kernel family for a, or 0 when a goes to
+// another kernel (stream-K, 256 x 128, 128 x 128).
+static int small_block(const Gemm64Args& a) {
+  if (use_sk(a)) return 0;
+  if (!a.a_lower && !a.b_lower && !a.dot[0] &&
+      ((a.M + 255) / 256) * ((a.N + 127) / 128) * a.batch >= 256)
+    return 0;
+  if (use_big(a)) return 0;
+  const int64_t b64 = ((a.M + 63) / 64) * ((a.N + 63) / 64) * a.batch;
+  return (!a.dot[0] && b64 <= 128) ? 32 : 64;
+}
+
+hipError_t launch_gemm64_pair(const Gemm64Args& a0, const Gemm64Args& a1, hipStream_t s) {
+  const int g0 = small_block(a0), g1 = small_block(a1);
+  const bool empty0 = a0.M <= 0 || a0.N <= 0, empty1 = a1.M <= 0 || a1.N <= 0;
+  if (empty0 || empty1 || g0 == 0 || g0 != g1 || a0.dot[0] || a1.dot[0] || a0.batch != a1.batch ||
+      a0.batch < 1 || a0.batch > 2) {
+    const hipError_t e = launch_gemm64(a0, s);
+    return e != hipSuccess ? e : launch_gemm64(a1, s);
+  }
+  const int GB = g0;
+  const int64_t X0 = (a0.N + GB - 1) / GB, Y0 = (a0.M + GB - 1) / GB;
+  const int64_t X1 = (a1.N + GB - 1) / GB, Y1 = (a1.M + GB - 1) / GB;
+  const int64_t nwg = (X0 * Y0 + X1 * Y1) * a0.batch;
+  if (GB == 32)
+    hipLaunchKernelGGL((gemm64_pair_kernel<32, true>), dim3((unsigned)nwg), dim3(256), 0, s, a0,
+                       a1, X0, Y0, X1, Y1);
+  else
+    hipLaunchKernelGGL((gemm64_pair_kernel<64, true>), dim3((unsigned)nwg), dim3(256), 0, s, a0,
+                       a1, X0, Y0, X1, Y1);
   return hipGetLastError();
 }
 

@@ -70,6 +70,7 @@ struct FactorSide {
   double* X;
   double* Y;
   double* Tmp;
+  double* TmpS;  // one C21 Y11 buffer per node-size class (orders up to 1024)
   int32_t* info;
 };
 // Y = Cholesky(X)^-1 for `nsides` (1 or 2) matrices of the same order n, in
@@ -113,6 +114,9 @@ struct Gemm64Args {
   int sym_dot;
 };
 hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s);
+// Two independent products: one launch when both go to the same 64 x 64 /
+// 32 x 32 kernel (no dot epilogue), else two launches in order.
+hipError_t launch_gemm64_pair(const Gemm64Args& a0, const Gemm64Args& a1, hipStream_t s);
 // Upper bound of the partials a dot-epilogue product of this shape writes
 // (per-block or per-workgroup; for workspace sizing), and the exact count a
 // given product writes.
