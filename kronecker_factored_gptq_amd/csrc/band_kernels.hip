@@ -326,13 +326,15 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
   }
 }
 
-// Macro-tile size: 4 x 4 solver tiles (64 x 64) for float and 2 x 2 (32 x 32)
-// for double, with a wide-band option kept for tuning. Measured on the
-// 4096 x 4096 float32 solve: 64 x 64 tiles everywhere (four workgroups per
-// CU) beat 128 x 128 tiles on the wide bands (two per CU): 5.2 ms against
-// 7.6 ms for all band products.
+// Macro-tile size by node width l - k (tile anti-diagonals): 2 x 2 solver
+// tiles (32 x 32) below QMIN_BIG, 4 x 4 (64 x 64) from it on. Measured on
+// the 4096 x 4096 float32 solve (leaf blocks of 12): 32 x 32 for every node
+// but the top one (widths up to 259) gives 8.05 ms for the solve against
+// 8.63 with 64 x 64 everywhere and 8.18 with 32 x 32 everywhere (more
+// workgroups and less padding on the narrow bands); 128 x 128 tiles were
+// slower still.
 template <typename R> struct BandChoice;
-template <> struct BandChoice<float> { static constexpr int BIG = 4, SMALL = 4, QMIN_BIG = 1 << 30; };
+template <> struct BandChoice<float> { static constexpr int BIG = 4, SMALL = 2, QMIN_BIG = 300; };
 template <> struct BandChoice<double> { static constexpr int BIG = 4, SMALL = 2, QMIN_BIG = 32; };
 
 template <typename R, int MB>
