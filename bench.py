@@ -47,7 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "w512"])
+    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "w512", "kv28"],
+                    help="attn4096: the 4096 x 4096 matrix (default); w512: 512 x 512; kv28: "
+                         "28 k/v projections of 1024 x 2048, batched solve")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true",
                     help="skip the instrumented steps (per-launch band events); roofline omitted")
@@ -137,6 +139,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.workload == "kv28":
+        bench_kv28(args, dev)
+        return
     p = config3() if args.workload == "attn4096" else config2()
     m, n = p.W.shape
     hi = p.scale_hi
@@ -252,6 +257,125 @@ def main():
             "useful_flop": fl["band"] + fl["small"], "small_node_flop": fl["small"]}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, hi)
+    print(json.dumps(result))
+
+
+def bench_kv28(args, dev):
+    """28 k/v projections (1024 x 2048, each with its own Wishart A and B,
+    4-bit per-row scales). One step = the 28 factorisations, the 28 row-scale
+    vectors, ONE batched solve of all 28 (bakron_solve_batched) and the 28
+    losses. Also timed: the same 28 solves issued one by one round-robin on
+    four streams, the way a caller without the batched entry point runs them."""
+    import numpy as np
+    import torch
+
+    import kronecker_factored_gptq_amd as bk
+    from synth import config5
+
+    nb = 28
+    probs = [config5(i) for i in range(nb)]
+    m, n = probs[0].W.shape
+    lo_, hi_, unb = probs[0].alphabet
+    hi = probs[0].scale_hi
+    W = torch.stack([torch.from_numpy(p.W) for p in probs]).to(dev)
+    A = [torch.from_numpy(p.A).to(dev) for p in probs]
+    B = [torch.from_numpy(p.B).to(dev) for p in probs]
+    code = bk.F32
+    wsF = torch.empty(bk.workspace_bytes("factor", code, m, n), dtype=torch.uint8, device=dev)
+    wsL = torch.empty(bk.workspace_bytes("loss", code, m, n), dtype=torch.uint8, device=dev)
+    wsB = torch.empty(int(bk.lib().bakron_solve_batched_workspace_bytes(code, nb, m, n)),
+                      dtype=torch.uint8, device=dev)
+    LA = torch.empty((nb, n, n), dtype=torch.float32, device=dev)
+    LB = torch.empty((nb, m, m), dtype=torch.float32, device=dev)
+    S = torch.empty((nb, m), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    streams = [torch.cuda.Stream(dev) for _ in range(4)]
+    wsS = [torch.empty(bk.workspace_bytes("solve", code, m, n), dtype=torch.uint8, device=dev)
+           for _ in streams]
+    Vs = torch.empty((nb, m, n), dtype=torch.int32, device=dev)
+    ev = {k: [] for k in ("t0", "t1", "t2", "t3", "t4")}
+
+    def step(record: bool):
+        es = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        if record:
+            es[0].record(stream)
+        for i in range(nb):
+            la, lb, _, _ = bk.factor(A[i], B[i], workspace=wsF)
+            LA[i].copy_(la)
+            LB[i].copy_(lb)
+        if record:
+            es[1].record(stream)
+        for i in range(nb):
+            S[i].copy_(bk.row_scales(W[i], hi))
+        if record:
+            es[2].record(stream)
+        V = bk.solve_batched(W, LA, LB, (lo_, hi_, unb), S, workspace=wsB)
+        if record:
+            es[3].record(stream)
+        out = [bk.loss(W[i], V[i], A[i], B[i], S[i], workspace=wsL, sync=False) for i in range(nb)]
+        if record:
+            es[4].record(stream)
+            for k, e in zip(("t0", "t1", "t2", "t3", "t4"), es):
+                ev[k].append(e)
+        return out
+
+    def solve_streams():
+        cur = torch.cuda.current_stream(dev)
+        for st in streams:
+            st.wait_stream(cur)
+        for i in range(nb):
+            j = i % len(streams)
+            with torch.cuda.stream(streams[j]):
+                bk.solve(W[i], LA[i], LB[i], (lo_, hi_, unb), S[i], workspace=wsS[j], out=Vs[i])
+        for st in streams:
+            cur.wait_stream(st)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    def phase(a, b):
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
+
+    phases = {"factor": phase("t0", "t1"), "scales": phase("t1", "t2"),
+              "solve": phase("t2", "t3"), "loss": phase("t3", "t4")}
+    # the solves alone: batched against four streams, same inputs
+    solve_streams()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        solve_streams()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    streams_ms = e0.elapsed_time(e1) / args.steps
+    total = nb * m * n
+    result = {
+        "metric": "weights quantized/s (m·n/solve-time), 28 x (1024x2048)",
+        "value": total / (ms_per_step / 1e3), "unit": "weights/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "28 k/v projections 1024x2048 float32, Wishart(4096 dof)/4096 A and B "
+                               "+1% mean-diag damping, alphabet {-8..7}, per-row absmax/7 scales",
+                   "m": m, "n": n, "batch": nb,
+                   "step": "28 factors + 28 row scales + one batched solve + 28 losses"},
+        "phases_ms": phases,
+        "solve_only": {"ms": phases["solve"], "weights_per_s": total / (phases["solve"] / 1e3),
+                       "entry": "bakron_solve_batched"},
+        "solve_four_streams": {"ms": streams_ms, "weights_per_s": total / (streams_ms / 1e3),
+                               "entry": "bakron_solve x 28, round-robin on 4 streams"},
+    }
+    if not args.no_cpu_baseline:
+        # bounded sample: the oracle on one of the 28 matrices
+        cb = cpu_baseline(probs[0], hi)
+        cb["sample"] = "one of the 28 matrices, " + cb["sample"]
+        result["cpu_baseline"] = cb
     print(json.dumps(result))
 
 

@@ -155,6 +155,33 @@ int bakron_solve_timed(int dtype, int64_t m, int64_t n,
                        double *op_ms, int64_t n_ops);
 
 /* ------------------------------------------------------------------------
+ * Batched solve: bakron_solve on `batch` problems of the same shape (m x n)
+ * in one sequence of launches, for many small matrices: every linear module
+ * of a model is its own problem (§3.6 costs the solve per module), and a
+ * small problem alone leaves most of the GPU idle (a 1024 x 2048 matrix has
+ * at most 64 tiles per tile anti-diagonal). Problem b uses W + b * stride_w, LA + b * stride_la,
+ * LB + b * stride_lb, scales + b * stride_s and writes V + b * stride_v,
+ * Wt + b * stride_wt; strides are in elements. Input strides may be 0 (one
+ * array shared by every problem, e.g. a common factor); for batch > 1 the
+ * output strides must be at least (m - 1) * ld + n, so that the outputs of
+ * different problems do not overlap. Each problem's result is bit-identical
+ * to bakron_solve on the same inputs (same kernels, same order of
+ * operations). 0 <= batch <= 65535. The workspace is batch times that of
+ * bakron_solve (bakron_solve_batched_workspace_bytes). Other arguments,
+ * errors and asynchrony as for bakron_solve.
+ * ------------------------------------------------------------------------ */
+size_t bakron_solve_batched_workspace_bytes(int dtype, int64_t batch, int64_t m, int64_t n);
+int bakron_solve_batched(int dtype, int64_t batch, int64_t m, int64_t n,
+                         const void *W, int64_t ldw, int64_t stride_w,
+                         const void *LA, int64_t ldla, int64_t stride_la,
+                         const void *LB, int64_t ldlb, int64_t stride_lb,
+                         int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded,
+                         int scale_mode, const void *scales, int64_t stride_s,
+                         int32_t *V, int64_t ldv, int64_t stride_v,
+                         void *Wt, int64_t ldwt, int64_t stride_wt,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Loss: tr(B (W - Q) A (W - Q)^T) with Q = s (.) V, the quadratic form of
  * vec(W - Q) under A (x) B (Proposition 3.1, §3.1). Evaluated in float64 as
  * sum_ij (B D)_ij (D A)_ij with D = W - Q (A symmetric).

@@ -18,7 +18,7 @@ from typing import Optional, Sequence, Tuple, Union
 import torch
 
 __all__ = ["F32", "F64", "SCALE_NONE", "SCALE_ROW", "SCALE_COL", "BakronError", "lib", "factor",
-           "solve", "loss", "row_scales", "solve_schedule", "tile_size", "workspace_bytes"]
+           "solve", "solve_batched", "loss", "row_scales", "solve_schedule", "tile_size", "workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libbakron.so")
@@ -73,6 +73,12 @@ def lib() -> ctypes.CDLL:
     L.bakron_solve_timed.restype = _int
     L.bakron_solve_schedule.argtypes = [_int, _i64, _i64, _vp, _i64]
     L.bakron_solve_schedule.restype = _i64
+    L.bakron_solve_batched_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
+    L.bakron_solve_batched_workspace_bytes.restype = _sz
+    L.bakron_solve_batched.argtypes = [_int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                       _vp, _i64, _i64, _i32, _i32, _i32, _int, _vp, _i64,
+                                       _vp, _i64, _i64, _vp, _i64, _i64, _vp, _sz, _vp]
+    L.bakron_solve_batched.restype = _int
     L.bakron_loss.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp, _vp, _i64, _vp,
                               _i64, _vp, _vp, _sz, _vp]
     L.bakron_loss.restype = _int
@@ -233,6 +239,70 @@ def solve(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: Alphabe
             rc = L.bakron_solve_timed(*args, ctypes.cast(op_ms, ctypes.c_void_p), len(op_ms))
     if rc != OK:
         raise BakronError(rc, "bakron_solve")
+    return (V, Wt) if return_wt else V
+
+
+def _batch_operand(t: torch.Tensor, rows: int, cols: int, batch: int, name: str):
+    """(pointer, ld, stride) of a batched operand: a (batch, rows, cols)
+    tensor, or a single (rows, cols) matrix shared by every problem."""
+    if t.dim() == 2:
+        if t.shape != (rows, cols):
+            raise ValueError(f"{name} must be {rows} x {cols}")
+        return _p(t), _ld(t, name), 0
+    if t.dim() != 3 or t.shape != (batch, rows, cols):
+        raise ValueError(f"{name} must be ({batch}, {rows}, {cols}) or ({rows}, {cols})")
+    if cols > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    ld = max(int(t.stride(1)), cols, 1)
+    return _p(t), ld, int(t.stride(0)) if batch > 1 else 0
+
+
+def solve_batched(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor,
+                  alphabet: AlphabetLike = (0, 0, 1), scales: Optional[torch.Tensor] = None,
+                  scale_mode: Optional[int] = None, return_wt: bool = False,
+                  workspace: Optional[torch.Tensor] = None):
+    """bakron_solve on a batch of problems of one shape in the same launches.
+    W is (batch, m, n); LA is (batch, n, n) or one (n, n) factor shared by
+    all problems, LB likewise (batch, m, m) or (m, m); scales (batch, m) /
+    (batch, n) or one shared vector. Returns int32 codes (batch, m, n) and,
+    with ``return_wt``, the values at rounding. Each problem's result equals
+    ``solve`` on the same inputs bit for bit."""
+    dev = _check_device(W, LA, LB, scales, workspace)
+    code = _dt(W)
+    if W.dim() != 3:
+        raise ValueError("W must be (batch, m, n)")
+    batch, m, n = W.shape
+    if LA.dtype != W.dtype or LB.dtype != W.dtype:
+        raise ValueError("LA and LB must have W's dtype")
+    pw, ldw, sw = _batch_operand(W, m, n, batch, "W")
+    pla, ldla, sla = _batch_operand(LA, n, n, batch, "LA")
+    plb, ldlb, slb = _batch_operand(LB, m, m, batch, "LB")
+    lo, hi, unb = (int(alphabet[0]), int(alphabet[1]), int(bool(alphabet[2])))
+    ss = 0
+    if scales is None:
+        if scale_mode not in (None, SCALE_NONE):
+            raise ValueError("scales required for this scale_mode")
+        mode = SCALE_NONE
+    else:
+        if scales.dtype != W.dtype or not scales.is_contiguous():
+            raise ValueError("scales must be contiguous with W's dtype")
+        vec = scales if scales.dim() == 1 else scales[0]
+        if scales.dim() not in (1, 2) or (scales.dim() == 2 and scales.size(0) != batch):
+            raise ValueError("scales must be (batch, length) or (length,)")
+        mode = _scale_mode(vec, m, n, scale_mode)
+        ss = int(scales.stride(0)) if scales.dim() == 2 and batch > 1 else 0
+    V = torch.empty((batch, m, n), dtype=torch.int32, device=dev)
+    Wt = torch.empty((batch, m, n), dtype=W.dtype, device=dev) if return_wt else None
+    L = lib()
+    ws = _workspace(L.bakron_solve_batched_workspace_bytes(code, batch, m, n), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.bakron_solve_batched(code, batch, m, n, pw, ldw, sw, pla, ldla, sla, plb, ldlb, slb,
+                                    lo, hi, unb, mode, _p(scales), ss, _p(V), max(n, 1), m * n,
+                                    _p(Wt), max(n, 1) if return_wt else 0,
+                                    m * n if return_wt else 0, _p(ws),
+                                    ws.numel() * ws.element_size(), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_solve_batched")
     return (V, Wt) if return_wt else V
 
 

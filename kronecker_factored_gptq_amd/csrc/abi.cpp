@@ -7,6 +7,7 @@
 // .hip files; nothing here touches matrix data.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 #include <cstring>
@@ -21,6 +22,8 @@ namespace {
 using namespace bk;
 
 constexpr size_t kAlign = 256;
+// largest batch of bakron_solve_batched: the grid's y extent
+constexpr int64_t kMaxBatch = 65535;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -84,13 +87,19 @@ template <typename R>
 int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64_t ldla,
                const R* LB, int64_t ldlb, int32_t lo, int32_t hi, int32_t unb, int scale_mode,
                const R* scales, int32_t* V, int64_t ldv, R* Wt, int64_t ldwt, void* ws,
-               hipStream_t s, double* op_ms = nullptr) {
+               hipStream_t s, double* op_ms = nullptr, int batch = 1,
+               const BatchStrides* strides = nullptr) {
   SolveGeom g;
   g.m = m;
   g.n = n;
   g.Mt = (int)tiles(m);
   g.Nt = (int)tiles(n);
   const SolveLayout lay = solve_layout(sizeof(R) == 8 ? BAKRON_F64 : BAKRON_F32, m, n);
+  // a batch: the same launches for every problem, each with its own
+  // workspace of lay.total bytes (a multiple of the alignment)
+  g.batch = batch;
+  if (strides) g.bs = *strides;
+  g.bs.ws = batch > 1 ? (int64_t)(lay.total / sizeof(R)) : 0;
   char* base = static_cast<char*>(ws);
   R* Wk = reinterpret_cast<R*>(base);
   R* LBp = reinterpret_cast<R*>(base + lay.wk);
@@ -107,8 +116,8 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   const R* scB = scale_mode == 1 ? scales : nullptr;
   const R* scA = scale_mode == 2 ? scales : nullptr;
   if (launch_pack_w<R>(g, W, ldw, scales, scale_mode, Wk, s) != hipSuccess) return BAKRON_EHIP;
-  if (launch_pack_l<R>(m, g.Mt, LB, ldlb, scB, LBp, s) != hipSuccess) return BAKRON_EHIP;
-  if (launch_pack_l<R>(n, g.Nt, LA, ldla, scA, LAp, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_pack_l<R>(g, true, LB, ldlb, scB, LBp, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_pack_l<R>(g, false, LA, ldla, scA, LAp, s) != hipSuccess) return BAKRON_EHIP;
 
   LeafParams<R> lp;
   lp.lo = unb ? -std::numeric_limits<R>::infinity() : (R)lo;
@@ -405,6 +414,60 @@ int bakron_solve_timed(int dtype, int64_t m, int64_t n, const void* W, int64_t l
   return solve_entry(dtype, m, n, W, ldw, LA, ldla, LB, ldlb, alpha_lo, alpha_hi, unbounded,
                      scale_mode, scales, V, ldv, Wt, ldwt, workspace, workspace_bytes, stream,
                      op_ms, n_ops);
+}
+
+size_t bakron_solve_batched_workspace_bytes(int dtype, int64_t batch, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || batch < 0 || m < 0 || n < 0) return 0;
+  const size_t one = solve_layout(dtype, m, n).total;
+  if (batch > 0 && one > std::numeric_limits<size_t>::max() / (size_t)batch) return 0;
+  return (size_t)batch * one;
+}
+
+int bakron_solve_batched(int dtype, int64_t batch, int64_t m, int64_t n, const void* W,
+                         int64_t ldw, int64_t stride_w, const void* LA, int64_t ldla,
+                         int64_t stride_la, const void* LB, int64_t ldlb, int64_t stride_lb,
+                         int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded, int scale_mode,
+                         const void* scales, int64_t stride_s, int32_t* V, int64_t ldv,
+                         int64_t stride_v, void* Wt, int64_t ldwt, int64_t stride_wt,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || batch < 0 || m < 0 || n < 0) return BAKRON_EINVAL;
+  if (batch > kMaxBatch) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (batch == 0 || m == 0 || n == 0) return BAKRON_OK;
+  if (!W || !LA || !LB || !V) return BAKRON_EINVAL;
+  if (ldw < n || ldla < n || ldlb < m || ldv < n) return BAKRON_EINVAL;
+  if (Wt && ldwt < n) return BAKRON_EINVAL;
+  if (!unbounded && alpha_lo > alpha_hi) return BAKRON_EINVAL;
+  if (scale_mode == BAKRON_SCALE_NONE) {
+    if (scales) return BAKRON_EINVAL;
+  } else if (scale_mode == BAKRON_SCALE_ROW || scale_mode == BAKRON_SCALE_COL) {
+    if (!scales) return BAKRON_EINVAL;
+  } else {
+    return BAKRON_EINVAL;
+  }
+  // inputs may be shared (stride 0); the outputs of different problems must
+  // not overlap
+  if (stride_w < 0 || stride_la < 0 || stride_lb < 0 || stride_s < 0) return BAKRON_EINVAL;
+  const int64_t span_v = (m - 1) * ldv + n, span_wt = Wt ? (m - 1) * ldwt + n : 0;
+  if (batch > 1 && (stride_v < span_v || (Wt && stride_wt < span_wt))) return BAKRON_EINVAL;
+  const int64_t top = batch - 1;
+  const int64_t big = std::max(std::max(std::max(stride_w, stride_la), std::max(stride_lb, stride_s)),
+                               std::max(batch > 1 ? stride_v : 0, Wt && batch > 1 ? stride_wt : 0));
+  if (top > 0 && big > std::numeric_limits<int64_t>::max() / 2 / top) return BAKRON_EINVAL;
+  const size_t need = bakron_solve_batched_workspace_bytes(dtype, batch, m, n);
+  if (!workspace || need == 0 || workspace_bytes < need) return BAKRON_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  BatchStrides bs = {stride_w, stride_s, stride_la, stride_lb, stride_v, Wt ? stride_wt : 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == BAKRON_F32)
+    return solve_impl<float>(m, n, (const float*)W, ldw, (const float*)LA, ldla,
+                             (const float*)LB, ldlb, alpha_lo, alpha_hi, unbounded, scale_mode,
+                             (const float*)scales, V, ldv, (float*)Wt, ldwt, workspace, s, nullptr,
+                             (int)batch, &bs);
+  return solve_impl<double>(m, n, (const double*)W, ldw, (const double*)LA, ldla,
+                            (const double*)LB, ldlb, alpha_lo, alpha_hi, unbounded, scale_mode,
+                            (const double*)scales, V, ldv, (double*)Wt, ldwt, workspace, s,
+                            nullptr, (int)batch, &bs);
 }
 
 int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t* ops, int64_t max_ops) {

@@ -115,9 +115,10 @@ struct BandArgs {
   const R* LBp;
   const R* LAp;
   R* Mb;
+  int64_t sws;  // workspace stride between the problems of a batch (elements)
 };
 
-// One-dimensional grid of nPb8 * maxw workgroups, nPb8 = row blocks rounded up
+// One-dimensional grid (per problem of a batch: blockIdx.y) of nPb8 * maxw workgroups, nPb8 = row blocks rounded up
 // to a multiple of the 8 XCDs. Workgroup w runs on XCD w % 8 (round-robin
 // dispatch), and all workgroups of one row block go to the same XCD, so a row
 // panel of the left operand is fetched into one L2 only. Within an XCD the
@@ -170,10 +171,11 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
   const int P0 = bt.P0, C0 = bt.C0;
   const int Klo = bt.Klo, Khi = bt.Khi;
 
-  R* __restrict__ Wk = a.Wk;
-  const R* __restrict__ LBp = a.LBp;
-  const R* __restrict__ LAp = a.LAp;
-  R* __restrict__ Mb = a.Mb;
+  const int64_t bo = (int64_t)blockIdx.y * a.sws;
+  R* __restrict__ Wk = a.Wk + bo;
+  const R* __restrict__ LBp = a.LBp + bo;
+  const R* __restrict__ LAp = a.LAp + bo;
+  R* __restrict__ Mb = a.Mb + bo;
 
   acc_t acc[S::NBW][S::NBW];
 #pragma unroll
@@ -359,8 +361,11 @@ static hipError_t launch_band_mb(const SolveGeom& g, int k, int mid, int l, int 
   a.k = k; a.mid = mid; a.l = l; a.Mt = g.Mt; a.Nt = g.Nt;
   a.maxw = maxw;
   a.Wk = bb.Wk; a.LBp = bb.LBp; a.LAp = bb.LAp; a.Mb = bb.Mb;
+  a.sws = g.bs.ws;
   const int nPb8 = (nPb + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid((unsigned)(nPb8 * maxw)), block(256);
+  // nPb8 * maxw is a multiple of the XCD count, so in the 2-D grid workgroup
+  // (x, y) still lands on XCD x % 8
+  const dim3 grid((unsigned)(nPb8 * maxw), (unsigned)(g.batch > 0 ? g.batch : 1)), block(256);
   if (ev0 || ev1) {
     // the events are stamped by the dispatch packet itself: exact kernel time
     if (stage == 1)

@@ -10,18 +10,31 @@ namespace bk {
 // and the masks of the band products.
 constexpr int kTile = 16;
 
+// Element strides between consecutive problems of a batched solve (problem b
+// of a launch is blockIdx.y); a stride of 0 shares one array across the batch.
+struct BatchStrides {
+  int64_t w;       // W
+  int64_t s;       // scales
+  int64_t la, lb;  // the caller's factors L^A, L^B
+  int64_t v, wt;   // outputs V and Wt
+  int64_t ws;      // the per-problem solve workspace, in elements
+};
+
 struct SolveGeom {
   int64_t m, n;
-  int Mt, Nt;  // tiles per column / row direction
+  int Mt, Nt;     // tiles per column / row direction
+  int batch = 1;  // problems of the same shape, solved in the same launches
+  BatchStrides bs = {0, 0, 0, 0, 0, 0, 0};
 };
 
 // ---- solve (solve_kernels.hip) --------------------------------------------
 template <typename R>
 hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, const R* scales,
                          int scale_mode, R* Wk, hipStream_t s);
+// L^B (lb = true) or L^A of every problem of g's batch.
 template <typename R>
-hipError_t launch_pack_l(int64_t dim, int Dt, const R* L, int64_t ld, const R* scales, R* Lp,
-                         hipStream_t s);
+hipError_t launch_pack_l(const SolveGeom& g, bool lb, const R* L, int64_t ld, const R* scales,
+                         R* Lp, hipStream_t s);
 
 template <typename R>
 struct LeafParams {

@@ -41,7 +41,12 @@ template <typename R, int T>
 __global__ __launch_bounds__(256) void pack_w_kernel(int64_t m, int64_t n, int Nt,
                                                      const R* __restrict__ W, int64_t ldw,
                                                      const R* __restrict__ sc, int mode,
-                                                     R* __restrict__ Wk) {
+                                                     R* __restrict__ Wk, BatchStrides bs) {
+  // problem blockIdx.y of a batch
+  const int64_t b = blockIdx.y;
+  W += b * bs.w;
+  if (sc) sc += b * bs.s;
+  Wk += b * bs.ws;
   const int64_t tile = blockIdx.x;
   const int64_t P = tile / Nt, Q = tile % Nt;
   R* dst = Wk + tile * T * T;
@@ -62,8 +67,13 @@ __global__ __launch_bounds__(256) void pack_w_kernel(int64_t m, int64_t n, int N
 // diagonal is 1, everything above it and on padding 0.
 template <typename R, int T>
 __global__ __launch_bounds__(256) void pack_l_kernel(int64_t dim, const R* __restrict__ L,
-                                                     int64_t ld, const R* __restrict__ sc,
-                                                     R* __restrict__ Lp) {
+                                                     int64_t ld, int64_t sL,
+                                                     const R* __restrict__ sc, int64_t sS,
+                                                     R* __restrict__ Lp, int64_t sLp) {
+  const int64_t b = blockIdx.y;  // problem of a batch
+  L += b * sL;
+  if (sc) sc += b * sS;
+  Lp += b * sLp;
   const int64_t t = blockIdx.x;
   int64_t P = (int64_t)((__builtin_sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
   while (P * (P + 1) / 2 > t) --P;
@@ -176,8 +186,18 @@ template <typename R>
 __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt, int64_t m,
                                                    int64_t n, R* __restrict__ Wk,
                                                    const R* __restrict__ LBp,
-                                                   const R* __restrict__ LAp, LeafParams<R> lp) {
+                                                   const R* __restrict__ LAp, LeafParams<R> lp,
+                                                   BatchStrides bs) {
   constexpr int T = 16;
+  {  // problem blockIdx.y of a batch: its workspace and outputs
+    const int64_t b = blockIdx.y;
+    Wk += b * bs.ws;
+    LBp += b * bs.ws;
+    LAp += b * bs.ws;
+    lp.V += b * bs.v;
+    if (lp.Wt) lp.Wt += b * bs.wt;
+    if (lp.scales) lp.scales += b * bs.s;
+  }
   typedef Mfma<R> MF;
   typedef typename MF::acc_t acc_t;
   __shared__ R red[3][T][T + 1];
@@ -336,19 +356,21 @@ template <typename R>
 hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, const R* scales,
                          int scale_mode, R* Wk, hipStream_t s) {
   const int64_t nt = (int64_t)g.Mt * g.Nt;
-  if (nt == 0) return hipSuccess;
-  hipLaunchKernelGGL((pack_w_kernel<R, kTile>), dim3((unsigned)nt), dim3(256), 0, s, g.m, g.n,
-                     g.Nt, W, ldw, scales, scale_mode, Wk);
+  if (nt == 0 || g.batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL((pack_w_kernel<R, kTile>), dim3((unsigned)nt, (unsigned)g.batch), dim3(256),
+                     0, s, g.m, g.n, g.Nt, W, ldw, scales, scale_mode, Wk, g.bs);
   return hipGetLastError();
 }
 
 template <typename R>
-hipError_t launch_pack_l(int64_t dim, int Dt, const R* L, int64_t ld, const R* scales, R* Lp,
-                         hipStream_t s) {
+hipError_t launch_pack_l(const SolveGeom& g, bool lb, const R* L, int64_t ld, const R* scales,
+                         R* Lp, hipStream_t s) {
+  const int64_t dim = lb ? g.m : g.n;
+  const int Dt = lb ? g.Mt : g.Nt;
   const int64_t nt = (int64_t)Dt * (Dt + 1) / 2;
-  if (nt == 0) return hipSuccess;
-  hipLaunchKernelGGL((pack_l_kernel<R, kTile>), dim3((unsigned)nt), dim3(256), 0, s, dim, L, ld,
-                     scales, Lp);
+  if (nt == 0 || g.batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL((pack_l_kernel<R, kTile>), dim3((unsigned)nt, (unsigned)g.batch), dim3(256),
+                     0, s, dim, L, ld, lb ? g.bs.lb : g.bs.la, scales, g.bs.s, Lp, g.bs.ws);
   return hipGetLastError();
 }
 
@@ -364,15 +386,16 @@ hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, c
   int lo, hi;
   diag_range(g, K, &lo, &hi);
   if (hi < lo) return hipSuccess;
-  hipLaunchKernelGGL((leaf_kernel<R>), dim3(hi - lo + 1), dim3(256), 0, s, K, K0, g.Mt, g.Nt,
-                     g.m, g.n, Wk, LBp, LAp, lp);
+  if (g.batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL((leaf_kernel<R>), dim3(hi - lo + 1, g.batch), dim3(256), 0, s, K, K0, g.Mt,
+                     g.Nt, g.m, g.n, Wk, LBp, LAp, lp, g.bs);
   return hipGetLastError();
 }
 
 #define BK_INST(R)                                                                              \
   template hipError_t launch_pack_w<R>(const SolveGeom&, const R*, int64_t, const R*, int, R*,  \
                                        hipStream_t);                                            \
-  template hipError_t launch_pack_l<R>(int64_t, int, const R*, int64_t, const R*, R*,          \
+  template hipError_t launch_pack_l<R>(const SolveGeom&, bool, const R*, int64_t, const R*, R*, \
                                        hipStream_t);                                            \
   template hipError_t launch_leaf<R>(const SolveGeom&, int, int, R*, const R*, const R*,        \
                                      const LeafParams<R>&, hipStream_t);

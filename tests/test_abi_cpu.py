@@ -75,6 +75,42 @@ def test_solve_empty_is_noop():
     assert _solve(n=0, W=None, LA=None, LB=None, V=None, ws=None) == bk.OK
 
 
+def _solve_batched(**kw):
+    a = dict(dtype=bk.F32, batch=3, m=4, n=4, W=FAKE, ldw=4, sw=16, LA=FAKE, ldla=4, sla=16,
+             LB=FAKE, ldlb=4, slb=16, lo=-8, hi=7, unb=0, mode=0, scales=None, ss=0, V=FAKE,
+             ldv=4, sv=16, Wt=None, ldwt=0, swt=0, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return bk.lib().bakron_solve_batched(
+        a["dtype"], a["batch"], a["m"], a["n"], a["W"], a["ldw"], a["sw"], a["LA"], a["ldla"],
+        a["sla"], a["LB"], a["ldlb"], a["slb"], a["lo"], a["hi"], a["unb"], a["mode"], a["scales"],
+        a["ss"], a["V"], a["ldv"], a["sv"], a["Wt"], a["ldwt"], a["swt"], a["ws"], a["wsb"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(dtype=5), dict(batch=-1), dict(batch=65536), dict(m=-1), dict(W=None), dict(LB=None),
+    dict(V=None), dict(ldw=3), dict(ldv=3), dict(lo=3, hi=2), dict(mode=1, scales=None),
+    dict(mode=0, scales=FAKE), dict(sw=-1), dict(sla=-4), dict(ss=-1, mode=1, scales=FAKE),
+    # outputs of different problems would overlap
+    dict(sv=15), dict(sv=0), dict(Wt=FAKE, ldwt=4, swt=8),
+    dict(ws=None), dict(wsb=16), dict(ws=ctypes.c_void_p(0x1001)),
+    # strides whose offsets overflow
+    dict(sw=1 << 62),
+])
+def test_solve_batched_rejects_bad_arguments(bad):
+    assert _solve_batched(**bad) == bk.EINVAL
+
+
+def test_solve_batched_empty_and_workspace():
+    assert _solve_batched(batch=0, W=None, LA=None, LB=None, V=None, ws=None) == bk.OK
+    assert _solve_batched(m=0, W=None, LA=None, LB=None, V=None, ws=None) == bk.OK
+    L = bk.lib()
+    one = L.bakron_solve_workspace_bytes(bk.F32, 100, 70)
+    assert L.bakron_solve_batched_workspace_bytes(bk.F32, 5, 100, 70) == 5 * one
+    assert L.bakron_solve_batched_workspace_bytes(bk.F32, -1, 100, 70) == 0
+    assert L.bakron_solve_batched_workspace_bytes(bk.F32, 0, 100, 70) == 0
+
+
 def test_factor_and_loss_reject_bad_arguments():
     L = bk.lib()
     bad = (ctypes.c_int64 * 2)(7, 7)

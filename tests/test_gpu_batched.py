@@ -1,0 +1,91 @@
+"""Batched solve (bakron_solve_batched): several problems of one shape in the
+same launches. Every problem's result must equal the single-problem solve on
+the same inputs bit for bit (same kernels, same order of operations), and,
+in float64, the oracle's codes exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import random_problem
+
+from parity_util import oracle_solve, prepare, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # (batch, m, n, alphabet, scale rule)
+    (3, 50, 70, (-8, 7, 0), "row"),
+    (4, 37, 1, (0, 0, 1), None),
+    (2, 130, 97, (-4, 3, 0), "col"),
+    (5, 17, 33, (-8, 7, 0), "row"),
+    (3, 200, 170, (-8, 7, 0), "row"),  # several band products per problem
+]
+
+
+def _batch_inputs(batch, m, n, dtype, alphabet, rule, seed0):
+    hi = alphabet[1] if not alphabet[2] else 7
+    out = []
+    for b in range(batch):
+        p = random_problem(m, n, dtype, seed=seed0 + 31 * b, w_std=2.0 if alphabet[2] else 0.02,
+                           heavy_tail=bool(b % 2), samples_factor=3)
+        out.append(prepare(p.W, p.A, p.B, dtype, alphabet, rule, hi=max(hi, 1)))
+    return out
+
+
+def _stack(inps, attr):
+    return torch.stack([to_dev(getattr(x, attr)) for x in inps])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("batch,m,n,alphabet,rule", CASES)
+def test_batched_equals_single(gpu_lib, dtype, batch, m, n, alphabet, rule):
+    bk = gpu_lib
+    inps = _batch_inputs(batch, m, n, dtype, alphabet, rule, seed0=m * 7 + n)
+    W, LA, LB = _stack(inps, "W"), _stack(inps, "LA"), _stack(inps, "LB")
+    s = _stack(inps, "s") if rule else None
+    mode = inps[0].mode if rule else None
+    Vb, Wtb = bk.solve_batched(W, LA, LB, alphabet, s, scale_mode=mode, return_wt=True)
+    for b, inp in enumerate(inps):
+        V1, Wt1 = bk.solve(W[b], LA[b], LB[b], alphabet, None if s is None else s[b],
+                           scale_mode=mode, return_wt=True)
+        torch.cuda.synchronize()
+        assert torch.equal(Vb[b], V1), (b, "codes differ from the single solve")
+        assert torch.equal(Wtb[b], Wt1), (b, "values at rounding differ from the single solve")
+        if dtype == "f64":
+            ref = oracle_solve(inp, naive=(m * n <= 4096))
+            np.testing.assert_array_equal(Vb[b].cpu().numpy(), ref.V.astype(np.int32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_batched_shared_factors(gpu_lib, dtype):
+    """One L^A and one L^B for the whole batch (stride 0), per-problem W and
+    row scales; also checked against the oracle in float64."""
+    bk = gpu_lib
+    batch, m, n = 4, 70, 90
+    base = random_problem(m, n, dtype, seed=11, heavy_tail=True, samples_factor=3)
+    inps = []
+    for b in range(batch):
+        p = random_problem(m, n, dtype, seed=100 + b, samples_factor=3)
+        inps.append(prepare(p.W, base.A, base.B, dtype, (-8, 7, 0), "row"))
+    W, s = _stack(inps, "W"), _stack(inps, "s")
+    LA, LB = to_dev(inps[0].LA), to_dev(inps[0].LB)
+    Vb = bk.solve_batched(W, LA, LB, (-8, 7, 0), s)
+    for b, inp in enumerate(inps):
+        V1 = bk.solve(W[b], LA, LB, (-8, 7, 0), s[b])
+        torch.cuda.synchronize()
+        assert torch.equal(Vb[b], V1), b
+        if dtype == "f64":
+            ref = oracle_solve(inp)
+            np.testing.assert_array_equal(Vb[b].cpu().numpy(), ref.V.astype(np.int32))
+
+
+def test_batched_single_problem_and_empty(gpu_lib):
+    bk = gpu_lib
+    inp = _batch_inputs(1, 40, 60, "f64", (-8, 7, 0), "row", seed0=5)[0]
+    W, LA, LB, s = (to_dev(getattr(inp, a))[None] for a in ("W", "LA", "LB", "s"))
+    Vb = bk.solve_batched(W, LA, LB, (-8, 7, 0), s)
+    ref = oracle_solve(inp, naive=True)
+    np.testing.assert_array_equal(Vb[0].cpu().numpy(), ref.V.astype(np.int32))
+    e = bk.solve_batched(torch.empty((0, 40, 60), dtype=torch.float64, device="cuda"), LA[0], LB[0],
+                         (-8, 7, 0))
+    assert e.shape == (0, 40, 60)

@@ -156,3 +156,12 @@ def test_kv_batch_on_streams(gpu_lib, b_identity):
     for a_, b_ in zip(res, seq):
         assert np.array_equal(a_["V"], b_["V"]) and np.array_equal(a_["Wt"], b_["Wt"])
         assert a_["loss"] == b_["loss"]
+    # and the batched entry point (all 28 in the same launches) equals both
+    stack = lambda key: torch.stack([to_dev(o[key]) for o in res])
+    W = torch.stack([to_dev(p.W) for p in probs])
+    Vb, Wtb = gpu_lib.solve_batched(W, stack("LA"), stack("LB"), probs[0].alphabet, stack("s"),
+                                    return_wt=True)
+    torch.cuda.synchronize()
+    for i, out in enumerate(res):
+        assert np.array_equal(Vb[i].cpu().numpy(), out["V"]), i
+        assert np.array_equal(Wtb[i].cpu().numpy(), out["Wt"]), i
