@@ -238,6 +238,22 @@ def main():
         "phases_ms": phases,
         "solve_only": {"ms": phases["solve"], "weights_per_s": m * n / (phases["solve"] / 1e3)},
     }
+    # per-row scale search of Appendix D (absmax/7 shrunk by up to 2 over 101
+    # candidates) on the same W: not part of the step (the workload uses the
+    # plain absmax rule), timed on its own
+    grid, shrink = 100, 0.5
+    bk.row_scales_mse(W, (lo_, hi_, unb), grid, shrink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        bk.row_scales_mse(W, (lo_, hi_, unb), grid, shrink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ss_ms = e0.elapsed_time(e1) / args.steps
+    result["scale_search"] = {
+        "ms": ss_ms, "rows": m, "candidates": grid + 1, "max_shrink": shrink,
+        "evaluations_per_s": m * n * (grid + 1) / (ss_ms / 1e3),
+        "hbm_gb_per_s": (m * n * 4 + m * 4) / (ss_ms / 1e3) / 1e9}
     if timed and band_ms_steps:
         band_ms = float(np.mean(band_ms_steps))
         nb = len(band_idx)
@@ -262,10 +278,12 @@ def main():
 
 def bench_kv28(args, dev):
     """28 k/v projections (1024 x 2048, each with its own Wishart A and B,
-    4-bit per-row scales). One step = the 28 factorisations, the 28 row-scale
-    vectors, ONE batched solve of all 28 (bakron_solve_batched) and the 28
-    losses. Also timed: the same 28 solves issued one by one round-robin on
-    four streams, the way a caller without the batched entry point runs them."""
+    4-bit per-row scales). One step = ONE batched factorisation of the 28
+    pairs (bakron_factor_batched), the 28 row-scale vectors, ONE batched
+    solve of all 28 (bakron_solve_batched) and the 28 losses. Also timed: the
+    28 factorisations one pair at a time and the 28 solves issued one by one
+    round-robin on four streams, the way a caller without the batched entry
+    points runs them."""
     import numpy as np
     import torch
 
@@ -278,10 +296,13 @@ def bench_kv28(args, dev):
     lo_, hi_, unb = probs[0].alphabet
     hi = probs[0].scale_hi
     W = torch.stack([torch.from_numpy(p.W) for p in probs]).to(dev)
-    A = [torch.from_numpy(p.A).to(dev) for p in probs]
-    B = [torch.from_numpy(p.B).to(dev) for p in probs]
+    Aall = torch.stack([torch.from_numpy(p.A) for p in probs]).to(dev)
+    Ball = torch.stack([torch.from_numpy(p.B) for p in probs]).to(dev)
+    A, B = list(Aall.unbind(0)), list(Ball.unbind(0))
     code = bk.F32
     wsF = torch.empty(bk.workspace_bytes("factor", code, m, n), dtype=torch.uint8, device=dev)
+    wsFB = torch.empty(int(bk.lib().bakron_factor_batched_workspace_bytes(code, nb, m, n)),
+                       dtype=torch.uint8, device=dev)
     wsL = torch.empty(bk.workspace_bytes("loss", code, m, n), dtype=torch.uint8, device=dev)
     wsB = torch.empty(int(bk.lib().bakron_solve_batched_workspace_bytes(code, nb, m, n)),
                       dtype=torch.uint8, device=dev)
@@ -299,17 +320,14 @@ def bench_kv28(args, dev):
         es = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
         if record:
             es[0].record(stream)
-        for i in range(nb):
-            la, lb, _, _ = bk.factor(A[i], B[i], workspace=wsF)
-            LA[i].copy_(la)
-            LB[i].copy_(lb)
+        la, lb, _, _ = bk.factor_batched(Aall, Ball, workspace=wsFB)
         if record:
             es[1].record(stream)
         for i in range(nb):
             S[i].copy_(bk.row_scales(W[i], hi))
         if record:
             es[2].record(stream)
-        V = bk.solve_batched(W, LA, LB, (lo_, hi_, unb), S, workspace=wsB)
+        V = bk.solve_batched(W, la, lb, (lo_, hi_, unb), S, workspace=wsB)
         if record:
             es[3].record(stream)
         out = [bk.loss(W[i], V[i], A[i], B[i], S[i], workspace=wsL, sync=False) for i in range(nb)]
@@ -318,6 +336,12 @@ def bench_kv28(args, dev):
             for k, e in zip(("t0", "t1", "t2", "t3", "t4"), es):
                 ev[k].append(e)
         return out
+
+    def factor_one_by_one():
+        for i in range(nb):
+            la, lb, _, _ = bk.factor(A[i], B[i], workspace=wsF)
+            LA[i].copy_(la)
+            LB[i].copy_(lb)
 
     def solve_streams():
         cur = torch.cuda.current_stream(dev)
@@ -344,7 +368,14 @@ def bench_kv28(args, dev):
 
     phases = {"factor": phase("t0", "t1"), "scales": phase("t1", "t2"),
               "solve": phase("t2", "t3"), "loss": phase("t3", "t4")}
-    # the solves alone: batched against four streams, same inputs
+    # the factors one pair at a time, and the solves issued one by one on
+    # four streams: what the batched entry points replace
+    factor_one_by_one()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    factor_one_by_one()
+    torch.cuda.synchronize()
+    factor_single_ms = (time.perf_counter() - t1) * 1e3
     solve_streams()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -364,12 +395,13 @@ def bench_kv28(args, dev):
         "config": {"workload": "28 k/v projections 1024x2048 float32, Wishart(4096 dof)/4096 A and B "
                                "+1% mean-diag damping, alphabet {-8..7}, per-row absmax/7 scales",
                    "m": m, "n": n, "batch": nb,
-                   "step": "28 factors + 28 row scales + one batched solve + 28 losses"},
+                   "step": "one batched factor + 28 row scales + one batched solve + 28 losses"},
         "phases_ms": phases,
         "solve_only": {"ms": phases["solve"], "weights_per_s": total / (phases["solve"] / 1e3),
                        "entry": "bakron_solve_batched"},
         "solve_four_streams": {"ms": streams_ms, "weights_per_s": total / (streams_ms / 1e3),
                                "entry": "bakron_solve x 28, round-robin on 4 streams"},
+        "factor_one_by_one_ms": factor_single_ms,
     }
     if not args.no_cpu_baseline:
         # bounded sample: the oracle on one of the 28 matrices

@@ -94,6 +94,31 @@ int bakron_factor(int dtype, int64_t m, int64_t n,
                   int64_t *bad_pivot, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Batched factor: bakron_factor on `batch` pairs (A, B) of the same orders
+ * (n, m) in one sequence of launches (every linear module of a model has its
+ * own pair, §3.6; factoring small pairs one at a time leaves the GPU idle).
+ * Pair b uses A + b * stride_a, B + b * stride_b and writes LA + b * stride_la,
+ * LB + b * stride_lb, dA + b * stride_da, dB + b * stride_db (element
+ * strides). Input strides may be 0 (a shared matrix); for batch > 1 the
+ * output strides must keep the outputs of different pairs apart
+ * (stride_la >= (n - 1) * ldla + n, stride_da >= n, and likewise for B).
+ * Each pair's result is bit-identical to bakron_factor on it.
+ * bad_pivot  HOST int64[3] (nullable): on BAKRON_ENOTSPD, {pair, side,
+ *        index} of the first failing pivot (pairs in order, A before B),
+ *        as for bakron_factor; otherwise {-1, -1, -1}.
+ * 0 <= batch <= 32767. SYNCHRONOUS, like bakron_factor.
+ * ------------------------------------------------------------------------ */
+size_t bakron_factor_batched_workspace_bytes(int dtype, int64_t batch, int64_t m, int64_t n);
+int bakron_factor_batched(int dtype, int64_t batch, int64_t m, int64_t n,
+                          const void *A, int64_t lda, int64_t stride_a,
+                          const void *B, int64_t ldb, int64_t stride_b,
+                          void *LA, int64_t ldla, int64_t stride_la,
+                          void *LB, int64_t ldlb, int64_t stride_lb,
+                          void *dA, int64_t stride_da, void *dB, int64_t stride_db,
+                          void *workspace, size_t workspace_bytes,
+                          int64_t *bad_pivot, void *stream);
+
+/* ------------------------------------------------------------------------
  * Solve: BaKron (Algorithm 6, §3.5) on a tiling of W, which yields the codes
  * of BaKron-naive (Algorithm 2) by Theorem 3.2 / Appendix B.
  *
@@ -208,6 +233,27 @@ int bakron_loss(int dtype, int64_t m, int64_t n,
  * ------------------------------------------------------------------------ */
 int bakron_row_scales(int dtype, int64_t m, int64_t n, const void *W, int64_t ldw,
                       int32_t hi, void *scales, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Per-row scale search: the absmax scale of bakron_row_scales, optionally
+ * shrunk by an MSE search (Appendix D, experimental setup: shrink by up to a
+ * factor of 2, i.e. max_shrink = 0.5). The pages leave the search open;
+ * this call evaluates grid + 1 candidates
+ *   s_k = (dtype)(s_max * f_k),  f_k = 1 - (max_shrink * k) / grid  (float64),
+ * k = 0..grid, s_max = max_j |W_ij| / alpha_hi, and returns for each row the
+ * candidate with the smallest round-to-nearest error
+ *   sum_j (W_ij - s_k c_j)^2,  c_j = clamp(rint(W_ij / s_k), lo, hi)
+ * (division in dtype; terms and sum in float64); ties go to the smaller k.
+ * An all-zero row gets scale 1. grid = 0 or max_shrink = 0 give exactly
+ * bakron_row_scales.
+ *
+ * W m x n (ldw); scales out, length m. alpha_lo <= alpha_hi, alpha_hi > 0;
+ * 0 <= grid <= 1024; 0 <= max_shrink < 1. BAKRON_EINVAL otherwise.
+ * Asynchronous. Deterministic.
+ * ------------------------------------------------------------------------ */
+int bakron_row_scales_mse(int dtype, int64_t m, int64_t n, const void *W, int64_t ldw,
+                          int32_t alpha_lo, int32_t alpha_hi, int32_t grid, double max_shrink,
+                          void *scales, void *stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,8 @@ from typing import Optional, Sequence, Tuple, Union
 import torch
 
 __all__ = ["F32", "F64", "SCALE_NONE", "SCALE_ROW", "SCALE_COL", "BakronError", "lib", "factor",
-           "solve", "solve_batched", "loss", "row_scales", "solve_schedule", "tile_size", "workspace_bytes"]
+           "factor_batched",
+           "solve", "solve_batched", "loss", "row_scales", "row_scales_mse", "solve_schedule", "tile_size", "workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libbakron.so")
@@ -73,6 +74,12 @@ def lib() -> ctypes.CDLL:
     L.bakron_solve_timed.restype = _int
     L.bakron_solve_schedule.argtypes = [_int, _i64, _i64, _vp, _i64]
     L.bakron_solve_schedule.restype = _i64
+    L.bakron_factor_batched_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
+    L.bakron_factor_batched_workspace_bytes.restype = _sz
+    L.bakron_factor_batched.argtypes = [_int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                        _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64,
+                                        _vp, _sz, ctypes.POINTER(_i64), _vp]
+    L.bakron_factor_batched.restype = _int
     L.bakron_solve_batched_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
     L.bakron_solve_batched_workspace_bytes.restype = _sz
     L.bakron_solve_batched.argtypes = [_int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
@@ -84,6 +91,9 @@ def lib() -> ctypes.CDLL:
     L.bakron_loss.restype = _int
     L.bakron_row_scales.argtypes = [_int, _i64, _i64, _vp, _i64, _i32, _vp, _vp]
     L.bakron_row_scales.restype = _int
+    L.bakron_row_scales_mse.argtypes = [_int, _i64, _i64, _vp, _i64, _i32, _i32, _i32,
+                                        ctypes.c_double, _vp, _vp]
+    L.bakron_row_scales_mse.restype = _int
     _lib = L
     return L
 
@@ -182,6 +192,39 @@ def factor(A: torch.Tensor, B: torch.Tensor, out_dtype: Optional[torch.dtype] = 
                              _p(LB), m, _p(dA), _p(dB), _p(ws), ws.numel(), bad, _stream(dev))
     if rc != OK:
         raise BakronError(rc, "bakron_factor", (int(bad[0]), int(bad[1])))
+    return LA, LB, dA, dB
+
+
+def factor_batched(A: torch.Tensor, B: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """bakron_factor on a batch of pairs of the same orders in the same
+    launches. A is (batch, n, n), B (batch, m, m). Returns LA (batch, n, n),
+    LB (batch, m, m), dA (batch, n), dB (batch, m); each pair's result is
+    bit-identical to ``factor``. Synchronous. Raises BakronError(ENOTSPD)
+    with ``bad_pivot`` = (pair, side, index)."""
+    dev = _check_device(A, B, workspace)
+    code = _dt(A)
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same dtype")
+    if A.dim() != 3 or B.dim() != 3 or A.size(0) != B.size(0):
+        raise ValueError("A must be (batch, n, n) and B (batch, m, m)")
+    batch, n, m = A.size(0), A.size(1), B.size(1)
+    pa, lda, sa = _batch_operand(A, n, n, batch, "A")
+    pb, ldb, sb = _batch_operand(B, m, m, batch, "B")
+    LA = torch.empty((batch, n, n), dtype=A.dtype, device=dev)
+    LB = torch.empty((batch, m, m), dtype=A.dtype, device=dev)
+    dA = torch.empty((batch, n), dtype=A.dtype, device=dev)
+    dB = torch.empty((batch, m), dtype=A.dtype, device=dev)
+    L = lib()
+    ws = _workspace(L.bakron_factor_batched_workspace_bytes(code, batch, m, n), dev, workspace)
+    bad = (_i64 * 3)(-1, -1, -1)
+    with torch.cuda.device(dev):
+        rc = L.bakron_factor_batched(code, batch, m, n, pa, lda, sa, pb, ldb, sb, _p(LA), max(n, 1),
+                                     n * n, _p(LB), max(m, 1), m * m, _p(dA), n, _p(dB), m, _p(ws),
+                                     ws.numel() * ws.element_size(), bad, _stream(dev))
+    if rc != OK:
+        err = BakronError(rc, "bakron_factor_batched", (int(bad[1]), int(bad[2])))
+        err.bad_pivot = (int(bad[0]), int(bad[1]), int(bad[2]))
+        raise err
     return LA, LB, dA, dB
 
 
@@ -339,6 +382,24 @@ def row_scales(W: torch.Tensor, hi: int) -> torch.Tensor:
         rc = lib().bakron_row_scales(code, m, n, _p(W), _ld(W, "W"), int(hi), _p(s), _stream(dev))
     if rc != OK:
         raise BakronError(rc, "bakron_row_scales")
+    return s
+
+
+def row_scales_mse(W: torch.Tensor, alphabet: AlphabetLike, grid: int = 100,
+                   max_shrink: float = 0.5) -> torch.Tensor:
+    """Per-row absmax / hi scales shrunk by up to 1 / (1 - max_shrink) by a
+    search over grid + 1 candidates for the smallest round-to-nearest squared
+    error of the row (bakron_row_scales_mse), in W's dtype."""
+    dev = _check_device(W)
+    code = _dt(W)
+    m, n = W.shape
+    lo, hi = int(alphabet[0]), int(alphabet[1])
+    s = torch.empty(m, dtype=W.dtype, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().bakron_row_scales_mse(code, m, n, _p(W), _ld(W, "W"), lo, hi, int(grid),
+                                         float(max_shrink), _p(s), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_row_scales_mse")
     return s
 
 

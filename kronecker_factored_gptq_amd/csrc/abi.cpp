@@ -192,14 +192,14 @@ size_t side_bytes(int64_t D) {
 }
 
 struct FactorLayout {
-  size_t a, b, info, total;
+  size_t a, b, info, total;  // a, b: one side's bytes; info: 2 * batch words
 };
-FactorLayout factor_layout(int64_t m, int64_t n) {
+FactorLayout factor_layout(int64_t m, int64_t n, int64_t batch = 1) {
   FactorLayout L;
   L.a = side_bytes(n);
   L.b = side_bytes(m);
-  L.info = align_up(2 * sizeof(int32_t));
-  L.total = L.a + L.b + L.info + kAlign;
+  L.info = align_up(2 * (size_t)batch * sizeof(int32_t));
+  L.total = (size_t)batch * (L.a + L.b) + L.info + kAlign;
   return L;
 }
 
@@ -215,44 +215,63 @@ FactorSide carve_side(char* base, int64_t D, int32_t* info) {
   return f;
 }
 
+// Caller strides (elements) between the matrices of a batched factor.
+struct FactorStrides {
+  int64_t a, b, la, lb, da, db;
+};
+
+// Factor `batch` pairs (A, B) of orders (n, m). Workspace: the batch's A
+// sides (side_bytes(n) each), then its B sides, then 2 * batch info words
+// (A sides first). When m == n all 2 * batch sides form one set and share
+// every launch; otherwise the A sides and the B sides are two sets.
+// bad (host, nullable) receives {problem, side, pivot} of the first failure.
 template <typename R>
-int factor_impl(int64_t m, int64_t n, const R* A, int64_t lda, const R* B, int64_t ldb, R* LA,
-                int64_t ldla, R* LB, int64_t ldlb, R* dA, R* dB, void* ws, int64_t* bad,
-                hipStream_t s) {
-  const FactorLayout lay = factor_layout(m, n);
+int factor_impl(int64_t batch, int64_t m, int64_t n, const R* A, int64_t lda, const R* B,
+                int64_t ldb, R* LA, int64_t ldla, R* LB, int64_t ldlb, R* dA, R* dB,
+                const FactorStrides& st, void* ws, int64_t* bad, hipStream_t s) {
+  const FactorLayout lay = factor_layout(m, n, batch);
   char* base = static_cast<char*>(ws);
-  int32_t* info = reinterpret_cast<int32_t*>(base + lay.a + lay.b);
-  const FactorSide sa = carve_side(base, n, info + 0);
-  const FactorSide sb = carve_side(base + lay.a, m, info + 1);
-  if (launch_fill_i32(info, 2, INT_MAX, s) != hipSuccess) return BAKRON_EHIP;
-  if (n > 0 && launch_load_reversed<R>(n, A, lda, sa.X, s) != hipSuccess) return BAKRON_EHIP;
-  if (m > 0 && launch_load_reversed<R>(m, B, ldb, sb.X, s) != hipSuccess) return BAKRON_EHIP;
+  char* base_b = base + (size_t)batch * lay.a;
+  int32_t* info = reinterpret_cast<int32_t*>(base_b + (size_t)batch * lay.b);
+  const FactorSide sa = carve_side(base, n, info);
+  const FactorSide sb = carve_side(base_b, m, info + batch);
+  const int nb = (int)batch;
+  const int64_t za = (int64_t)(lay.a / 8), zb = (int64_t)(lay.b / 8);
+  if (launch_fill_i32(info, 2 * batch, INT_MAX, s) != hipSuccess) return BAKRON_EHIP;
+  if (n > 0 && launch_load_reversed<R>(n, A, lda, st.a, sa.X, za, nb, s) != hipSuccess)
+    return BAKRON_EHIP;
+  if (m > 0 && launch_load_reversed<R>(m, B, ldb, st.b, sb.X, zb, nb, s) != hipSuccess)
+    return BAKRON_EHIP;
   if (m == n) {
-    const FactorSide both[2] = {sa, sb};
-    if (factor_cholesky_inverse(n, both, 2, s) != hipSuccess) return BAKRON_EHIP;
+    // the B sides follow the A sides at the same stride: one set of 2 * batch
+    if (factor_cholesky_inverse(n, FactorSet{sa, za, 2 * nb}, s) != hipSuccess) return BAKRON_EHIP;
   } else {
-    if (factor_cholesky_inverse(n, &sa, 1, s) != hipSuccess) return BAKRON_EHIP;
-    if (factor_cholesky_inverse(m, &sb, 1, s) != hipSuccess) return BAKRON_EHIP;
+    if (factor_cholesky_inverse(n, FactorSet{sa, za, nb}, s) != hipSuccess) return BAKRON_EHIP;
+    if (factor_cholesky_inverse(m, FactorSet{sb, zb, nb}, s) != hipSuccess) return BAKRON_EHIP;
   }
-  if (n > 0 && launch_store_normalized<R>(n, sa.Y, LA, ldla, dA, s) != hipSuccess) return BAKRON_EHIP;
-  if (m > 0 && launch_store_normalized<R>(m, sb.Y, LB, ldlb, dB, s) != hipSuccess) return BAKRON_EHIP;
-  int32_t hinfo[2] = {INT_MAX, INT_MAX};
-  if (hipMemcpyAsync(hinfo, info, sizeof(hinfo), hipMemcpyDeviceToHost, s) != hipSuccess)
+  if (n > 0 &&
+      launch_store_normalized<R>(n, sa.Y, za, LA, ldla, st.la, dA, st.da, nb, s) != hipSuccess)
+    return BAKRON_EHIP;
+  if (m > 0 &&
+      launch_store_normalized<R>(m, sb.Y, zb, LB, ldlb, st.lb, dB, st.db, nb, s) != hipSuccess)
+    return BAKRON_EHIP;
+  std::vector<int32_t> hinfo((size_t)(2 * batch), INT_MAX);
+  if (hipMemcpyAsync(hinfo.data(), info, hinfo.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     s) != hipSuccess)
     return BAKRON_EHIP;
   if (hipStreamSynchronize(s) != hipSuccess) return BAKRON_EHIP;
-  if (bad) {
-    bad[0] = -1;
-    bad[1] = -1;
-  }
-  for (int side = 0; side < 2; ++side) {
-    if (hinfo[side] != INT_MAX) {
-      if (bad) {
-        bad[0] = side;
-        bad[1] = hinfo[side];
+  for (int64_t z = 0; z < batch; ++z)
+    for (int side = 0; side < 2; ++side) {
+      const int32_t v = hinfo[(size_t)(side * batch + z)];
+      if (v != INT_MAX) {
+        if (bad) {
+          bad[0] = z;
+          bad[1] = side;
+          bad[2] = v;
+        }
+        return BAKRON_ENOTSPD;
       }
-      return BAKRON_ENOTSPD;
     }
-  }
   return BAKRON_OK;
 }
 
@@ -293,18 +312,18 @@ int loss_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V, i
   // below the diagonal and 1 on it (3 m n^2-type products instead of 4)
   Gemm64Args g1{};
   g1.M = m; g1.N = n; g1.K = n; g1.batch = 1;
-  g1.A[0] = D; g1.lda = n;
-  g1.B[0] = A64; g1.ldb = n; g1.transB = 0;
-  g1.C[0] = BE; g1.ldc = n;
+  g1.A = D; g1.lda = n;
+  g1.B = A64; g1.ldb = n; g1.transB = 0;
+  g1.C = BE; g1.ldc = n;
   g1.alpha = 1.0; g1.beta = 0.0;
   if (launch_gemm64(g1, s) != hipSuccess) return BAKRON_EHIP;
   Gemm64Args g2{};
   g2.M = m; g2.N = m; g2.K = n; g2.batch = 1;
-  g2.A[0] = BE; g2.lda = n;
-  g2.B[0] = D; g2.ldb = n; g2.transB = 1;
+  g2.A = BE; g2.lda = n;
+  g2.B = D; g2.ldb = n; g2.transB = 1;
   g2.lower_out = 1;
   g2.alpha = 1.0;
-  g2.dot[0] = B64; g2.lddot = m; g2.partial[0] = part; g2.sym_dot = 1;
+  g2.dot = B64; g2.lddot = m; g2.partial = part; g2.sym_dot = 1;
   if (launch_gemm64(g2, s) != hipSuccess) return BAKRON_EHIP;
   if (launch_sum_partials(part, gemm64_partials(g2), loss, s) != hipSuccess) return BAKRON_EHIP;
   return BAKRON_OK;
@@ -349,12 +368,68 @@ int bakron_factor(int dtype, int64_t m, int64_t n, const void* A, int64_t lda, c
     return BAKRON_EINVAL;
   if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const FactorStrides st = {0, 0, 0, 0, 0, 0};
+  int64_t bad3[3] = {-1, -1, -1};
+  int rc;
   if (dtype == BAKRON_F32)
-    return factor_impl<float>(m, n, (const float*)A, lda, (const float*)B, ldb, (float*)LA, ldla,
-                              (float*)LB, ldlb, (float*)dA, (float*)dB, workspace, bad_pivot, s);
-  return factor_impl<double>(m, n, (const double*)A, lda, (const double*)B, ldb, (double*)LA,
-                             ldla, (double*)LB, ldlb, (double*)dA, (double*)dB, workspace,
-                             bad_pivot, s);
+    rc = factor_impl<float>(1, m, n, (const float*)A, lda, (const float*)B, ldb, (float*)LA, ldla,
+                            (float*)LB, ldlb, (float*)dA, (float*)dB, st, workspace, bad3, s);
+  else
+    rc = factor_impl<double>(1, m, n, (const double*)A, lda, (const double*)B, ldb, (double*)LA,
+                             ldla, (double*)LB, ldlb, (double*)dA, (double*)dB, st, workspace,
+                             bad3, s);
+  if (rc == BAKRON_ENOTSPD && bad_pivot) {
+    bad_pivot[0] = bad3[1];
+    bad_pivot[1] = bad3[2];
+  }
+  return rc;
+}
+
+size_t bakron_factor_batched_workspace_bytes(int dtype, int64_t batch, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || batch < 0 || m < 0 || n < 0) return 0;
+  if (batch == 0) return 0;
+  const FactorLayout one = factor_layout(m, n, 1);
+  if ((one.a + one.b) > (std::numeric_limits<size_t>::max() / 2) / (size_t)batch) return 0;
+  return factor_layout(m, n, batch).total;
+}
+
+int bakron_factor_batched(int dtype, int64_t batch, int64_t m, int64_t n, const void* A,
+                          int64_t lda, int64_t stride_a, const void* B, int64_t ldb,
+                          int64_t stride_b, void* LA, int64_t ldla, int64_t stride_la, void* LB,
+                          int64_t ldlb, int64_t stride_lb, void* dA, int64_t stride_da, void* dB,
+                          int64_t stride_db, void* workspace, size_t workspace_bytes,
+                          int64_t* bad_pivot, void* stream) {
+  if (bad_pivot) bad_pivot[0] = bad_pivot[1] = bad_pivot[2] = -1;
+  if (!dtype_ok(dtype) || batch < 0 || m < 0 || n < 0) return BAKRON_EINVAL;
+  // both sides of every pair may share one launch: 2 * batch problems
+  if (batch > kMaxBatch / 2) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (batch == 0 || (m == 0 && n == 0)) return BAKRON_OK;
+  if (n > 0 && (!A || !LA || lda < n || ldla < n)) return BAKRON_EINVAL;
+  if (m > 0 && (!B || !LB || ldb < m || ldlb < m)) return BAKRON_EINVAL;
+  if (stride_a < 0 || stride_b < 0) return BAKRON_EINVAL;
+  if (batch > 1) {
+    // outputs of different problems must not overlap
+    if (n > 0 && stride_la < (n - 1) * ldla + n) return BAKRON_EINVAL;
+    if (m > 0 && stride_lb < (m - 1) * ldlb + m) return BAKRON_EINVAL;
+    if (dA && n > 0 && stride_da < n) return BAKRON_EINVAL;
+    if (dB && m > 0 && stride_db < m) return BAKRON_EINVAL;
+    const int64_t big = std::max(std::max(std::max(stride_a, stride_b), std::max(stride_la, stride_lb)),
+                                 std::max(stride_da, stride_db));
+    if (big > std::numeric_limits<int64_t>::max() / 2 / (batch - 1)) return BAKRON_EINVAL;
+  }
+  const size_t need = bakron_factor_batched_workspace_bytes(dtype, batch, m, n);
+  if (!workspace || need == 0 || workspace_bytes < need) return BAKRON_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const FactorStrides st = {stride_a, stride_b, stride_la, stride_lb, stride_da, stride_db};
+  if (dtype == BAKRON_F32)
+    return factor_impl<float>(batch, m, n, (const float*)A, lda, (const float*)B, ldb, (float*)LA,
+                              ldla, (float*)LB, ldlb, (float*)dA, (float*)dB, st, workspace,
+                              bad_pivot, s);
+  return factor_impl<double>(batch, m, n, (const double*)A, lda, (const double*)B, ldb,
+                             (double*)LA, ldla, (double*)LB, ldlb, (double*)dA, (double*)dB, st,
+                             workspace, bad_pivot, s);
 }
 
 size_t bakron_solve_workspace_bytes(int dtype, int64_t m, int64_t n) {
@@ -534,6 +609,26 @@ int bakron_row_scales(int dtype, int64_t m, int64_t n, const void* W, int64_t ld
     e = launch_row_scales<float>(m, n, (const float*)W, ldw, hi, (float*)scales, s);
   else
     e = launch_row_scales<double>(m, n, (const double*)W, ldw, hi, (double*)scales, s);
+  return e == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
+}
+
+int bakron_row_scales_mse(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
+                          int32_t alpha_lo, int32_t alpha_hi, int32_t grid, double max_shrink,
+                          void* scales, void* stream) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0 || alpha_hi <= 0 || alpha_lo > alpha_hi)
+    return BAKRON_EINVAL;
+  if (grid < 0 || grid > kScaleMaxGrid) return BAKRON_EINVAL;
+  if (!(max_shrink >= 0.0 && max_shrink < 1.0)) return BAKRON_EINVAL;
+  if (m == 0) return BAKRON_OK;
+  if (!scales || (n > 0 && (!W || ldw < n))) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == BAKRON_F32)
+    e = launch_row_scales_mse<float>(m, n, (const float*)W, ldw, alpha_lo, alpha_hi, alpha_hi, grid,
+                                     max_shrink, (float*)scales, s);
+  else
+    e = launch_row_scales_mse<double>(m, n, (const double*)W, ldw, alpha_lo, alpha_hi, alpha_hi,
+                                      grid, max_shrink, (double*)scales, s);
   return e == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
 }
 

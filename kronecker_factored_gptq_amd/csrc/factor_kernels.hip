@@ -34,8 +34,11 @@ constexpr int kLeafPatchCols = 2;  // columns of a thread's patch: 4 x 2 patches
 // the lower triangle of A), 0 above the diagonal. 32 x 32 tiles through LDS.
 template <typename R>
 __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* __restrict__ A,
-                                                            int64_t lda, double* __restrict__ X) {
+                                                            int64_t lda, int64_t sA,
+                                                            double* __restrict__ X, int64_t sX) {
   __shared__ double tile[32][33];
+  A += (int64_t)blockIdx.z * sA;  // matrix blockIdx.z of a batch
+  X += (int64_t)blockIdx.z * sX;
   const int64_t i0 = (int64_t)blockIdx.y * 32, j0 = (int64_t)blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // ty 0..7
   const bool lower_tile = i0 + 31 >= j0;
@@ -75,8 +78,7 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* 
 // that is not positive and finite records off + j + q in *info (smallest
 // wins) and the factorisation continues with NaN.
 template <int NC, int PCW>
-__global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSide s0,
-                                                                       FactorSide s1, int64_t n,
+__global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSet set, int64_t n,
                                                                        int64_t off, int bs) {
   static_assert(NC % 4 == 0 && NC % PCW == 0, "whole patch rows and columns per step");
   constexpr int PRS = NC / 4;  // patch rows per step
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSi
   __shared__ double pblk[2][NC][NC];
   __shared__ double colp[2][NC][64];
   __shared__ double rowp[2][NC][64];
-  const FactorSide S = blockIdx.x == 0 ? s0 : s1;
+  const FactorSide S = factor_side(set, (int)blockIdx.x);  // one matrix per workgroup
   const int tid = threadIdx.x;
   const int ty = tid / TX, tx = tid % TX;
   double Lr[4][PCW], Yr[4][PCW];
@@ -238,10 +240,14 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {
 template <typename R>
 __global__ __launch_bounds__(256) void store_normalized_kernel(int64_t n,
                                                                const double* __restrict__ Y,
-                                                               R* __restrict__ L, int64_t ldl,
-                                                               R* __restrict__ d) {
+                                                               int64_t sY, R* __restrict__ L,
+                                                               int64_t ldl, int64_t sL,
+                                                               R* __restrict__ d, int64_t sd) {
   __shared__ double tile[32][33];
   __shared__ double diag[32];
+  Y += (int64_t)blockIdx.z * sY;  // matrix blockIdx.z of a batch
+  L += (int64_t)blockIdx.z * sL;
+  if (d) d += (int64_t)blockIdx.z * sd;
   const int64_t i0 = (int64_t)blockIdx.y * 32, j0 = (int64_t)blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const bool lower_tile = i0 + 31 >= j0;
@@ -278,20 +284,22 @@ __global__ __launch_bounds__(256) void store_normalized_kernel(int64_t n,
 
 // ---------------------------------------------------------------------------
 template <typename R>
-hipError_t launch_load_reversed(int64_t n, const R* A, int64_t lda, double* X, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
+hipError_t launch_load_reversed(int64_t n, const R* A, int64_t lda, int64_t sA, double* X,
+                                int64_t sX, int batch, hipStream_t s) {
+  if (n <= 0 || batch <= 0) return hipSuccess;
   const unsigned nb = (unsigned)((n + 31) / 32);
-  hipLaunchKernelGGL((load_reversed_kernel<R>), dim3(nb, nb), dim3(256), 0, s, n, A, lda, X);
+  hipLaunchKernelGGL((load_reversed_kernel<R>), dim3(nb, nb, (unsigned)batch), dim3(256), 0, s, n,
+                     A, lda, sA, X, sX);
   return hipGetLastError();
 }
 
 template <typename R>
-hipError_t launch_store_normalized(int64_t n, const double* Y, R* L, int64_t ldl, R* d,
-                                   hipStream_t s) {
-  if (n <= 0) return hipSuccess;
+hipError_t launch_store_normalized(int64_t n, const double* Y, int64_t sY, R* L, int64_t ldl,
+                                   int64_t sL, R* d, int64_t sd, int batch, hipStream_t s) {
+  if (n <= 0 || batch <= 0) return hipSuccess;
   const unsigned nb = (unsigned)((n + 31) / 32);
-  hipLaunchKernelGGL((store_normalized_kernel<R>), dim3(nb, nb), dim3(256), 0, s, n, Y, L, ldl,
-                     d);
+  hipLaunchKernelGGL((store_normalized_kernel<R>), dim3(nb, nb, (unsigned)batch), dim3(256), 0, s,
+                     n, Y, sY, L, ldl, sL, d, sd);
   return hipGetLastError();
 }
 
@@ -309,30 +317,32 @@ static inline int64_t split_point(int64_t n) {
   return n1;
 }
 
-static hipError_t chol_inv_rec(int64_t n, const FactorSide* sd, int ns, int64_t off, int64_t len,
+static hipError_t chol_inv_rec(int64_t n, const FactorSet& sd, int64_t off, int64_t len,
                                hipStream_t s) {
   hipError_t err;
+  const int ns = sd.count;
+  const FactorSide& f0 = sd.first;
+  const int64_t zs = sd.stride;
   if (len <= NB) {
     hipLaunchKernelGGL((chol_inv_leaf_kernel<kLeafCols, kLeafPatchCols>), dim3(ns),
-                       dim3(16 * (64 / kLeafPatchCols)), 0, s, sd[0], sd[ns > 1 ? 1 : 0], n, off,
-                       (int)len);
+                       dim3(16 * (64 / kLeafPatchCols)), 0, s, sd, n, off, (int)len);
     return hipGetLastError();
   }
   const int64_t n1 = split_point(len), n2 = len - n1;
-  if ((err = chol_inv_rec(n, sd, ns, off, n1, s)) != hipSuccess) return err;
+  if ((err = chol_inv_rec(n, sd, off, n1, s)) != hipSuccess) return err;
   const int64_t o11 = off * n + off;            // (off, off)
   const int64_t o21 = (off + n1) * n + off;     // (off + n1, off)
   const int64_t o22 = (off + n1) * n + off + n1;
   // C21 = X21 Y11^T, written where Y21 will go (that block of Y is free until then)
   Gemm64Args g{};
   g.M = n2; g.N = n1; g.K = n1; g.batch = ns;
-  for (int z = 0; z < ns; ++z) { g.A[z] = sd[z].X + o21; g.B[z] = sd[z].Y + o11; g.C[z] = sd[z].Y + o21; }
+  g.A = f0.X + o21; g.B = f0.Y + o11; g.C = f0.Y + o21; g.sA = g.sB = g.sC = zs;
   g.lda = n; g.ldb = n; g.ldc = n; g.transB = 1; g.b_lower = 1; g.alpha = 1.0; g.beta = 0.0;
   if ((err = launch_gemm64(g, s)) != hipSuccess) return err;
   // X22 -= C21 C21^T (lower blocks)
   Gemm64Args h{};
   h.M = n2; h.N = n2; h.K = n1; h.batch = ns;
-  for (int z = 0; z < ns; ++z) { h.A[z] = sd[z].Y + o21; h.B[z] = sd[z].Y + o21; h.C[z] = sd[z].X + o22; }
+  h.A = f0.Y + o21; h.B = f0.Y + o21; h.C = f0.X + o22; h.sA = h.sB = h.sC = zs;
   h.lda = n; h.ldb = n; h.ldc = n; h.transB = 1; h.lower_out = 1; h.alpha = -1.0; h.beta = 1.0;
   // Tmp = C21 Y11 (Y11 lower: column block c needs k >= c * 64). A node of
   // order up to 1024 forms it together with the Schur update, in one
@@ -345,40 +355,43 @@ static hipError_t chol_inv_rec(int64_t n, const FactorSide* sd, int ns, int64_t 
   Gemm64Args t{};
   t.M = n2; t.N = n1; t.K = n1; t.batch = ns;
   t.lda = n; t.ldb = n; t.ldc = n1; t.transB = 0; t.b_lower = 1; t.alpha = 1.0; t.beta = 0.0;
-  for (int z = 0; z < ns; ++z) {
-    double* tmp = sd[z].Tmp;
-    if (cls >= 0) {
-      int64_t o = 0;
-      for (int c = 0; c < cls; ++c) o += ((int64_t)64 << c) * ((int64_t)64 << c);
-      tmp = sd[z].TmpS + o;
-    }
-    t.A[z] = sd[z].Y + o21; t.B[z] = sd[z].Y + o11; t.C[z] = tmp;
+  double* tmp = f0.Tmp;
+  if (cls >= 0) {
+    int64_t o = 0;
+    for (int c = 0; c < cls; ++c) o += ((int64_t)64 << c) * ((int64_t)64 << c);
+    tmp = f0.TmpS + o;
   }
+  t.A = f0.Y + o21; t.B = f0.Y + o11; t.C = tmp; t.sA = t.sB = t.sC = zs;
   if (cls >= 0) {
     if ((err = launch_gemm64_pair(h, t, s)) != hipSuccess) return err;
-    if ((err = chol_inv_rec(n, sd, ns, off + n1, n2, s)) != hipSuccess) return err;
+    if ((err = chol_inv_rec(n, sd, off + n1, n2, s)) != hipSuccess) return err;
   } else {
     if ((err = launch_gemm64(h, s)) != hipSuccess) return err;
-    if ((err = chol_inv_rec(n, sd, ns, off + n1, n2, s)) != hipSuccess) return err;
+    if ((err = chol_inv_rec(n, sd, off + n1, n2, s)) != hipSuccess) return err;
     if ((err = launch_gemm64(t, s)) != hipSuccess) return err;
   }
   // Y21 = -Y22 Tmp (Y22 lower)
   Gemm64Args u{};
   u.M = n2; u.N = n1; u.K = n2; u.batch = ns;
-  for (int z = 0; z < ns; ++z) { u.A[z] = sd[z].Y + o22; u.B[z] = t.C[z]; u.C[z] = sd[z].Y + o21; }
+  u.A = f0.Y + o22; u.B = t.C; u.C = f0.Y + o21; u.sA = u.sB = u.sC = zs;
   u.lda = n; u.ldb = n1; u.ldc = n; u.transB = 0; u.a_lower = 1; u.alpha = -1.0; u.beta = 0.0;
   return launch_gemm64(u, s);
 }
 
-hipError_t factor_cholesky_inverse(int64_t n, const FactorSide* sides, int nsides, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  if (nsides < 1 || nsides > 2) return hipErrorInvalidValue;
-  return chol_inv_rec(n, sides, nsides, 0, n, s);
+hipError_t factor_cholesky_inverse(int64_t n, const FactorSet& set, hipStream_t s) {
+  if (n <= 0 || set.count <= 0) return hipSuccess;
+  if (set.count > kMaxGemmBatch) return hipErrorInvalidValue;
+  return chol_inv_rec(n, set, 0, n, s);
 }
 
-template hipError_t launch_load_reversed<float>(int64_t, const float*, int64_t, double*, hipStream_t);
-template hipError_t launch_load_reversed<double>(int64_t, const double*, int64_t, double*, hipStream_t);
-template hipError_t launch_store_normalized<float>(int64_t, const double*, float*, int64_t, float*, hipStream_t);
-template hipError_t launch_store_normalized<double>(int64_t, const double*, double*, int64_t, double*, hipStream_t);
+template hipError_t launch_load_reversed<float>(int64_t, const float*, int64_t, int64_t, double*,
+                                                int64_t, int, hipStream_t);
+template hipError_t launch_load_reversed<double>(int64_t, const double*, int64_t, int64_t, double*,
+                                                 int64_t, int, hipStream_t);
+template hipError_t launch_store_normalized<float>(int64_t, const double*, int64_t, float*, int64_t,
+                                                   int64_t, float*, int64_t, int, hipStream_t);
+template hipError_t launch_store_normalized<double>(int64_t, const double*, int64_t, double*,
+                                                    int64_t, int64_t, double*, int64_t, int,
+                                                    hipStream_t);
 
 }  // namespace bk

@@ -7,8 +7,7 @@
 // least 256 such blocks. Options: only lower output blocks (symmetric rank-k
 // update), A lower triangular (K ends with the row block), B lower
 // triangular (K ends with the column block when op(B) = B^T, starts with it
-// when op(B) = B), a batch of two independent problems of one shape (grid
-// z), and a dot epilogue that reduces sum(C_block .* D_block) per block
+// when op(B) = B), a batch of independent problems of one shape (grid z), and a dot epilogue that reduces sum(C_block .* D_block) per block
 // instead of storing C (loss). With a triangular operand the blocks with the
 // longest K ranges are dispatched first.
 #include <type_traits>
@@ -82,9 +81,9 @@ __device__ __forceinline__ void gemm64_block(const Gemm64Args& a, const BlockMap
   const int r16 = lane & 15, kg = lane >> 4;
   const int64_t bm = bmap.bm, bn = bmap.bn;
   const int z = bmap.z;
-  const double* __restrict__ Ap = a.A[z];
-  const double* __restrict__ Bp = a.B[z];
-  double* Cp = a.C[z];
+  const double* __restrict__ Ap = a.A + z * a.sA;
+  const double* __restrict__ Bp = a.B + z * a.sB;
+  double* Cp = a.C + z * a.sC;
   const int64_t row0 = bm * GB, col0 = bn * GB;
   // lower_out is decided on the 64-granular triangle: a block is computed if
   // any of its 64 x 64 sub-blocks is on or below the diagonal
@@ -238,7 +237,7 @@ __device__ __forceinline__ void gemm64_block(const Gemm64Args& a, const BlockMap
     }
   }
 
-  if (a.dot[0]) {
+  if (a.dot) {
     double part = 0.0;
     if (!skip) {
 #pragma unroll
@@ -252,7 +251,7 @@ __device__ __forceinline__ void gemm64_block(const Gemm64Args& a, const BlockMap
             if (gr < a.M && gc < a.N) {
               double wgt = 1.0;
               if (a.sym_dot) wgt = gr > gc ? 2.0 : (gr == gc ? 1.0 : 0.0);
-              part += wgt * a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
+              part += wgt * a.alpha * acc[i][j][r] * a.dot[gr * a.lddot + gc];
             }
           }
     }
@@ -261,7 +260,7 @@ __device__ __forceinline__ void gemm64_block(const Gemm64Args& a, const BlockMap
     for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
     if (lane == 0) red[wave] = part;
     __syncthreads();
-    if (tid == 0) a.partial[z][bm * nbx + bn] = ((red[0] + red[1]) + red[2]) + red[3];
+    if (tid == 0) a.partial[bm * nbx + bn] = ((red[0] + red[1]) + red[2]) + red[3];
     return;
   }
   if (skip) return;
@@ -330,8 +329,8 @@ __device__ __forceinline__ void big_mainloop(const Gemm64Args& a, int z, int64_t
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, kg = lane >> 4;
-  const double* __restrict__ Ap = a.A[z];
-  const double* __restrict__ Bp = a.B[z];
+  const double* __restrict__ Ap = a.A + z * a.sA;
+  const double* __restrict__ Bp = a.B + z * a.sB;
   auto kin = [&](int64_t gk) { return gk < kend && gk >= kbeg; };
   auto ain = [&](int64_t gr, int64_t gk) {
     return gr < a.M && kin(gk) && (!TRI || !a.a_lower || gk < (gr / GTRI + 1) * GTRI);
@@ -425,7 +424,7 @@ __device__ __forceinline__ double big_dot(const Gemm64Args& a, int z, int64_t ro
         if (gr < a.M && gc < a.N) {
           double wgt = 1.0;
           if (a.sym_dot) wgt = gr > gc ? 2.0 : (gr == gc ? 1.0 : 0.0);
-          part += wgt * a.alpha * acc[i][j][r] * a.dot[z][gr * a.lddot + gc];
+          part += wgt * a.alpha * acc[i][j][r] * a.dot[gr * a.lddot + gc];
         }
       }
   return part;
@@ -459,7 +458,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
   const BlockMap bmap = map_block<TRI>(a);
   const int64_t bm = bmap.bm, bn = bmap.bn;
   const int z = bmap.z;
-  double* Cp = a.C[z];
+  double* Cp = a.C + z * a.sC;
   const int64_t row0 = bm * BM, col0 = bn * BN;
   const bool skip = a.lower_out && col0 >= row0 + BM;
 
@@ -480,10 +479,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
   }
   if (!skip) big_mainloop<BM, BN, WM, WN, TRI>(a, z, row0, col0, kbeg, kend, acc, As, Bs);
 
-  if (a.dot[0]) {
+  if (a.dot) {
     const double part = skip ? 0.0 : big_dot<BM, BN, WM, WN>(a, z, row0, col0, acc);
     const double t = wg_sum<WM * WN>(part, red);
-    if (tid == 0) a.partial[z][bm * gridDim.x + bn] = t;
+    if (tid == 0) a.partial[bm * gridDim.x + bn] = t;
     return;
   }
   if (skip) return;
@@ -546,7 +545,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sk_lower_dot_kernel(Gemm64A
     it += cnt;
   }
   const double t = wg_sum<WM * WN>(part, red);
-  if (threadIdx.x == 0) a.partial[0][g] = t;
+  if (threadIdx.x == 0) a.partial[g] = t;
 }
 
 // Kernel choice: the 128 x 128 eight-wave kernel when it still gives at
@@ -556,7 +555,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sk_lower_dot_kernel(Gemm64A
 // no triangular operand), on one workgroup per compute unit.
 constexpr int kSkGrid = 256;
 static bool use_sk(const Gemm64Args& a) {
-  return a.lower_out && a.dot[0] && a.sym_dot && a.batch == 1 && !a.a_lower && !a.b_lower &&
+  return a.lower_out && a.dot && a.sym_dot && a.batch == 1 && !a.a_lower && !a.b_lower &&
          a.M == a.N;
 }
 // blocks of 128 x 128 (256 x 128 blocks measured slower here: the stream-K
@@ -608,19 +607,19 @@ static hipError_t launch_gb(const Gemm64Args& a, bool vec, hipStream_t s) {
 // another kernel (stream-K, 256 x 128, 128 x 128).
 static int small_block(const Gemm64Args& a) {
   if (use_sk(a)) return 0;
-  if (!a.a_lower && !a.b_lower && !a.dot[0] &&
+  if (!a.a_lower && !a.b_lower && !a.dot &&
       ((a.M + 255) / 256) * ((a.N + 127) / 128) * a.batch >= 256)
     return 0;
   if (use_big(a)) return 0;
   const int64_t b64 = ((a.M + 63) / 64) * ((a.N + 63) / 64) * a.batch;
-  return (!a.dot[0] && b64 <= 128) ? 32 : 64;
+  return (!a.dot && b64 <= 128) ? 32 : 64;
 }
 
 hipError_t launch_gemm64_pair(const Gemm64Args& a0, const Gemm64Args& a1, hipStream_t s) {
   const int g0 = small_block(a0), g1 = small_block(a1);
   const bool empty0 = a0.M <= 0 || a0.N <= 0, empty1 = a1.M <= 0 || a1.N <= 0;
-  if (empty0 || empty1 || g0 == 0 || g0 != g1 || a0.dot[0] || a1.dot[0] || a0.batch != a1.batch ||
-      a0.batch < 1 || a0.batch > 2) {
+  if (empty0 || empty1 || g0 == 0 || g0 != g1 || a0.dot || a1.dot || a0.batch != a1.batch ||
+      a0.batch < 1 || a0.batch > kMaxGemmBatch) {
     const hipError_t e = launch_gemm64(a0, s);
     return e != hipSuccess ? e : launch_gemm64(a1, s);
   }
@@ -639,14 +638,14 @@ hipError_t launch_gemm64_pair(const Gemm64Args& a0, const Gemm64Args& a1, hipStr
 
 hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.batch < 1 || a.batch > 2) return hipErrorInvalidValue;
+  if (a.batch < 1 || a.batch > kMaxGemmBatch) return hipErrorInvalidValue;
+  if (a.dot && a.batch != 1) return hipErrorInvalidValue;
   // 16-byte vectors need every row start of A and B 16-byte aligned; they
   // measured slower than element loads here (more registers, lower
   // occupancy), so they are off
-  bool vec = false && (a.lda % 2 == 0) && (a.ldb % 2 == 0);
-  for (int z = 0; z < a.batch; ++z)
-    vec = vec && (reinterpret_cast<uintptr_t>(a.A[z]) % 16 == 0) &&
-          (reinterpret_cast<uintptr_t>(a.B[z]) % 16 == 0);
+  const bool vec = false && (a.lda % 2 == 0) && (a.ldb % 2 == 0) && (a.sA % 2 == 0) &&
+                   (a.sB % 2 == 0) && (reinterpret_cast<uintptr_t>(a.A) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);
   if (use_sk(a)) {
     int64_t nk;
     const int64_t t = sk_total(a, &nk);
@@ -659,7 +658,7 @@ hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
   // products with at least 256 blocks of 256 x 128 (the loss's D A, the
   // factor's top Schur complement on its lower blocks): 4 x 2 waves of
   // 64 x 64, a third more MFMA work per loaded byte again
-  if (!a.a_lower && !a.b_lower && !a.dot[0] &&
+  if (!a.a_lower && !a.b_lower && !a.dot &&
       ((a.M + 255) / 256) * ((a.N + 127) / 128) * a.batch >= 256) {
     dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)((a.M + 255) / 256), (unsigned)a.batch);
     hipLaunchKernelGGL((gemm_big_kernel<256, 128, 4, 2, false>), grid, dim3(512), 0, s, a);
@@ -676,7 +675,7 @@ hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
   // small products (the factor's lower levels): 32 x 32 blocks give four
   // times the workgroups, each with a quarter of the dependent MFMA chain
   const int64_t b64 = ((a.M + 63) / 64) * ((a.N + 63) / 64) * a.batch;
-  if (!a.dot[0] && b64 <= 128) return launch_gb<32>(a, vec, s);
+  if (!a.dot && b64 <= 128) return launch_gb<32>(a, vec, s);
   return launch_gb<64>(a, vec, s);
 }
 

@@ -72,8 +72,10 @@ hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage
 constexpr int kLeafBlock = 12;
 
 // ---- factor (factor_kernels.hip), always float64 inside --------------------
+// X = J A J for `batch` matrices: A + z * sA -> X + z * sX (elements).
 template <typename R>
-hipError_t launch_load_reversed(int64_t n, const R* A, int64_t lda, double* X, hipStream_t s);
+hipError_t launch_load_reversed(int64_t n, const R* A, int64_t lda, int64_t sA, double* X,
+                                int64_t sX, int batch, hipStream_t s);
 // One matrix being factored: X (n x n, ld n) holds the lower triangle of the
 // (reversed) input and is overwritten with Schur complements; Y (n x n, ld n)
 // receives the inverse of its Cholesky factor (lower, zeros above the
@@ -86,47 +88,69 @@ struct FactorSide {
   double* TmpS;  // one C21 Y11 buffer per node-size class (orders up to 1024)
   int32_t* info;
 };
-// Y = Cholesky(X)^-1 for `nsides` (1 or 2) matrices of the same order n, in
-// one sequence of launches (the two sides share every launch).
-hipError_t factor_cholesky_inverse(int64_t n, const FactorSide* sides, int nsides, hipStream_t s);
+// `count` matrices of one order factored in the same launches: side z is
+// `first` with X, Y, Tmp and TmpS advanced by z * stride doubles and info by
+// z words.
+struct FactorSet {
+  FactorSide first;
+  int64_t stride;
+  int count;
+};
+__host__ __device__ inline FactorSide factor_side(const FactorSet& f, int z) {
+  FactorSide s = f.first;
+  const int64_t o = (int64_t)z * f.stride;
+  s.X += o;
+  s.Y += o;
+  s.Tmp += o;
+  s.TmpS += o;
+  s.info += z;
+  return s;
+}
+// Y = Cholesky(X)^-1 for every matrix of the set (order n), in one sequence
+// of launches.
+hipError_t factor_cholesky_inverse(int64_t n, const FactorSet& set, hipStream_t s);
+// L (and d, nullable) of `batch` matrices: Y + z * sY -> L + z * sL, d + z * sd.
 template <typename R>
-hipError_t launch_store_normalized(int64_t n, const double* Y, R* L, int64_t ldl, R* d,
-                                   hipStream_t s);
+hipError_t launch_store_normalized(int64_t n, const double* Y, int64_t sY, R* L, int64_t ldl,
+                                   int64_t sL, R* d, int64_t sd, int batch, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t v, hipStream_t s);
 
 // ---- float64 GEMM (gemm64.hip) --------------------------------------------
 // C = alpha * A * op(B) + beta * C, op(B) = B (K x N) or B^T (B is N x K), for
-// `batch` (1 or 2) problems of one shape (pointers [z]).
+// `batch` problems of one shape: problem z uses A + z * sA, B + z * sB,
+// C + z * sC (element strides).
 // lower_out: only 64x64 output blocks with block_row >= block_col are
 // computed (the others are left untouched). a_lower: A is lower triangular,
 // so row block r only needs k < (r + 1) * 64. b_lower: B as stored is lower
 // triangular: with transB the column block c only needs k < (c + 1) * 64,
 // without it only k >= c * 64.
-// dot[0] != nullptr: instead of storing C, the block's sum of
-// alpha (A op(B)) .* dot is written to partial[z][block] (C unused); with
+// dot != nullptr (batch 1 only): instead of storing C, the block's sum of
+// alpha (A op(B)) .* dot is written to partial[block] (C unused); with
 // sym_dot the elements are weighted 2 below the diagonal, 1 on it, 0 above.
 struct Gemm64Args {
   int64_t M, N, K;
-  const double* A[2];
-  int64_t lda;
-  const double* B[2];
-  int64_t ldb;
-  double* C[2];
-  int64_t ldc;
+  const double* A;
+  int64_t lda, sA;
+  const double* B;
+  int64_t ldb, sB;
+  double* C;
+  int64_t ldc, sC;
   double alpha, beta;
   int transB;
   int lower_out;
   int a_lower;
   int b_lower;
-  const double* dot[2];
+  const double* dot;
   int64_t lddot;
-  double* partial[2];
+  double* partial;
   int batch;
   // dot epilogue of a symmetric product computed on its lower blocks only:
   // element (r, c) counts twice below the diagonal, once on it, not above
   int sym_dot;
 };
 hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s);
+// Largest batch of one launch (the grid's z extent).
+constexpr int kMaxGemmBatch = 65535;
 // Two independent products: one launch when both go to the same 64 x 64 /
 // 32 x 32 kernel (no dot epilogue), else two launches in order.
 hipError_t launch_gemm64_pair(const Gemm64Args& a0, const Gemm64Args& a1, hipStream_t s);
@@ -147,5 +171,13 @@ hipError_t launch_sum_partials(const double* partial, int64_t count, double* out
 template <typename R>
 hipError_t launch_row_scales(int64_t m, int64_t n, const R* W, int64_t ldw, int32_t hi, R* s_out,
                              hipStream_t s);
+
+// ---- scale search (scale_kernels.hip) -------------------------------------
+// Largest candidate count - 1 of the per-row scale search.
+constexpr int kScaleMaxGrid = 1024;
+template <typename R>
+hipError_t launch_row_scales_mse(int64_t m, int64_t n, const R* W, int64_t ldw, int32_t lo,
+                                 int32_t hi, int32_t hi_code, int32_t grid, double max_shrink,
+                                 R* s_out, hipStream_t s);
 
 }  // namespace bk

@@ -114,6 +114,58 @@ def row_scales(W: np.ndarray, hi: int, dtype=None) -> np.ndarray:
     return s.astype(dt)
 
 
+def shrink_factor(k: int, grid: int, max_shrink: float) -> float:
+    """Candidate k of the scale search: 1 - max_shrink * k / grid, evaluated
+    in float64 in exactly this order (max_shrink * k, then / grid, then
+    1 - that), so that every implementation forms the same candidates."""
+    if grid == 0:
+        return 1.0
+    return 1.0 - (float(max_shrink) * float(k)) / float(grid)
+
+
+def row_scales_mse(W: np.ndarray, lo: int, hi: int, grid: int, max_shrink: float,
+                   dtype=None) -> np.ndarray:
+    """Per-row scale search of Appendix D (experimental setup): start from the
+    row's absmax divided by the largest code, then shrink it by up to a
+    factor 1 / (1 - max_shrink) (the pages: up to 2, max_shrink = 1/2)
+    choosing the candidate with the smallest round-to-nearest squared error
+    of the row. Reading of the unspecified search: grid + 1 candidates
+    s_k = s_max * (1 - max_shrink * k / grid), k = 0..grid (product in
+    float64, rounded once to ``dtype``); the row's error for s_k is
+    sum_j (W_ij - s_k c_j)^2 with c_j = clamp(rint(W_ij / s_k), lo, hi) (the
+    quantizer of §3.1, division in ``dtype``), summed in float64; the
+    smallest error wins and ties go to the smaller k (the larger scale). An
+    all-zero row keeps the scale 1 of the plain rule."""
+    W = np.asarray(W)
+    dt = np.dtype(dtype) if dtype is not None else W.dtype
+    Wd = W.astype(dt)
+    base = row_scales(Wd, hi, dt)
+    out = base.copy()
+    for i in range(Wd.shape[0]):
+        row = Wd[i]
+        if not np.any(row != 0):
+            continue
+        best, best_s = None, base[i]
+        for k in range(grid + 1):
+            sk = dt.type(np.float64(base[i]) * shrink_factor(k, grid, max_shrink))
+            c = np.clip(np.rint(row / sk), lo, hi)
+            e = row.astype(np.float64) - np.float64(sk) * c.astype(np.float64)
+            err = float(np.sum(e * e))
+            if best is None or err < best:
+                best, best_s = err, sk
+        out[i] = best_s
+    return out.astype(dt)
+
+
+def row_rtn_error(W: np.ndarray, s: np.ndarray, lo: int, hi: int) -> np.ndarray:
+    """Per-row squared round-to-nearest error sum_j (W_ij - s_i c_ij)^2,
+    c = clamp(rint(W / s), lo, hi), in float64 (division in W's dtype)."""
+    W = np.asarray(W)
+    c = np.clip(np.rint(W / s[:, None].astype(W.dtype)), lo, hi)
+    e = W.astype(np.float64) - s[:, None].astype(np.float64) * c
+    return np.sum(e * e, axis=1)
+
+
 # ---------------------------------------------------------------------------
 # Factor (first two steps of Algorithms 1-3, 5, 6)
 # ---------------------------------------------------------------------------

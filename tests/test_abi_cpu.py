@@ -111,6 +111,41 @@ def test_solve_batched_empty_and_workspace():
     assert L.bakron_solve_batched_workspace_bytes(bk.F32, 0, 100, 70) == 0
 
 
+def _factor_batched(**kw):
+    a = dict(dtype=bk.F32, batch=3, m=4, n=4, A=FAKE, lda=4, sa=16, B=FAKE, ldb=4, sb=16,
+             LA=FAKE, ldla=4, sla=16, LB=FAKE, ldlb=4, slb=16, dA=None, sda=0, dB=None, sdb=0,
+             ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    bad = (ctypes.c_int64 * 3)(7, 7, 7)
+    rc = bk.lib().bakron_factor_batched(
+        a["dtype"], a["batch"], a["m"], a["n"], a["A"], a["lda"], a["sa"], a["B"], a["ldb"], a["sb"],
+        a["LA"], a["ldla"], a["sla"], a["LB"], a["ldlb"], a["slb"], a["dA"], a["sda"], a["dB"],
+        a["sdb"], a["ws"], a["wsb"], bad, None)
+    return rc, tuple(bad)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(dtype=4), dict(batch=-1), dict(batch=32768), dict(m=-2), dict(A=None), dict(LB=None),
+    dict(lda=3), dict(ldlb=2), dict(sa=-1), dict(sla=15), dict(slb=0), dict(dA=FAKE, sda=3),
+    dict(dB=FAKE, sdb=0), dict(ws=None), dict(wsb=64), dict(ws=ctypes.c_void_p(0x1008)),
+    dict(sb=1 << 62),
+])
+def test_factor_batched_rejects_bad_arguments(bad):
+    rc, piv = _factor_batched(**bad)
+    assert rc == bk.EINVAL and piv == (-1, -1, -1)
+
+
+def test_factor_batched_empty_and_workspace():
+    assert _factor_batched(batch=0, A=None, B=None, LA=None, LB=None, ws=None)[0] == bk.OK
+    assert _factor_batched(m=0, n=0, A=None, B=None, LA=None, LB=None, ws=None)[0] == bk.OK
+    L = bk.lib()
+    one = L.bakron_factor_workspace_bytes(bk.F32, 100, 70)
+    five = L.bakron_factor_batched_workspace_bytes(bk.F32, 5, 100, 70)
+    assert L.bakron_factor_batched_workspace_bytes(bk.F32, 1, 100, 70) == one
+    assert 4 * one < five <= 5 * one
+    assert L.bakron_factor_batched_workspace_bytes(bk.F32, -1, 100, 70) == 0
+
+
 def test_factor_and_loss_reject_bad_arguments():
     L = bk.lib()
     bad = (ctypes.c_int64 * 2)(7, 7)
@@ -131,6 +166,21 @@ def test_factor_and_loss_reject_bad_arguments():
     assert rc == bk.EINVAL
     assert L.bakron_row_scales(bk.F32, 4, 4, FAKE, 4, 0, FAKE, None) == bk.EINVAL
     assert L.bakron_row_scales(bk.F32, 4, 4, FAKE, 3, 7, FAKE, None) == bk.EINVAL
+
+
+@pytest.mark.parametrize("bad", [
+    dict(dtype=3), dict(m=-1), dict(hi=0), dict(lo=5, hi=4), dict(grid=-1), dict(grid=1025),
+    dict(shrink=-0.1), dict(shrink=1.0), dict(shrink=float("nan")), dict(W=None), dict(ldw=3),
+    dict(s=None),
+])
+def test_row_scales_mse_rejects_bad_arguments(bad):
+    a = dict(dtype=bk.F32, m=4, n=4, W=FAKE, ldw=4, lo=-8, hi=7, grid=100, shrink=0.5, s=FAKE)
+    a.update(bad)
+    L = bk.lib()
+    rc = L.bakron_row_scales_mse(a["dtype"], a["m"], a["n"], a["W"], a["ldw"], a["lo"], a["hi"],
+                                 a["grid"], a["shrink"], a["s"], None)
+    assert rc == bk.EINVAL
+    assert L.bakron_row_scales_mse(bk.F32, 0, 4, None, 4, -8, 7, 100, 0.5, None, None) == bk.OK
 
 
 def _closed_form_leaves(m, n, T=16):

@@ -89,3 +89,46 @@ def test_batched_single_problem_and_empty(gpu_lib):
     e = bk.solve_batched(torch.empty((0, 40, 60), dtype=torch.float64, device="cuda"), LA[0], LB[0],
                          (-8, 7, 0))
     assert e.shape == (0, 40, 60)
+
+
+# ----------------------------------------------------------- batched factor ---
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("batch,m,n", [(3, 70, 70), (4, 50, 130), (2, 200, 64), (5, 1, 9),
+                                       (3, 257, 257)])
+def test_factor_batched_equals_single(gpu_lib, dtype, batch, m, n):
+    """Every pair's factors equal bakron_factor's bit for bit (both the
+    shared-launch case m == n and the two-set case m != n), and match the
+    oracle's factor to the factor parity bound."""
+    bk = gpu_lib
+    probs = [random_problem(m, n, dtype, seed=97 * b + m + n, heavy_tail=bool(b % 2))
+             for b in range(batch)]
+    A = torch.stack([to_dev(p.A) for p in probs])
+    B = torch.stack([to_dev(p.B) for p in probs])
+    LA, LB, dA, dB = bk.factor_batched(A, B)
+    for b, p in enumerate(probs):
+        la, lb, da, db = bk.factor(A[b], B[b])
+        torch.cuda.synchronize()
+        for x, y in ((LA[b], la), (LB[b], lb), (dA[b], da), (dB[b], db)):
+            assert torch.equal(x, y), b
+        ref, _ = O.factor(p.A)
+        cond = np.linalg.cond(O.sym_from_lower(p.A))
+        eps = 1e-16 if dtype == "f64" else 6e-8
+        err = np.max(np.abs(LA[b].cpu().numpy().astype(np.float64) - ref))
+        assert err <= 8 * eps + 64 * cond * 1.1e-16 * n, err
+
+
+def test_factor_batched_reports_failing_pair(gpu_lib):
+    bk = gpu_lib
+    probs = [random_problem(40, 100, "f64", seed=200 + b) for b in range(4)]
+    A = torch.stack([to_dev(p.A) for p in probs])
+    B = torch.stack([to_dev(p.B) for p in probs])
+    A[2, 30, 30] = -5.0  # pair 2, side A, row 30: reversed pivot 100 - 1 - 30
+    with pytest.raises(bk.BakronError) as ei:
+        bk.factor_batched(A, B)
+    assert ei.value.status == bk.ENOTSPD
+    assert tuple(ei.value.bad_pivot) == (2, 0, 69)
+    B[1, 5, 5] = -1.0  # an earlier pair fails on side B
+    with pytest.raises(bk.BakronError) as ei:
+        bk.factor_batched(A, B)
+    assert tuple(ei.value.bad_pivot) == (1, 1, 34)

@@ -156,9 +156,16 @@ def test_kv_batch_on_streams(gpu_lib, b_identity):
     for a_, b_ in zip(res, seq):
         assert np.array_equal(a_["V"], b_["V"]) and np.array_equal(a_["Wt"], b_["Wt"])
         assert a_["loss"] == b_["loss"]
-    # and the batched entry point (all 28 in the same launches) equals both
+    # and the batched entry points (all 28 in the same launches) equal both
     stack = lambda key: torch.stack([to_dev(o[key]) for o in res])
     W = torch.stack([to_dev(p.W) for p in probs])
+    LAb, LBb, dAb, dBb = gpu_lib.factor_batched(torch.stack([to_dev(p.A) for p in probs]),
+                                                torch.stack([to_dev(p.B) for p in probs]))
+    for i, out in enumerate(res):
+        assert np.array_equal(LAb[i].cpu().numpy(), out["LA"]), i
+        assert np.array_equal(LBb[i].cpu().numpy(), out["LB"]), i
+        assert np.array_equal(dAb[i].cpu().numpy().astype(np.float64), out["dA"]), i
+    del LAb, LBb
     Vb, Wtb = gpu_lib.solve_batched(W, stack("LA"), stack("LB"), probs[0].alphabet, stack("s"),
                                     return_wt=True)
     torch.cuda.synchronize()
