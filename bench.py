@@ -36,8 +36,8 @@ PEAK_FP64_MFMA_TFLOPS = 78.6    # MI355X dense FP64 matrix
 # over one step of this workload, scaled by a plain 512 MiB copy (FETCH_SIZE
 # x2.0, WRITE_SIZE x1.0), valid only for the band-kernel source and build
 # options with this hash: after any change to either the figure is null.
-BAND_TRAFFIC = {"sha256": "a921d3f1f1ab0d76e3c35bf38c57f3bf45c22adb045ea07ddb87fb219c6d58d4",
-                "bytes_per_launch": 1.2913e+08, "launches": 84,
+BAND_TRAFFIC = {"sha256": "b83584ce995b6559a351d2185189b9c4da1f0bd49e064b166f3753723100d812",
+                "bytes_per_launch": 1.2930e+08, "launches": 84,
                 "summary": "profiles/band_kernel_attn4096_f32_counters.md"}
 METRIC = "weights quantized/s (m·n/solve-time) + % FP32 MFMA peak, 4096×4096"
 
