@@ -254,6 +254,26 @@ def main():
         "ms": ss_ms, "rows": m, "candidates": grid + 1, "max_shrink": shrink,
         "evaluations_per_s": m * n * (grid + 1) / (ss_ms / 1e3),
         "hbm_gb_per_s": (m * n * 4 + m * 4) / (ss_ms / 1e3) / 1e9}
+    # Kronecker-factor estimation (§4.2): the input-side Gram of the 8192
+    # activations behind this workload's A (K-FAC factor, 1% damping), not
+    # part of the step; useful flops = N d (d + 1) (the lower triangle)
+    if args.workload == "attn4096":
+        from synth import config3_samples
+        Xa = torch.from_numpy(config3_samples()[0]).to(dev)
+        Ns, ds = Xa.shape
+        Gbuf = torch.empty((ds, ds), dtype=torch.float32, device=dev)
+        bk.gram(Xa, None, 1e-2, out=Gbuf)
+        e0.record(stream)
+        for _ in range(args.steps):
+            bk.gram(Xa, None, 1e-2, out=Gbuf)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        g_ms = e0.elapsed_time(e1) / args.steps
+        g_tf = Ns * ds * (ds + 1) / (g_ms / 1e3) / 1e12
+        result["gram"] = {"ms": g_ms, "samples": Ns, "dim": ds, "tflops": g_tf,
+                          "frac_fp32_mfma": g_tf / PEAK_FP32_MFMA_TFLOPS,
+                          "note": "K-FAC factor E[a a^T] + 1% damping (gram, mirror and damp kernels)"}
+        del Xa, Gbuf
     if timed and band_ms_steps:
         band_ms = float(np.mean(band_ms_steps))
         nb = len(band_idx)

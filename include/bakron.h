@@ -255,6 +255,33 @@ int bakron_row_scales_mse(int dtype, int64_t m, int64_t n, const void *W, int64_
                           int32_t alpha_lo, int32_t alpha_hi, int32_t grid, double max_shrink,
                           void *scales, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Kronecker factors from samples (§4.2 and Appendix A.2): for a Hessian
+ * H = E[a a^T (x) b b^T] over N samples (a in R^n on the input side, b in
+ * R^m on the output side),
+ *   K-FAC style   (independence):        A = E[a a^T],          B = E[b b^T];
+ *   Shampoo style (one power-iteration step from A = I, B = I):
+ *                                        A = E[|b|^2 a a^T],    B = E[|a|^2 b b^T].
+ * bakron_gram computes one such factor,
+ *   G = (1/N) sum_k w_k x_k x_k^T  +  damp_rel * mean(diag) * I,
+ * the damping applied after the mean of the undamped diagonal (the
+ * experiments regularise each Gram by a multiple of its mean diagonal).
+ * X      N x d (ldx >= d), row k = sample x_k (a for A, b for B).
+ * weights  length N (nullable = all 1): 1 for K-FAC, the other side's
+ *        bakron_sample_sqnorms for Shampoo.
+ * G      out, d x d (ldg >= d), both triangles written (exactly symmetric);
+ *        must not overlap X.
+ * Accumulates in `dtype` on MFMA (float32 or float64 sums over the samples).
+ * N = 0 gives G = 0. damp_rel >= 0. Asynchronous.
+ *
+ * bakron_sample_sqnorms: out[k] = sum_j X[k][j]^2 (float64 sum, rounded
+ * once to `dtype`), length N. Asynchronous.
+ * ------------------------------------------------------------------------ */
+int bakron_gram(int dtype, int64_t N, int64_t d, const void *X, int64_t ldx,
+                const void *weights, double damp_rel, void *G, int64_t ldg, void *stream);
+int bakron_sample_sqnorms(int dtype, int64_t N, int64_t d, const void *X, int64_t ldx,
+                          void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

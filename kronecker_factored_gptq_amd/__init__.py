@@ -19,7 +19,8 @@ import torch
 
 __all__ = ["F32", "F64", "SCALE_NONE", "SCALE_ROW", "SCALE_COL", "BakronError", "lib", "factor",
            "factor_batched",
-           "solve", "solve_batched", "loss", "row_scales", "row_scales_mse", "solve_schedule", "tile_size", "workspace_bytes"]
+           "solve", "solve_batched", "loss", "row_scales", "row_scales_mse", "gram",
+           "sample_sqnorms", "kfac_factors", "shampoo_factors", "solve_schedule", "tile_size", "workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libbakron.so")
@@ -94,6 +95,10 @@ def lib() -> ctypes.CDLL:
     L.bakron_row_scales_mse.argtypes = [_int, _i64, _i64, _vp, _i64, _i32, _i32, _i32,
                                         ctypes.c_double, _vp, _vp]
     L.bakron_row_scales_mse.restype = _int
+    L.bakron_gram.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, ctypes.c_double, _vp, _i64, _vp]
+    L.bakron_gram.restype = _int
+    L.bakron_sample_sqnorms.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _vp]
+    L.bakron_sample_sqnorms.restype = _int
     _lib = L
     return L
 
@@ -401,6 +406,51 @@ def row_scales_mse(W: torch.Tensor, alphabet: AlphabetLike, grid: int = 100,
     if rc != OK:
         raise BakronError(rc, "bakron_row_scales_mse")
     return s
+
+
+def gram(X: torch.Tensor, weights: Optional[torch.Tensor] = None, damp_rel: float = 0.0,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """(1/N) sum_k w_k x_k x_k^T over the rows of X (N x d), plus
+    damp_rel * mean(diag) * I (bakron_gram): the K-FAC factor with no
+    weights, the one-step Shampoo factor with the other side's squared norms."""
+    dev = _check_device(X, weights, out)
+    code = _dt(X)
+    N, d = X.shape
+    if weights is not None and (weights.dtype != X.dtype or weights.numel() != N
+                                or not weights.is_contiguous()):
+        raise ValueError("weights must be a contiguous length-N vector of X's dtype")
+    G = out if out is not None else torch.empty((d, d), dtype=X.dtype, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().bakron_gram(code, N, d, _p(X), _ld(X, "X"), _p(weights), float(damp_rel),
+                               _p(G), _ld(G, "G"), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_gram")
+    return G
+
+
+def sample_sqnorms(X: torch.Tensor) -> torch.Tensor:
+    """|x_k|^2 of every row of X (bakron_sample_sqnorms)."""
+    dev = _check_device(X)
+    code = _dt(X)
+    N, d = X.shape
+    out = torch.empty(N, dtype=X.dtype, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().bakron_sample_sqnorms(code, N, d, _p(X), _ld(X, "X"), _p(out), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_sample_sqnorms")
+    return out
+
+
+def kfac_factors(Xa: torch.Tensor, Xb: torch.Tensor, damp_rel: float = 0.0):
+    """K-FAC-style Kronecker factors A = E[a a^T], B = E[b b^T] (§4.2) from
+    the sample rows of Xa (N x n) and Xb (N x m)."""
+    return gram(Xa, None, damp_rel), gram(Xb, None, damp_rel)
+
+
+def shampoo_factors(Xa: torch.Tensor, Xb: torch.Tensor, damp_rel: float = 0.0):
+    """One-step Shampoo-style factors A = E[|b|^2 a a^T], B = E[|a|^2 b b^T]
+    (§4.2, Appendix A.2)."""
+    return gram(Xa, sample_sqnorms(Xb), damp_rel), gram(Xb, sample_sqnorms(Xa), damp_rel)
 
 
 def solve_schedule(dtype: int, m: int, n: int):

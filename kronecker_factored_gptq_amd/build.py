@@ -21,7 +21,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libbakron.so")
 
 SOURCES = ["abi.cpp", "solve_kernels.hip", "band_kernels.hip", "factor_kernels.hip", "gemm64.hip", "loss_kernels.hip",
-           "scale_kernels.hip"]
+           "scale_kernels.hip", "gram_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -632,4 +632,37 @@ int bakron_row_scales_mse(int dtype, int64_t m, int64_t n, const void* W, int64_
   return e == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
 }
 
+int bakron_gram(int dtype, int64_t N, int64_t d, const void* X, int64_t ldx, const void* weights,
+                double damp_rel, void* G, int64_t ldg, void* stream) {
+  if (!dtype_ok(dtype) || N < 0 || d < 0) return BAKRON_EINVAL;
+  if (N > INT_MAX || d > INT_MAX / 2) return BAKRON_EINVAL;
+  if (!(damp_rel >= 0.0) || damp_rel > 1e300) return BAKRON_EINVAL;
+  if (d == 0) return BAKRON_OK;
+  if (!G || ldg < d) return BAKRON_EINVAL;
+  if (N > 0 && (!X || ldx < d)) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == BAKRON_F32)
+    e = launch_gram<float>(N, d, (const float*)X, ldx, (const float*)weights, damp_rel, (float*)G,
+                           ldg, s);
+  else
+    e = launch_gram<double>(N, d, (const double*)X, ldx, (const double*)weights, damp_rel,
+                            (double*)G, ldg, s);
+  return e == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
+}
+
+int bakron_sample_sqnorms(int dtype, int64_t N, int64_t d, const void* X, int64_t ldx, void* out,
+                          void* stream) {
+  if (!dtype_ok(dtype) || N < 0 || d < 0 || N > INT_MAX) return BAKRON_EINVAL;
+  if (N == 0) return BAKRON_OK;
+  if (!out || (d > 0 && (!X || ldx < d))) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == BAKRON_F32)
+    e = launch_sample_sqnorms<float>(N, d, (const float*)X, ldx, (float*)out, s);
+  else
+    e = launch_sample_sqnorms<double>(N, d, (const double*)X, ldx, (double*)out, s);
+  return e == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
+}
+
 }  // extern "C"

@@ -180,4 +180,15 @@ hipError_t launch_row_scales_mse(int64_t m, int64_t n, const R* W, int64_t ldw, 
                                  int32_t hi, int32_t hi_code, int32_t grid, double max_shrink,
                                  R* s_out, hipStream_t s);
 
+// ---- Kronecker factors from samples (gram_kernels.hip) ----------------------
+// G = (1/N) X^T diag(w) X (w nullable = 1), then + damp_rel * mean(diag) * I;
+// X is N x d (ldx), G d x d (ldg), both triangles written.
+template <typename R>
+hipError_t launch_gram(int64_t N, int64_t d, const R* X, int64_t ldx, const R* w, double damp_rel,
+                       R* G, int64_t ldg, hipStream_t s);
+// out[k] = |row k of X|^2.
+template <typename R>
+hipError_t launch_sample_sqnorms(int64_t N, int64_t d, const R* X, int64_t ldx, R* out,
+                                 hipStream_t s);
+
 }  // namespace bk

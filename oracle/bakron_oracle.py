@@ -167,6 +167,63 @@ def row_rtn_error(W: np.ndarray, s: np.ndarray, lo: int, hi: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Kronecker factors from samples (§4.2, Appendix A.2)
+# ---------------------------------------------------------------------------
+
+def weighted_gram(X: np.ndarray, w: Optional[np.ndarray] = None) -> np.ndarray:
+    """(1/N) sum_k w_k x_k x_k^T over the N rows x_k of X (w = 1 when None),
+    in float64: the sample expectation E[w x x^T]."""
+    X = np.asarray(X, dtype=np.float64)
+    N = X.shape[0]
+    if N == 0:
+        return np.zeros((X.shape[1], X.shape[1]))
+    Xw = X if w is None else X * np.asarray(w, dtype=np.float64)[:, None]
+    return (X.T @ Xw) / N
+
+
+def damp(G: np.ndarray, rel: float) -> np.ndarray:
+    """G + rel * mean(diag(G)) * I: the Gram regularisation of the
+    experiments (Appendix D adds a multiple of the mean diagonal)."""
+    G = np.array(G, dtype=np.float64)
+    if G.shape[0]:
+        G[np.diag_indices_from(G)] += rel * float(np.mean(np.diag(G)))
+    return G
+
+
+def kfac_factors(Xa: np.ndarray, Xb: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """K-FAC-style factors (§4.2: independence pulls the expectation apart):
+    H = E[a a^T (x) b b^T] ~ E[a a^T] (x) E[b b^T]; sample k is row k of Xa
+    (input side, n) and of Xb (output side, m)."""
+    return weighted_gram(Xa), weighted_gram(Xb)
+
+
+def shampoo_factors(Xa: np.ndarray, Xb: np.ndarray, iters: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Shampoo-style factors (§4.2, Appendix A.2): the power iteration for the
+    top singular vectors of the rearranged Hessian, written on the factors,
+    from A = I, B = I: both new factors from the previous pair,
+        A' = E[(b^T B b) a a^T],   B' = E[(a^T A a) b b^T],
+    without normalisation (the solver is invariant to scaling either factor).
+    One iteration gives E[|b|^2 a a^T] and E[|a|^2 b b^T]."""
+    Xa = np.asarray(Xa, dtype=np.float64)
+    Xb = np.asarray(Xb, dtype=np.float64)
+    A = np.eye(Xa.shape[1])
+    B = np.eye(Xb.shape[1])
+    for it in range(iters):
+        if it > 0:  # keep many iterations finite; the scale is irrelevant
+            A, B = A / np.linalg.norm(A), B / np.linalg.norm(B)
+        wa = np.einsum("ki,ij,kj->k", Xb, B, Xb)  # b_k^T B b_k
+        wb = np.einsum("ki,ij,kj->k", Xa, A, Xa)  # a_k^T A a_k
+        A, B = weighted_gram(Xa, wa), weighted_gram(Xb, wb)
+    return A, B
+
+
+def sample_sqnorms(X: np.ndarray) -> np.ndarray:
+    """|x_k|^2 of every row, in float64 (the one-step Shampoo weights)."""
+    X = np.asarray(X, dtype=np.float64)
+    return np.sum(X * X, axis=1)
+
+
+# ---------------------------------------------------------------------------
 # Factor (first two steps of Algorithms 1-3, 5, 6)
 # ---------------------------------------------------------------------------
 

@@ -111,6 +111,19 @@ def config2(matrix_idx: int = 0) -> Problem:
                    B.astype(np.float32), "f32", (-8, 7, 0), 7)
 
 
+def config3_samples(matrix_idx: int = 0):
+    """The samples behind config 3's Grams, one sample per ROW (N x dim,
+    float32): the 8192 activations (with the 41 outlier channels x20) and the
+    8192 gradient vectors, drawn exactly as config3 draws them."""
+    cid, m, n, N = 3, 4096, 4096, 8192
+    XA = _gaussian(rng(cid, matrix_idx, ROLE_A), (n, N), np.float32)
+    n_out = int(round(0.01 * n))
+    out = rng(cid, matrix_idx, ROLE_OUTLIER).choice(n, size=n_out, replace=False)
+    XA[out, :] *= 20.0
+    XB = _gaussian(rng(cid, matrix_idx, ROLE_B), (m, N), np.float32)
+    return np.ascontiguousarray(XA.T), np.ascontiguousarray(XB.T)
+
+
 def config3(matrix_idx: int = 0) -> Problem:
     """4096x4096 fp32 (Llama-3-8B attention projection shape). W ~ N(0,0.02^2).
     A = Gram/8192 of 8192 N(0,I) activations in which round(1% of n) = 41

@@ -146,6 +146,22 @@ def test_factor_batched_empty_and_workspace():
     assert L.bakron_factor_batched_workspace_bytes(bk.F32, -1, 100, 70) == 0
 
 
+@pytest.mark.parametrize("bad", [
+    dict(dtype=2), dict(N=-1), dict(d=-1), dict(X=None), dict(ldx=3), dict(G=None), dict(ldg=3),
+    dict(damp=-0.5), dict(damp=float("nan")),
+])
+def test_gram_rejects_bad_arguments(bad):
+    a = dict(dtype=bk.F32, N=5, d=4, X=FAKE, ldx=4, w=None, damp=0.0, G=FAKE, ldg=4)
+    a.update(bad)
+    L = bk.lib()
+    assert L.bakron_gram(a["dtype"], a["N"], a["d"], a["X"], a["ldx"], a["w"], a["damp"], a["G"],
+                         a["ldg"], None) == bk.EINVAL
+    assert L.bakron_gram(bk.F32, 5, 0, None, 0, None, 0.0, None, 0, None) == bk.OK
+    assert L.bakron_sample_sqnorms(bk.F32, 5, 4, FAKE, 3, FAKE, None) == bk.EINVAL
+    assert L.bakron_sample_sqnorms(bk.F32, 5, 4, FAKE, 4, None, None) == bk.EINVAL
+    assert L.bakron_sample_sqnorms(bk.F32, 0, 4, None, 4, None, None) == bk.OK
+
+
 def test_factor_and_loss_reject_bad_arguments():
     L = bk.lib()
     bad = (ctypes.c_int64 * 2)(7, 7)
