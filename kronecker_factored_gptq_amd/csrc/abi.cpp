@@ -151,7 +151,7 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
     const bool timed = op_ms && (op.kind == OP_BAND1 || op.kind == OP_BAND2);
     hipEvent_t e0 = timed ? ev[evi] : nullptr, e1 = timed ? ev[evi + 1] : nullptr;
     switch (op.kind) {
-      case OP_LEAF: e = launch_leaf<R>(g, op.k, op.mid, Wk, LBp, LAp, lp, s); break;
+      case OP_LEAF: e = launch_leaf<R>(g, op.k, op.mid, Wk, LBp, LAp, Mb, lp, s); break;
       case OP_BAND1:
         e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, bb, s, e0, e1);
         break;

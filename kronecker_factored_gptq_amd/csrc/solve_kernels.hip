@@ -101,10 +101,12 @@ __global__ __launch_bounds__(256) void pack_l_kernel(int64_t dim, const R* __res
 //    sum_J (sum_I L^B[P,I] E[I,J]) L^A[Q,J]^T — the updates between tile
 //    anti-diagonals of one block are done here, left-looking, instead of by
 //    internal nodes (any grouping of the updates gives the same codes,
-//    Appendix B). Each wave takes every fourth J. The inner sum is computed
-//    transposed, M^T = E^T L^B^T, because the MFMA result layout of M^T is
-//    exactly the A-operand layout of the outer product with k = its row
-//    index: no data movement between the two products.
+//    Appendix B). The inner sums M[P][J] of row P are carried from leaf to
+//    leaf of the block (only two columns change per leaf); each wave takes
+//    every fourth J and a quarter of the new column's terms. The inner sum is
+//    computed transposed, M^T = E^T L^B^T, because the MFMA result layout of
+//    M^T is exactly the A-operand layout of the outer product with k = its
+//    row index: no data movement between the two products.
 // 2. Sweep (wave 0): the tile lives in the MFMA accumulator. In-tile step t
 //    rounds the entries (p, t - p) (one per column, §3.3's anti-diagonal
 //    order) to c = clamp(rint(u)) and adds L^B e L^A^T for the step's errors
@@ -120,12 +122,19 @@ template <> struct EVec<float> {
     const float4 v = *reinterpret_cast<const float4*>(p);
     out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
   }
+  __device__ static inline void store4(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
 };
 template <> struct EVec<double> {
   __device__ static inline void load4(const double* p, double* out) {
     const double2 v0 = reinterpret_cast<const double2*>(p)[0];
     const double2 v1 = reinterpret_cast<const double2*>(p)[1];
     out[0] = v0.x; out[1] = v0.y; out[2] = v1.x; out[3] = v1.y;
+  }
+  __device__ static inline void store4(double* p, const double* v) {
+    reinterpret_cast<double2*>(p)[0] = make_double2(v[0], v[1]);
+    reinterpret_cast<double2*>(p)[1] = make_double2(v[2], v[3]);
   }
 };
 
@@ -182,11 +191,16 @@ __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Waves of a leaf workgroup: wave w of the prologue takes the block's earlier
+// tiles of columns J = Jlo + w, Jlo + w + kLeafWaves, ...
+constexpr int kLeafWaves = 4;
+
 template <typename R>
-__global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt, int64_t m,
+__global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, int Mt, int Nt, int64_t m,
                                                    int64_t n, R* __restrict__ Wk,
                                                    const R* __restrict__ LBp,
-                                                   const R* __restrict__ LAp, LeafParams<R> lp,
+                                                   const R* __restrict__ LAp,
+                                                   R* __restrict__ Mc, LeafParams<R> lp,
                                                    BatchStrides bs) {
   constexpr int T = 16;
   {  // problem blockIdx.y of a batch: its workspace and outputs
@@ -194,13 +208,15 @@ __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt
     Wk += b * bs.ws;
     LBp += b * bs.ws;
     LAp += b * bs.ws;
+    Mc += b * bs.ws;
     lp.V += b * bs.v;
     if (lp.Wt) lp.Wt += b * bs.wt;
     if (lp.scales) lp.scales += b * bs.s;
   }
   typedef Mfma<R> MF;
   typedef typename MF::acc_t acc_t;
-  __shared__ R red[3][T][T + 1];
+  __shared__ R red[kLeafWaves - 1][T][T + 1];
+  __shared__ __attribute__((aligned(16))) R fm[kLeafWaves][T * T];  // fresh-column shares
   __shared__ R lat[T][T + 1];
   __shared__ R ow[T][T + 1];
 
@@ -215,7 +231,7 @@ __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt
   // overlaps it: this thread's element of L^A[Q,Q] and, on wave 0, the tile
   // and its lbK operands (lbK[s] = L^B[P,P][c][KA kg + KB s])
   constexpr int KA = SweepK<R>::KA, KB = SweepK<R>::KB;
-  const R lat_v = LAp[tri_index(Q, Q) * T * T + tid];
+  const R lat_v = tid < T * T ? LAp[tri_index(Q, Q) * T * T + tid] : R(0);
   R w0[4], lbK[4];
   if (wave == 0) {
     const R* lb = LBp + tri_index(P, P) * T * T + c * T + KA * kg;
@@ -226,59 +242,116 @@ __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt
     }
   }
 
-  // ---- 1. prologue
+  // ---- 1. prologue: acc = sum over J of M[P][J] L^A[Q,J]^T, with
+  // M[P][J] = sum_I L^B[P,I] E[I,J] over the block's earlier tiles (I, J).
+  // Row P's partial sums are kept between the leaves of a block in Mc (slot
+  // J of row P, MFMA lane layout: lane l holds M[c][row(l, r)] at l * 4 + r):
+  // from leaf K - 1 to K only column J = Q - 1 gains a term (I = P) and
+  // column J = Q is new (I < P), so a leaf adds d + 1 tile products instead
+  // of recomputing all (d + 1)(d + 2) / 2 - 1 of them (d = K - K0).
+  constexpr int NJ = (kLeafBlock - 1 + kLeafWaves - 1) / kLeafWaves;  // cached columns per wave
+  constexpr int NI = (kLeafBlock - 1 + kLeafWaves - 1) / kLeafWaves;  // fresh-column terms per wave
+  const int d = K - K0;
+  const bool keep = d + 1 < kLeafBlock;  // a later leaf of this block reads the cache
   acc_t acc = MF::zero();
-  if (K > K0) {
+  acc_t fresh = MF::zero();  // this wave's share of M[P][Q]
+  R* McP = Mc + (int64_t)P * Nt * T * T;
+  if (d > 0) {
     const int Jlo = K0 - P > 0 ? K0 - P : 0;
-    for (int J = Jlo + wave; J <= Q; J += 4) {
-      const int Ilo = K0 - J > 0 ? K0 - J : 0;
-      const int Ihi = P < K - 1 - J ? P : K - 1 - J;
-      if (Ilo > Ihi) continue;
-      // the block's earlier tiles (I, J), Ilo <= I <= Ihi (at most
-      // kLeafBlock - 1), in kChunks chunks of up to kPro: all loads of a
-      // chunk are issued before its first MFMA
-      constexpr int kChunks = (kLeafBlock - 1 + 7) / 8;
-      constexpr int kPro = (kLeafBlock - 1 + kChunks - 1) / kChunks;
-      R la[4];
-      const R* La = LAp + tri_index(Q, J) * T * T;
+    const int Ilo = K0 - Q > 0 ? K0 - Q : 0;  // fresh column: Ilo <= I <= P - 1
+    // every load first: cached columns J = Jlo + wave + kLeafWaves t < Q,
+    // their L^A tiles, the update term of J = Q - 1, this wave's terms of
+    // the fresh column, and L^A[Q,Q]
+    R la[NJ][4], mc[NJ][4], laq[4], eu[4], lu[4], ef[NI][4], lf[NI][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) la[s] = La[c * T + MF::row(lane, s)];
-      acc_t mt = MF::zero();  // lane holds M^T[row(lane, r)][c] = M[c][row(lane, r)]
+    for (int t = 0; t < NJ; ++t) {
+      const int J = Jlo + wave + kLeafWaves * t;
 #pragma unroll
-      for (int ch = 0; ch < kChunks; ++ch) {
-        const int I0 = Ilo + ch * kPro;
-        if (I0 > Ihi) break;
-        R ev[kPro][4], lv[kPro][4];
+      for (int s = 0; s < 4; ++s) { la[t][s] = R(0); mc[t][s] = R(0); }
+      if (J < Q) {
+        const R* La = LAp + tri_index(Q, J) * T * T;
 #pragma unroll
-        for (int u = 0; u < kPro; ++u) {
-          const int I = I0 + u;
-          if (I <= Ihi) {
-            const R* E = Wk + ((int64_t)I * Nt + J) * T * T;
-            EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lv[u]);
+        for (int s = 0; s < 4; ++s) la[t][s] = La[c * T + MF::row(lane, s)];
+        if (d >= 2) EVec<R>::load4(McP + (int64_t)J * T * T + lane * 4, mc[t]);
+      }
+    }
+    {
+      const R* La = LAp + tri_index(Q, Q) * T * T;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) ev[u][s] = E[(4 * kg + s) * T + c];
-          } else {
+      for (int s = 0; s < 4; ++s) laq[s] = La[c * T + MF::row(lane, s)];
+    }
+    const bool upd = Q >= 1 && Q - 1 >= Jlo && (Q - 1 - Jlo) % kLeafWaves == wave;
+    if (upd) {
+      const R* E = Wk + ((int64_t)P * Nt + Q - 1) * T * T;
+      EVec<R>::load4(LBp + tri_index(P, P) * T * T + c * T + 4 * kg, lu);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) { ev[u][s] = R(0); lv[u][s] = R(0); }
-          }
-        }
+      for (int s = 0; s < 4; ++s) eu[s] = E[(4 * kg + s) * T + c];
+    }
 #pragma unroll
-        for (int u = 0; u < kPro; ++u) {
-          if (I0 + u > Ihi) break;
+    for (int u = 0; u < NI; ++u) {
+      const int I = Ilo + wave + kLeafWaves * u;
+      if (I <= P - 1) {
+        const R* E = Wk + ((int64_t)I * Nt + Q) * T * T;
+        EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lf[u]);
 #pragma unroll
-          for (int s = 0; s < 4; ++s) mt = MF::mma(ev[u][s], lv[u][s], mt);
+        for (int s = 0; s < 4; ++s) ef[u][s] = E[(4 * kg + s) * T + c];
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) { ef[u][s] = R(0); lf[u][s] = R(0); }
+      }
+    }
+    // fresh column: this wave's terms, and its part of the outer product
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      if (Ilo + wave + kLeafWaves * u > P - 1) break;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) fresh = MF::mma(ef[u][s], lf[u][s], fresh);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = MF::mma(fresh[s], laq[s], acc);
+    // cached columns (J = Q - 1 gains its term and is stored back)
+#pragma unroll
+    for (int t = 0; t < NJ; ++t) {
+      const int J = Jlo + wave + kLeafWaves * t;
+      if (J >= Q) break;
+      acc_t mt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mt[r] = mc[t][r];
+      if (J == Q - 1) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mt = MF::mma(eu[s], lu[s], mt);
+        if (keep) {
+          R o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = mt[r];
+          EVec<R>::store4(McP + (int64_t)J * T * T + lane * 4, o);
         }
       }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], la[s], acc);
+      for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], la[t][s], acc);
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) fm[wave][lane * 4 + r] = fresh[r];
   }
   if (wave > 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave - 1][MF::row(lane, r)][c] = acc[r];
   }
-  lat[tid >> 4][tid & 15] = lat_v;
+  if (tid < T * T) lat[tid >> 4][tid & 15] = lat_v;
   __syncthreads();
+  if (wave == 1 && d > 0 && keep) {
+    // the fresh column M[P][Q] for the next leaf of the block, summed over
+    // the waves in a fixed order
+    R o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      R v = fm[0][lane * 4 + r];
+#pragma unroll
+      for (int w = 1; w < kLeafWaves; ++w) v += fm[w][lane * 4 + r];
+      o[r] = v;
+    }
+    EVec<R>::store4(McP + (int64_t)Q * T * T + lane * 4, o);
+  }
   if (wave > 0) return;
 
   // ---- 2. sweep on wave 0
@@ -289,7 +362,10 @@ __global__ __launch_bounds__(256) void leaf_kernel(int K, int K0, int Mt, int Nt
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = MF::row(lane, r);
-    acc[r] += w0[r] + red[0][row][c] + red[1][row][c] + red[2][row][c];
+    R pro = w0[r];
+#pragma unroll
+    for (int w = 0; w < kLeafWaves - 1; ++w) pro += red[w][row][c];
+    acc[r] += pro;
     const bool valid = (int64_t)P * T + row < m && gj < n;
     dr[r] = valid ? row + c : -1;
   }
@@ -381,14 +457,14 @@ static inline void diag_range(const SolveGeom& g, int K, int* lo, int* hi) {
 
 template <typename R>
 hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
-                       const LeafParams<R>& lp, hipStream_t s) {
+                       R* Mc, const LeafParams<R>& lp, hipStream_t s) {
   static_assert(kTile == 16, "the leaf kernel works on 16 x 16 tiles");
   int lo, hi;
   diag_range(g, K, &lo, &hi);
   if (hi < lo) return hipSuccess;
   if (g.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL((leaf_kernel<R>), dim3(hi - lo + 1, g.batch), dim3(256), 0, s, K, K0, g.Mt,
-                     g.Nt, g.m, g.n, Wk, LBp, LAp, lp, g.bs);
+  hipLaunchKernelGGL((leaf_kernel<R>), dim3(hi - lo + 1, g.batch), dim3(64 * kLeafWaves), 0, s,
+                     K, K0, g.Mt, g.Nt, g.m, g.n, Wk, LBp, LAp, Mc, lp, g.bs);
   return hipGetLastError();
 }
 
@@ -397,7 +473,7 @@ hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, c
                                        hipStream_t);                                            \
   template hipError_t launch_pack_l<R>(const SolveGeom&, bool, const R*, int64_t, const R*, R*, \
                                        hipStream_t);                                            \
-  template hipError_t launch_leaf<R>(const SolveGeom&, int, int, R*, const R*, const R*,        \
+  template hipError_t launch_leaf<R>(const SolveGeom&, int, int, R*, const R*, const R*, R*,    \
                                      const LeafParams<R>&, hipStream_t);
 BK_INST(float)
 BK_INST(double)
