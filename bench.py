@@ -47,9 +47,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "w512", "kv28"],
+    ap.add_argument("--workload", default="attn4096",
+                    choices=["attn4096", "w512", "kv28", "mlp_gate_up", "mlp_down"],
                     help="attn4096: the 4096 x 4096 matrix (default); w512: 512 x 512; kv28: "
-                         "28 k/v projections of 1024 x 2048, batched solve")
+                         "28 k/v projections of 1024 x 2048, batched solve; mlp_gate_up / "
+                         "mlp_down: the 14336 x 4096 / 4096 x 14336 MLP matrices (3-bit)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true",
                     help="skip the instrumented steps (per-launch band events); roofline omitted")
@@ -142,7 +144,13 @@ def main():
     if args.workload == "kv28":
         bench_kv28(args, dev)
         return
-    p = config3() if args.workload == "attn4096" else config2()
+    from synth import config4
+    if args.workload == "attn4096":
+        p = config3()
+    elif args.workload.startswith("mlp_"):
+        p = config4(args.workload[4:])
+    else:
+        p = config2()
     m, n = p.W.shape
     hi = p.scale_hi
     lo_, hi_, unb = p.alphabet
@@ -231,7 +239,11 @@ def main():
                          "A = Gram/8192 of 8192 Gaussian activations with 41 channels x20, "
                          "B = Gram/8192 of 8192 Gaussian gradients, both +1% mean-diag damping; "
                          "alphabet {-8..7}, per-row absmax/7 scales")
-            if args.workload == "attn4096" else f"{m}x{n} float32, heavy-tailed input Gram, 4-bit",
+            if args.workload == "attn4096" else
+            (f"{m}x{n} float32 weight (Llama-3-8B MLP {args.workload[4:]} shape); A, B = Grams/16384 "
+             "of 16384 Gaussian vectors, +1% mean-diag damping; alphabet {-4..3}, per-row absmax/3 "
+             "scales") if args.workload.startswith("mlp_") else
+            f"{m}x{n} float32, heavy-tailed input Gram, 4-bit",
             "m": m, "n": n, "step": "factor + row scales + BaKron solve + loss",
             "tile": T,
         },
@@ -292,7 +304,11 @@ def main():
         result["trailing_all_nodes"] = {
             "useful_flop": fl["band"] + fl["small"], "small_node_flop": fl["small"]}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(p, hi)
+        if args.workload.startswith("mlp_"):
+            # the oracle on a full MLP matrix takes minutes; not run here
+            result["cpu_baseline"] = None
+        else:
+            result["cpu_baseline"] = cpu_baseline(p, hi)
     print(json.dumps(result))
 
 
