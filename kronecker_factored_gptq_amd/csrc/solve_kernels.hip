@@ -395,7 +395,11 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
     const R es = row_skew(e);
     static_for<0, 4>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
-      if constexpr (t - KB * s >= 0) {
+      // MFMA s takes the rows k = KA kg + KB s: it contributes only if some
+      // such k has its column t - k inside the tile (k >= t - (T - 1)) and
+      // k <= t; the last step's update reaches no later anti-diagonal. The
+      // skipped products add exact zeros or are never read.
+      if constexpr (t - KB * s >= 0 && KA * 3 + KB * s >= t - (T - 1) && t < 2 * T - 2) {
         const R ev = dpp_mov<kDppRowNewBcast + ((t - KB * s) & 15), 0xF>(R(0), es);
         acc = MF::mma(lbK[s] * ev, laK[t - KB * s], acc);
       }
