@@ -36,8 +36,8 @@ PEAK_FP64_MFMA_TFLOPS = 78.6    # MI355X dense FP64 matrix
 # over one step of this workload, scaled by a plain 512 MiB copy (FETCH_SIZE
 # x2.0, WRITE_SIZE x1.0), valid only for the band-kernel source and build
 # options with this hash: after any change to either the figure is null.
-BAND_TRAFFIC = {"sha256": "b83584ce995b6559a351d2185189b9c4da1f0bd49e064b166f3753723100d812",
-                "bytes_per_launch": 1.2930e+08, "launches": 84,
+BAND_TRAFFIC = {"sha256": "c0a15b5aa0079d3d467c0c87ca7c324a6abafac6744f2ff4e95c3027e59be317",
+                "bytes_per_launch": 1.3055e+08, "launches": 84,
                 "summary": "profiles/band_kernel_attn4096_f32_counters.md"}
 METRIC = "weights quantized/s (m·n/solve-time) + % FP32 MFMA peak, 4096×4096"
 
@@ -52,6 +52,9 @@ def parse():
                     help="attn4096: the 4096 x 4096 matrix (default); w512: 512 x 512; kv28: "
                          "28 k/v projections of 1024 x 2048, batched solve; mlp_gate_up / "
                          "mlp_down: the 14336 x 4096 / 4096 x 14336 MLP matrices (3-bit)")
+    ap.add_argument("--dtype", default="f32", choices=["f32", "f64"],
+                    help="solve dtype: f32 (default; band products on the FP32 matrix cores) or "
+                         "f64 (the same workload cast to float64, FP64 matrix cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true",
                     help="skip the instrumented steps (per-launch band events); roofline omitted")
@@ -154,10 +157,13 @@ def main():
     m, n = p.W.shape
     hi = p.scale_hi
     lo_, hi_, unb = p.alphabet
-    W = torch.from_numpy(p.W).to(dev)
-    A = torch.from_numpy(p.A).to(dev)
-    B = torch.from_numpy(p.B).to(dev)
-    code = bk.F32
+    f64 = args.dtype == "f64"
+    tdt = torch.float64 if f64 else torch.float32
+    W = torch.from_numpy(p.W).to(dev, tdt)
+    A = torch.from_numpy(p.A).to(dev, tdt)
+    B = torch.from_numpy(p.B).to(dev, tdt)
+    code = bk.F64 if f64 else bk.F32
+    peak = PEAK_FP64_MFMA_TFLOPS if f64 else PEAK_FP32_MFMA_TFLOPS
     wsF = torch.empty(bk.workspace_bytes("factor", code, m, n), dtype=torch.uint8, device=dev)
     wsS = torch.empty(bk.workspace_bytes("solve", code, m, n), dtype=torch.uint8, device=dev)
     wsL = torch.empty(bk.workspace_bytes("loss", code, m, n), dtype=torch.uint8, device=dev)
@@ -232,7 +238,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {
             "workload": (f"{m}x{n} float32 weight (Llama-3-8B attention projection shape); "
@@ -245,7 +251,7 @@ def main():
              "scales") if args.workload.startswith("mlp_") else
             f"{m}x{n} float32, heavy-tailed input Gram, 4-bit",
             "m": m, "n": n, "step": "factor + row scales + BaKron solve + loss",
-            "tile": T,
+            "tile": T, "solve_dtype": "float64 (the float32 inputs cast exactly)" if f64 else "float32",
         },
         "phases_ms": phases,
         "solve_only": {"ms": phases["solve"], "weights_per_s": m * n / (phases["solve"] / 1e3)},
@@ -269,7 +275,7 @@ def main():
     # Kronecker-factor estimation (§4.2): the input-side Gram of the 8192
     # activations behind this workload's A (K-FAC factor, 1% damping), not
     # part of the step; useful flops = N d (d + 1) (the lower triangle)
-    if args.workload == "attn4096":
+    if args.workload == "attn4096" and not f64:
         from synth import config3_samples
         Xa = torch.from_numpy(config3_samples()[0]).to(dev)
         Ns, ds = Xa.shape
@@ -291,9 +297,9 @@ def main():
         nb = len(band_idx)
         achieved = fl["band"] / (band_ms / 1e3) / 1e12
         result["roofline"] = {
-            "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
-            "traffic": band_traffic(nb) if args.workload == "attn4096" else None,
+            "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": band_traffic(nb) if args.workload == "attn4096" and not f64 else None,
             "traffic_unit": "HBM bytes per launch (counters)",
             "kernel": "band_kernel (both stages)", "launches_per_step": nb,
             "useful_flop_per_step": fl["band"], "ms_per_step": band_ms,
