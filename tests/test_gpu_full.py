@@ -67,3 +67,27 @@ def test_attn4096_fp64_bit_exact(gpu_lib, cfg3):
     print("fp64 4096 mismatches", mism, "max dev", float(np.max(np.abs(Wt - ref.Wt) / inp.s[:, None])))
     assert mism == 0
     assert np.max(np.abs(Wt - ref.Wt) / inp.s[:, None]) <= 1e-9
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("m,n,alpha,rule", [
+    (1509, 2291, (-8, 7, 0), "row"),   # ragged in both directions, 64x64 band tiles on the wide nodes
+    (2301, 777, (-4, 3, 0), "col"),    # taller than wide, column scales
+    (1111, 1111, (0, 0, 1), None),     # square, integer alphabet, no scales
+])
+def test_ragged_midsize_fp64_bit_exact(gpu_lib, m, n, alpha, rule):
+    """Float64 mode at sizes with many leaf blocks, both band-tile sizes and
+    ragged edges in both directions: codes identical to the oracle (its fast
+    form, Algorithm 5, pinned to Algorithm 2 on the CPU)."""
+    from synth import random_problem
+    p = random_problem(m, n, "f64", seed=m * 31 + n, w_std=2.0 if alpha[2] else 0.02,
+                       heavy_tail=True, samples_factor=2)
+    inp = prepare(p.W, p.A, p.B, "f64", alpha, rule, hi=alpha[1] if not alpha[2] else 7)
+    V, Wt = gpu_solve(gpu_lib, inp)
+    ref = oracle_solve(inp)
+    mism = int(np.count_nonzero(V != ref.V.astype(np.int32)))
+    S = O.scale_grid(m, n, inp.mode, inp.s)
+    dev = float(np.max(np.abs(Wt - ref.Wt) / S))
+    print(m, n, alpha, rule, "mismatches", mism, "max dev", dev)
+    assert mism == 0
+    assert dev <= 1e-9

@@ -243,3 +243,22 @@ def test_empty_shapes(gpu_lib):
     W = torch.zeros((0, 5), dtype=torch.float32, device="cuda")
     V = bk.solve(W, torch.eye(5, device="cuda"), torch.zeros((0, 0), device="cuda"), (-8, 7, 0))
     assert V.shape == (0, 5)
+
+
+def test_fp64_bit_exact_random_shapes(gpu_lib):
+    """A seeded sweep over 40 random shapes (1..420 rows and columns, so
+    every ragged-tail residue mod 16 and up to several leaf blocks and band
+    nodes occur), alphabets and scale modes: float64 codes identical to the
+    oracle's on every one."""
+    rng = np.random.default_rng(2024)
+    alphas = [((0, 0, 1), None, 7), ((-8, 7, 0), "row", 7), ((-4, 3, 0), "col", 3),
+              ((-3, 3, 0), "row", 3), ((0, 15, 0), "col", 15)]
+    for case in range(40):
+        m, n = (int(x) for x in rng.integers(1, 421, size=2))
+        al, rule, hi = alphas[case % len(alphas)]
+        p = random_problem(m, n, "f64", seed=5000 + case, w_std=2.0 if al[2] else 0.02,
+                           heavy_tail=bool(case % 2), samples_factor=2)
+        inp = prepare(p.W, p.A, p.B, "f64", al, rule, hi=hi)
+        V, _ = gpu_solve(gpu_lib, inp, return_wt=False)
+        ref = oracle_solve(inp, naive=(m * n <= 2000))
+        assert np.array_equal(V, ref.V.astype(np.int32)), (case, m, n, al, rule)
