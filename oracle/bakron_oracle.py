@@ -19,7 +19,7 @@ entry by entry (Algorithm 2); ``solve_antidiag`` (Algorithm 3),
 reorderings that Theorem 3.2 proves equal. ``solve_recursive`` with a plain-C
 naive leaf is the fast oracle used at large sizes.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 * ties in rounding go to even (``rint``); Appendix B only says a rule is fixed;
 * quantize(x) = clamp(rint(x / s), lo, hi) with a true division by the
   entry's row (or column) scale; unbounded alphabets use rint(x / s);

@@ -46,7 +46,7 @@ def test_closed_form_matches_brute_force(m, n, T):
         assert node_useful_flops(m, n, T, k, mid, l) == brute(m, n, T, k, mid, l), (k, mid, l)
 
 
-def test_total_matches_survey_scale_at_4096():
+def test_total_is_of_order_mn_m_plus_n_at_4096():
     """Sum over all nodes at 4096^2 with 16-wide tiles: ~1.8 mn(m+n) flop in
     total (Appendix C's O(mn(m+n))), the bulk of it in the band products (the
     leaves' in-block updates take the rest: 7 % with 12 tile anti-diagonals
