@@ -270,7 +270,7 @@ int bakron_row_scales_mse(int dtype, int64_t m, int64_t n, const void *W, int64_
  * weights  length N (nullable = all 1): 1 for K-FAC, the other side's
  *        bakron_sample_sqnorms for Shampoo.
  * G      out, d x d (ldg >= d), both triangles written (exactly symmetric);
- *        must not overlap X.
+ *        must not overlap X (BAKRON_EINVAL if the two ranges intersect).
  * Accumulates in `dtype` on MFMA (float32 or float64 sums over the samples).
  * N = 0 gives G = 0. damp_rel >= 0. Asynchronous.
  *

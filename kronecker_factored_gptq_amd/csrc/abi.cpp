@@ -640,6 +640,13 @@ int bakron_gram(int dtype, int64_t N, int64_t d, const void* X, int64_t ldx, con
   if (d == 0) return BAKRON_OK;
   if (!G || ldg < d) return BAKRON_EINVAL;
   if (N > 0 && (!X || ldx < d)) return BAKRON_EINVAL;
+  if (N > 0) {  // G is written while X is read: the two byte ranges must be disjoint
+    const size_t es = esize(dtype);
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(X), g0 = reinterpret_cast<uintptr_t>(G);
+    const uintptr_t x1 = x0 + ((size_t)(N - 1) * (size_t)ldx + (size_t)d) * es;
+    const uintptr_t g1 = g0 + ((size_t)(d - 1) * (size_t)ldg + (size_t)d) * es;
+    if (x0 < g1 && g0 < x1) return BAKRON_EINVAL;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == BAKRON_F32)

@@ -157,6 +157,10 @@ def test_gram_rejects_bad_arguments(bad):
     assert L.bakron_gram(a["dtype"], a["N"], a["d"], a["X"], a["ldx"], a["w"], a["damp"], a["G"],
                          a["ldg"], None) == bk.EINVAL
     assert L.bakron_gram(bk.F32, 5, 0, None, 0, None, 0.0, None, 0, None) == bk.OK
+    # G overlapping X (in place, or the tail of X) is rejected
+    assert L.bakron_gram(bk.F32, 5, 4, FAKE, 4, None, 0.0, FAKE, 4, None) == bk.EINVAL
+    assert L.bakron_gram(bk.F32, 5, 4, FAKE, 4, None, 0.0, ctypes.c_void_p(0x1000 + 4 * 19), 4,
+                         None) == bk.EINVAL
     assert L.bakron_sample_sqnorms(bk.F32, 5, 4, FAKE, 3, FAKE, None) == bk.EINVAL
     assert L.bakron_sample_sqnorms(bk.F32, 5, 4, FAKE, 4, None, None) == bk.EINVAL
     assert L.bakron_sample_sqnorms(bk.F32, 0, 4, None, 4, None, None) == bk.OK
