@@ -242,9 +242,35 @@ int factor_impl(int64_t batch, int64_t m, int64_t n, const R* A, int64_t lda, co
     return BAKRON_EHIP;
   if (m > 0 && launch_load_reversed<R>(m, B, ldb, st.b, sb.X, zb, nb, s) != hipSuccess)
     return BAKRON_EHIP;
+  // helper stream and events of this call (released when the call returns,
+  // after the final synchronisation)
+  struct Aux {
+    hipStream_t st = nullptr;
+    hipEvent_t ready = nullptr, done = nullptr;
+    ~Aux() {
+      if (ready) (void)hipEventDestroy(ready);
+      if (done) (void)hipEventDestroy(done);
+      if (st) (void)hipStreamDestroy(st);
+    }
+  } aux;
   if (m == n) {
     // the B sides follow the A sides at the same stride: one set of 2 * batch
     if (factor_cholesky_inverse(n, FactorSet{sa, za, 2 * nb}, s) != hipSuccess) return BAKRON_EHIP;
+  } else if (m > 0 && n > 0) {
+    // orders differ, so the sides cannot share launches: the B set runs on a
+    // stream of this call, concurrently with the A set (both sequences are
+    // launch- and latency-bound and leave most of the GPU idle)
+    if (hipStreamCreateWithFlags(&aux.st, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&aux.ready, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&aux.done, hipEventDisableTiming) != hipSuccess)
+      return BAKRON_EHIP;
+    if (hipEventRecord(aux.ready, s) != hipSuccess ||
+        hipStreamWaitEvent(aux.st, aux.ready, 0) != hipSuccess)
+      return BAKRON_EHIP;
+    if (factor_cholesky_inverse(m, FactorSet{sb, zb, nb}, aux.st) != hipSuccess) return BAKRON_EHIP;
+    if (hipEventRecord(aux.done, aux.st) != hipSuccess) return BAKRON_EHIP;
+    if (factor_cholesky_inverse(n, FactorSet{sa, za, nb}, s) != hipSuccess) return BAKRON_EHIP;
+    if (hipStreamWaitEvent(s, aux.done, 0) != hipSuccess) return BAKRON_EHIP;
   } else {
     if (factor_cholesky_inverse(n, FactorSet{sa, za, nb}, s) != hipSuccess) return BAKRON_EHIP;
     if (factor_cholesky_inverse(m, FactorSet{sb, zb, nb}, s) != hipSuccess) return BAKRON_EHIP;
