@@ -181,15 +181,45 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
 }
 
 // ---- factor ---------------------------------------------------------------
-// Per side of order D: X (D^2), Y (D^2), Tmp ((D/2 + 64)^2) doubles, and
-// the small nodes' Tmp buffers (64^2 + 128^2 + 256^2 + 512^2 doubles); one
-// info word per side. When m == n both sides run in the same launches.
-constexpr int64_t kTmpSmall = 64 * 64 + 128 * 128 + 256 * 256 + 512 * 512;
+// Per side of order D: X (D^2), Y (D^2) and the per-size-class C21 Y11
+// buffers (factor_tmp_layout) in doubles; one info word per side. When
+// m == n both sides run in the same launches.
 size_t side_bytes(int64_t D) {
-  const int64_t h = D / 2 + 64;
-  return 2 * align_up((size_t)(D * D) * 8) + align_up((size_t)(h * h) * 8) +
-         align_up((size_t)kTmpSmall * 8);
+  return 2 * align_up((size_t)(D * D) * 8) + align_up((size_t)factor_tmp_layout(D, nullptr) * 8);
 }
+
+constexpr int64_t kHelperMinOrder = 8192;
+
+// Helper stream and events of one factor set (created per call; the call
+// is synchronous, so they are destroyed after its final synchronisation).
+struct HelperStream {
+  std::vector<hipEvent_t> ev;
+  FactorAux fa;
+  int init(int64_t order) {
+    // creating the stream and its events costs ~0.1 ms per call: measured on
+    // one box, the overlap loses 7 % at order 2048 and 2-4 % at 4096, breaks
+    // even at 8192 and gains 3 % at 14336
+    if (order <= kHelperMinOrder) return BAKRON_OK;
+    const int64_t ne = factor_helper_events(order);
+    if (ne == 0) return BAKRON_OK;
+    if (hipStreamCreateWithFlags(&fa.ts, hipStreamNonBlocking) != hipSuccess) {
+      fa.ts = nullptr;
+      return BAKRON_EHIP;
+    }
+    ev.assign((size_t)ne, nullptr);
+    for (auto& e : ev)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return BAKRON_EHIP;
+    fa.ev = ev.data();
+    fa.nev = (int)ev.size();
+    return BAKRON_OK;
+  }
+  FactorAux* get() { return fa.ts ? &fa : nullptr; }
+  ~HelperStream() {
+    for (auto& e : ev)
+      if (e) (void)hipEventDestroy(e);
+    if (fa.ts) (void)hipStreamDestroy(fa.ts);
+  }
+};
 
 struct FactorLayout {
   size_t a, b, info, total;  // a, b: one side's bytes; info: 2 * batch words
@@ -208,9 +238,6 @@ FactorSide carve_side(char* base, int64_t D, int32_t* info) {
   f.X = reinterpret_cast<double*>(base);
   f.Y = reinterpret_cast<double*>(base + align_up((size_t)(D * D) * 8));
   f.Tmp = reinterpret_cast<double*>(base + 2 * align_up((size_t)(D * D) * 8));
-  const int64_t h = D / 2 + 64;
-  f.TmpS = reinterpret_cast<double*>(base + 2 * align_up((size_t)(D * D) * 8) +
-                                     align_up((size_t)(h * h) * 8));
   f.info = info;
   return f;
 }
@@ -253,9 +280,14 @@ int factor_impl(int64_t batch, int64_t m, int64_t n, const R* A, int64_t lda, co
       if (st) (void)hipStreamDestroy(st);
     }
   } aux;
+  // each set's large nodes form their C21 Y11 products on a helper stream
+  HelperStream ha, hb;
+  if (ha.init(n) != BAKRON_OK) return BAKRON_EHIP;
+  if (m != n && hb.init(m) != BAKRON_OK) return BAKRON_EHIP;
   if (m == n) {
     // the B sides follow the A sides at the same stride: one set of 2 * batch
-    if (factor_cholesky_inverse(n, FactorSet{sa, za, 2 * nb}, s) != hipSuccess) return BAKRON_EHIP;
+    if (factor_cholesky_inverse(n, FactorSet{sa, za, 2 * nb}, s, ha.get()) != hipSuccess)
+      return BAKRON_EHIP;
   } else if (m > 0 && n > 0) {
     // orders differ, so the sides cannot share launches: the B set runs on a
     // stream of this call, concurrently with the A set (both sequences are
@@ -267,13 +299,17 @@ int factor_impl(int64_t batch, int64_t m, int64_t n, const R* A, int64_t lda, co
     if (hipEventRecord(aux.ready, s) != hipSuccess ||
         hipStreamWaitEvent(aux.st, aux.ready, 0) != hipSuccess)
       return BAKRON_EHIP;
-    if (factor_cholesky_inverse(m, FactorSet{sb, zb, nb}, aux.st) != hipSuccess) return BAKRON_EHIP;
+    if (factor_cholesky_inverse(m, FactorSet{sb, zb, nb}, aux.st, hb.get()) != hipSuccess)
+      return BAKRON_EHIP;
     if (hipEventRecord(aux.done, aux.st) != hipSuccess) return BAKRON_EHIP;
-    if (factor_cholesky_inverse(n, FactorSet{sa, za, nb}, s) != hipSuccess) return BAKRON_EHIP;
+    if (factor_cholesky_inverse(n, FactorSet{sa, za, nb}, s, ha.get()) != hipSuccess)
+      return BAKRON_EHIP;
     if (hipStreamWaitEvent(s, aux.done, 0) != hipSuccess) return BAKRON_EHIP;
   } else {
-    if (factor_cholesky_inverse(n, FactorSet{sa, za, nb}, s) != hipSuccess) return BAKRON_EHIP;
-    if (factor_cholesky_inverse(m, FactorSet{sb, zb, nb}, s) != hipSuccess) return BAKRON_EHIP;
+    if (factor_cholesky_inverse(n, FactorSet{sa, za, nb}, s, ha.get()) != hipSuccess)
+      return BAKRON_EHIP;
+    if (factor_cholesky_inverse(m, FactorSet{sb, zb, nb}, s, hb.get()) != hipSuccess)
+      return BAKRON_EHIP;
   }
   if (n > 0 &&
       launch_store_normalized<R>(n, sa.Y, za, LA, ldla, st.la, dA, st.da, nb, s) != hipSuccess)

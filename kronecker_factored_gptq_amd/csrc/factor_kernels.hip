@@ -317,8 +317,47 @@ static inline int64_t split_point(int64_t n) {
   return n1;
 }
 
+// Size class of a node of order len: the smallest c with len <= 128 << c.
+static inline int tmp_class(int64_t len) {
+  int c = 0;
+  while (c + 1 < kTmpClasses && len > ((int64_t)128 << c)) ++c;
+  return c;
+}
+
+static void tmp_need(int64_t len, int64_t* need) {
+  if (len <= NB) return;
+  const int64_t n1 = split_point(len), n2 = len - n1;
+  const int c = tmp_class(len);
+  if (n2 * n1 > need[c]) need[c] = n2 * n1;
+  tmp_need(n1, need);
+  tmp_need(n2, need);
+}
+
+int64_t factor_tmp_layout(int64_t n, int64_t* off) {
+  int64_t need[kTmpClasses] = {0};
+  if (n > 0) tmp_need(n, need);
+  int64_t total = 0;
+  for (int c = 0; c < kTmpClasses; ++c) {
+    if (off) off[c] = total;
+    total += (need[c] + 31) / 32 * 32;  // 256-byte aligned buffers
+  }
+  return total;
+}
+
+// Nodes above this order form Tmp = C21 Y11 on the helper stream (when there
+// is one), concurrently with the recursion into X22; smaller nodes form it
+// in the same launch as the Schur update.
+constexpr int64_t kPairMaxOrder = 1024;
+
+static int64_t large_nodes(int64_t len) {
+  if (len <= kPairMaxOrder) return 0;
+  const int64_t n1 = split_point(len);
+  return 1 + large_nodes(n1) + large_nodes(len - n1);
+}
+int64_t factor_helper_events(int64_t n) { return n > 0 ? 2 * large_nodes(n) : 0; }
+
 static hipError_t chol_inv_rec(int64_t n, const FactorSet& sd, int64_t off, int64_t len,
-                               hipStream_t s) {
+                               hipStream_t s, FactorAux* aux, const int64_t* toff) {
   hipError_t err;
   const int ns = sd.count;
   const FactorSide& f0 = sd.first;
@@ -329,7 +368,7 @@ static hipError_t chol_inv_rec(int64_t n, const FactorSet& sd, int64_t off, int6
     return hipGetLastError();
   }
   const int64_t n1 = split_point(len), n2 = len - n1;
-  if ((err = chol_inv_rec(n, sd, off, n1, s)) != hipSuccess) return err;
+  if ((err = chol_inv_rec(n, sd, off, n1, s, aux, toff)) != hipSuccess) return err;
   const int64_t o11 = off * n + off;            // (off, off)
   const int64_t o21 = (off + n1) * n + off;     // (off + n1, off)
   const int64_t o22 = (off + n1) * n + off + n1;
@@ -344,31 +383,30 @@ static hipError_t chol_inv_rec(int64_t n, const FactorSet& sd, int64_t off, int6
   h.M = n2; h.N = n2; h.K = n1; h.batch = ns;
   h.A = f0.Y + o21; h.B = f0.Y + o21; h.C = f0.X + o22; h.sA = h.sB = h.sC = zs;
   h.lda = n; h.ldb = n; h.ldc = n; h.transB = 1; h.lower_out = 1; h.alpha = -1.0; h.beta = 1.0;
-  // Tmp = C21 Y11 (Y11 lower: column block c needs k >= c * 64). A node of
-  // order up to 1024 forms it together with the Schur update, in one
-  // launch, into the buffer of its size class (the nodes inside the X22
-  // recursion are of smaller classes); larger nodes form it after the
-  // recursion, in the shared buffer.
-  int cls = -1;
-  for (int c = 0; c < 4; ++c)
-    if (len <= (int64_t)128 << c) { cls = c; break; }
+  // Tmp = C21 Y11 (Y11 lower: column block c needs k >= c * 64), into the
+  // buffer of this node's size class: the nodes inside the X22 recursion are
+  // of smaller classes, and the previous node of this class finished with
+  // its buffer before this node's C21 was formed
   Gemm64Args t{};
   t.M = n2; t.N = n1; t.K = n1; t.batch = ns;
   t.lda = n; t.ldb = n; t.ldc = n1; t.transB = 0; t.b_lower = 1; t.alpha = 1.0; t.beta = 0.0;
-  double* tmp = f0.Tmp;
-  if (cls >= 0) {
-    int64_t o = 0;
-    for (int c = 0; c < cls; ++c) o += ((int64_t)64 << c) * ((int64_t)64 << c);
-    tmp = f0.TmpS + o;
-  }
-  t.A = f0.Y + o21; t.B = f0.Y + o11; t.C = tmp; t.sA = t.sB = t.sC = zs;
-  if (cls >= 0) {
+  t.A = f0.Y + o21; t.B = f0.Y + o11; t.C = f0.Tmp + toff[tmp_class(len)];
+  t.sA = t.sB = t.sC = zs;
+  if (len <= kPairMaxOrder || !aux || !aux->ts) {
     if ((err = launch_gemm64_pair(h, t, s)) != hipSuccess) return err;
-    if ((err = chol_inv_rec(n, sd, off + n1, n2, s)) != hipSuccess) return err;
+    if ((err = chol_inv_rec(n, sd, off + n1, n2, s, aux, toff)) != hipSuccess) return err;
   } else {
+    // t only has to be done before Y21 below: on the helper stream, while
+    // this stream updates X22 and recurses into it
+    hipEvent_t eg = aux->event(), et = aux->event();
+    if (!eg || !et) return hipErrorOutOfMemory;
+    if ((err = hipEventRecord(eg, s)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(aux->ts, eg, 0)) != hipSuccess) return err;
+    if ((err = launch_gemm64(t, aux->ts)) != hipSuccess) return err;
+    if ((err = hipEventRecord(et, aux->ts)) != hipSuccess) return err;
     if ((err = launch_gemm64(h, s)) != hipSuccess) return err;
-    if ((err = chol_inv_rec(n, sd, off + n1, n2, s)) != hipSuccess) return err;
-    if ((err = launch_gemm64(t, s)) != hipSuccess) return err;
+    if ((err = chol_inv_rec(n, sd, off + n1, n2, s, aux, toff)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(s, et, 0)) != hipSuccess) return err;
   }
   // Y21 = -Y22 Tmp (Y22 lower)
   Gemm64Args u{};
@@ -378,10 +416,13 @@ static hipError_t chol_inv_rec(int64_t n, const FactorSet& sd, int64_t off, int6
   return launch_gemm64(u, s);
 }
 
-hipError_t factor_cholesky_inverse(int64_t n, const FactorSet& set, hipStream_t s) {
+hipError_t factor_cholesky_inverse(int64_t n, const FactorSet& set, hipStream_t s,
+                                   FactorAux* aux) {
   if (n <= 0 || set.count <= 0) return hipSuccess;
   if (set.count > kMaxGemmBatch) return hipErrorInvalidValue;
-  return chol_inv_rec(n, set, 0, n, s);
+  int64_t toff[kTmpClasses];
+  factor_tmp_layout(n, toff);
+  return chol_inv_rec(n, set, 0, n, s, aux, toff);
 }
 
 template hipError_t launch_load_reversed<float>(int64_t, const float*, int64_t, int64_t, double*,

@@ -86,9 +86,23 @@ hipError_t launch_load_reversed(int64_t n, const R* A, int64_t lda, int64_t sA, 
 struct FactorSide {
   double* X;
   double* Y;
-  double* Tmp;
-  double* TmpS;  // one C21 Y11 buffer per node-size class (orders up to 1024)
+  double* Tmp;  // one C21 Y11 buffer per node-size class (factor_tmp_layout)
   int32_t* info;
+};
+// Node-size classes of the recursion (class c: orders in (64 << c, 128 << c]).
+constexpr int kTmpClasses = 24;
+// Doubles of the per-class C21 Y11 buffers of a factor of order n; off
+// (nullable, kTmpClasses entries) receives each class's offset.
+int64_t factor_tmp_layout(int64_t n, int64_t* off);
+// Events the large nodes of a factor of order n take from a FactorAux.
+int64_t factor_helper_events(int64_t n);
+// Helper stream of a factor call and the events it hands out (the owner
+// creates and destroys them; nullptr from event() means creation failed).
+struct FactorAux {
+  hipStream_t ts = nullptr;
+  hipEvent_t* ev = nullptr;
+  int nev = 0, used = 0;
+  hipEvent_t event() { return used < nev ? ev[used++] : nullptr; }
 };
 // `count` matrices of one order factored in the same launches: side z is
 // `first` with X, Y, Tmp and TmpS advanced by z * stride doubles and info by
@@ -104,13 +118,14 @@ __host__ __device__ inline FactorSide factor_side(const FactorSet& f, int z) {
   s.X += o;
   s.Y += o;
   s.Tmp += o;
-  s.TmpS += o;
   s.info += z;
   return s;
 }
 // Y = Cholesky(X)^-1 for every matrix of the set (order n), in one sequence
-// of launches.
-hipError_t factor_cholesky_inverse(int64_t n, const FactorSet& set, hipStream_t s);
+// of launches on s; with aux (nullable), the large nodes' C21 Y11 products run
+// on aux->ts, joined back to s by events.
+hipError_t factor_cholesky_inverse(int64_t n, const FactorSet& set, hipStream_t s,
+                                   FactorAux* aux = nullptr);
 // L (and d, nullable) of `batch` matrices: Y + z * sY -> L + z * sL, d + z * sd.
 template <typename R>
 hipError_t launch_store_normalized(int64_t n, const double* Y, int64_t sY, R* L, int64_t ldl,
