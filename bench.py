@@ -322,7 +322,8 @@ def bench_kv28(args, dev):
     """28 k/v projections (1024 x 2048, each with its own Wishart A and B,
     4-bit per-row scales). One step = ONE batched factorisation of the 28
     pairs (bakron_factor_batched), the 28 row-scale vectors, ONE batched
-    solve of all 28 (bakron_solve_batched) and the 28 losses. Also timed: the
+    solve of all 28 (bakron_solve_batched) and ONE batched loss
+    (bakron_loss_batched). Also timed: the
     28 factorisations one pair at a time and the 28 solves issued one by one
     round-robin on four streams, the way a caller without the batched entry
     points runs them."""
@@ -345,7 +346,8 @@ def bench_kv28(args, dev):
     wsF = torch.empty(bk.workspace_bytes("factor", code, m, n), dtype=torch.uint8, device=dev)
     wsFB = torch.empty(int(bk.lib().bakron_factor_batched_workspace_bytes(code, nb, m, n)),
                        dtype=torch.uint8, device=dev)
-    wsL = torch.empty(bk.workspace_bytes("loss", code, m, n), dtype=torch.uint8, device=dev)
+    wsLB = torch.empty(int(bk.lib().bakron_loss_batched_workspace_bytes(code, nb, m, n)),
+                       dtype=torch.uint8, device=dev)
     wsB = torch.empty(int(bk.lib().bakron_solve_batched_workspace_bytes(code, nb, m, n)),
                       dtype=torch.uint8, device=dev)
     LA = torch.empty((nb, n, n), dtype=torch.float32, device=dev)
@@ -372,7 +374,7 @@ def bench_kv28(args, dev):
         V = bk.solve_batched(W, la, lb, (lo_, hi_, unb), S, workspace=wsB)
         if record:
             es[3].record(stream)
-        out = [bk.loss(W[i], V[i], A[i], B[i], S[i], workspace=wsL, sync=False) for i in range(nb)]
+        out = bk.loss_batched(W, V, Aall, Ball, S, workspace=wsLB)
         if record:
             es[4].record(stream)
             for k, e in zip(("t0", "t1", "t2", "t3", "t4"), es):
@@ -437,7 +439,7 @@ def bench_kv28(args, dev):
         "config": {"workload": "28 k/v projections 1024x2048 float32, Wishart(4096 dof)/4096 A and B "
                                "+1% mean-diag damping, alphabet {-8..7}, per-row absmax/7 scales",
                    "m": m, "n": n, "batch": nb,
-                   "step": "one batched factor + 28 row scales + one batched solve + 28 losses"},
+                   "step": "one batched factor + 28 row scales + one batched solve + one batched loss"},
         "phases_ms": phases,
         "solve_only": {"ms": phases["solve"], "weights_per_s": total / (phases["solve"] / 1e3),
                        "entry": "bakron_solve_batched"},

@@ -225,6 +225,25 @@ int bakron_loss(int dtype, int64_t m, int64_t n,
                 double *loss, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Batched loss: bakron_loss on `batch` problems of one shape in the same
+ * launches (the companion of bakron_factor_batched / bakron_solve_batched).
+ * Problem b uses W + b * stride_w, V + b * stride_v, scales + b * stride_s,
+ * A + b * stride_a, B + b * stride_b (element strides; 0 shares an array)
+ * and writes loss[b] (DEVICE array of batch doubles). Same definition and
+ * float64 arithmetic as bakron_loss; the products are reduced per 64 x 64
+ * block instead of per stream-K range, so results agree with bakron_loss to
+ * float64 rounding, not bit for bit. 0 <= batch <= 65535. Asynchronous.
+ * ------------------------------------------------------------------------ */
+size_t bakron_loss_batched_workspace_bytes(int dtype, int64_t batch, int64_t m, int64_t n);
+int bakron_loss_batched(int dtype, int64_t batch, int64_t m, int64_t n,
+                        const void *W, int64_t ldw, int64_t stride_w,
+                        const int32_t *V, int64_t ldv, int64_t stride_v,
+                        int scale_mode, const void *scales, int64_t stride_s,
+                        const void *A, int64_t lda, int64_t stride_a,
+                        const void *B, int64_t ldb, int64_t stride_b,
+                        double *loss, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Per-row scales: s_i = max_j |W_ij| / hi (1 for an all-zero row), the
  * per-output-feature absmax rule of Appendix D with hi the largest code
  * (7 for {-8..7}, 3 for {-4..3}). Computed in `dtype`.

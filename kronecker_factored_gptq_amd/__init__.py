@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["F32", "F64", "SCALE_NONE", "SCALE_ROW", "SCALE_COL", "BakronError", "lib", "factor",
            "factor_batched",
-           "solve", "solve_batched", "loss", "row_scales", "row_scales_mse", "gram",
+           "solve", "solve_batched", "loss", "loss_batched", "row_scales", "row_scales_mse", "gram",
            "sample_sqnorms", "kfac_factors", "shampoo_factors", "solve_schedule", "tile_size", "workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +90,12 @@ def lib() -> ctypes.CDLL:
     L.bakron_loss.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp, _vp, _i64, _vp,
                               _i64, _vp, _vp, _sz, _vp]
     L.bakron_loss.restype = _int
+    L.bakron_loss_batched_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
+    L.bakron_loss_batched_workspace_bytes.restype = _sz
+    L.bakron_loss_batched.argtypes = [_int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                      _int, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp,
+                                      _sz, _vp]
+    L.bakron_loss_batched.restype = _int
     L.bakron_row_scales.argtypes = [_int, _i64, _i64, _vp, _i64, _i32, _vp, _vp]
     L.bakron_row_scales.restype = _int
     L.bakron_row_scales_mse.argtypes = [_int, _i64, _i64, _vp, _i64, _i32, _i32, _i32,
@@ -375,6 +381,45 @@ def loss(W: torch.Tensor, V: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
     if rc != OK:
         raise BakronError(rc, "bakron_loss")
     return float(out.item()) if sync else out
+
+
+def loss_batched(W: torch.Tensor, V: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                 scales: Optional[torch.Tensor] = None, scale_mode: Optional[int] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bakron_loss for a batch in the same launches: W, V (batch, m, n); A
+    (batch, n, n) or one (n, n); B (batch, m, m) or one (m, m); scales
+    (batch, length) or one vector. Returns a float64 device tensor of
+    ``batch`` losses (asynchronous)."""
+    dev = _check_device(W, V, A, B, scales, workspace)
+    code = _dt(W)
+    if W.dim() != 3 or V.dim() != 3 or V.shape != W.shape or V.dtype != torch.int32:
+        raise ValueError("W and V must be (batch, m, n), V int32")
+    batch, m, n = W.shape
+    pw, ldw, sw = _batch_operand(W, m, n, batch, "W")
+    pv, ldv, sv = _batch_operand(V, m, n, batch, "V")
+    pa, lda, sa = _batch_operand(A, n, n, batch, "A")
+    pb, ldb, sb = _batch_operand(B, m, m, batch, "B")
+    ss = 0
+    if scales is None:
+        if scale_mode not in (None, SCALE_NONE):
+            raise ValueError("scales required for this scale_mode")
+        mode = SCALE_NONE
+    else:
+        if scales.dtype != W.dtype or not scales.is_contiguous():
+            raise ValueError("scales must be contiguous with W's dtype")
+        vec = scales if scales.dim() == 1 else scales[0]
+        mode = _scale_mode(vec, m, n, scale_mode)
+        ss = int(scales.stride(0)) if scales.dim() == 2 and batch > 1 else 0
+    out = torch.zeros(batch, dtype=torch.float64, device=dev)
+    L = lib()
+    ws = _workspace(L.bakron_loss_batched_workspace_bytes(code, batch, m, n), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.bakron_loss_batched(code, batch, m, n, pw, ldw, sw, pv, ldv, sv, mode, _p(scales), ss,
+                                   pa, lda, sa, pb, ldb, sb, _p(out), _p(ws),
+                                   ws.numel() * ws.element_size(), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_loss_batched")
+    return out
 
 
 def row_scales(W: torch.Tensor, hi: int) -> torch.Tensor:

@@ -354,40 +354,53 @@ LossLayout loss_layout(int64_t m, int64_t n) {
   return L;
 }
 
+// Caller strides (elements) between the problems of a batched loss.
+struct LossStrides {
+  int64_t w, v, s, a, b;
+};
+
+// Loss of `batch` problems; workspace regions are batch copies of the
+// single-problem layout's regions.
 template <typename R>
-int loss_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V, int64_t ldv,
-              int scale_mode, const R* scales, const R* A, int64_t lda, const R* B, int64_t ldb,
-              double* loss, void* ws, hipStream_t s) {
+int loss_impl(int64_t batch, int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V,
+              int64_t ldv, int scale_mode, const R* scales, const R* A, int64_t lda, const R* B,
+              int64_t ldb, const LossStrides& st, double* loss, void* ws, hipStream_t s) {
   const LossLayout lay = loss_layout(m, n);
+  const size_t nb = (size_t)batch;
   char* base = static_cast<char*>(ws);
   double* A64 = reinterpret_cast<double*>(base);
-  double* B64 = reinterpret_cast<double*>(base + lay.a);
-  double* D = reinterpret_cast<double*>(base + lay.a + lay.b);
-  double* BE = reinterpret_cast<double*>(base + lay.a + lay.b + lay.d);
-  double* part = reinterpret_cast<double*>(base + lay.a + lay.b + lay.d + lay.be);
-  if (launch_sym_to_f64<R>(n, A, lda, A64, s) != hipSuccess) return BAKRON_EHIP;
-  if (launch_sym_to_f64<R>(m, B, ldb, B64, s) != hipSuccess) return BAKRON_EHIP;
-  if (launch_residual_f64<R>(m, n, W, ldw, V, ldv, scale_mode, scales, D, s) != hipSuccess)
+  double* B64 = reinterpret_cast<double*>(base + nb * lay.a);
+  double* D = reinterpret_cast<double*>(base + nb * (lay.a + lay.b));
+  double* BE = reinterpret_cast<double*>(base + nb * (lay.a + lay.b + lay.d));
+  double* part = reinterpret_cast<double*>(base + nb * (lay.a + lay.b + lay.d + lay.be));
+  const int64_t za = (int64_t)(lay.a / 8), zb = (int64_t)(lay.b / 8), zd = (int64_t)(lay.d / 8);
+  const int64_t zp = (int64_t)(lay.part / 8);
+  const int bt = (int)batch;
+  if (launch_sym_to_f64<R>(n, A, lda, A64, s, bt, st.a, za) != hipSuccess) return BAKRON_EHIP;
+  if (launch_sym_to_f64<R>(m, B, ldb, B64, s, bt, st.b, zb) != hipSuccess) return BAKRON_EHIP;
+  if (launch_residual_f64<R>(m, n, W, ldw, V, ldv, scale_mode, scales, D, s, bt,
+                             ResidualStrides{st.w, st.v, st.s, zd}) != hipSuccess)
     return BAKRON_EHIP;
   // tr(B D A D^T) = sum_ij B_ij H_ij with H = (D A) D^T symmetric: G = D A in
   // full, then H on its lower blocks only, reduced against B with weight 2
   // below the diagonal and 1 on it (3 m n^2-type products instead of 4)
   Gemm64Args g1{};
-  g1.M = m; g1.N = n; g1.K = n; g1.batch = 1;
-  g1.A = D; g1.lda = n;
-  g1.B = A64; g1.ldb = n; g1.transB = 0;
-  g1.C = BE; g1.ldc = n;
+  g1.M = m; g1.N = n; g1.K = n; g1.batch = bt;
+  g1.A = D; g1.lda = n; g1.sA = zd;
+  g1.B = A64; g1.ldb = n; g1.sB = za; g1.transB = 0;
+  g1.C = BE; g1.ldc = n; g1.sC = zd;
   g1.alpha = 1.0; g1.beta = 0.0;
   if (launch_gemm64(g1, s) != hipSuccess) return BAKRON_EHIP;
   Gemm64Args g2{};
-  g2.M = m; g2.N = m; g2.K = n; g2.batch = 1;
-  g2.A = BE; g2.lda = n;
-  g2.B = D; g2.ldb = n; g2.transB = 1;
+  g2.M = m; g2.N = m; g2.K = n; g2.batch = bt;
+  g2.A = BE; g2.lda = n; g2.sA = zd;
+  g2.B = D; g2.ldb = n; g2.sB = zd; g2.transB = 1;
   g2.lower_out = 1;
   g2.alpha = 1.0;
-  g2.dot = B64; g2.lddot = m; g2.partial = part; g2.sym_dot = 1;
+  g2.dot = B64; g2.lddot = m; g2.sDot = zb; g2.partial = part; g2.sPart = zp; g2.sym_dot = 1;
   if (launch_gemm64(g2, s) != hipSuccess) return BAKRON_EHIP;
-  if (launch_sum_partials(part, gemm64_partials(g2), loss, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_sum_partials(part, gemm64_partials(g2), loss, s, bt, zp) != hipSuccess)
+    return BAKRON_EHIP;
   return BAKRON_OK;
 }
 
@@ -653,11 +666,68 @@ int bakron_loss(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, con
     // empty problem: loss 0, written by the same reduction kernel over no partials
     return launch_sum_partials(nullptr, 0, loss, s) == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
   }
+  const LossStrides st = {0, 0, 0, 0, 0};
   if (dtype == BAKRON_F32)
-    return loss_impl<float>(m, n, (const float*)W, ldw, V, ldv, scale_mode, (const float*)scales,
-                            (const float*)A, lda, (const float*)B, ldb, loss, workspace, s);
-  return loss_impl<double>(m, n, (const double*)W, ldw, V, ldv, scale_mode, (const double*)scales,
-                           (const double*)A, lda, (const double*)B, ldb, loss, workspace, s);
+    return loss_impl<float>(1, m, n, (const float*)W, ldw, V, ldv, scale_mode,
+                            (const float*)scales, (const float*)A, lda, (const float*)B, ldb, st,
+                            loss, workspace, s);
+  return loss_impl<double>(1, m, n, (const double*)W, ldw, V, ldv, scale_mode,
+                           (const double*)scales, (const double*)A, lda, (const double*)B, ldb, st,
+                           loss, workspace, s);
+}
+
+size_t bakron_loss_batched_workspace_bytes(int dtype, int64_t batch, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || batch < 0 || m < 0 || n < 0) return 0;
+  const size_t one = loss_layout(m, n).total;
+  if (batch > 0 && one > std::numeric_limits<size_t>::max() / (size_t)batch) return 0;
+  return (size_t)batch * one;
+}
+
+int bakron_loss_batched(int dtype, int64_t batch, int64_t m, int64_t n, const void* W,
+                        int64_t ldw, int64_t stride_w, const int32_t* V, int64_t ldv,
+                        int64_t stride_v, int scale_mode, const void* scales, int64_t stride_s,
+                        const void* A, int64_t lda, int64_t stride_a, const void* B, int64_t ldb,
+                        int64_t stride_b, double* loss, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!dtype_ok(dtype) || batch < 0 || m < 0 || n < 0) return BAKRON_EINVAL;
+  if (batch > kMaxBatch || m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (batch == 0) return BAKRON_OK;
+  if (!loss) return BAKRON_EINVAL;
+  if (m > 0 && n > 0) {
+    if (!W || !V || !A || !B) return BAKRON_EINVAL;
+    if (ldw < n || ldv < n || lda < n || ldb < m) return BAKRON_EINVAL;
+  }
+  if (scale_mode == BAKRON_SCALE_NONE) {
+    if (scales) return BAKRON_EINVAL;
+  } else if (scale_mode == BAKRON_SCALE_ROW || scale_mode == BAKRON_SCALE_COL) {
+    if (!scales) return BAKRON_EINVAL;
+  } else {
+    return BAKRON_EINVAL;
+  }
+  if (stride_w < 0 || stride_v < 0 || stride_s < 0 || stride_a < 0 || stride_b < 0)
+    return BAKRON_EINVAL;
+  if (batch > 1) {
+    const int64_t big = std::max(std::max(std::max(stride_w, stride_v), std::max(stride_s, stride_a)),
+                                 stride_b);
+    if (big > std::numeric_limits<int64_t>::max() / 2 / (batch - 1)) return BAKRON_EINVAL;
+  }
+  const size_t need = bakron_loss_batched_workspace_bytes(dtype, batch, m, n);
+  if (!workspace || need == 0 || workspace_bytes < need) return BAKRON_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m == 0 || n == 0) {
+    // empty problems: every loss 0, written by the same reduction over no partials
+    return launch_sum_partials(nullptr, 0, loss, s, (int)batch, 0) == hipSuccess ? BAKRON_OK
+                                                                                : BAKRON_EHIP;
+  }
+  const LossStrides st = {stride_w, stride_v, stride_s, stride_a, stride_b};
+  if (dtype == BAKRON_F32)
+    return loss_impl<float>(batch, m, n, (const float*)W, ldw, V, ldv, scale_mode,
+                            (const float*)scales, (const float*)A, lda, (const float*)B, ldb, st,
+                            loss, workspace, s);
+  return loss_impl<double>(batch, m, n, (const double*)W, ldw, V, ldv, scale_mode,
+                           (const double*)scales, (const double*)A, lda, (const double*)B, ldb, st,
+                           loss, workspace, s);
 }
 
 int bakron_row_scales(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, int32_t hi,

@@ -251,7 +251,7 @@ __device__ __forceinline__ void gemm64_block(const Gemm64Args& a, const BlockMap
             if (gr < a.M && gc < a.N) {
               double wgt = 1.0;
               if (a.sym_dot) wgt = gr > gc ? 2.0 : (gr == gc ? 1.0 : 0.0);
-              part += wgt * a.alpha * acc[i][j][r] * a.dot[gr * a.lddot + gc];
+              part += wgt * a.alpha * acc[i][j][r] * a.dot[z * a.sDot + gr * a.lddot + gc];
             }
           }
     }
@@ -260,7 +260,8 @@ __device__ __forceinline__ void gemm64_block(const Gemm64Args& a, const BlockMap
     for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
     if (lane == 0) red[wave] = part;
     __syncthreads();
-    if (tid == 0) a.partial[bm * nbx + bn] = ((red[0] + red[1]) + red[2]) + red[3];
+    if (tid == 0)
+      a.partial[z * a.sPart + bm * nbx + bn] = ((red[0] + red[1]) + red[2]) + red[3];
     return;
   }
   if (skip) return;
@@ -424,7 +425,7 @@ __device__ __forceinline__ double big_dot(const Gemm64Args& a, int z, int64_t ro
         if (gr < a.M && gc < a.N) {
           double wgt = 1.0;
           if (a.sym_dot) wgt = gr > gc ? 2.0 : (gr == gc ? 1.0 : 0.0);
-          part += wgt * a.alpha * acc[i][j][r] * a.dot[gr * a.lddot + gc];
+          part += wgt * a.alpha * acc[i][j][r] * a.dot[z * a.sDot + gr * a.lddot + gc];
         }
       }
   return part;
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
   if (a.dot) {
     const double part = skip ? 0.0 : big_dot<BM, BN, WM, WN>(a, z, row0, col0, acc);
     const double t = wg_sum<WM * WN>(part, red);
-    if (tid == 0) a.partial[bm * gridDim.x + bn] = t;
+    if (tid == 0) a.partial[z * a.sPart + bm * gridDim.x + bn] = t;
     return;
   }
   if (skip) return;
@@ -639,7 +640,6 @@ hipError_t launch_gemm64_pair(const Gemm64Args& a0, const Gemm64Args& a1, hipStr
 hipError_t launch_gemm64(const Gemm64Args& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.batch < 1 || a.batch > kMaxGemmBatch) return hipErrorInvalidValue;
-  if (a.dot && a.batch != 1) return hipErrorInvalidValue;
   // 16-byte vectors need every row start of A and B 16-byte aligned; they
   // measured slower than element loads here (more registers, lower
   // occupancy), so they are off

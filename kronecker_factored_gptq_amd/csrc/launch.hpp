@@ -141,9 +141,11 @@ hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t v, hipStream_t s);
 // so row block r only needs k < (r + 1) * 64. b_lower: B as stored is lower
 // triangular: with transB the column block c only needs k < (c + 1) * 64,
 // without it only k >= c * 64.
-// dot != nullptr (batch 1 only): instead of storing C, the block's sum of
-// alpha (A op(B)) .* dot is written to partial[block] (C unused); with
-// sym_dot the elements are weighted 2 below the diagonal, 1 on it, 0 above.
+// dot != nullptr: instead of storing C, the block's sum of alpha (A op(B)) .*
+// dot is written to partial[z * sPart + block] (C unused); with sym_dot the
+// elements are weighted 2 below the diagonal, 1 on it, 0 above. (Batch 1
+// products of the loss's shape use a stream-K kernel with per-workgroup
+// partials instead.)
 struct Gemm64Args {
   int64_t M, N, K;
   const double* A;
@@ -158,8 +160,9 @@ struct Gemm64Args {
   int a_lower;
   int b_lower;
   const double* dot;
-  int64_t lddot;
+  int64_t lddot, sDot;  // problem z's dot matrix at dot + z * sDot
   double* partial;
+  int64_t sPart;        // problem z's partials start at partial + z * sPart
   int batch;
   // dot epilogue of a symmetric product computed on its lower blocks only:
   // element (r, c) counts twice below the diagonal, once on it, not above
@@ -178,13 +181,22 @@ int64_t gemm64_num_blocks(int64_t M, int64_t N);
 int64_t gemm64_partials(const Gemm64Args& a);
 
 // ---- loss and scales (loss_kernels.hip) -----------------------------------
+// The loss's elementwise steps for `batch` problems (grid z): A + z * sA ->
+// X + z * sX, and D = W - s (.) V per problem.
 template <typename R>
-hipError_t launch_sym_to_f64(int64_t n, const R* A, int64_t lda, double* X, hipStream_t s);
+hipError_t launch_sym_to_f64(int64_t n, const R* A, int64_t lda, double* X, hipStream_t s,
+                             int batch = 1, int64_t sA = 0, int64_t sX = 0);
+struct ResidualStrides {
+  int64_t w, v, s, d;
+};
 template <typename R>
 hipError_t launch_residual_f64(int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V,
                                int64_t ldv, int scale_mode, const R* scales, double* D,
-                               hipStream_t s);
-hipError_t launch_sum_partials(const double* partial, int64_t count, double* out, hipStream_t s);
+                               hipStream_t s, int batch = 1,
+                               ResidualStrides st = ResidualStrides{0, 0, 0, 0});
+// out[z] = sum of partial[z * sPart .. z * sPart + count), fixed order.
+hipError_t launch_sum_partials(const double* partial, int64_t count, double* out, hipStream_t s,
+                               int batch = 1, int64_t sPart = 0);
 template <typename R>
 hipError_t launch_row_scales(int64_t m, int64_t n, const R* W, int64_t ldw, int32_t hi, R* s_out,
                              hipStream_t s);

@@ -13,8 +13,11 @@ namespace bk {
 // X = symmetric float64 copy of A built from its lower triangle.
 template <typename R>
 __global__ __launch_bounds__(256) void sym_to_f64_kernel(int64_t n, const R* __restrict__ A,
-                                                         int64_t lda, double* __restrict__ X) {
+                                                         int64_t lda, double* __restrict__ X,
+                                                         int64_t sA, int64_t sX) {
   __shared__ double t[32][33];
+  A += (int64_t)blockIdx.z * sA;  // problem blockIdx.z of a batch
+  X += (int64_t)blockIdx.z * sX;
   const int bi = blockIdx.y, bj = blockIdx.x;
   const int sbr = bi > bj ? bi : bj, sbc = bi > bj ? bj : bi;  // source tile (lower)
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
@@ -42,7 +45,15 @@ __global__ __launch_bounds__(256) void residual_kernel(int64_t m, int64_t n, con
                                                        int64_t ldw, const int32_t* __restrict__ V,
                                                        int64_t ldv, int scale_mode,
                                                        const R* __restrict__ scales,
-                                                       double* __restrict__ D) {
+                                                       double* __restrict__ D,
+                                                       ResidualStrides st) {
+  {  // problem blockIdx.z of a batch
+    const int64_t b = blockIdx.z;
+    W += b * st.w;
+    V += b * st.v;
+    if (scales) scales += b * st.s;
+    D += b * st.d;
+  }
   const int64_t i = blockIdx.y;
   for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (int64_t)gridDim.x * 256) {
     double s = 1.0;
@@ -54,8 +65,11 @@ __global__ __launch_bounds__(256) void residual_kernel(int64_t m, int64_t n, con
 
 // out = sum of partial[0..count), in a fixed order (deterministic).
 __global__ __launch_bounds__(256) void sum_partials_kernel(const double* __restrict__ partial,
-                                                           int64_t count, double* __restrict__ out) {
+                                                           int64_t count, double* __restrict__ out,
+                                                           int64_t sPart) {
   __shared__ double red[256];
+  partial += (int64_t)blockIdx.x * sPart;  // problem blockIdx.x of a batch
+  out += blockIdx.x;
   double s = 0.0;
   for (int64_t i = threadIdx.x; i < count; i += 256) s += partial[i];
   red[threadIdx.x] = s;
@@ -89,27 +103,32 @@ __global__ __launch_bounds__(256) void row_scales_kernel(int64_t n, const R* __r
 
 // ---------------------------------------------------------------------------
 template <typename R>
-hipError_t launch_sym_to_f64(int64_t n, const R* A, int64_t lda, double* X, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
+hipError_t launch_sym_to_f64(int64_t n, const R* A, int64_t lda, double* X, hipStream_t s,
+                             int batch, int64_t sA, int64_t sX) {
+  if (n <= 0 || batch <= 0) return hipSuccess;
   const unsigned nb = (unsigned)((n + 31) / 32);
-  hipLaunchKernelGGL((sym_to_f64_kernel<R>), dim3(nb, nb), dim3(256), 0, s, n, A, lda, X);
+  hipLaunchKernelGGL((sym_to_f64_kernel<R>), dim3(nb, nb, (unsigned)batch), dim3(256), 0, s, n, A,
+                     lda, X, sA, sX);
   return hipGetLastError();
 }
 
 template <typename R>
 hipError_t launch_residual_f64(int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V,
                                int64_t ldv, int scale_mode, const R* scales, double* D,
-                               hipStream_t s) {
-  if (m <= 0 || n <= 0) return hipSuccess;
+                               hipStream_t s, int batch, ResidualStrides st) {
+  if (m <= 0 || n <= 0 || batch <= 0) return hipSuccess;
   unsigned gx = (unsigned)((n + 255) / 256);
   if (gx > 64) gx = 64;
-  hipLaunchKernelGGL((residual_kernel<R>), dim3(gx, (unsigned)m), dim3(256), 0, s, m, n, W, ldw,
-                     V, ldv, scale_mode, scales, D);
+  hipLaunchKernelGGL((residual_kernel<R>), dim3(gx, (unsigned)m, (unsigned)batch), dim3(256), 0, s,
+                     m, n, W, ldw, V, ldv, scale_mode, scales, D, st);
   return hipGetLastError();
 }
 
-hipError_t launch_sum_partials(const double* partial, int64_t count, double* out, hipStream_t s) {
-  hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(256), 0, s, partial, count, out);
+hipError_t launch_sum_partials(const double* partial, int64_t count, double* out, hipStream_t s,
+                               int batch, int64_t sPart) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)batch), dim3(256), 0, s, partial, count,
+                     out, sPart);
   return hipGetLastError();
 }
 
@@ -123,9 +142,11 @@ hipError_t launch_row_scales(int64_t m, int64_t n, const R* W, int64_t ldw, int3
 }
 
 #define BK_INST(R)                                                                               \
-  template hipError_t launch_sym_to_f64<R>(int64_t, const R*, int64_t, double*, hipStream_t);   \
+  template hipError_t launch_sym_to_f64<R>(int64_t, const R*, int64_t, double*, hipStream_t,    \
+                                           int, int64_t, int64_t);                               \
   template hipError_t launch_residual_f64<R>(int64_t, int64_t, const R*, int64_t, const int32_t*, \
-                                             int64_t, int, const R*, double*, hipStream_t);      \
+                                             int64_t, int, const R*, double*, hipStream_t, int,  \
+                                             ResidualStrides);                                   \
   template hipError_t launch_row_scales<R>(int64_t, int64_t, const R*, int64_t, int32_t, R*,     \
                                            hipStream_t);
 BK_INST(float)

@@ -166,6 +166,27 @@ def test_gram_rejects_bad_arguments(bad):
     assert L.bakron_sample_sqnorms(bk.F32, 0, 4, None, 4, None, None) == bk.OK
 
 
+@pytest.mark.parametrize("bad", [
+    dict(dtype=9), dict(batch=-1), dict(batch=65536), dict(W=None), dict(V=None), dict(ldw=3),
+    dict(ldb=3), dict(mode=1, scales=None), dict(mode=0, scales=FAKE), dict(mode=5),
+    dict(sw=-1), dict(sb=-2), dict(loss=None), dict(ws=None), dict(wsb=32),
+    dict(ws=ctypes.c_void_p(0x1004)), dict(sa=1 << 62),
+])
+def test_loss_batched_rejects_bad_arguments(bad):
+    a = dict(dtype=bk.F32, batch=3, m=4, n=4, W=FAKE, ldw=4, sw=16, V=FAKE, ldv=4, sv=16, mode=0,
+             scales=None, ss=0, A=FAKE, lda=4, sa=16, B=FAKE, ldb=4, sb=16, loss=FAKE, ws=FAKE,
+             wsb=1 << 40)
+    a.update(bad)
+    rc = bk.lib().bakron_loss_batched(a["dtype"], a["batch"], a["m"], a["n"], a["W"], a["ldw"],
+                                      a["sw"], a["V"], a["ldv"], a["sv"], a["mode"], a["scales"],
+                                      a["ss"], a["A"], a["lda"], a["sa"], a["B"], a["ldb"], a["sb"],
+                                      a["loss"], a["ws"], a["wsb"], None)
+    assert rc == bk.EINVAL
+    L = bk.lib()
+    assert L.bakron_loss_batched_workspace_bytes(bk.F32, 3, 40, 50) == \
+        3 * L.bakron_loss_workspace_bytes(bk.F32, 40, 50)
+
+
 def test_factor_and_loss_reject_bad_arguments():
     L = bk.lib()
     bad = (ctypes.c_int64 * 2)(7, 7)

@@ -132,3 +132,46 @@ def test_factor_batched_reports_failing_pair(gpu_lib):
     with pytest.raises(bk.BakronError) as ei:
         bk.factor_batched(A, B)
     assert tuple(ei.value.bad_pivot) == (1, 1, 34)
+
+
+# ------------------------------------------------------------- batched loss ---
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("batch,m,n,rule", [(3, 50, 70, "row"), (2, 130, 97, "col"),
+                                            (4, 33, 200, None), (2, 300, 170, "row")])
+def test_loss_batched_matches_single_and_oracle(gpu_lib, dtype, batch, m, n, rule):
+    """Every problem's batched loss equals bakron_loss to float64 rounding
+    (the batched form reduces per block, the single one per stream-K range)
+    and the oracle's loss of the same codes to 1e-10."""
+    bk = gpu_lib
+    alphabet = (-8, 7, 0) if rule else (0, 0, 1)
+    inps = _batch_inputs(batch, m, n, dtype, alphabet, rule, seed0=m + 3 * n)
+    W, LA, LB = _stack(inps, "W"), _stack(inps, "LA"), _stack(inps, "LB")
+    s = _stack(inps, "s") if rule else None
+    mode = inps[0].mode if rule else None
+    V = bk.solve_batched(W, LA, LB, alphabet, s, scale_mode=mode)
+    probs = [random_problem(m, n, dtype, seed=m + 3 * n + 31 * b, w_std=2.0 if alphabet[2] else 0.02,
+                            heavy_tail=bool(b % 2), samples_factor=3) for b in range(batch)]
+    A = torch.stack([to_dev(p.A) for p in probs])
+    B = torch.stack([to_dev(p.B) for p in probs])
+    lb = bk.loss_batched(W, V, A, B, s, scale_mode=mode).cpu().numpy()
+    for b, inp in enumerate(inps):
+        l1 = bk.loss(W[b], V[b], A[b], B[b], None if s is None else s[b], scale_mode=mode)
+        assert abs(lb[b] - l1) <= 1e-12 * abs(l1), (b, lb[b], l1)
+        lo = O.loss(inp.W, V[b].cpu().numpy(), probs[b].A, probs[b].B, inp.mode, inp.s)
+        assert abs(lb[b] - lo) <= 1e-10 * abs(lo), (b, lb[b], lo)
+
+
+def test_loss_batched_shared_hessians_and_empty(gpu_lib):
+    bk = gpu_lib
+    p = random_problem(40, 60, "f64", seed=9, samples_factor=3)
+    Ws = torch.stack([to_dev(p.W) * (1 + 0.1 * b) for b in range(3)])
+    V = torch.zeros(Ws.shape, dtype=torch.int32, device="cuda")
+    A, B = to_dev(p.A), to_dev(p.B)
+    lb = bk.loss_batched(Ws, V, A, B).cpu().numpy()
+    for b in range(3):
+        l1 = bk.loss(Ws[b], V[b], A, B)
+        assert abs(lb[b] - l1) <= 1e-12 * abs(l1)
+    e = bk.loss_batched(torch.zeros((0, 40, 60), dtype=torch.float64, device="cuda"),
+                        torch.zeros((0, 40, 60), dtype=torch.int32, device="cuda"), A, B)
+    assert e.shape == (0,)

@@ -172,3 +172,8 @@ def test_kv_batch_on_streams(gpu_lib, b_identity):
     for i, out in enumerate(res):
         assert np.array_equal(Vb[i].cpu().numpy(), out["V"]), i
         assert np.array_equal(Wtb[i].cpu().numpy(), out["Wt"]), i
+    # the batched loss of all 28 equals the per-matrix losses to float64 rounding
+    lb = gpu_lib.loss_batched(W, Vb, torch.stack([to_dev(p.A) for p in probs]),
+                              torch.stack([to_dev(p.B) for p in probs]), stack("s")).cpu().numpy()
+    for i, out in enumerate(res):
+        assert abs(lb[i] - out["loss"]) <= 1e-12 * abs(out["loss"]), (i, lb[i], out["loss"])
