@@ -28,6 +28,8 @@
 // (code units), which is what the band products read. The scaled L^A, L^B as
 // packed lower-triangular tile arrays (tile (P,I), I <= P, at P(P+1)/2 + I),
 // unit diagonal, zero above it and on padding.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -219,6 +221,11 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
   __shared__ __attribute__((aligned(16))) R fm[kLeafWaves][T * T];  // fresh-column shares
   __shared__ R lat[T][T + 1];
   __shared__ R ow[T][T + 1];
+  // float sweep: value at rounding, one copy per lane row kg; lane (kg, c)
+  // writes step t to row t - c + (T - 1) of its copy (a real entry's slot
+  // when row t - c is one of its own rows, an unread one otherwise)
+  constexpr int kOwRows = 3 * T - 2, kOwLd = T + 2;
+  __shared__ float owf[std::is_same<R, float>::value ? 4 : 1][kOwRows][kOwLd];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -380,31 +387,75 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
   // an exact zero
   const R c0 = fmin_(fmax_(R(0), lo), hi);
 
-  static_for<0, 2 * T - 1>([&](auto tc) {
-    constexpr int t = decltype(tc)::value;
-    R x = c0;
-    bool act = false;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool on = dr[r] == t;
-      x = on ? acc[r] : x;
-      act = act || on;
-    }
-    const R e = quant_unit(x, lo, hi) - x;
-    if (act) ow[t - c][c] = x;
-    const R es = row_skew(e);
-    static_for<0, 4>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      // MFMA s takes the rows k = KA kg + KB s: it contributes only if some
-      // such k has its column t - k inside the tile (k >= t - (T - 1)) and
-      // k <= t; the last step's update reaches no later anti-diagonal. The
-      // skipped products add exact zeros or are never read.
-      if constexpr (t - KB * s >= 0 && KA * 3 + KB * s >= t - (T - 1) && t < 2 * T - 2) {
-        const R ev = dpp_mov<kDppRowNewBcast + ((t - KB * s) & 15), 0xF>(R(0), es);
-        acc = MF::mma(lbK[s] * ev, laK[t - KB * s], acc);
+  if constexpr (std::is_same<R, float>::value) {
+    // Float: one wave's vector instructions do not overlap its own MFMA
+    // chain on gfx950 (measured: every independent fma adds its ~6 cycles
+    // to a chain of four dependent 16x16x4 MFMAs), so the step is kept to
+    // the fewest vector instructions. Entry r of this lane lies on in-tile
+    // anti-diagonal base + r; one compare per step feeds a sliding window of
+    // three masks. A lane with no entry on the step keeps acc[0], any finite
+    // value: the only lanes whose errors the broadcasts read are those at
+    // columns t - k inside the tile, which do have an entry, and the other
+    // broadcast values meet exact zeros of laK. Padding entries may be
+    // selected: they start at exact zero, and an error reaches an entry only
+    // through factors that are exact zeros between padding and real rows or
+    // columns, so neither side changes the other. The value at rounding goes
+    // to the lane row's own LDS copy at a constant offset per step (real
+    // entries' slots are written once, on their step; the rest are never
+    // read), and the clamp is one median-of-three.
+    const int base = 4 * kg + c;
+    bool m1 = false, m2 = false, m3 = false;  // entry 1, 2, 3 on the current step
+    float* owl = &owf[kg][T - 1 - c][c];
+    static_for<0, 2 * T - 1>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      R x = acc[0];
+      x = m1 ? acc[1] : x;
+      x = m2 ? acc[2] : x;
+      x = m3 ? acc[3] : x;
+      m3 = m2;
+      m2 = m1;
+      m1 = base == t;
+      owl[t * kOwLd] = x;
+      if constexpr (t < 2 * T - 2) {
+        const R es = row_skew(__builtin_amdgcn_fmed3f(__builtin_rintf(x), lo, hi) - x);
+        static_for<0, 4>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          // MFMA s holds rows k = 4 kg + s: needed when some such k has its
+          // column t - k inside the tile (k <= t, k >= t - (T - 1))
+          if constexpr (t - s >= 0 && 12 + s >= t - (T - 1)) {
+            const R ev = dpp_mov<kDppRowNewBcast + ((t - s) & 15), 0xF>(R(0), es);
+            acc = MF::mma(lbK[s] * ev, laK[t - s], acc);
+          }
+        });
       }
     });
-  });
+  } else {
+    static_for<0, 2 * T - 1>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      R x = c0;
+      bool act = false;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool on = dr[r] == t;
+        x = on ? acc[r] : x;
+        act = act || on;
+      }
+      const R e = quant_unit(x, lo, hi) - x;
+      if (act) ow[t - c][c] = x;
+      const R es = row_skew(e);
+      static_for<0, 4>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        // MFMA s takes the rows k = KA kg + KB s: it contributes only if some
+        // such k has its column t - k inside the tile (k >= t - (T - 1)) and
+        // k <= t; the last step's update reaches no later anti-diagonal. The
+        // skipped products add exact zeros or are never read.
+        if constexpr (t - KB * s >= 0 && KA * 3 + KB * s >= t - (T - 1) && t < 2 * T - 2) {
+          const R ev = dpp_mov<kDppRowNewBcast + ((t - KB * s) & 15), 0xF>(R(0), es);
+          acc = MF::mma(lbK[s] * ev, laK[t - KB * s], acc);
+        }
+      });
+    });
+  }
   wave_sync_lds();
   // write back: errors (code units) into the workspace, codes and the values
   // at rounding (back in the units of W) to the outputs
@@ -414,7 +465,9 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
     const int p = idx >> 4, q = idx & 15;
     const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + q;
     const bool valid = gi < m && gjj < n;
-    const R x = ow[p][q];
+    R x;
+    if constexpr (std::is_same<R, float>::value) x = owf[p >> 2][p + T - 1][q];
+    else x = ow[p][q];
     const R cq = quant_unit(x, lo, hi);
     tW[idx] = valid ? cq - x : R(0);
     if (valid) {
