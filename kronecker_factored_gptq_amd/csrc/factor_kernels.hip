@@ -158,8 +158,11 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSe
     }
     if (tid == 0 && bad >= 0 && j + bad < bs) atomicMin(S.info, (int32_t)(off + j + bad));
     // columns j.. of C at this thread's rows i and at its columns c taken as
-    // rows (zero on and above the pivot block), and rows j.. of Y at its
-    // columns c (final after this step)
+    // rows, and rows j.. of Y at its columns c (final after this step). No
+    // masks: above the pivot block these are exact zeros (C and Y keep exact
+    // zeros above their diagonals, and 0 * dinv = 0); the pivot block's own
+    // rows of C only reach entries of C in columns < j + NC, which no later
+    // step reads, and its rows of Y are overwritten with yq after the update
     double ci[4][NC], cc[PCW][NC], yq[NC][PCW];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSe
 #pragma unroll
         for (int p = 0; p < NC; ++p)
           if (p < q) vi -= ci[a][p] * l[q][p];
-        ci[a][q] = i < j + NC ? 0.0 : vi * dinv[q];
+        ci[a][q] = vi * dinv[q];
       }
     }
 #pragma unroll
@@ -185,26 +188,13 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSe
         cc[b][q] = vc * dinv[q];
       }
 #pragma unroll
-      for (int q = 0; q < NC; ++q)
-        if (c < j + NC) cc[b][q] = 0.0;
-#pragma unroll
       for (int q = 0; q < NC; ++q) {
         double v = rowp[pb][q][c];
 #pragma unroll
         for (int p = 0; p < NC; ++p)
           if (p < q) v -= l[q][p] * yq[p][b];
-        yq[q][b] = c < j + NC ? v * dinv[q] : 0.0;
+        yq[q][b] = v * dinv[q];
       }
-    }
-    if (ownr) {  // rows j.. of Y are final now
-#pragma unroll
-      for (int pr = 0; pr < PRS; ++pr)
-        if (rq == 4 * pr) {
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < PCW; ++b) Yr[a][b] = yq[4 * pr + a][b];
-        }
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -217,9 +207,19 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSe
           dl += ci[a][q] * cc[b][q];
           dy += ci[a][q] * yq[q][b];
         }
-        if (c <= i) Lr[a][b] -= dl;  // zero unless j + NC <= c <= i
-        Yr[a][b] -= dy;              // zero unless i >= j + NC
+        if (c <= i) Lr[a][b] -= dl;  // C keeps exact zeros above its diagonal
+        Yr[a][b] -= dy;
       }
+    if (ownr) {  // rows j.. of Y are final now
+#pragma unroll
+      for (int pr = 0; pr < PRS; ++pr)
+        if (rq == 4 * pr) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < PCW; ++b) Yr[a][b] = yq[4 * pr + a][b];
+        }
+    }
   }
 #pragma unroll
   for (int a = 0; a < 4; ++a)
