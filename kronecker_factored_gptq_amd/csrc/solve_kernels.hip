@@ -171,12 +171,37 @@ __device__ inline double dpp_mov(double old, double v) {
   return __builtin_bit_cast(double, r);
 }
 
+// Broadcast of lane n of each row to its row. Float: written with an old
+// value of 0 so that the compiler folds it into the multiply that uses it;
+// double: two full-row moves (every lane written, no old value needed).
+template <int N>
+__device__ inline float row_bcast(float v) {
+  return dpp_mov<kDppRowNewBcast + N, 0xF>(0.0f, v);
+}
+template <int N>
+__device__ inline double row_bcast(double v) {
+  const int2 x = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __builtin_amdgcn_mov_dpp(x.x, kDppRowNewBcast + N, 0xF, 0xF, false);
+  r.y = __builtin_amdgcn_mov_dpp(x.y, kDppRowNewBcast + N, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, r);
+}
+
 // lane row kg: result column c holds the input's column (c - KA kg) mod 16
 template <typename R>
 __device__ inline R row_skew(R e) {
   constexpr int A = SweepK<R>::KA;
   const R a = dpp_mov<kDppRowRor + A, 0xA>(e, e);      // rows 1 and 3
   return dpp_mov<kDppRowRor + 2 * A, 0xC>(a, a);       // rows 2 and 3
+}
+
+// clamp(rint(x), lo, hi) as in quant_unit (lo <= hi): one median-of-three
+// for float
+__device__ inline float round_clamp(float x, float lo, float hi) {
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(x), lo, hi);
+}
+__device__ inline double round_clamp(double x, double lo, double hi) {
+  return quant_unit(x, lo, hi);
 }
 
 template <int I, int N, typename F>
@@ -220,12 +245,11 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
   __shared__ R red[kLeafWaves - 1][T][T + 1];
   __shared__ __attribute__((aligned(16))) R fm[kLeafWaves][T * T];  // fresh-column shares
   __shared__ R lat[T][T + 1];
-  __shared__ R ow[T][T + 1];
-  // float sweep: value at rounding, one copy per lane row kg; lane (kg, c)
-  // writes step t to row t - c + (T - 1) of its copy (a real entry's slot
-  // when row t - c is one of its own rows, an unread one otherwise)
-  constexpr int kOwRows = 3 * T - 2, kOwLd = T + 2;
-  __shared__ float owf[std::is_same<R, float>::value ? 4 : 1][kOwRows][kOwLd];
+  // sweep: value at rounding, one copy per lane row kg; lane (kg, c) writes
+  // step t to row t - c + (T - 1) of its copy (a real entry's slot when row
+  // t - c is one of its own rows, an unread one otherwise)
+  constexpr int kOwRows = 3 * T - 2, kOwLd = T + 1 + (int)(sizeof(float) / sizeof(R));
+  __shared__ R owv[4][kOwRows][kOwLd];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -362,10 +386,6 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
   if (wave > 0) return;
 
   // ---- 2. sweep on wave 0
-  const int64_t gj = (int64_t)Q * T + c;
-  // an entry outside the matrix is never selected: it keeps its exact zero
-  // and contributes no error
-  int dr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = MF::row(lane, r);
@@ -373,8 +393,6 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
 #pragma unroll
     for (int w = 0; w < kLeafWaves - 1; ++w) pro += red[w][row][c];
     acc[r] += pro;
-    const bool valid = (int64_t)P * T + row < m && gj < n;
-    dr[r] = valid ? row + c : -1;
   }
   R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - KA kg]
 #pragma unroll
@@ -383,79 +401,49 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
     laK[j] = (jj >= 0 && jj < T) ? lat[c][jj] : R(0);
   }
   const R lo = lp.lo, hi = lp.hi;  // +-infinity for the unbounded alphabet
-  // lanes without an entry on the step see the code of 0, so their error is
-  // an exact zero
-  const R c0 = fmin_(fmax_(R(0), lo), hi);
 
-  if constexpr (std::is_same<R, float>::value) {
-    // Float: one wave's vector instructions do not overlap its own MFMA
-    // chain on gfx950 (measured: every independent fma adds its ~6 cycles
-    // to a chain of four dependent 16x16x4 MFMAs), so the step is kept to
-    // the fewest vector instructions. Entry r of this lane lies on in-tile
-    // anti-diagonal base + r; one compare per step feeds a sliding window of
-    // three masks. A lane with no entry on the step keeps acc[0], any finite
-    // value: the only lanes whose errors the broadcasts read are those at
-    // columns t - k inside the tile, which do have an entry, and the other
-    // broadcast values meet exact zeros of laK. Padding entries may be
-    // selected: they start at exact zero, and an error reaches an entry only
-    // through factors that are exact zeros between padding and real rows or
-    // columns, so neither side changes the other. The value at rounding goes
-    // to the lane row's own LDS copy at a constant offset per step (real
-    // entries' slots are written once, on their step; the rest are never
-    // read), and the clamp is one median-of-three.
-    const int base = 4 * kg + c;
-    bool m1 = false, m2 = false, m3 = false;  // entry 1, 2, 3 on the current step
-    float* owl = &owf[kg][T - 1 - c][c];
-    static_for<0, 2 * T - 1>([&](auto tc) {
-      constexpr int t = decltype(tc)::value;
-      R x = acc[0];
-      x = m1 ? acc[1] : x;
-      x = m2 ? acc[2] : x;
-      x = m3 ? acc[3] : x;
-      m3 = m2;
-      m2 = m1;
-      m1 = base == t;
-      owl[t * kOwLd] = x;
-      if constexpr (t < 2 * T - 2) {
-        const R es = row_skew(__builtin_amdgcn_fmed3f(__builtin_rintf(x), lo, hi) - x);
-        static_for<0, 4>([&](auto sc) {
-          constexpr int s = decltype(sc)::value;
-          // MFMA s holds rows k = 4 kg + s: needed when some such k has its
-          // column t - k inside the tile (k <= t, k >= t - (T - 1))
-          if constexpr (t - s >= 0 && 12 + s >= t - (T - 1)) {
-            const R ev = dpp_mov<kDppRowNewBcast + ((t - s) & 15), 0xF>(R(0), es);
-            acc = MF::mma(lbK[s] * ev, laK[t - s], acc);
-          }
-        });
-      }
+  // One wave's vector instructions do not overlap its own MFMA chain on
+  // gfx950 (measured: each independent fma adds its ~6 cycles to a chain of
+  // four dependent 16x16x4 MFMAs), so the step is kept to the fewest vector
+  // instructions. Entry r of lane (kg, c) lies on in-tile anti-diagonal
+  // base + RS r (its rows are row(lane, r)); one compare per step records
+  // (base == t), and entry r is on step t when that compare came out true
+  // RS r steps earlier. A lane with no entry on the step keeps acc[0], any
+  // finite value: the broadcasts read only lanes at columns t - k inside the
+  // tile, which do have an entry, and the other broadcast values meet exact
+  // zeros of laK. Padding entries may be selected: they start at exact zero,
+  // and an error reaches an entry only through factors that are exact zeros
+  // between padding and real rows or columns, so neither side changes the
+  // other. The value at rounding goes to the lane row's own LDS copy at a
+  // constant offset per step.
+  constexpr int RS = std::is_same<R, float>::value ? 1 : 4;
+  const int base = MF::row(lane, 0) + c;
+  bool hm[2 * T - 1];
+  R* owl = &owv[kg][T - 1 - c][c];
+  static_for<0, 2 * T - 1>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    hm[t] = base == t;
+    R x = acc[0];
+    static_for<1, 4>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      if constexpr (t - RS * r >= 0) x = hm[t - RS * r] ? acc[r] : x;
     });
-  } else {
-    static_for<0, 2 * T - 1>([&](auto tc) {
-      constexpr int t = decltype(tc)::value;
-      R x = c0;
-      bool act = false;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool on = dr[r] == t;
-        x = on ? acc[r] : x;
-        act = act || on;
-      }
-      const R e = quant_unit(x, lo, hi) - x;
-      if (act) ow[t - c][c] = x;
-      const R es = row_skew(e);
+    owl[t * kOwLd] = x;
+    if constexpr (t < 2 * T - 2) {
+      const R es = row_skew(round_clamp(x, lo, hi) - x);
       static_for<0, 4>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         // MFMA s takes the rows k = KA kg + KB s: it contributes only if some
         // such k has its column t - k inside the tile (k >= t - (T - 1)) and
         // k <= t; the last step's update reaches no later anti-diagonal. The
         // skipped products add exact zeros or are never read.
-        if constexpr (t - KB * s >= 0 && KA * 3 + KB * s >= t - (T - 1) && t < 2 * T - 2) {
-          const R ev = dpp_mov<kDppRowNewBcast + ((t - KB * s) & 15), 0xF>(R(0), es);
+        if constexpr (t - KB * s >= 0 && KA * 3 + KB * s >= t - (T - 1)) {
+          const R ev = row_bcast<(t - KB * s) & 15>(es);
           acc = MF::mma(lbK[s] * ev, laK[t - KB * s], acc);
         }
       });
-    });
-  }
+    }
+  });
   wave_sync_lds();
   // write back: errors (code units) into the workspace, codes and the values
   // at rounding (back in the units of W) to the outputs
@@ -465,9 +453,7 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
     const int p = idx >> 4, q = idx & 15;
     const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + q;
     const bool valid = gi < m && gjj < n;
-    R x;
-    if constexpr (std::is_same<R, float>::value) x = owf[p >> 2][p + T - 1][q];
-    else x = ow[p][q];
+    const R x = owv[std::is_same<R, float>::value ? p >> 2 : p & 3][p + T - 1][q];
     const R cq = quant_unit(x, lo, hi);
     tW[idx] = valid ? cq - x : R(0);
     if (valid) {
