@@ -128,6 +128,10 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSe
         for (int b = 0; b < PCW; ++b) rowp[pb][rq + a][PCW * tx + b] = Yr[a][b];
     }
     __syncthreads();
+    // A thread whose rows all lie above the pivot block is done with them:
+    // its rows of Y are final and its rows of C are never read again (its
+    // entries of C in later columns are exact zeros, published as such).
+    if (ty < PRS * st) continue;
     // Cholesky factor of the NC x NC pivot block (every thread, same values)
     double l[NC][NC], dinv[NC];
     int bad = -1;
@@ -156,7 +160,8 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSe
         }
       }
     }
-    if (tid == 0 && bad >= 0 && j + bad < bs) atomicMin(S.info, (int32_t)(off + j + bad));
+    if (ty == PRS * st && tx == 0 && bad >= 0 && j + bad < bs)
+      atomicMin(S.info, (int32_t)(off + j + bad));
     // columns j.. of C at this thread's rows i and at its columns c taken as
     // rows, and rows j.. of Y at its columns c (final after this step). No
     // masks: above the pivot block these are exact zeros (C and Y keep exact
