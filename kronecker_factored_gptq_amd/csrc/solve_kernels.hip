@@ -294,16 +294,30 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
     // their L^A tiles, the update term of J = Q - 1, this wave's terms of
     // the fresh column, and L^A[Q,Q]
     R la[NJ][4], mc[NJ][4], laq[4], eu[4], lu[4], ef[NI][4], lf[NI][4];
+    // Float: no branch around these loads (a load under a branch made the
+    // compiler wait there for every load in flight, the sweep operands
+    // included; columns J >= Q read slot Q instead and are never used, and
+    // the cache is selected away before the block's third leaf): 1.8 %
+    // faster solve. Double: 3.6 % slower that way, so it keeps the guards.
+    constexpr bool kFlatLoads = std::is_same<R, float>::value;
 #pragma unroll
     for (int t = 0; t < NJ; ++t) {
       const int J = Jlo + wave + kLeafWaves * t;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) { la[t][s] = R(0); mc[t][s] = R(0); }
-      if (J < Q) {
-        const R* La = LAp + tri_index(Q, J) * T * T;
+      if constexpr (kFlatLoads) {
+        const int Jc = J < Q ? J : Q;
+        const R* La = LAp + tri_index(Q, Jc) * T * T;
 #pragma unroll
         for (int s = 0; s < 4; ++s) la[t][s] = La[c * T + MF::row(lane, s)];
-        if (d >= 2) EVec<R>::load4(McP + (int64_t)J * T * T + lane * 4, mc[t]);
+        EVec<R>::load4(McP + (int64_t)Jc * T * T + lane * 4, mc[t]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) { la[t][s] = R(0); mc[t][s] = R(0); }
+        if (J < Q) {
+          const R* La = LAp + tri_index(Q, J) * T * T;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) la[t][s] = La[c * T + MF::row(lane, s)];
+          if (d >= 2) EVec<R>::load4(McP + (int64_t)J * T * T + lane * 4, mc[t]);
+        }
       }
     }
     {
@@ -347,7 +361,7 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
       if (J >= Q) break;
       acc_t mt;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mt[r] = mc[t][r];
+      for (int r = 0; r < 4; ++r) mt[r] = (!kFlatLoads || d >= 2) ? mc[t][r] : R(0);
       if (J == Q - 1) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) mt = MF::mma(eu[s], lu[s], mt);
