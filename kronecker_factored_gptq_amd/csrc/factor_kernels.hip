@@ -64,11 +64,13 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* 
 // grid keeps the 4 x 4 patch rows 4ty.., columns 4tx.. of both C and Y in
 // registers; rows and columns past bs are padded with the identity.
 // Right-looking, NC columns j .. j+NC-1 per step (whole patch columns) and
-// one barrier per step: the owners publish the raw NC x NC pivot block, the
-// raw columns j.. and the raw rows j.. of Y; after the barrier every thread
-// forms the pivot block's Cholesky factor l (NC x NC lower; reciprocal
-// square roots by one Newton step from the hardware estimate) and, by forward
-// substitution,
+// one barrier per step: the owners publish the raw columns j.. and the raw
+// rows j.. of Y (and the next step's pivot block as it stands); the pivot
+// factor l (NC x NC lower; reciprocal square roots by one Newton step from
+// the hardware estimate) of each step comes from one extra wave, which
+// forms it during the step before (applying that step's update to the pivot
+// block itself). After the barrier every patch thread reads l and, by
+// forward substitution, forms
 //   C[i][j+q] = (X[i][j+q] - sum_{p<q} C[i][j+p] l[q][p]) / l[q][q],
 //   Y[j+q]    = (Y[j+q]    - sum_{p<q} l[q][p] Y[j+p]) / l[q][q]   (rows),
 // then updates its patch with the rank-NC terms
@@ -77,17 +79,128 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* 
 // Published values are double-buffered by the parity of the step. A pivot
 // that is not positive and finite records off + j + q in *info (smallest
 // wins) and the factorisation continues with NaN.
+// Cholesky factor l (NC x NC, lower) of the pivot block blk and the
+// reciprocals dinv of its diagonal; bad = the first pivot that is not
+// positive and finite (-1 if none), whose dinv becomes NaN.
+template <int NC>
+__device__ __forceinline__ void pivot_factor(const double (&blk)[NC][NC], double (&l)[NC][NC],
+                                             double (&dinv)[NC], int& bad) {
+  bad = -1;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+#pragma unroll
+    for (int p = 0; p < NC; ++p) {
+      if (p > q) continue;
+      double v = blk[q][p];
+#pragma unroll
+      for (int r = 0; r < NC; ++r)
+        if (r < p) v -= l[q][r] * l[p][r];
+      if (p < q) {
+        l[q][p] = v * dinv[p];
+      } else {
+        const bool ok = v > 0.0 && v < INFINITY;
+        if (!ok && bad < 0) bad = q;
+        // 1/sqrt(v) from the hardware estimate and one Newton step
+        // (y += y (1 - v y^2) / 2), then sqrt(v) = v / sqrt(v): a short
+        // dependent chain instead of a rounded square root and a division
+        const double y0 = __builtin_amdgcn_rsq(v);
+        const double r = __builtin_fma(-v * y0, y0, 1.0);
+        const double y = __builtin_fma(0.5 * y0, r, y0);
+        dinv[q] = ok ? y : __builtin_nan("");
+        l[q][q] = v * dinv[q];
+      }
+    }
+  }
+}
+
 template <int NC, int PCW>
-__global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSet set, int64_t n,
-                                                                       int64_t off, int bs) {
+__global__ __launch_bounds__(16 * (64 / PCW) + 64) void chol_inv_leaf_kernel(FactorSet set,
+                                                                            int64_t n, int64_t off,
+                                                                            int bs) {
   static_assert(NC % 4 == 0 && NC % PCW == 0, "whole patch rows and columns per step");
   constexpr int PRS = NC / 4;  // patch rows per step
   constexpr int TX = 64 / PCW;  // thread columns; 16 thread rows of 4 rows each
-  __shared__ double pblk[2][NC][NC];
+  constexpr int NCT = 16 * TX;  // patch threads; one more wave factors the pivot blocks
+  __shared__ double pnext[2][NC][NC];     // next step's pivot block before this step's update
+  __shared__ double lpub[2][NC][NC + 1];  // a step's pivot factor l, and dinv in column NC
   __shared__ double colp[2][NC][64];
   __shared__ double rowp[2][NC][64];
   const FactorSide S = factor_side(set, (int)blockIdx.x);  // one matrix per workgroup
   const int tid = threadIdx.x;
+  const int steps = (bs + NC - 1) / NC;
+  if (tid >= NCT) {
+    // Pivot wave: during step st it applies step st's update to the pivot
+    // block of step st + 1 (with the same operations the patch threads use
+    // for those entries), factors it and publishes l and dinv for step
+    // st + 1, so that the patch threads never wait for a pivot factor.
+    const bool lead = tid == NCT;
+    double l[NC][NC], dinv[NC];
+    {
+      double blk[NC][NC];
+#pragma unroll
+      for (int q = 0; q < NC; ++q)
+#pragma unroll
+        for (int p = 0; p < NC; ++p) {
+          double v = 0.0;
+          if (q < bs && p < bs) v = p <= q ? S.X[(off + q) * n + off + p] : 0.0;
+          else if (q == p) v = 1.0;
+          blk[q][p] = v;
+        }
+      int bad;
+      pivot_factor<NC>(blk, l, dinv, bad);
+      if (lead && bad >= 0 && bad < bs) atomicMin(S.info, (int32_t)(off + bad));
+      if (lead) {
+#pragma unroll
+        for (int q = 0; q < NC; ++q) {
+#pragma unroll
+          for (int p = 0; p < NC; ++p) lpub[0][q][p] = l[q][p];
+          lpub[0][q][NC] = dinv[q];
+        }
+      }
+    }
+    for (int st = 0; st < steps; ++st) {
+      const int pb = st & 1;
+      __syncthreads();
+      if (st + 1 >= steps) continue;
+      const int j1 = NC * (st + 1);
+      double ci[NC][NC];  // step st's panel C[j1 + a][j + q]
+#pragma unroll
+      for (int a = 0; a < NC; ++a) {
+#pragma unroll
+        for (int q = 0; q < NC; ++q) {
+          double vi = colp[pb][q][j1 + a];
+#pragma unroll
+          for (int p = 0; p < NC; ++p)
+            if (p < q) vi -= ci[a][p] * l[q][p];
+          ci[a][q] = vi * dinv[q];
+        }
+      }
+      double blk[NC][NC];
+#pragma unroll
+      for (int a = 0; a < NC; ++a)
+#pragma unroll
+        for (int b = 0; b < NC; ++b) {
+          double dl = 0.0;
+#pragma unroll
+          for (int q = 0; q < NC; ++q) dl += ci[a][q] * ci[b][q];
+          double v = pnext[pb][a][b];
+          if (b <= a) v -= dl;
+          blk[a][b] = v;
+        }
+      int bad;
+      pivot_factor<NC>(blk, l, dinv, bad);
+      if (lead && bad >= 0 && j1 + bad < bs) atomicMin(S.info, (int32_t)(off + j1 + bad));
+      if (lead) {
+#pragma unroll
+        for (int q = 0; q < NC; ++q) {
+#pragma unroll
+          for (int p = 0; p < NC; ++p) lpub[pb ^ 1][q][p] = l[q][p];
+          lpub[pb ^ 1][q][NC] = dinv[q];
+        }
+      }
+    }
+    return;
+  }
   const int ty = tid / TX, tx = tid % TX;
   double Lr[4][PCW], Yr[4][PCW];
 #pragma unroll
@@ -101,19 +214,21 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSe
       Lr[a][b] = v;
       Yr[a][b] = (i == c) ? 1.0 : 0.0;
     }
-  const int steps = (bs + NC - 1) / NC;
   for (int st = 0; st < steps; ++st) {
     const int j = NC * st, pb = st & 1;
     // owners of columns j..j+NC-1 and of rows j..j+NC-1
     const bool ownc = tx >= j / PCW && tx < (j + NC) / PCW;
     const bool ownr = ty >= PRS * st && ty < PRS * (st + 1);
     const int rq = 4 * (ty - PRS * st);  // first pivot row of this thread row
-    // publish the raw pivot block, columns j..j+NC-1 and rows j..j+NC-1 of Y
-    if (ownc && ownr) {
+    // publish the next step's pivot block, columns j..j+NC-1 and rows
+    // j..j+NC-1 of Y
+    if (tx >= (j + NC) / PCW && tx < (j + 2 * NC) / PCW && ty >= PRS * (st + 1) &&
+        ty < PRS * (st + 2)) {
+      const int rn = 4 * (ty - PRS * (st + 1));
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < PCW; ++b) pblk[pb][rq + a][PCW * tx + b - j] = Lr[a][b];
+        for (int b = 0; b < PCW; ++b) pnext[pb][rn + a][PCW * tx + b - j - NC] = Lr[a][b];
     }
     if (ownc) {
 #pragma unroll
@@ -132,36 +247,14 @@ __global__ __launch_bounds__(16 * (64 / PCW)) void chol_inv_leaf_kernel(FactorSe
     // its rows of Y are final and its rows of C are never read again (its
     // entries of C in later columns are exact zeros, published as such).
     if (ty < PRS * st) continue;
-    // Cholesky factor of the NC x NC pivot block (every thread, same values)
+    // this step's pivot factor, from the pivot wave
     double l[NC][NC], dinv[NC];
-    int bad = -1;
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
 #pragma unroll
-      for (int p = 0; p < NC; ++p) {
-        if (p > q) continue;
-        double v = pblk[pb][q][p];
-#pragma unroll
-        for (int r = 0; r < NC; ++r)
-          if (r < p) v -= l[q][r] * l[p][r];
-        if (p < q) {
-          l[q][p] = v * dinv[p];
-        } else {
-          const bool ok = v > 0.0 && v < INFINITY;
-          if (!ok && bad < 0) bad = q;
-          // 1/sqrt(v) from the hardware estimate and one Newton step
-          // (y += y (1 - v y^2) / 2), then sqrt(v) = v / sqrt(v): a short
-          // dependent chain instead of a rounded square root and a division
-          const double y0 = __builtin_amdgcn_rsq(v);
-          const double r = __builtin_fma(-v * y0, y0, 1.0);
-          const double y = __builtin_fma(0.5 * y0, r, y0);
-          dinv[q] = ok ? y : __builtin_nan("");
-          l[q][q] = v * dinv[q];
-        }
-      }
+      for (int p = 0; p < NC; ++p) l[q][p] = lpub[pb][q][p];
+      dinv[q] = lpub[pb][q][NC];
     }
-    if (ty == PRS * st && tx == 0 && bad >= 0 && j + bad < bs)
-      atomicMin(S.info, (int32_t)(off + j + bad));
     // columns j.. of C at this thread's rows i and at its columns c taken as
     // rows, and rows j.. of Y at its columns c (final after this step). No
     // masks: above the pivot block these are exact zeros (C and Y keep exact
@@ -369,7 +462,7 @@ static hipError_t chol_inv_rec(int64_t n, const FactorSet& sd, int64_t off, int6
   const int64_t zs = sd.stride;
   if (len <= NB) {
     hipLaunchKernelGGL((chol_inv_leaf_kernel<kLeafCols, kLeafPatchCols>), dim3(ns),
-                       dim3(16 * (64 / kLeafPatchCols)), 0, s, sd, n, off, (int)len);
+                       dim3(16 * (64 / kLeafPatchCols) + 64), 0, s, sd, n, off, (int)len);
     return hipGetLastError();
   }
   const int64_t n1 = split_point(len), n2 = len - n1;
