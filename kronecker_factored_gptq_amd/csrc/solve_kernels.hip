@@ -204,6 +204,18 @@ __device__ inline double round_clamp(double x, double lo, double hi) {
   return quant_unit(x, lo, hi);
 }
 
+// Lanes whose accumulator entry r lies on in-tile anti-diagonal t (lane l
+// holds row(l, r) of column l % 16), as a wave mask.
+template <typename R>
+constexpr uint64_t entry_lanes(int t, int r) {
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l) {
+    const int row = std::is_same<R, float>::value ? 4 * (l >> 4) + r : (l >> 4) + 4 * r;
+    if (row + (l & 15) == t) m |= uint64_t(1) << l;
+  }
+  return m;
+}
+
 template <int I, int N, typename F>
 __device__ inline void static_for(F&& f) {
   if constexpr (I < N) {
@@ -419,10 +431,9 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
   // One wave's vector instructions do not overlap its own MFMA chain on
   // gfx950 (measured: each independent fma adds its ~6 cycles to a chain of
   // four dependent 16x16x4 MFMAs), so the step is kept to the fewest vector
-  // instructions. Entry r of lane (kg, c) lies on in-tile anti-diagonal
-  // base + RS r (its rows are row(lane, r)); one compare per step records
-  // (base == t), and entry r is on step t when that compare came out true
-  // RS r steps earlier. A lane with no entry on the step keeps acc[0], any
+  // instructions. Which lanes hold their entry r on step t is fixed by the
+  // lane layout, so the select masks are compile-time wave masks (scalar
+  // moves, no compares). A lane with no entry on the step keeps acc[0], any
   // finite value: the broadcasts read only lanes at columns t - k inside the
   // tile, which do have an entry, and the other broadcast values meet exact
   // zeros of laK. Padding entries may be selected: they start at exact zero,
@@ -430,17 +441,14 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
   // between padding and real rows or columns, so neither side changes the
   // other. The value at rounding goes to the lane row's own LDS copy at a
   // constant offset per step.
-  constexpr int RS = std::is_same<R, float>::value ? 1 : 4;
-  const int base = MF::row(lane, 0) + c;
-  bool hm[2 * T - 1];
   R* owl = &owv[kg][T - 1 - c][c];
   static_for<0, 2 * T - 1>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
-    hm[t] = base == t;
     R x = acc[0];
     static_for<1, 4>([&](auto rc) {
       constexpr int r = decltype(rc)::value;
-      if constexpr (t - RS * r >= 0) x = hm[t - RS * r] ? acc[r] : x;
+      constexpr uint64_t msk = entry_lanes<R>(t, r);
+      if constexpr (msk != 0) x = __builtin_amdgcn_inverse_ballot_w64(msk) ? acc[r] : x;
     });
     owl[t * kOwLd] = x;
     if constexpr (t < 2 * T - 2) {
