@@ -14,9 +14,18 @@
  *    convention of the math only; by the symmetry of the dependency order a
  *    column-major caller can pass (n, m, W^T, B, A) with column scales.
  *  - Every pointer except `bad_pivot` is a device pointer owned by the
- *    caller. The library allocates and frees nothing and keeps no global
- *    state; scratch memory is the caller's `workspace` of at least the
- *    size the matching *_workspace_bytes query returns (256-byte aligned).
+ *    caller. The library allocates and frees no device memory and keeps no
+ *    global state; scratch memory is the caller's `workspace` of at least
+ *    the size the matching *_workspace_bytes query returns (256-byte
+ *    aligned). The synchronous factor calls are the one place that creates
+ *    HIP objects: when m != n, or an order exceeds 8192, bakron_factor and
+ *    bakron_factor_batched create helper streams and events for the call
+ *    and destroy them before returning (every return path, errors included,
+ *    first waits for all work the call enqueued). bakron_solve_timed
+ *    creates and destroys its timing events the same way.
+ *  - There is no out-of-memory status: no call allocates device memory, so
+ *    none can run out of it. A workspace smaller than its query is
+ *    BAKRON_EINVAL.
  *  - `stream` is a hipStream_t (NULL = the default stream). Calls are
  *    asynchronous unless stated otherwise; argument errors are reported
  *    before anything is enqueued. Calls on different streams with distinct

@@ -136,6 +136,28 @@ def _ld(t: torch.Tensor, name: str) -> int:
     return max(int(t.stride(0)), int(t.size(1)), 1)
 
 
+def _check_out(t: torch.Tensor, shape, dtype: torch.dtype, name: str) -> None:
+    """A caller-supplied output must have exactly the shape and element type
+    the kernels write, with unit column stride (the C ABI only sees its
+    pointer and leading dimension)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() == 2 and t.size(1) > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    if t.dim() == 2 and t.size(0) > 1 and t.stride(0) < t.size(1):
+        raise ValueError(f"{name} rows overlap (leading dimension below the row length)")
+
+
+def _check_operand(t: torch.Tensor, shape, dtype: torch.dtype, name: str) -> None:
+    """An input read by the kernels: exact shape and element type."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
 def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -278,6 +300,8 @@ def solve(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: Alphabe
     if scales is not None:
         if scales.dtype != W.dtype or not scales.is_contiguous():
             raise ValueError("scales must be contiguous with W's dtype")
+    if out is not None:
+        _check_out(out, (m, n), torch.int32, "out")
     V = out if out is not None else torch.empty((m, n), dtype=torch.int32, device=dev)
     Wt = torch.empty((m, n), dtype=W.dtype, device=dev) if return_wt else None
     L = lib()
@@ -369,8 +393,11 @@ def loss(W: torch.Tensor, V: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
     code = _dt(W)
     m, n = W.shape
     mode = _scale_mode(scales, m, n, scale_mode)
-    if V.dtype != torch.int32:
-        raise TypeError("V must be int32")
+    _check_operand(V, (m, n), torch.int32, "V")
+    _check_operand(A, (n, n), W.dtype, "A")
+    _check_operand(B, (m, m), W.dtype, "B")
+    if scales is not None and (scales.dtype != W.dtype or not scales.is_contiguous()):
+        raise ValueError("scales must be contiguous with W's dtype")
     out = torch.zeros(1, dtype=torch.float64, device=dev)
     L = lib()
     ws = _workspace(L.bakron_loss_workspace_bytes(code, m, n), dev, workspace)
@@ -395,6 +422,8 @@ def loss_batched(W: torch.Tensor, V: torch.Tensor, A: torch.Tensor, B: torch.Ten
     if W.dim() != 3 or V.dim() != 3 or V.shape != W.shape or V.dtype != torch.int32:
         raise ValueError("W and V must be (batch, m, n), V int32")
     batch, m, n = W.shape
+    if A.dtype != W.dtype or B.dtype != W.dtype:
+        raise TypeError("A and B must have W's dtype")
     pw, ldw, sw = _batch_operand(W, m, n, batch, "W")
     pv, ldv, sv = _batch_operand(V, m, n, batch, "V")
     pa, lda, sa = _batch_operand(A, n, n, batch, "A")
@@ -407,6 +436,8 @@ def loss_batched(W: torch.Tensor, V: torch.Tensor, A: torch.Tensor, B: torch.Ten
     else:
         if scales.dtype != W.dtype or not scales.is_contiguous():
             raise ValueError("scales must be contiguous with W's dtype")
+        if scales.dim() not in (1, 2) or (scales.dim() == 2 and scales.size(0) != batch):
+            raise ValueError("scales must be (batch, length) or (length,)")
         vec = scales if scales.dim() == 1 else scales[0]
         mode = _scale_mode(vec, m, n, scale_mode)
         ss = int(scales.stride(0)) if scales.dim() == 2 and batch > 1 else 0
@@ -464,6 +495,8 @@ def gram(X: torch.Tensor, weights: Optional[torch.Tensor] = None, damp_rel: floa
     if weights is not None and (weights.dtype != X.dtype or weights.numel() != N
                                 or not weights.is_contiguous()):
         raise ValueError("weights must be a contiguous length-N vector of X's dtype")
+    if out is not None:
+        _check_out(out, (d, d), X.dtype, "out")
     G = out if out is not None else torch.empty((d, d), dtype=X.dtype, device=dev)
     with torch.cuda.device(dev):
         rc = lib().bakron_gram(code, N, d, _p(X), _ld(X, "X"), _p(weights), float(damp_rel),

@@ -264,13 +264,8 @@ int factor_impl(int64_t batch, int64_t m, int64_t n, const R* A, int64_t lda, co
   const FactorSide sb = carve_side(base_b, m, info + batch);
   const int nb = (int)batch;
   const int64_t za = (int64_t)(lay.a / 8), zb = (int64_t)(lay.b / 8);
-  if (launch_fill_i32(info, 2 * batch, INT_MAX, s) != hipSuccess) return BAKRON_EHIP;
-  if (n > 0 && launch_load_reversed<R>(n, A, lda, st.a, sa.X, za, nb, s) != hipSuccess)
-    return BAKRON_EHIP;
-  if (m > 0 && launch_load_reversed<R>(m, B, ldb, st.b, sb.X, zb, nb, s) != hipSuccess)
-    return BAKRON_EHIP;
-  // helper stream and events of this call (released when the call returns,
-  // after the final synchronisation)
+  // helper streams and events of this call (created here, destroyed when the
+  // call returns, after the final synchronisation)
   struct Aux {
     hipStream_t st = nullptr;
     hipEvent_t ready = nullptr, done = nullptr;
@@ -282,46 +277,66 @@ int factor_impl(int64_t batch, int64_t m, int64_t n, const R* A, int64_t lda, co
   } aux;
   // each set's large nodes form their C21 Y11 products on a helper stream
   HelperStream ha, hb;
+  // Once anything is enqueued, an error return first waits for every stream
+  // of the call, so that no kernel still uses the caller's workspace (or a
+  // helper stream about to be destroyed) after the call returns.
+  auto fail = [&]() {
+    (void)hipStreamSynchronize(s);
+    if (aux.st) (void)hipStreamSynchronize(aux.st);
+    if (ha.fa.ts) (void)hipStreamSynchronize(ha.fa.ts);
+    if (hb.fa.ts) (void)hipStreamSynchronize(hb.fa.ts);
+    return BAKRON_EHIP;
+  };
   if (ha.init(n) != BAKRON_OK) return BAKRON_EHIP;
   if (m != n && hb.init(m) != BAKRON_OK) return BAKRON_EHIP;
+  if (m != n && m > 0 && n > 0) {
+    if (hipStreamCreateWithFlags(&aux.st, hipStreamNonBlocking) != hipSuccess) {
+      aux.st = nullptr;
+      return BAKRON_EHIP;
+    }
+    if (hipEventCreateWithFlags(&aux.ready, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&aux.done, hipEventDisableTiming) != hipSuccess)
+      return BAKRON_EHIP;
+  }
+  if (launch_fill_i32(info, 2 * batch, INT_MAX, s) != hipSuccess) return fail();
+  if (n > 0 && launch_load_reversed<R>(n, A, lda, st.a, sa.X, za, nb, s) != hipSuccess)
+    return fail();
+  if (m > 0 && launch_load_reversed<R>(m, B, ldb, st.b, sb.X, zb, nb, s) != hipSuccess)
+    return fail();
   if (m == n) {
     // the B sides follow the A sides at the same stride: one set of 2 * batch
     if (factor_cholesky_inverse(n, FactorSet{sa, za, 2 * nb}, s, ha.get()) != hipSuccess)
-      return BAKRON_EHIP;
+      return fail();
   } else if (m > 0 && n > 0) {
     // orders differ, so the sides cannot share launches: the B set runs on a
     // stream of this call, concurrently with the A set (both sequences are
     // launch- and latency-bound and leave most of the GPU idle)
-    if (hipStreamCreateWithFlags(&aux.st, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&aux.ready, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&aux.done, hipEventDisableTiming) != hipSuccess)
-      return BAKRON_EHIP;
     if (hipEventRecord(aux.ready, s) != hipSuccess ||
         hipStreamWaitEvent(aux.st, aux.ready, 0) != hipSuccess)
-      return BAKRON_EHIP;
+      return fail();
     if (factor_cholesky_inverse(m, FactorSet{sb, zb, nb}, aux.st, hb.get()) != hipSuccess)
-      return BAKRON_EHIP;
-    if (hipEventRecord(aux.done, aux.st) != hipSuccess) return BAKRON_EHIP;
+      return fail();
+    if (hipEventRecord(aux.done, aux.st) != hipSuccess) return fail();
     if (factor_cholesky_inverse(n, FactorSet{sa, za, nb}, s, ha.get()) != hipSuccess)
-      return BAKRON_EHIP;
-    if (hipStreamWaitEvent(s, aux.done, 0) != hipSuccess) return BAKRON_EHIP;
+      return fail();
+    if (hipStreamWaitEvent(s, aux.done, 0) != hipSuccess) return fail();
   } else {
     if (factor_cholesky_inverse(n, FactorSet{sa, za, nb}, s, ha.get()) != hipSuccess)
-      return BAKRON_EHIP;
+      return fail();
     if (factor_cholesky_inverse(m, FactorSet{sb, zb, nb}, s, hb.get()) != hipSuccess)
-      return BAKRON_EHIP;
+      return fail();
   }
   if (n > 0 &&
       launch_store_normalized<R>(n, sa.Y, za, LA, ldla, st.la, dA, st.da, nb, s) != hipSuccess)
-    return BAKRON_EHIP;
+    return fail();
   if (m > 0 &&
       launch_store_normalized<R>(m, sb.Y, zb, LB, ldlb, st.lb, dB, st.db, nb, s) != hipSuccess)
-    return BAKRON_EHIP;
+    return fail();
   std::vector<int32_t> hinfo((size_t)(2 * batch), INT_MAX);
   if (hipMemcpyAsync(hinfo.data(), info, hinfo.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
                      s) != hipSuccess)
-    return BAKRON_EHIP;
-  if (hipStreamSynchronize(s) != hipSuccess) return BAKRON_EHIP;
+    return fail();
+  if (hipStreamSynchronize(s) != hipSuccess) return fail();
   for (int64_t z = 0; z < batch; ++z)
     for (int side = 0; side < 2; ++side) {
       const int32_t v = hinfo[(size_t)(side * batch + z)];

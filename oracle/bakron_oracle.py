@@ -543,6 +543,8 @@ class ReplayReport:
     inconsistent: int          # entries whose imposed code is not quantize(replayed value)
     max_inconsistent_gap: float  # largest |frac(x/s) - 1/2| over those entries (0 if none)
     Wt: np.ndarray             # replayed pre-rounding values
+    gaps: np.ndarray = None    # |frac(x/s) - 1/2| of every inconsistent entry
+    E: np.ndarray = None       # replayed errors s*V_given - Wt
 
 
 def replay(W, LA, LB, alphabet, scale_mode, scales, V_given, leaf: int = 32) -> ReplayReport:
@@ -555,11 +557,9 @@ def replay(W, LA, LB, alphabet, scale_mode, scales, V_given, leaf: int = 32) -> 
     S = scale_grid(m, n, scale_mode, scales)
     free = quantize(res.Wt, S, alphabet)
     bad = free != np.asarray(V_given, dtype=np.float64)
-    gap = 0.0
-    if np.any(bad):
-        y = res.Wt[bad] / S[bad]
-        gap = float(np.max(np.abs(y - np.floor(y) - 0.5)))
-    return ReplayReport(int(np.count_nonzero(bad)), gap, res.Wt)
+    gaps = frac_gap(res.Wt[bad] / S[bad])
+    gap = float(np.max(gaps)) if gaps.size else 0.0
+    return ReplayReport(int(np.count_nonzero(bad)), gap, res.Wt, gaps, res.E)
 
 
 def frac_gap(x: np.ndarray) -> np.ndarray:

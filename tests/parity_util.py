@@ -80,25 +80,38 @@ class Fp32Report:
     agreement: float
     mismatches: int
     first_mismatch_gap: float     # |frac - 1/2| of the earliest raw mismatch (oracle value)
-    replay_inconsistent: int
-    replay_max_gap: float
-    max_dev: float                # max |Wt_gpu - Wt_replay| / s, in code units
+    replay_inconsistent: int      # GPU decisions the float64 replay would not take
+    replay_max_gap: float         # largest |frac - 1/2| among them
+    max_dev: float                # tau_obs = max |Wt_gpu - Wt_replay| / s, in code units
     loss_rel: float
     loss_signed: float = 0.0      # (loss(V_gpu) - loss(V_ref)) / loss(V_ref)
     m: int = 0
     n: int = 0
+    replay_outside_1e6: int = 0   # inconsistent decisions at |frac - 1/2| >= 1e-6
+    replay_outside_tau_obs: int = 0  # inconsistent decisions at |frac - 1/2| > tau_obs
+    branch_spread: Optional[float] = None   # the oracle's own loss spread (see below)
+    branch_detail: Optional[list] = None
 
-    def cascade_loss_bound(self) -> float:
-        """Loss spread between two valid solutions that took different
-        near-tie branches. Measured with the float64 oracle alone on the
-        4096x4096 workload: perturbing W by one float32 ulp flips a near-tie
-        (gap 2.9e-8 code units) and moves the oracle's own loss by 1.1e-3 and
-        1.7e-3 (agreement 82.5%); round-to-nearest is 72% worse. Allow 3x the
-        larger measured spread, 5e-3, once branches differ; 1e-4 otherwise."""
-        return 5e-3 if self.mismatches else 1e-4
+    def as_dict(self) -> dict:
+        return {"agreement": self.agreement, "mismatches": self.mismatches,
+                "first_mismatch_gap": self.first_mismatch_gap,
+                "replay_inconsistent": self.replay_inconsistent,
+                "replay_inconsistent_at_tau_1e-6": self.replay_outside_1e6,
+                "tau_obs": self.max_dev,
+                "replay_inconsistent_at_tau_obs": self.replay_outside_tau_obs,
+                "replay_max_gap": self.replay_max_gap, "loss_rel": self.loss_signed,
+                "oracle_branch_spread": self.branch_spread}
 
 
-def fp32_parity(inp: Inputs, V_gpu: np.ndarray, Wt_gpu: np.ndarray, ref: O.Result, A, B) -> Fp32Report:
+def fp32_parity(inp: Inputs, V_gpu: np.ndarray, Wt_gpu: np.ndarray, ref: O.Result, A=None, B=None,
+                dA=None, dB=None) -> Fp32Report:
+    """Raw agreement with the oracle's free solve, the replay check, and the
+    relative loss difference of the GPU codes against the oracle's codes.
+    The loss is tr(B (W - Q) A (W - Q)^T) from A and B when given;
+    otherwise (dA, dB given) it is the exact identity
+    sum_ij E_ij^2 / (d^B_i d^A_j)^2 on the recurrence's errors, i.e. the loss
+    under the Hessian the factors define (pinned on the CPU against the
+    quadratic form)."""
     m, n = inp.W.shape
     V_ref = ref.V.astype(np.int64)
     mism = V_gpu.astype(np.int64) != V_ref
@@ -111,11 +124,57 @@ def fp32_parity(inp: Inputs, V_gpu: np.ndarray, Wt_gpu: np.ndarray, ref: O.Resul
         gap_first = float(O.frac_gap(ref.Wt[i0, j0] / S[i0, j0]))
     rep = O.replay(inp.W, inp.LA, inp.LB, inp.alphabet, inp.mode, inp.s, V_gpu.astype(np.float64))
     max_dev = float(np.max(np.abs(Wt_gpu.astype(np.float64) - rep.Wt) / S)) if Wt_gpu is not None else float("nan")
-    l_gpu = O.loss(inp.W, V_gpu, A, B, inp.mode, inp.s)
-    l_ref = O.loss(inp.W, ref.V, A, B, inp.mode, inp.s)
+    if A is not None:
+        l_gpu = O.loss(inp.W, V_gpu, A, B, inp.mode, inp.s)
+        l_ref = O.loss(inp.W, ref.V, A, B, inp.mode, inp.s)
+    else:
+        l_gpu = O.loss_from_errors(rep.E, dA, dB)
+        l_ref = O.loss_from_errors(ref.E, dA, dB)
     rel = (l_gpu - l_ref) / abs(l_ref) if l_ref != 0 else l_gpu
     return Fp32Report(float(np.mean(~mism)), int(np.count_nonzero(mism)), gap_first,
-                      rep.inconsistent, rep.max_inconsistent_gap, max_dev, abs(rel), rel, m, n)
+                      rep.inconsistent, rep.max_inconsistent_gap, max_dev, abs(rel), rel, m, n,
+                      int(np.count_nonzero(rep.gaps >= 1e-6)),
+                      int(np.count_nonzero(rep.gaps > max_dev)))
+
+
+def oracle_branch_spread(inp: Inputs, ref: O.Result, dA, dB, ulp_seeds=(1, 2, 3, 4),
+                         noise_seeds=(1, 2)):
+    """The float64 oracle's own loss spread between valid solutions. The
+    oracle solves again from a nudged W and the loss of the new codes is
+    compared with the loss of the reference codes (both by the error
+    identity under the factors' Hessian). Two kinds of nudge:
+      * one float32 ulp, in a seeded random direction per entry: the
+        smallest change any float32 implementation's inputs can differ by;
+      * a seeded relative Gaussian change of 2^-20 (16 float32 ulps) per
+        entry: the size of the deviation a float32 solve accumulates over
+        its ~10^3 roundings per entry (about 1e-5 code units).
+    A near-tie closer to its midpoint than the nudge flips, and the flip
+    cascades into its downstream quadrant, so the spread measures how far
+    two valid branches end up apart on this matrix. Returns (max relative
+    spread, [(kind, seed, agreement, relative loss change)])."""
+    l_ref = O.loss_from_errors(ref.E, dA, dB)
+    W32 = np.asarray(inp.W, dtype=np.float32)
+    nudged = []
+    for sd in ulp_seeds:
+        g = np.random.default_rng([7, int(sd)])
+        toward = np.where(g.random(W32.shape) < 0.5, np.float32(-np.inf), np.float32(np.inf))
+        nudged.append(("ulp", sd, np.nextafter(W32, toward).astype(np.float32)))
+    for sd in noise_seeds:
+        g = np.random.default_rng([8, int(sd)])
+        Wp = W32.astype(np.float64) * (1.0 + 2.0 ** -20 * g.standard_normal(W32.shape))
+        nudged.append(("rel2^-20", sd, Wp.astype(np.float32)))
+    out = []
+    for kind, sd, Wp in nudged:
+        r = oracle_solve(Inputs(Wp, inp.LA, inp.LB, inp.dA, inp.dB, inp.s, inp.mode, inp.alphabet))
+        l = O.loss_from_errors(r.E, dA, dB)
+        out.append((kind, sd, float(np.mean(r.V == ref.V)), (l - l_ref) / abs(l_ref)))
+    return max(abs(x[3]) for x in out), out
+
+
+# Multiple of the oracle's own branch spread a float32 solve may deviate by:
+# the spread is a sample of a few branches, and a float32 solve may take an
+# earlier (larger) one.
+SPREAD_MULTIPLE = 3.0
 
 
 def assert_fp32_parity(rep: Fp32Report, min_agreement: float = 0.999, loss_rel: float = 1e-4,
@@ -137,11 +196,58 @@ def assert_fp32_validity(rep: Fp32Report, gap_tol: float = 1e-5):
     """Size-independent conditions (fp32) for sizes where a single near-tie
     flip cascades: every GPU decision is the quantizer's choice at the float64
     replayed value except within the measured fp32 deviation of a midpoint;
-    the first raw divergence is itself a near-tie; the loss differs by no more
-    than the spread of two valid solutions that differ on that many entries."""
+    the first raw divergence is itself a near-tie; and the loss differs from
+    the oracle's by at most the benchmark spec's 1e-4 or SPREAD_MULTIPLE times the
+    oracle's own spread between branches measured on the same matrix
+    (``branch_spread``, required once the raw codes differ)."""
     if rep.replay_inconsistent:
         assert rep.replay_max_gap <= max(rep.max_dev, 1e-6) + 1e-7, rep
         assert rep.replay_max_gap <= gap_tol, rep
     if rep.mismatches:
         assert rep.first_mismatch_gap <= gap_tol, rep
-    assert rep.loss_rel <= rep.cascade_loss_bound(), rep
+    bound = 1e-4
+    if rep.mismatches:
+        assert rep.branch_spread is not None, "measure the oracle's branch spread first"
+        bound = max(bound, SPREAD_MULTIPLE * rep.branch_spread)
+    assert rep.loss_rel <= bound, (rep, bound)
+
+
+def cond_estimate(A: np.ndarray, Lhat: np.ndarray, d: np.ndarray, iters: int = 30) -> float:
+    """2-norm condition number of the SPD matrix A, estimated without an
+    O(n^3) decomposition: lambda_max(A) and lambda_max(A^-1) = ||L||_2^2
+    (L = Lhat diag(d) = Cholesky(A^-1)) by block power iteration (four
+    seeded start vectors, float32 products: only the magnitude matters),
+    then doubled as a margin (the iteration approaches the largest
+    eigenvalue from below)."""
+    A32 = O.sym_from_lower(A).astype(np.float32)
+    L32 = (np.asarray(Lhat, dtype=np.float64) * np.asarray(d, dtype=np.float64)[None, :]).astype(np.float32)
+    g = np.random.default_rng(11)
+
+    def top(mv):
+        V = g.standard_normal((A32.shape[0], 4)).astype(np.float32)
+        lam = 0.0
+        for _ in range(iters):
+            V, _ = np.linalg.qr(V)
+            Y = mv(V)
+            lam = float(np.max(np.linalg.norm(Y, axis=0)))
+            V = Y
+        return lam
+
+    return 2.0 * top(lambda V: A32 @ V) * top(lambda V: L32 @ (L32.T @ V))
+
+
+def assert_factor_close(L_gpu, d_gpu, Lhat_ref, d_ref, cond: float, eps: float):
+    """A GPU factor against the oracle's: unit diagonal and zero upper
+    triangle exactly, entries within 8 eps + 64 cond u n (u = 1.1e-16, the
+    float64 forward-error scale of a Cholesky-type factorisation of order n
+    with condition number cond, plus the final rounding to the dtype)."""
+    n = Lhat_ref.shape[0]
+    L_gpu = np.asarray(L_gpu, dtype=np.float64)
+    assert np.all(np.diag(L_gpu) == 1.0)
+    assert not np.any(np.triu(L_gpu, 1))
+    tol = 8 * eps + 64 * cond * 1.1e-16 * max(n, 1)
+    err = float(np.max(np.abs(L_gpu - Lhat_ref)))
+    assert err <= tol, (err, tol)
+    np.testing.assert_allclose(np.asarray(d_gpu, dtype=np.float64), d_ref,
+                               rtol=64 * cond * 1.1e-16 * n + 4 * eps)
+    return err, tol

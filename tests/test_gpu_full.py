@@ -8,8 +8,8 @@ import torch
 import oracle as O
 from synth import config3
 
-from parity_util import (assert_fp32_validity, fp32_parity, gpu_solve, oracle_solve, prepare,
-                         to_dev)
+from parity_util import (assert_factor_close, assert_fp32_validity, cond_estimate, fp32_parity,
+                         gpu_solve, oracle_branch_spread, oracle_solve, prepare, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,11 @@ def test_attn4096_factor_matches_oracle(gpu_lib, cfg3):
 
 @pytest.mark.timeout(600)
 def test_attn4096_solve_parity(gpu_lib, cfg3):
+    """Float32 at 4096 x 4096 (the parity criteria of the hot path's
+    float32 mode, replay and loss parts): every GPU decision the float64
+    replay disagrees with is a near-tie within the measured float32
+    deviation; the loss differs from the oracle's by at most the oracle's
+    own branch spread (measured here) times SPREAD_MULTIPLE, or 1e-4."""
     p, inp = cfg3
     # row scales: the GPU helper equals the oracle's rule bit for bit
     s_gpu = gpu_lib.row_scales(to_dev(inp.W), 7).cpu().numpy()
@@ -44,7 +49,9 @@ def test_attn4096_solve_parity(gpu_lib, cfg3):
     V, Wt = gpu_solve(gpu_lib, inp)
     ref = oracle_solve(inp)
     rep = fp32_parity(inp, V, Wt, ref, p.A, p.B)
-    print(rep)
+    if rep.mismatches:
+        rep.branch_spread, rep.branch_detail = oracle_branch_spread(inp, ref, inp.dA, inp.dB)
+    print(rep.as_dict(), rep.branch_detail)
     # A float32 solve differs from the float64 one by ~1e-5 code units, so
     # among 16.7M decisions some near-ties flip and each flip cascades into its
     # downstream quadrant: raw agreement is reported, validity is asserted.
@@ -54,6 +61,21 @@ def test_attn4096_solve_parity(gpu_lib, cfg3):
     l_gpu = gpu_lib.loss(to_dev(inp.W), to_dev(V), to_dev(p.A), to_dev(p.B), to_dev(inp.s))
     l_ora = O.loss(inp.W, V, p.A, p.B, O.SCALE_ROW, inp.s)
     assert abs(l_gpu - l_ora) <= 1e-9 * abs(l_ora)
+
+
+@pytest.mark.timeout(600)
+def test_attn4096_factor_fp64_matches_oracle(gpu_lib, cfg3):
+    """The float64 factor at order 4096 (the workload's A with its 41 outlier
+    channels, and B) against the oracle's inverse-then-Cholesky, within the
+    condition-scaled bound."""
+    p, _ = cfg3
+    A64, B64 = p.A.astype(np.float64), p.B.astype(np.float64)
+    LA, LB, dA, dB = gpu_lib.factor(to_dev(A64), to_dev(B64))
+    for M, L, d in ((A64, LA, dA), (B64, LB, dB)):
+        R, rd = O.factor(M)
+        c = cond_estimate(M, R, rd)
+        err, tol = assert_factor_close(L.cpu().numpy(), d.cpu().numpy(), R, rd, c, 1e-16)
+        print("order 4096 fp64 factor: cond <=", c, "max err", err, "tol", tol)
 
 
 @pytest.mark.timeout(600)
