@@ -160,6 +160,32 @@ int bakron_solve(int dtype, int64_t m, int64_t n,
                  void *Wt, int64_t ldwt,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * No-allocation solve, for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, result and asynchrony as
+ * bakron_solve minus the workspace: the scratch is a device array of
+ * BAKRON_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held by
+ * that GPU until the process ends (the first call on a device looks up its
+ * address; no call allocates or frees anything). A problem whose
+ * bakron_solve_workspace_bytes exceeds BAKRON_NOALLOC_SCRATCH_BYTES is
+ * BAKRON_EINVAL (checked before any HIP call): 64 MiB holds 2048 x 2048 in
+ * float32 or 1024 x 2048 in float64.
+ * All calls on one GPU share its scratch, and it keeps the last call's
+ * contents (no part needs to start at zero: the solve writes every word
+ * before reading it): calls that may overlap on one GPU (different streams,
+ * or host threads) race and must be serialised by the caller. The device
+ * is the current one (hipGetDevice), and `stream` must belong to it.
+ * ------------------------------------------------------------------------ */
+#define BAKRON_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int bakron_solve_noalloc(int dtype, int64_t m, int64_t n,
+                         const void *W, int64_t ldw,
+                         const void *LA, int64_t ldla, const void *LB, int64_t ldlb,
+                         int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded,
+                         int scale_mode, const void *scales,
+                         int32_t *V, int64_t ldv,
+                         void *Wt, int64_t ldwt, void *stream);
+
 /* The launch schedule bakron_solve uses for (dtype, m, n), for measurement:
  * writes up to `max_ops` records of 4 int32 {kind, a, b, c} to the HOST
  * array `ops` (nullable) and returns the total number of records, or a

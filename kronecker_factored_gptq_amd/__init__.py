@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["F32", "F64", "SCALE_NONE", "SCALE_ROW", "SCALE_COL", "BakronError", "lib", "factor",
            "factor_batched",
-           "solve", "solve_batched", "loss", "loss_batched", "row_scales", "row_scales_mse", "gram",
+           "solve", "solve_noalloc", "solve_batched", "loss", "loss_batched", "row_scales", "row_scales_mse", "gram",
            "sample_sqnorms", "kfac_factors", "shampoo_factors", "solve_schedule", "tile_size", "workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.bakron_solve.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
                                _int, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
     L.bakron_solve.restype = _int
+    L.bakron_solve_noalloc.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32,
+                                       _i32, _i32, _int, _vp, _vp, _i64, _vp, _i64, _vp]
+    L.bakron_solve_noalloc.restype = _int
     L.bakron_solve_timed.argtypes = L.bakron_solve.argtypes + [_vp, _i64]
     L.bakron_solve_timed.restype = _int
     L.bakron_solve_schedule.argtypes = [_int, _i64, _i64, _vp, _i64]
@@ -318,6 +321,40 @@ def solve(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: Alphabe
     if rc != OK:
         raise BakronError(rc, "bakron_solve")
     return (V, Wt) if return_wt else V
+
+
+# Largest workspace bakron_solve_noalloc takes from its in-library scratch
+# (BAKRON_NOALLOC_SCRATCH_BYTES in include/bakron.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def solve_noalloc(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: AlphabetLike,
+                  scales: Optional[torch.Tensor], V: torch.Tensor, Wt: Optional[torch.Tensor] = None,
+                  scale_mode: Optional[int] = None) -> torch.Tensor:
+    """bakron_solve_noalloc: the solve of ``solve`` with the library's own
+    per-GPU scratch instead of a workspace. The caller passes the outputs
+    (V int32 m x n, optional Wt of W's dtype); nothing is allocated. Calls
+    that overlap on one GPU race on the scratch."""
+    dev = _check_device(W, LA, LB, scales, V, Wt)
+    code = _dt(W)
+    m, n = W.shape
+    if LA.shape != (n, n) or LB.shape != (m, m) or LA.dtype != W.dtype or LB.dtype != W.dtype:
+        raise ValueError("LA must be n x n and LB m x m, same dtype as W")
+    lo, hi, unb = (int(alphabet[0]), int(alphabet[1]), int(bool(alphabet[2])))
+    mode = _scale_mode(scales, m, n, scale_mode)
+    if scales is not None and (scales.dtype != W.dtype or not scales.is_contiguous()):
+        raise ValueError("scales must be contiguous with W's dtype")
+    _check_out(V, (m, n), torch.int32, "V")
+    if Wt is not None:
+        _check_out(Wt, (m, n), W.dtype, "Wt")
+    with torch.cuda.device(dev):
+        rc = lib().bakron_solve_noalloc(code, m, n, _p(W), _ld(W, "W"), _p(LA), _ld(LA, "LA"),
+                                        _p(LB), _ld(LB, "LB"), lo, hi, unb, mode, _p(scales),
+                                        _p(V), _ld(V, "V"), _p(Wt),
+                                        _ld(Wt, "Wt") if Wt is not None else 0, _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_solve_noalloc")
+    return V
 
 
 def _batch_operand(t: torch.Tensor, rows: int, cols: int, batch: int, name: str):

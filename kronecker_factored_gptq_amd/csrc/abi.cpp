@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <vector>
 
 #include "bakron.h"
@@ -419,6 +420,38 @@ int loss_impl(int64_t batch, int64_t m, int64_t n, const R* W, int64_t ldw, cons
   return BAKRON_OK;
 }
 
+// ---- no-allocation solve ----------------------------------------------------
+// Scratch of bakron_solve_noalloc: one array per GPU, held by that GPU from
+// the library's load until the process ends. In host code `scratch` names a
+// host-side stand-in, never the device memory: its per-device address comes
+// from hipGetSymbolAddress, taken once per device (with that device current)
+// on the entry point's first call there, and only that address is used.
+static_assert(BAKRON_NOALLOC_SCRATCH_BYTES % kAlign == 0, "scratch size must keep 256-byte alignment");
+static __device__ __align__(256) unsigned char scratch[BAKRON_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (nullptr and *rc set on failure).
+void* device_scratch(int* rc) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = BAKRON_EHIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *rc = BAKRON_EHIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -567,6 +600,26 @@ int bakron_solve(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, co
   return solve_entry(dtype, m, n, W, ldw, LA, ldla, LB, ldlb, alpha_lo, alpha_hi, unbounded,
                      scale_mode, scales, V, ldv, Wt, ldwt, workspace, workspace_bytes, stream,
                      nullptr, 0);
+}
+
+int bakron_solve_noalloc(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
+                         const void* LA, int64_t ldla, const void* LB, int64_t ldlb,
+                         int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded, int scale_mode,
+                         const void* scales, int32_t* V, int64_t ldv, void* Wt, int64_t ldwt,
+                         void* stream) {
+  // the size check comes before any HIP call, so an oversized problem is
+  // rejected without touching the device
+  if (!dtype_ok(dtype) || m < 0 || n < 0) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (m == 0 || n == 0) return BAKRON_OK;
+  const size_t need = bakron_solve_workspace_bytes(dtype, m, n);
+  if (need == 0 || need > (size_t)BAKRON_NOALLOC_SCRATCH_BYTES) return BAKRON_EINVAL;
+  int rc = BAKRON_OK;
+  void* ws = device_scratch(&rc);
+  if (!ws) return rc;
+  return solve_entry(dtype, m, n, W, ldw, LA, ldla, LB, ldlb, alpha_lo, alpha_hi, unbounded,
+                     scale_mode, scales, V, ldv, Wt, ldwt, ws, (size_t)BAKRON_NOALLOC_SCRATCH_BYTES,
+                     stream, nullptr, 0);
 }
 
 int bakron_solve_timed(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw,

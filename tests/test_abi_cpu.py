@@ -260,3 +260,39 @@ def test_schedule_is_algorithm_6_over_blocks_of_tile_antidiagonals(m, n):
     for i, (kind, k, mid, l) in enumerate(ops):
         if kind in (2, 3):
             assert pos[mid - 1] < i < pos[mid]
+
+
+def _noalloc(**kw):
+    a = dict(dtype=bk.F32, m=4, n=4, W=FAKE, ldw=4, LA=FAKE, ldla=4, LB=FAKE, ldlb=4, lo=-8, hi=7,
+             unb=0, mode=0, scales=None, V=FAKE, ldv=4, Wt=None, ldwt=0, stream=None)
+    a.update(kw)
+    return bk.lib().bakron_solve_noalloc(a["dtype"], a["m"], a["n"], a["W"], a["ldw"], a["LA"],
+                                         a["ldla"], a["LB"], a["ldlb"], a["lo"], a["hi"], a["unb"],
+                                         a["mode"], a["scales"], a["V"], a["ldv"], a["Wt"],
+                                         a["ldwt"], a["stream"])
+
+
+@pytest.mark.parametrize("dtype,m,n", [
+    (bk.F32, 2400, 2400),   # a float32 square just over 64 MiB of workspace
+    (bk.F32, 4096, 4096),
+    (bk.F64, 2048, 2048),
+    (bk.F64, 1 << 20, 1),
+])
+def test_noalloc_rejects_sizes_beyond_its_scratch(dtype, m, n):
+    """The size check runs before any HIP call (so it is testable here)."""
+    L = bk.lib()
+    assert L.bakron_solve_workspace_bytes(dtype, m, n) > bk.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(dtype=dtype, m=m, n=n, ldw=n, ldla=n, ldlb=m, ldv=n) == bk.EINVAL
+
+
+def test_noalloc_limit_admits_the_stated_shapes():
+    L = bk.lib()
+    assert L.bakron_solve_workspace_bytes(bk.F32, 2048, 2048) <= bk.NOALLOC_SCRATCH_BYTES
+    assert L.bakron_solve_workspace_bytes(bk.F64, 1024, 2048) <= bk.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_argument_errors_and_empty():
+    assert _noalloc(dtype=5) == bk.EINVAL
+    assert _noalloc(m=-1) == bk.EINVAL
+    assert _noalloc(m=0, W=None, LA=None, LB=None, V=None) == bk.OK
+    assert _noalloc(n=0, W=None, LA=None, LB=None, V=None) == bk.OK
