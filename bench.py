@@ -6,10 +6,14 @@ factor (L^A, L^B) -> per-row scales -> BaKron solve -> loss. The workload is
 the 4096 x 4096 float32 attention-projection matrix (Llama-3-8B shape) with
 synthetic Grams, 4-bit {-8..7} alphabet and per-row absmax/7 scales.
 
-Prints ONE JSON line. `value` = m*n / (time of one whole step), in weights
-quantised per second, from K timed steps run exactly as a caller runs them.
-The roofline object is for the dominant solve kernel, the MFMA band product
-of the large internal nodes: useful flops (Appendix C's restricted band
+Prints ONE JSON line. `value` = m*n / (solve time), in weights quantised per
+second: the quantity of the paper's Table 3 (the solve, excluding the
+factorisation), timed with events around every solve of K timed steps run
+exactly as a caller runs them. The whole step's rate is `step_weights_per_s`.
+`vs_baseline` divides `value` by the paper's own BaKron figure for the same
+shape (Table 3, an RTX PRO 6000: context, not a target).
+The roofline object is for the kernel the metric names, the MFMA band product
+of the internal nodes (the trailing updates): useful flops (Appendix C's restricted band
 products, counted exactly at entry granularity) divided by the kernel's
 durations, measured with HIP events that the dispatch packets of every band
 launch stamp on the library's stream, over K further timed steps of the same
@@ -40,6 +44,11 @@ BAND_TRAFFIC = {"sha256": "c0a15b5aa0079d3d467c0c87ca7c324a6abafac6744f2ff4e95c3
                 "bytes_per_launch": 1.3055e+08, "launches": 84,
                 "summary": "profiles/band_kernel_attn4096_f32_counters.md"}
 METRIC = "weights quantized/s (m·n/solve-time) + % FP32 MFMA peak, 4096×4096"
+
+# The paper's BaKron solve times (Table 3, float32, one RTX PRO 6000, core
+# solver only), seconds by (m, n): the only published figures for this metric.
+PAPER_TABLE3_S = {(4096, 4096): 0.288, (14336, 4096): 1.600, (4096, 14336): 1.717,
+                  (1024, 1024): 0.025, (2048, 2048): 0.074, (8192, 8192): 1.839}
 
 
 def parse():
@@ -97,9 +106,12 @@ def band_traffic(launches: int):
     return BAND_TRAFFIC["bytes_per_launch"] if ok else None
 
 
-def cpu_baseline(p, hi: int):
+def cpu_baseline(p, hi: int, f64: bool):
     """The float64 oracle, as it stands, on the host cores: the same four
-    stages on the same matrix (factor, scales, recursive solve, loss)."""
+    stages on the same matrix (factor, scales, recursive solve, loss), with
+    the factors and scales rounded to the solve's dtype as the GPU path
+    rounds them. Returns (record, the oracle's intermediate results), the
+    latter reused by the parity leg."""
     import numpy as np
     import oracle as O
     try:
@@ -108,16 +120,53 @@ def cpu_baseline(p, hi: int):
                       or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    dt = np.float64 if f64 else np.float32
+    W = p.W.astype(dt)
     t0 = time.perf_counter()
-    LA, _ = O.factor(p.A)
-    LB, _ = O.factor(p.B)
-    s = O.row_scales(p.W, hi, np.float64)
-    r = O.solve_recursive(p.W, LA, LB, p.alphabet, O.SCALE_ROW, s)
-    O.loss(p.W, r.V, p.A, p.B, O.SCALE_ROW, s)
+    LA, dA = O.factor(p.A)
+    LB, dB = O.factor(p.B)
+    LA, LB = LA.astype(dt), LB.astype(dt)
+    s = O.row_scales(W, hi, dt)
+    r = O.solve_recursive(W, LA, LB, p.alphabet, O.SCALE_ROW, s)
+    loss = O.loss(W, r.V, p.A, p.B, O.SCALE_ROW, s)
     t = time.perf_counter() - t0
     m, n = p.W.shape
-    return {"value": m * n / t, "unit": "weights/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the full {m}x{n} workload, one step (factor+scales+recursive solve+loss), float64, {t:.1f} s"}
+    rec = {"value": m * n / t, "unit": "weights/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"the full {m}x{n} workload, one step (factor+scales+recursive solve+loss), "
+                     f"float64 arithmetic, {t:.1f} s", "host_cpu_count": os.cpu_count()}
+    return rec, dict(W=W, LA=LA, LB=LB, dA=dA, dB=dB, s=s, ref=r, loss=loss)
+
+
+def parity_leg(bk, p, o, dev):
+    """GPU vs oracle on the bench matrix: the GPU solve runs on exactly the
+    oracle's inputs (W, the factors and scales in the solve dtype), and its
+    codes are compared with the oracle's solve from the CPU-baseline leg.
+    Reports raw agreement, the replay check (the oracle re-runs recurrence
+    (2) with the GPU's codes imposed: decisions it would not take, counted
+    at gaps >= 1e-6 from a rounding midpoint and > tau_obs = the largest
+    deviation of the GPU's values at rounding from the replayed ones, in
+    code units) and the relative loss difference."""
+    import numpy as np
+    import torch
+    import oracle as O
+    td = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    V, Wt = bk.solve(td(o["W"]), td(o["LA"]), td(o["LB"]), p.alphabet, td(o["s"]), return_wt=True)
+    V, Wt = V.cpu().numpy(), Wt.cpu().numpy()
+    ref = o["ref"]
+    agree = float(np.mean(V == ref.V.astype(np.int32)))
+    rep = O.replay(o["W"], o["LA"], o["LB"], p.alphabet, O.SCALE_ROW, o["s"], V.astype(np.float64))
+    sc = o["s"].astype(np.float64)[:, None]
+    tau_obs = float(np.max(np.abs(Wt.astype(np.float64) - rep.Wt) / sc))
+    l_gpu = O.loss(o["W"], V, p.A, p.B, O.SCALE_ROW, o["s"])
+    return {"agreement": agree, "mismatches": int(np.count_nonzero(V != ref.V.astype(np.int32))),
+            "replay_inconsistent": rep.inconsistent,
+            "replay_inconsistent_at_tau_1e-6": int(np.count_nonzero(rep.gaps >= 1e-6)),
+            "tau_obs": tau_obs,
+            "replay_inconsistent_at_tau_obs": int(np.count_nonzero(rep.gaps > tau_obs)),
+            "replay_max_gap": rep.max_inconsistent_gap,
+            "loss_rel": (l_gpu - o["loss"]) / abs(o["loss"]),
+            "note": "float32: a near-tie flip cascades, so raw agreement below 99.9% is expected "
+                    "at this size; the GPU tests bound the loss by the oracle's own branch spread"}
 
 
 def main():
@@ -172,12 +221,14 @@ def main():
     T = bk.tile_size(code)
     fl = schedule_flops(m, n, T, ops)
     band_idx = [i for i, op in enumerate(ops) if op[0] in (2, 3)]
+    leaf_idx = [i for i, op in enumerate(ops) if op[0] == 0]
     op_ms = (ctypes.c_double * len(ops))()
     timed = not args.no_roofline
     stream = torch.cuda.current_stream(dev)
 
     ev = {k: [] for k in ("t0", "t1", "t2", "t3", "t4")}
     band_ms_steps = []
+    leaf_ms_steps = []
 
     def step(record: bool, per_launch: bool = False):
         es = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
@@ -193,6 +244,7 @@ def main():
                  op_ms=op_ms if per_launch else None)
         if per_launch:
             band_ms_steps.append(sum(op_ms[i] for i in band_idx))
+            leaf_ms_steps.append(sum(op_ms[i] for i in leaf_idx))
         if record:
             es[3].record(stream)
         out = bk.loss(W, V, A, B, s, workspace=wsL, sync=False)
@@ -227,9 +279,12 @@ def main():
     phases = {"factor": phase("t0", "t1"), "scales": phase("t1", "t2"),
               "solve": phase("t2", "t3"), "loss": phase("t3", "t4")}
 
+    solve_ms = phases["solve"]
+    paper_s = PAPER_TABLE3_S.get((m, n))
+    value = m * n / (solve_ms / 1e3)
     result = {
         "metric": METRIC,
-        "value": m * n / (ms_per_step / 1e3),
+        "value": value,
         "unit": "weights/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -237,7 +292,11 @@ def main():
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        "vs_baseline": (value / (m * n / paper_s)) if paper_s else None,
+        "vs_baseline_basis": (f"the paper's Table 3 BaKron time for {m}x{n}, {paper_s} s on an "
+                              "RTX PRO 6000 (float32): other hardware, context only")
+                             if paper_s else None,
+        "step_weights_per_s": m * n / (ms_per_step / 1e3),
         "dtype": args.dtype,
         "data": "synthetic",
         "config": {
@@ -307,14 +366,28 @@ def main():
             "measured_over": f"{args.steps} further timed steps with per-launch events",
             "instrumented_ms_per_step": inst_ms,
         }
+        leaf_ms = float(np.mean(leaf_ms_steps))
+        result["leaf"] = {
+            "kernel": "leaf_kernel (in-block updates + 31-step in-tile sweep)", "bound": "latency",
+            "launches_per_step": len(leaf_idx), "ms_per_step": leaf_ms,
+            "avg_launch_us": leaf_ms * 1e3 / max(len(leaf_idx), 1),
+            "note": "kernel execution time from dispatch-stamped events; the rest of the solve "
+                    "(solve ms - band ms - leaf ms) is the gaps between dependent launches "
+                    "plus the pack kernels"}
         result["trailing_all_nodes"] = {
-            "useful_flop": fl["band"] + fl["small"], "small_node_flop": fl["small"]}
+            "useful_flop": fl["band"] + fl["in_block"], "band_flop": fl["band"],
+            "in_block_flop": fl["in_block"],
+            "note": "updates between tiles: band products of the internal nodes plus the "
+                    "leaves' in-block updates (each carried inner-sum term counted once); "
+                    "the sweeps' in-tile updates are not included"}
     if not args.no_cpu_baseline:
         if args.workload.startswith("mlp_"):
             # the oracle on a full MLP matrix takes minutes; not run here
             result["cpu_baseline"] = None
         else:
-            result["cpu_baseline"] = cpu_baseline(p, hi)
+            rec, o = cpu_baseline(p, hi, f64)
+            result["cpu_baseline"] = rec
+            result["parity"] = parity_leg(bk, p, o, dev)
     print(json.dumps(result))
 
 
@@ -434,8 +507,9 @@ def bench_kv28(args, dev):
     total = nb * m * n
     result = {
         "metric": "weights quantized/s (m·n/solve-time), 28 x (1024x2048)",
-        "value": total / (ms_per_step / 1e3), "unit": "weights/s", "n_gpus": 1,
+        "value": total / (phases["solve"] / 1e3), "unit": "weights/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "step_weights_per_s": total / (ms_per_step / 1e3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "28 k/v projections 1024x2048 float32, Wishart(4096 dof)/4096 A and B "
@@ -451,7 +525,7 @@ def bench_kv28(args, dev):
     }
     if not args.no_cpu_baseline:
         # bounded sample: the oracle on one of the 28 matrices
-        cb = cpu_baseline(probs[0], hi)
+        cb, _ = cpu_baseline(probs[0], hi, False)
         cb["sample"] = "one of the 28 matrices, " + cb["sample"]
         result["cpu_baseline"] = cb
     print(json.dumps(result))

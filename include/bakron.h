@@ -196,11 +196,11 @@ int bakron_solve_noalloc(int dtype, int64_t m, int64_t n,
 int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t *ops, int64_t max_ops);
 
 /* Measurement variant of bakron_solve: same arguments and result, and it
- * also times its band-product launches. For every record i of
- * bakron_solve_schedule with kind 2 or 3, op_ms[i] receives that kernel's
- * execution time in milliseconds, from HIP events stamped by its own
- * dispatch on `stream` (hipExtLaunchKernel start/stop events); every other
- * slot receives -1. `op_ms` is a HOST
+ * also times every leaf and band-product launch. For every record i of
+ * bakron_solve_schedule, op_ms[i] receives that kernel's execution time in
+ * milliseconds, from HIP events stamped by its own dispatch on `stream`
+ * (hipExtLaunchKernel start/stop events; 0 for a launch with no work);
+ * on an error every slot receives -1. `op_ms` is a HOST
  * array of `n_ops` doubles and n_ops must equal the schedule length.
  * SYNCHRONOUS (waits for the last event). Creates and destroys its events;
  * returns BAKRON_EHIP if that fails. */

@@ -132,12 +132,11 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   lp.ldwt = ldwt;
 
   const std::vector<Op> ops = schedule_for(m, n);
-  // optional per-launch timing of the band products (measurement entry point)
+  // optional per-launch timing of every leaf and band launch (measurement
+  // entry point)
   std::vector<hipEvent_t> ev;
   if (op_ms) {
-    size_t nb = 0;
-    for (const Op& op : ops) nb += (op.kind == OP_BAND1 || op.kind == OP_BAND2) ? 1 : 0;
-    ev.assign(2 * nb, nullptr);
+    ev.assign(2 * ops.size(), nullptr);
     for (auto& e : ev)
       if (hipEventCreate(&e) != hipSuccess) {
         for (auto& d : ev)
@@ -149,10 +148,10 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   int rc = BAKRON_OK;
   for (const Op& op : ops) {
     hipError_t e = hipSuccess;
-    const bool timed = op_ms && (op.kind == OP_BAND1 || op.kind == OP_BAND2);
+    const bool timed = op_ms != nullptr;
     hipEvent_t e0 = timed ? ev[evi] : nullptr, e1 = timed ? ev[evi + 1] : nullptr;
     switch (op.kind) {
-      case OP_LEAF: e = launch_leaf<R>(g, op.k, op.mid, Wk, LBp, LAp, Mb, lp, s); break;
+      case OP_LEAF: e = launch_leaf<R>(g, op.k, op.mid, Wk, LBp, LAp, Mb, lp, s, e0, e1); break;
       case OP_BAND1:
         e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, bb, s, e0, e1);
         break;
@@ -166,14 +165,12 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   if (op_ms) {
     if (rc == BAKRON_OK && !ev.empty() && hipEventSynchronize(ev.back()) != hipSuccess)
       rc = BAKRON_EHIP;
-    size_t k = 0;
     for (size_t i = 0; i < ops.size(); ++i) {
       op_ms[i] = -1.0;
-      if (rc == BAKRON_OK && (ops[i].kind == OP_BAND1 || ops[i].kind == OP_BAND2)) {
+      if (rc == BAKRON_OK) {
         float ms = 0.f;
-        if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) != hipSuccess) rc = BAKRON_EHIP;
+        if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) != hipSuccess) rc = BAKRON_EHIP;
         op_ms[i] = ms;
-        k += 2;
       }
     }
     for (auto& d : ev) (void)hipEventDestroy(d);

@@ -50,9 +50,12 @@ struct LeafParams {
 // Leaf for tile anti-diagonal K whose block of tile anti-diagonals starts at K0.
 // Mc (Mt x Nt tiles, the band products' stage-1 buffer, idle inside a block)
 // carries each tile row's partial sums from one leaf of the block to the next.
+// ev0 / ev1 (nullable): events stamped with the kernel's start and end by
+// its dispatch (for measurement).
 template <typename R>
 hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
-                       R* Mc, const LeafParams<R>& lp, hipStream_t s);
+                       R* Mc, const LeafParams<R>& lp, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 
 // Buffers of the band products: W tiles (errors on finished tiles), packed
 // L^B and L^A tiles, and the stage-1 product M.

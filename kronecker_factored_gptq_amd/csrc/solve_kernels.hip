@@ -28,6 +28,8 @@
 // (code units), which is what the band products read. The scaled L^A, L^B as
 // packed lower-triangular tile arrays (tile (P,I), I <= P, at P(P+1)/2 + I),
 // unit diagonal, zero above it and on padding.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "device.hpp"
@@ -522,14 +524,24 @@ static inline void diag_range(const SolveGeom& g, int K, int* lo, int* hi) {
 
 template <typename R>
 hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
-                       R* Mc, const LeafParams<R>& lp, hipStream_t s) {
+                       R* Mc, const LeafParams<R>& lp, hipStream_t s, hipEvent_t ev0,
+                       hipEvent_t ev1) {
   static_assert(kTile == 16, "the leaf kernel works on 16 x 16 tiles");
   int lo, hi;
   diag_range(g, K, &lo, &hi);
-  if (hi < lo) return hipSuccess;
-  if (g.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL((leaf_kernel<R>), dim3(hi - lo + 1, g.batch), dim3(64 * kLeafWaves), 0, s,
-                     K, K0, g.Mt, g.Nt, g.m, g.n, Wk, LBp, LAp, Mc, lp, g.bs);
+  if (hi < lo || g.batch <= 0) {
+    // nothing to do; keep the timing events valid (zero duration)
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return hipErrorUnknown;
+    if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return hipErrorUnknown;
+    return hipSuccess;
+  }
+  const dim3 grid(hi - lo + 1, g.batch), block(64 * kLeafWaves);
+  if (ev0 || ev1)  // the events are stamped by the dispatch packet itself
+    hipExtLaunchKernelGGL((leaf_kernel<R>), grid, block, 0, s, ev0, ev1, 0, K, K0, g.Mt, g.Nt,
+                          g.m, g.n, Wk, LBp, LAp, Mc, lp, g.bs);
+  else
+    hipLaunchKernelGGL((leaf_kernel<R>), grid, block, 0, s, K, K0, g.Mt, g.Nt, g.m, g.n, Wk, LBp,
+                       LAp, Mc, lp, g.bs);
   return hipGetLastError();
 }
 
@@ -539,7 +551,7 @@ hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, c
   template hipError_t launch_pack_l<R>(const SolveGeom&, bool, const R*, int64_t, const R*, R*, \
                                        hipStream_t);                                            \
   template hipError_t launch_leaf<R>(const SolveGeom&, int, int, R*, const R*, const R*, R*,    \
-                                     const LeafParams<R>&, hipStream_t);
+                                     const LeafParams<R>&, hipStream_t, hipEvent_t, hipEvent_t);
 BK_INST(float)
 BK_INST(double)
 #undef BK_INST

@@ -75,25 +75,69 @@ def node_useful_flops(m: int, n: int, T: int, k: int, mid: int, l: int) -> Tuple
     return 2 * s1, 2 * s2
 
 
+def in_block_useful_flops(m: int, n: int, T: int, K0: int, K1: int) -> Tuple[int, int]:
+    """(stage-1 flops, stage-2 flops) of the updates between the tiles of one
+    leaf block, tile anti-diagonals [K0, K1), as the leaves compute them
+    (left-looking, with each row's inner sums carried from leaf to leaf):
+        M[P, J]  = sum_I L^B[P, I] E[I, J]     over block tiles (I, J), I <= P
+        W[P, Q] += sum_J M[P, J] L^A[Q, J]^T   for every block tile (P, Q),
+    where target (P, Q) takes only errors of the tiles before it
+    ((I, J) != (P, Q), I <= P, J <= Q). Every inner-sum term (P, I, J) is
+    counted ONCE, whatever number of later leaves reads the carried sum,
+    and only if some target reads it; triangular zeros of the diagonal
+    tiles and tile padding are not counted (entry granularity)."""
+    Mt, Nt = -(-m // T), -(-n // T)
+    rows = _tile_sizes(m, T)
+    cols = _tile_sizes(n, T)
+    s1 = s2 = 0
+    for P in range(Mt):
+        rp = int(rows[P])
+        tri = rp * (rp + 1) // 2
+        Qlo, Qhi = max(K0 - P, 0), min(K1 - 1 - P, Nt - 1)
+        # stage 1: source tiles (I, J) of the block with I <= P
+        for J in range(0, min(K1 - 1, Nt - 1) + 1):
+            Ilo, Ihi = max(K0 - J, 0), min(P, K1 - 1 - J, Mt - 1)
+            if Ilo > Ihi:
+                continue
+            cj = int(cols[J])
+            for I in range(Ilo, Ihi + 1):
+                if I < P:
+                    if P + J <= K1 - 1:          # target (P, J) reads it
+                        s1 += rp * int(rows[I]) * cj
+                elif J + 1 <= Nt - 1 and P + J + 1 <= K1 - 1:  # I == P: targets (P, Q > J)
+                    s1 += tri * cj
+        # stage 2: targets (P, Q) of the block
+        for Q in range(Qlo, Qhi + 1):
+            cq = int(cols[Q])
+            for J in range(0, Q):
+                if P + J >= K0:                  # some (I <= P, J) lies in the block
+                    s2 += rp * cq * int(cols[J])
+            if P >= 1 and P - 1 + Q >= K0:       # J == Q: sources (I < P, Q)
+                s2 += rp * (cq * (cq + 1) // 2)
+    return 2 * s1, 2 * s2
+
+
 def schedule_flops(m: int, n: int, T: int, ops: Iterable[Tuple[int, int, int, int]]
                    ) -> Dict[str, int]:
     """Useful flops of the updates between tiles in a solve schedule: kinds
-    2 and 3 are the two band products of an internal node; a leaf (kind 0)
-    of tile anti-diagonal K in a block starting at K0 applies the updates
-    from [K0, K) to K, counted as the node [K0, K) -> [K, K+1) ("small").
-    Returns totals and per-op values."""
-    out = {"small": 0, "band": 0, "band_stage1": 0, "band_stage2": 0, "per_op": []}
+    2 and 3 are the two band products of an internal node; the leaves
+    (kind 0) of one block of tile anti-diagonals [K0, K1) together apply the
+    block's in-block updates (``in_block_useful_flops``), reported as
+    "in_block" and attributed to the block's first leaf in ``per_op``."""
+    ops = list(ops)
+    out = {"in_block": 0, "band": 0, "band_stage1": 0, "band_stage2": 0, "per_op": []}
+    block_end: Dict[int, int] = {}
     for (kind, k, mid, l) in ops:
         if kind == 0:
-            f = sum(node_useful_flops(m, n, T, mid, k, k + 1)) if k > mid else 0
-            out["small"] += f
+            block_end[mid] = max(block_end.get(mid, mid), k + 1)
+    for (kind, k, mid, l) in ops:
+        if kind == 0:
+            f = sum(in_block_useful_flops(m, n, T, mid, block_end[mid])) if k == mid else 0
+            out["in_block"] += f
             out["per_op"].append(f)
             continue
         f1, f2 = node_useful_flops(m, n, T, k, mid, l)
-        if kind == 1:
-            out["small"] += f1 + f2
-            out["per_op"].append(f1 + f2)
-        elif kind == 2:
+        if kind == 2:
             out["band"] += f1
             out["band_stage1"] += f1
             out["per_op"].append(f1)

@@ -262,3 +262,23 @@ def test_fp64_bit_exact_random_shapes(gpu_lib):
         V, _ = gpu_solve(gpu_lib, inp, return_wt=False)
         ref = oracle_solve(inp, naive=(m * n <= 2000))
         assert np.array_equal(V, ref.V.astype(np.int32)), (case, m, n, al, rule)
+
+
+def test_timed_solve_equals_solve_and_times_every_launch(gpu_lib):
+    """bakron_solve_timed: the same codes as bakron_solve, and a non-negative
+    kernel time for every record of the schedule (leaves and band products)."""
+    import ctypes
+    bk = gpu_lib
+    p = random_problem(700, 500, "f32", seed=9, w_std=0.02, heavy_tail=True, samples_factor=2)
+    inp = prepare(p.W, p.A, p.B, "f32", (-8, 7, 0), "row", 7)
+    W, LA, LB, s = to_dev(inp.W), to_dev(inp.LA), to_dev(inp.LB), to_dev(inp.s)
+    V0 = bk.solve(W, LA, LB, (-8, 7, 0), s)
+    ops = bk.solve_schedule(bk.F32, 700, 500)
+    op_ms = (ctypes.c_double * len(ops))(*([-5.0] * len(ops)))
+    V1 = bk.solve(W, LA, LB, (-8, 7, 0), s, op_ms=op_ms)
+    torch.cuda.synchronize()
+    assert torch.equal(V0, V1)
+    t = list(op_ms)
+    assert all(x >= 0.0 for x in t), t
+    assert sum(x > 0.0 for x in t) >= len([o for o in ops if o[0] == 0])  # every leaf has work
+    assert sum(t) < 1000.0
