@@ -161,6 +161,27 @@ int bakron_solve(int dtype, int64_t m, int64_t n,
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * BaKron-antidiagonal: Algorithm 3 (§3.3) on the whole matrix, the solver
+ * the paper compares BaKron with (§6 Table 3; equivalent to YAQA). For each
+ * anti-diagonal i + j = k in turn, every entry on it is rounded at once and
+ * the errors are applied to all later entries as one rank-d product
+ * (Appendix C: O(m^2 n^2) total work, m + n - 1 sequential steps). Same
+ * arguments, codes (Theorem 3.2: all four algorithms give the same V),
+ * values at rounding and asynchrony as bakron_solve; its own workspace
+ * (bakron_solve_antidiag_workspace_bytes). One kernel launch per
+ * anti-diagonal.
+ * ------------------------------------------------------------------------ */
+size_t bakron_solve_antidiag_workspace_bytes(int dtype, int64_t m, int64_t n);
+int bakron_solve_antidiag(int dtype, int64_t m, int64_t n,
+                          const void *W, int64_t ldw,
+                          const void *LA, int64_t ldla, const void *LB, int64_t ldlb,
+                          int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded,
+                          int scale_mode, const void *scales,
+                          int32_t *V, int64_t ldv,
+                          void *Wt, int64_t ldwt,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * No-allocation solve, for callers that cannot allocate device memory or
  * pass a workspace: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc. Same arguments, result and asynchrony as

@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["F32", "F64", "SCALE_NONE", "SCALE_ROW", "SCALE_COL", "BakronError", "lib", "factor",
            "factor_batched",
-           "solve", "solve_noalloc", "solve_batched", "loss", "loss_batched", "row_scales", "row_scales_mse", "gram",
+           "solve", "solve_antidiag", "solve_noalloc", "solve_batched", "loss", "loss_batched", "row_scales", "row_scales_mse", "gram",
            "sample_sqnorms", "kfac_factors", "shampoo_factors", "solve_schedule", "tile_size", "workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
     L.bakron_solve.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
                                _int, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
     L.bakron_solve.restype = _int
+    L.bakron_solve_antidiag_workspace_bytes.argtypes = [_int, _i64, _i64]
+    L.bakron_solve_antidiag_workspace_bytes.restype = _sz
+    L.bakron_solve_antidiag.argtypes = L.bakron_solve.argtypes
+    L.bakron_solve_antidiag.restype = _int
     L.bakron_solve_noalloc.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32,
                                        _i32, _i32, _int, _vp, _vp, _i64, _vp, _i64, _vp]
     L.bakron_solve_noalloc.restype = _int
@@ -320,6 +324,39 @@ def solve(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: Alphabe
             rc = L.bakron_solve_timed(*args, ctypes.cast(op_ms, ctypes.c_void_p), len(op_ms))
     if rc != OK:
         raise BakronError(rc, "bakron_solve")
+    return (V, Wt) if return_wt else V
+
+
+def solve_antidiag(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor,
+                   alphabet: AlphabetLike = (0, 0, 1), scales: Optional[torch.Tensor] = None,
+                   scale_mode: Optional[int] = None, return_wt: bool = False,
+                   workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """BaKron-antidiagonal (§3.3 Algorithm 3 on the whole matrix, one launch
+    per anti-diagonal): the same codes as ``solve`` (Theorem 3.2) with
+    O(m^2 n^2) work, the paper's point of comparison. Arguments and results
+    as for ``solve``. Asynchronous on the current stream."""
+    dev = _check_device(W, LA, LB, scales, workspace, out)
+    code = _dt(W)
+    m, n = W.shape
+    if LA.shape != (n, n) or LB.shape != (m, m) or LA.dtype != W.dtype or LB.dtype != W.dtype:
+        raise ValueError("LA must be n x n and LB m x m, same dtype as W")
+    lo, hi, unb = (int(alphabet[0]), int(alphabet[1]), int(bool(alphabet[2])))
+    mode = _scale_mode(scales, m, n, scale_mode)
+    if scales is not None and (scales.dtype != W.dtype or not scales.is_contiguous()):
+        raise ValueError("scales must be contiguous with W's dtype")
+    if out is not None:
+        _check_out(out, (m, n), torch.int32, "out")
+    V = out if out is not None else torch.empty((m, n), dtype=torch.int32, device=dev)
+    Wt = torch.empty((m, n), dtype=W.dtype, device=dev) if return_wt else None
+    L = lib()
+    ws = _workspace(L.bakron_solve_antidiag_workspace_bytes(code, m, n), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.bakron_solve_antidiag(code, m, n, _p(W), _ld(W, "W"), _p(LA), _ld(LA, "LA"), _p(LB),
+                                     _ld(LB, "LB"), lo, hi, unb, mode, _p(scales), _p(V),
+                                     _ld(V, "V"), _p(Wt), _ld(Wt, "Wt") if Wt is not None else 0,
+                                     _p(ws), ws.numel() * ws.element_size(), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_solve_antidiag")
     return (V, Wt) if return_wt else V
 
 

@@ -21,7 +21,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libbakron.so")
 
 SOURCES = ["abi.cpp", "solve_kernels.hip", "band_kernels.hip", "factor_kernels.hip", "gemm64.hip", "loss_kernels.hip",
-           "scale_kernels.hip", "gram_kernels.hip"]
+           "scale_kernels.hip", "gram_kernels.hip", "antidiag_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -38,7 +38,8 @@ COMMON = [
 # reads its accumulator every in-tile step, and accumulation registers would
 # need a copy per read; measured slightly faster for the band products too)
 EXTRA = {"solve_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "band_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "band_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "antidiag_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

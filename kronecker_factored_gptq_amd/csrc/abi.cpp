@@ -631,6 +631,53 @@ int bakron_solve_timed(int dtype, int64_t m, int64_t n, const void* W, int64_t l
                      op_ms, n_ops);
 }
 
+size_t bakron_solve_antidiag_workspace_bytes(int dtype, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0) return 0;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return 0;
+  return antidiag_layout(esize(dtype), m, n).total;
+}
+
+int bakron_solve_antidiag(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
+                          const void* LA, int64_t ldla, const void* LB, int64_t ldlb,
+                          int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded, int scale_mode,
+                          const void* scales, int32_t* V, int64_t ldv, void* Wt, int64_t ldwt,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (m == 0 || n == 0) return BAKRON_OK;
+  if (!W || !LA || !LB || !V) return BAKRON_EINVAL;
+  if (ldw < n || ldla < n || ldlb < m || ldv < n) return BAKRON_EINVAL;
+  if (Wt && ldwt < n) return BAKRON_EINVAL;
+  if (!unbounded && alpha_lo > alpha_hi) return BAKRON_EINVAL;
+  if (scale_mode == BAKRON_SCALE_NONE) {
+    if (scales) return BAKRON_EINVAL;
+  } else if (scale_mode == BAKRON_SCALE_ROW || scale_mode == BAKRON_SCALE_COL) {
+    if (!scales) return BAKRON_EINVAL;
+  } else {
+    return BAKRON_EINVAL;
+  }
+  if (!workspace || workspace_bytes < bakron_solve_antidiag_workspace_bytes(dtype, m, n))
+    return BAKRON_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == BAKRON_F32) {
+    const float lo = unbounded ? -std::numeric_limits<float>::infinity() : (float)alpha_lo;
+    const float hi = unbounded ? std::numeric_limits<float>::infinity() : (float)alpha_hi;
+    e = launch_antidiag_solve<float>(m, n, (const float*)W, ldw, (const float*)LA, ldla,
+                                     (const float*)LB, ldlb, lo, hi, scale_mode,
+                                     (const float*)scales, V, ldv, (float*)Wt, ldwt, workspace, s);
+  } else {
+    const double lo = unbounded ? -std::numeric_limits<double>::infinity() : (double)alpha_lo;
+    const double hi = unbounded ? std::numeric_limits<double>::infinity() : (double)alpha_hi;
+    e = launch_antidiag_solve<double>(m, n, (const double*)W, ldw, (const double*)LA, ldla,
+                                      (const double*)LB, ldlb, lo, hi, scale_mode,
+                                      (const double*)scales, V, ldv, (double*)Wt, ldwt, workspace,
+                                      s);
+  }
+  return e == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
+}
+
 size_t bakron_solve_batched_workspace_bytes(int dtype, int64_t batch, int64_t m, int64_t n) {
   if (!dtype_ok(dtype) || batch < 0 || m < 0 || n < 0) return 0;
   const size_t one = solve_layout(dtype, m, n).total;

@@ -76,6 +76,37 @@ hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage
 // Tile anti-diagonals per leaf block (updates inside a block are left-looking).
 constexpr int kLeafBlock = 12;
 
+// ---- BaKron-antidiagonal (antidiag_kernels.hip) ----------------------------
+// Workspace of the whole-matrix anti-diagonal solver (element size es): U
+// (Mp x Np), the transposed factors LBt (m x Mp) and LAt (n x Np), and two
+// error vectors of min(m, n) entries; Mp, Np = m, n rounded up to 64.
+struct AntidiagLayout {
+  int64_t Mp, Np;
+  size_t u, lbt, lat, d0, d1, total;
+};
+inline AntidiagLayout antidiag_layout(size_t es, int64_t m, int64_t n) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  AntidiagLayout L;
+  L.Mp = (m + 63) / 64 * 64;
+  L.Np = (n + 63) / 64 * 64;
+  const int64_t r = m < n ? m : n;
+  L.u = 0;
+  L.lbt = L.u + al((size_t)(L.Mp * L.Np) * es);
+  L.lat = L.lbt + al((size_t)(m * L.Mp) * es);
+  L.d0 = L.lat + al((size_t)(n * L.Np) * es);
+  L.d1 = L.d0 + al((size_t)(r + 64) * es);
+  L.total = L.d1 + al((size_t)(r + 64) * es) + 256;
+  return L;
+}
+// Algorithm 3 on the whole matrix: pack, then one launch per anti-diagonal
+// (m + n - 1 launches) on stream s. lo / hi: +-infinity for the unbounded
+// alphabet.
+template <typename R>
+hipError_t launch_antidiag_solve(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA,
+                                 int64_t ldla, const R* LB, int64_t ldlb, R lo, R hi,
+                                 int scale_mode, const R* scales, int32_t* V, int64_t ldv, R* Wt,
+                                 int64_t ldwt, void* ws, hipStream_t s);
+
 // ---- factor (factor_kernels.hip), always float64 inside --------------------
 // X = J A J for `batch` matrices: A + z * sA -> X + z * sX (elements).
 template <typename R>

@@ -296,3 +296,32 @@ def test_noalloc_argument_errors_and_empty():
     assert _noalloc(m=-1) == bk.EINVAL
     assert _noalloc(m=0, W=None, LA=None, LB=None, V=None) == bk.OK
     assert _noalloc(n=0, W=None, LA=None, LB=None, V=None) == bk.OK
+
+
+def _antidiag(**kw):
+    a = dict(dtype=bk.F32, m=4, n=4, W=FAKE, ldw=4, LA=FAKE, ldla=4, LB=FAKE, ldlb=4, lo=-8, hi=7,
+             unb=0, mode=0, scales=None, V=FAKE, ldv=4, Wt=None, ldwt=0, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    return bk.lib().bakron_solve_antidiag(a["dtype"], a["m"], a["n"], a["W"], a["ldw"], a["LA"],
+                                          a["ldla"], a["LB"], a["ldlb"], a["lo"], a["hi"], a["unb"],
+                                          a["mode"], a["scales"], a["V"], a["ldv"], a["Wt"],
+                                          a["ldwt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(dtype=5), dict(m=-1), dict(W=None), dict(LA=None), dict(V=None), dict(ldw=3),
+    dict(ldla=2), dict(ldlb=3), dict(ldv=1), dict(lo=3, hi=2), dict(mode=1, scales=None),
+    dict(mode=0, scales=FAKE), dict(mode=9), dict(ws=None), dict(wsb=16),
+    dict(ws=ctypes.c_void_p(0x1001)), dict(Wt=FAKE, ldwt=2),
+])
+def test_antidiag_rejects_bad_arguments(bad):
+    assert _antidiag(**bad) == bk.EINVAL
+
+
+def test_antidiag_empty_is_noop_and_workspace_grows():
+    assert _antidiag(m=0, W=None, LA=None, LB=None, V=None, ws=None) == bk.OK
+    L = bk.lib()
+    assert 0 < L.bakron_solve_antidiag_workspace_bytes(bk.F32, 64, 64) < \
+        L.bakron_solve_antidiag_workspace_bytes(bk.F32, 512, 512) < \
+        L.bakron_solve_antidiag_workspace_bytes(bk.F64, 512, 512)
