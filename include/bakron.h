@@ -300,6 +300,63 @@ int bakron_loss_batched(int dtype, int64_t batch, int64_t m, int64_t n,
                         double *loss, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Block-diagonal output factor (Appendix D, experimental setup: the
+ * attention-local Hessians of the query, key and value projections, whose
+ * per-head output-side Grams are assembled into one block-diagonal matrix
+ * over the whole projection; Table 4). B = blockdiag(B_0, ..., B_{h-1}),
+ * `heads` = h blocks of order b = m / h (m % h == 0). B^-1 and its Cholesky
+ * factor are then block-diagonal, an error reaches only rows of its own
+ * block, and the problem splits exactly into h problems of b x n sharing
+ * L^A: the calls below run all heads in the same launches (the batched
+ * machinery), never touching the zero blocks. Results equal the dense calls
+ * on the assembled block-diagonal B (codes, in exact arithmetic; float64
+ * codes bit for bit in the tests).
+ *
+ * Block h of B is at B + h * stride_b (b x b, ldb >= b; lower triangle
+ * read); block h of L^B at LB + h * stride_lb (stride_lb >= (b-1) ldlb + b);
+ * dB (nullable) is length m, block h at dB + h * b.
+ *
+ * bakron_factor_blockdiag: L^A (n x n) and dA as bakron_factor, and the h
+ * blocks of L^B, each the normalised Cholesky(B_h^-1). bad_pivot (HOST
+ * int64[3], nullable): on BAKRON_ENOTSPD {side, block, index} (side 0 = A
+ * with block -1, side 1 = B), index as for bakron_factor; else {-1,-1,-1}.
+ * SYNCHRONOUS.
+ * bakron_solve_blockdiag: the solve of bakron_solve with L^B given by its
+ * blocks; W, V, Wt, scales as for bakron_solve (row scales length m, column
+ * scales length n). Asynchronous.
+ * bakron_loss_blockdiag: tr(B (W - Q) A (W - Q)^T) = sum_h tr(B_h D_h A
+ * D_h^T) in float64 (the per-head sums added in head order); *loss is a
+ * DEVICE double. Asynchronous.
+ * 1 <= heads <= 32767.
+ * ------------------------------------------------------------------------ */
+size_t bakron_factor_blockdiag_workspace_bytes(int dtype, int64_t heads, int64_t m, int64_t n);
+int bakron_factor_blockdiag(int dtype, int64_t heads, int64_t m, int64_t n,
+                            const void *A, int64_t lda,
+                            const void *B, int64_t ldb, int64_t stride_b,
+                            void *LA, int64_t ldla,
+                            void *LB, int64_t ldlb, int64_t stride_lb,
+                            void *dA, void *dB,
+                            void *workspace, size_t workspace_bytes,
+                            int64_t *bad_pivot, void *stream);
+size_t bakron_solve_blockdiag_workspace_bytes(int dtype, int64_t heads, int64_t m, int64_t n);
+int bakron_solve_blockdiag(int dtype, int64_t heads, int64_t m, int64_t n,
+                           const void *W, int64_t ldw,
+                           const void *LA, int64_t ldla,
+                           const void *LB, int64_t ldlb, int64_t stride_lb,
+                           int32_t alpha_lo, int32_t alpha_hi, int32_t unbounded,
+                           int scale_mode, const void *scales,
+                           int32_t *V, int64_t ldv,
+                           void *Wt, int64_t ldwt,
+                           void *workspace, size_t workspace_bytes, void *stream);
+size_t bakron_loss_blockdiag_workspace_bytes(int dtype, int64_t heads, int64_t m, int64_t n);
+int bakron_loss_blockdiag(int dtype, int64_t heads, int64_t m, int64_t n,
+                          const void *W, int64_t ldw, const int32_t *V, int64_t ldv,
+                          int scale_mode, const void *scales,
+                          const void *A, int64_t lda,
+                          const void *B, int64_t ldb, int64_t stride_b,
+                          double *loss, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Per-row scales: s_i = max_j |W_ij| / hi (1 for an all-zero row), the
  * per-output-feature absmax rule of Appendix D with hi the largest code
  * (7 for {-8..7}, 3 for {-4..3}). Computed in `dtype`.

@@ -19,7 +19,8 @@ import torch
 
 __all__ = ["F32", "F64", "SCALE_NONE", "SCALE_ROW", "SCALE_COL", "BakronError", "lib", "factor",
            "factor_batched",
-           "solve", "solve_antidiag", "solve_noalloc", "solve_batched", "loss", "loss_batched", "row_scales", "row_scales_mse", "gram",
+           "solve", "solve_antidiag", "solve_noalloc", "factor_blockdiag", "solve_blockdiag",
+           "loss_blockdiag", "solve_batched", "loss", "loss_batched", "row_scales", "row_scales_mse", "gram",
            "sample_sqnorms", "kfac_factors", "shampoo_factors", "solve_schedule", "tile_size", "workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +72,22 @@ def lib() -> ctypes.CDLL:
     L.bakron_solve.argtypes = [_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
                                _int, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
     L.bakron_solve.restype = _int
+    for name in ("bakron_factor_blockdiag_workspace_bytes", "bakron_solve_blockdiag_workspace_bytes",
+                 "bakron_loss_blockdiag_workspace_bytes"):
+        f = getattr(L, name)
+        f.argtypes = [_int, _i64, _i64, _i64]
+        f.restype = _sz
+    L.bakron_factor_blockdiag.argtypes = [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp,
+                                          _i64, _vp, _i64, _i64, _vp, _vp, _vp, _sz,
+                                          ctypes.POINTER(_i64), _vp]
+    L.bakron_factor_blockdiag.restype = _int
+    L.bakron_solve_blockdiag.argtypes = [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                         _i64, _i32, _i32, _i32, _int, _vp, _vp, _i64, _vp, _i64,
+                                         _vp, _sz, _vp]
+    L.bakron_solve_blockdiag.restype = _int
+    L.bakron_loss_blockdiag.argtypes = [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp,
+                                        _vp, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp]
+    L.bakron_loss_blockdiag.restype = _int
     L.bakron_solve_antidiag_workspace_bytes.argtypes = [_int, _i64, _i64]
     L.bakron_solve_antidiag_workspace_bytes.restype = _sz
     L.bakron_solve_antidiag.argtypes = L.bakron_solve.argtypes
@@ -358,6 +375,111 @@ def solve_antidiag(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor,
     if rc != OK:
         raise BakronError(rc, "bakron_solve_antidiag")
     return (V, Wt) if return_wt else V
+
+
+def _blocks(t: torch.Tensor, heads: int, b: int, name: str):
+    """(pointer, ld, stride) of h square blocks given as a (heads, b, b) tensor."""
+    if t.dim() != 3 or t.shape != (heads, b, b):
+        raise ValueError(f"{name} must be ({heads}, {b}, {b})")
+    if b > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    ld = max(int(t.stride(1)), b, 1)
+    return _p(t), ld, int(t.stride(0)) if heads > 1 else 0
+
+
+def factor_blockdiag(A: torch.Tensor, Bblocks: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """L^A of A (n x n) and the normalised Cholesky(B_h^-1) of every block of
+    a block-diagonal output factor B = blockdiag(Bblocks[h]) (Bblocks is
+    (heads, b, b)). Returns LA (n x n), LB blocks (heads, b, b), dA (n),
+    dB (heads * b). Synchronous. BakronError.bad_pivot = (side, block, index)."""
+    dev = _check_device(A, Bblocks, workspace)
+    code = _dt(A)
+    if Bblocks.dtype != A.dtype:
+        raise TypeError("A and the B blocks must have the same dtype")
+    n = A.size(0)
+    if A.shape != (n, n) or Bblocks.dim() != 3:
+        raise ValueError("A must be n x n and Bblocks (heads, b, b)")
+    heads, b = Bblocks.size(0), Bblocks.size(1)
+    pb, ldb, sb = _blocks(Bblocks, heads, b, "Bblocks")
+    LA = torch.empty((n, n), dtype=A.dtype, device=dev)
+    LB = torch.empty((heads, b, b), dtype=A.dtype, device=dev)
+    dA = torch.empty(n, dtype=A.dtype, device=dev)
+    dB = torch.empty(heads * b, dtype=A.dtype, device=dev)
+    L = lib()
+    ws = _workspace(L.bakron_factor_blockdiag_workspace_bytes(code, heads, heads * b, n), dev, workspace)
+    bad = (_i64 * 3)(-1, -1, -1)
+    with torch.cuda.device(dev):
+        rc = L.bakron_factor_blockdiag(code, heads, heads * b, n, _p(A), _ld(A, "A"), pb, ldb, sb,
+                                       _p(LA), max(n, 1), _p(LB), max(b, 1), b * b, _p(dA), _p(dB),
+                                       _p(ws), ws.numel() * ws.element_size(), bad, _stream(dev))
+    if rc != OK:
+        err = BakronError(rc, "bakron_factor_blockdiag")
+        err.bad_pivot = (int(bad[0]), int(bad[1]), int(bad[2]))
+        raise err
+    return LA, LB, dA, dB
+
+
+def solve_blockdiag(W: torch.Tensor, LA: torch.Tensor, LBblocks: torch.Tensor,
+                    alphabet: AlphabetLike = (0, 0, 1), scales: Optional[torch.Tensor] = None,
+                    scale_mode: Optional[int] = None, return_wt: bool = False,
+                    workspace: Optional[torch.Tensor] = None):
+    """The BaKron solve with a block-diagonal L^B given by its blocks
+    (heads, b, b), m = heads * b: all heads in the same launches."""
+    dev = _check_device(W, LA, LBblocks, scales, workspace)
+    code = _dt(W)
+    m, n = W.shape
+    if LBblocks.dim() != 3 or LBblocks.size(0) * LBblocks.size(1) != m:
+        raise ValueError("LBblocks must be (heads, b, b) with heads * b = m")
+    heads, b = LBblocks.size(0), LBblocks.size(1)
+    if LA.shape != (n, n) or LA.dtype != W.dtype or LBblocks.dtype != W.dtype:
+        raise ValueError("LA must be n x n, all of W's dtype")
+    plb, ldlb, slb = _blocks(LBblocks, heads, b, "LBblocks")
+    lo, hi, unb = (int(alphabet[0]), int(alphabet[1]), int(bool(alphabet[2])))
+    mode = _scale_mode(scales, m, n, scale_mode)
+    if scales is not None and (scales.dtype != W.dtype or not scales.is_contiguous()):
+        raise ValueError("scales must be contiguous with W's dtype")
+    V = torch.empty((m, n), dtype=torch.int32, device=dev)
+    Wt = torch.empty((m, n), dtype=W.dtype, device=dev) if return_wt else None
+    L = lib()
+    ws = _workspace(L.bakron_solve_blockdiag_workspace_bytes(code, heads, m, n), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.bakron_solve_blockdiag(code, heads, m, n, _p(W), _ld(W, "W"), _p(LA), _ld(LA, "LA"),
+                                      plb, ldlb, slb, lo, hi, unb, mode, _p(scales), _p(V),
+                                      _ld(V, "V"), _p(Wt), _ld(Wt, "Wt") if Wt is not None else 0,
+                                      _p(ws), ws.numel() * ws.element_size(), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_solve_blockdiag")
+    return (V, Wt) if return_wt else V
+
+
+def loss_blockdiag(W: torch.Tensor, V: torch.Tensor, A: torch.Tensor, Bblocks: torch.Tensor,
+                   scales: Optional[torch.Tensor] = None, scale_mode: Optional[int] = None,
+                   workspace: Optional[torch.Tensor] = None, sync: bool = True):
+    """tr(B (W - s V) A (W - s V)^T) for B = blockdiag(Bblocks[h]), in float64."""
+    dev = _check_device(W, V, A, Bblocks, scales, workspace)
+    code = _dt(W)
+    m, n = W.shape
+    if Bblocks.dim() != 3 or Bblocks.size(0) * Bblocks.size(1) != m:
+        raise ValueError("Bblocks must be (heads, b, b) with heads * b = m")
+    heads, b = Bblocks.size(0), Bblocks.size(1)
+    _check_operand(V, (m, n), torch.int32, "V")
+    _check_operand(A, (n, n), W.dtype, "A")
+    if Bblocks.dtype != W.dtype:
+        raise TypeError("Bblocks must have W's dtype")
+    pb, ldb, sb = _blocks(Bblocks, heads, b, "Bblocks")
+    mode = _scale_mode(scales, m, n, scale_mode)
+    if scales is not None and (scales.dtype != W.dtype or not scales.is_contiguous()):
+        raise ValueError("scales must be contiguous with W's dtype")
+    out = torch.zeros(1, dtype=torch.float64, device=dev)
+    L = lib()
+    ws = _workspace(L.bakron_loss_blockdiag_workspace_bytes(code, heads, m, n), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.bakron_loss_blockdiag(code, heads, m, n, _p(W), _ld(W, "W"), _p(V), _ld(V, "V"), mode,
+                                     _p(scales), _p(A), _ld(A, "A"), pb, ldb, sb, _p(out), _p(ws),
+                                     ws.numel() * ws.element_size(), _stream(dev))
+    if rc != OK:
+        raise BakronError(rc, "bakron_loss_blockdiag")
+    return float(out.item()) if sync else out
 
 
 # Largest workspace bakron_solve_noalloc takes from its in-library scratch

@@ -374,22 +374,36 @@ struct LossStrides {
 
 // Loss of `batch` problems; workspace regions are batch copies of the
 // single-problem layout's regions.
+// Workspace of `batch` losses of one shape: the float64 copies of A (one
+// when every problem shares A, share_a), of B, D = W - s V and D A per
+// problem, and the per-problem partial sums.
+size_t loss_ws_bytes(int64_t batch, int64_t m, int64_t n, bool share_a) {
+  const LossLayout lay = loss_layout(m, n);
+  const size_t nb = (size_t)batch;
+  return (share_a ? 1 : nb) * lay.a + nb * (lay.b + lay.d + lay.be + lay.part) + kAlign;
+}
+
 template <typename R>
 int loss_impl(int64_t batch, int64_t m, int64_t n, const R* W, int64_t ldw, const int32_t* V,
               int64_t ldv, int scale_mode, const R* scales, const R* A, int64_t lda, const R* B,
               int64_t ldb, const LossStrides& st, double* loss, void* ws, hipStream_t s) {
   const LossLayout lay = loss_layout(m, n);
   const size_t nb = (size_t)batch;
+  // a shared A (stride 0) is converted once and read by every problem
+  const bool share_a = st.a == 0;
+  const size_t na = share_a ? 1 : nb;
   char* base = static_cast<char*>(ws);
   double* A64 = reinterpret_cast<double*>(base);
-  double* B64 = reinterpret_cast<double*>(base + nb * lay.a);
-  double* D = reinterpret_cast<double*>(base + nb * (lay.a + lay.b));
-  double* BE = reinterpret_cast<double*>(base + nb * (lay.a + lay.b + lay.d));
-  double* part = reinterpret_cast<double*>(base + nb * (lay.a + lay.b + lay.d + lay.be));
-  const int64_t za = (int64_t)(lay.a / 8), zb = (int64_t)(lay.b / 8), zd = (int64_t)(lay.d / 8);
+  double* B64 = reinterpret_cast<double*>(base + na * lay.a);
+  double* D = reinterpret_cast<double*>(base + na * lay.a + nb * lay.b);
+  double* BE = reinterpret_cast<double*>(base + na * lay.a + nb * (lay.b + lay.d));
+  double* part = reinterpret_cast<double*>(base + na * lay.a + nb * (lay.b + lay.d + lay.be));
+  const int64_t za = share_a ? 0 : (int64_t)(lay.a / 8), zb = (int64_t)(lay.b / 8),
+                zd = (int64_t)(lay.d / 8);
   const int64_t zp = (int64_t)(lay.part / 8);
   const int bt = (int)batch;
-  if (launch_sym_to_f64<R>(n, A, lda, A64, s, bt, st.a, za) != hipSuccess) return BAKRON_EHIP;
+  if (launch_sym_to_f64<R>(n, A, lda, A64, s, share_a ? 1 : bt, st.a, za) != hipSuccess)
+    return BAKRON_EHIP;
   if (launch_sym_to_f64<R>(m, B, ldb, B64, s, bt, st.b, zb) != hipSuccess) return BAKRON_EHIP;
   if (launch_residual_f64<R>(m, n, W, ldw, V, ldv, scale_mode, scales, D, s, bt,
                              ResidualStrides{st.w, st.v, st.s, zd}) != hipSuccess)
@@ -840,6 +854,152 @@ int bakron_loss_batched(int dtype, int64_t batch, int64_t m, int64_t n, const vo
   return loss_impl<double>(batch, m, n, (const double*)W, ldw, V, ldv, scale_mode,
                            (const double*)scales, (const double*)A, lda, (const double*)B, ldb, st,
                            loss, workspace, s);
+}
+
+// ---- block-diagonal output factor ------------------------------------------
+// B = blockdiag(B_0 .. B_{h-1}) of h blocks of order b = m / h. Then B^-1 and
+// its Cholesky factor are block-diagonal too, L^B[p][i] = 0 unless rows p and
+// i share a block, so an error reaches only rows of its own block: the solve
+// splits exactly into h problems of b x n that share L^A, and the loss into
+// sum_h tr(B_h D_h A D_h^T). Each call maps onto the batched machinery (one
+// set of launches for all heads), which never touches the zero blocks.
+
+static bool heads_ok(int64_t heads, int64_t m) {
+  return heads >= 1 && heads <= kMaxBatch / 2 && m % heads == 0;
+}
+
+size_t bakron_factor_blockdiag_workspace_bytes(int dtype, int64_t heads, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0 || !heads_ok(heads, m)) return 0;
+  const size_t fa = factor_layout(0, n, 1).total;
+  const size_t fb = factor_layout(m / heads, 0, heads).total;
+  return fa > fb ? fa : fb;
+}
+
+int bakron_factor_blockdiag(int dtype, int64_t heads, int64_t m, int64_t n, const void* A,
+                            int64_t lda, const void* B, int64_t ldb, int64_t stride_b, void* LA,
+                            int64_t ldla, void* LB, int64_t ldlb, int64_t stride_lb, void* dA,
+                            void* dB, void* workspace, size_t workspace_bytes,
+                            int64_t* bad_pivot, void* stream) {
+  if (bad_pivot) bad_pivot[0] = bad_pivot[1] = bad_pivot[2] = -1;
+  if (!dtype_ok(dtype) || m < 0 || n < 0 || !heads_ok(heads, m)) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  const int64_t b = m / heads;
+  if (n > 0 && (!A || !LA || lda < n || ldla < n)) return BAKRON_EINVAL;
+  if (b > 0 && (!B || !LB || ldb < b || ldlb < b)) return BAKRON_EINVAL;
+  if (b > 0 && heads > 1 && (stride_b < 0 || stride_lb < (b - 1) * ldlb + b)) return BAKRON_EINVAL;
+  if (b > 0 && heads > 1 && std::max(stride_b, stride_lb) > std::numeric_limits<int64_t>::max() / 2 / (heads - 1))
+    return BAKRON_EINVAL;
+  const size_t need = bakron_factor_blockdiag_workspace_bytes(dtype, heads, m, n);
+  if (!workspace || workspace_bytes < need) return BAKRON_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const FactorStrides sta = {0, 0, 0, 0, 0, 0};
+  const FactorStrides stb = {0, stride_b, 0, stride_lb, 0, b};
+  int64_t bad3[3] = {-1, -1, -1};
+  int rc = BAKRON_OK;
+  // the input side (one factor of order n), then the h output blocks in the
+  // same launches (the batched factor with no input side); both synchronous
+  if (n > 0) {
+    rc = dtype == BAKRON_F32
+             ? factor_impl<float>(1, 0, n, (const float*)A, lda, nullptr, 1, (float*)LA, ldla,
+                                  nullptr, 1, (float*)dA, nullptr, sta, workspace, bad3, s)
+             : factor_impl<double>(1, 0, n, (const double*)A, lda, nullptr, 1, (double*)LA, ldla,
+                                   nullptr, 1, (double*)dA, nullptr, sta, workspace, bad3, s);
+    if (rc == BAKRON_ENOTSPD && bad_pivot) {
+      bad_pivot[0] = 0;
+      bad_pivot[1] = -1;
+      bad_pivot[2] = bad3[2];
+    }
+    if (rc != BAKRON_OK) return rc;
+  }
+  if (b > 0) {
+    rc = dtype == BAKRON_F32
+             ? factor_impl<float>(heads, b, 0, nullptr, 1, (const float*)B, ldb, nullptr, 1,
+                                  (float*)LB, ldlb, nullptr, (float*)dB, stb, workspace, bad3, s)
+             : factor_impl<double>(heads, b, 0, nullptr, 1, (const double*)B, ldb, nullptr, 1,
+                                   (double*)LB, ldlb, nullptr, (double*)dB, stb, workspace, bad3, s);
+    if (rc == BAKRON_ENOTSPD && bad_pivot) {
+      bad_pivot[0] = 1;
+      bad_pivot[1] = bad3[0];
+      bad_pivot[2] = bad3[2];
+    }
+  }
+  return rc;
+}
+
+size_t bakron_solve_blockdiag_workspace_bytes(int dtype, int64_t heads, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0 || !heads_ok(heads, m)) return 0;
+  return bakron_solve_batched_workspace_bytes(dtype, heads, m / heads, n);
+}
+
+int bakron_solve_blockdiag(int dtype, int64_t heads, int64_t m, int64_t n, const void* W,
+                           int64_t ldw, const void* LA, int64_t ldla, const void* LB, int64_t ldlb,
+                           int64_t stride_lb, int32_t alpha_lo, int32_t alpha_hi,
+                           int32_t unbounded, int scale_mode, const void* scales, int32_t* V,
+                           int64_t ldv, void* Wt, int64_t ldwt, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0 || !heads_ok(heads, m)) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (m == 0 || n == 0) return BAKRON_OK;
+  if (ldw < n || ldv < n || (Wt && ldwt < n)) return BAKRON_EINVAL;
+  const int64_t b = m / heads;
+  // head h: rows [h b, (h + 1) b) of W, V, Wt and of the row scales; the
+  // column scales and L^A are shared (stride 0)
+  const int64_t ss = scale_mode == BAKRON_SCALE_ROW ? b : 0;
+  return bakron_solve_batched(dtype, heads, b, n, W, ldw, b * ldw, LA, ldla, 0, LB, ldlb,
+                              heads > 1 ? stride_lb : 0, alpha_lo, alpha_hi, unbounded, scale_mode,
+                              scales, ss, V, ldv, b * ldv, Wt, ldwt, Wt ? b * ldwt : 0, workspace,
+                              workspace_bytes, stream);
+}
+
+size_t bakron_loss_blockdiag_workspace_bytes(int dtype, int64_t heads, int64_t m, int64_t n) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0 || !heads_ok(heads, m)) return 0;
+  return loss_ws_bytes(heads, m / heads, n, true) + align_up((size_t)heads * 8);
+}
+
+int bakron_loss_blockdiag(int dtype, int64_t heads, int64_t m, int64_t n, const void* W,
+                          int64_t ldw, const int32_t* V, int64_t ldv, int scale_mode,
+                          const void* scales, const void* A, int64_t lda, const void* B,
+                          int64_t ldb, int64_t stride_b, double* loss, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || m < 0 || n < 0 || !heads_ok(heads, m)) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (!loss) return BAKRON_EINVAL;
+  const int64_t b = m / heads;
+  if (m > 0 && n > 0) {
+    if (!W || !V || !A || !B) return BAKRON_EINVAL;
+    if (ldw < n || ldv < n || lda < n || ldb < b) return BAKRON_EINVAL;
+    if (heads > 1 && (stride_b < 0 || stride_b > std::numeric_limits<int64_t>::max() / 2 / (heads - 1)))
+      return BAKRON_EINVAL;
+  }
+  if (scale_mode == BAKRON_SCALE_NONE) {
+    if (scales) return BAKRON_EINVAL;
+  } else if (scale_mode == BAKRON_SCALE_ROW || scale_mode == BAKRON_SCALE_COL) {
+    if (!scales) return BAKRON_EINVAL;
+  } else {
+    return BAKRON_EINVAL;
+  }
+  const size_t need = bakron_loss_blockdiag_workspace_bytes(dtype, heads, m, n);
+  if (!workspace || need == 0 || workspace_bytes < need) return BAKRON_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return BAKRON_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m == 0 || n == 0)
+    return launch_sum_partials(nullptr, 0, loss, s) == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
+  // per-head losses at the end of the workspace, then their sum in a fixed order
+  double* per_head = reinterpret_cast<double*>(static_cast<char*>(workspace) +
+                                               loss_ws_bytes(heads, b, n, true));
+  const LossStrides st = {b * ldw, b * ldv, scale_mode == BAKRON_SCALE_ROW ? b : 0, 0,
+                          heads > 1 ? stride_b : 0};
+  const int rc =
+      dtype == BAKRON_F32
+          ? loss_impl<float>(heads, b, n, (const float*)W, ldw, V, ldv, scale_mode,
+                             (const float*)scales, (const float*)A, lda, (const float*)B, ldb, st,
+                             per_head, workspace, s)
+          : loss_impl<double>(heads, b, n, (const double*)W, ldw, V, ldv, scale_mode,
+                              (const double*)scales, (const double*)A, lda, (const double*)B, ldb,
+                              st, per_head, workspace, s);
+  if (rc != BAKRON_OK) return rc;
+  return launch_sum_partials(per_head, heads, loss, s) == hipSuccess ? BAKRON_OK : BAKRON_EHIP;
 }
 
 int bakron_row_scales(int dtype, int64_t m, int64_t n, const void* W, int64_t ldw, int32_t hi,

@@ -189,6 +189,42 @@ def config5(matrix_idx: int, b_identity: bool = False) -> Problem:
                    "f32", (-8, 7, 0), 7)
 
 
+def head_grams(config_id: int, heads: int, b: int, samples: int, damp_rel: float = 1e-2,
+               dtype=np.float64) -> np.ndarray:
+    """Per-head output-side Grams, (heads, b, b): head h is the Gram/N of
+    ``samples`` N(0, I) vectors of dimension b (seed [config_id, h, ROLE_B]),
+    damped by ``damp_rel`` of its mean diagonal. Stand-ins for the per-head
+    attention-local output factors the pages assemble block-diagonally."""
+    out = np.empty((heads, b, b), dtype=np.float64)
+    for h in range(heads):
+        out[h] = gram(_gaussian(rng(config_id, h, ROLE_B), (b, samples)), damp_rel=damp_rel)
+    return out.astype(dtype)
+
+
+def block_diag(blocks: np.ndarray) -> np.ndarray:
+    """The (h b) x (h b) matrix with the given (h, b, b) blocks on its diagonal."""
+    h, b, _ = blocks.shape
+    M = np.zeros((h * b, h * b), dtype=blocks.dtype)
+    for i in range(h):
+        M[i * b:(i + 1) * b, i * b:(i + 1) * b] = blocks[i]
+    return M
+
+
+def config3_heads(heads: int = 32, base: Optional[Problem] = None) -> tuple:
+    """The 4096 x 4096 attention workload with a block-diagonal output side:
+    W and A of ``config3`` (or of ``base``), and B = blockdiag of ``heads``
+    per-head Grams (b = 4096 / heads = 128 for 32 heads) of 8192 Gaussian
+    output vectors each, 1% damping. Returns (problem with the assembled
+    dense B, the (heads, b, b) blocks)."""
+    p = base if base is not None else config3()
+    m = p.W.shape[0]
+    b = m // heads
+    blocks = head_grams(6, heads, b, 8192).astype(np.float32)
+    q = Problem(f"cfg3_heads{heads}_{m}x{p.W.shape[1]}_f32", p.W, p.A, block_diag(blocks), p.dtype,
+                p.alphabet, p.scale_hi, meta={"heads": heads})
+    return q, blocks
+
+
 # ---------------------------------------------------------------------------
 # Generic small problems for tests (any shape / dtype / alphabet).
 # ---------------------------------------------------------------------------
