@@ -170,8 +170,9 @@ def parity_leg(bk, p, o, dev):
             "replay_inconsistent_at_tau_obs": int(np.count_nonzero(rep.gaps > tau_obs)),
             "replay_max_gap": rep.max_inconsistent_gap,
             "loss_rel": (l_gpu - o["loss"]) / abs(o["loss"]),
-            "note": "float32: a near-tie flip cascades, so raw agreement below 99.9% is expected "
-                    "at this size; the GPU tests bound the loss by the oracle's own branch spread"}
+            "note": ("float64: codes must equal the oracle's bit for bit" if o["W"].dtype.itemsize == 8 else
+                     "float32: a near-tie flip cascades, so raw agreement below 99.9% is expected "
+                     "at this size; the GPU tests bound the loss by the oracle's own branch spread")}
 
 
 def main():

@@ -175,3 +175,25 @@ def test_loss_batched_shared_hessians_and_empty(gpu_lib):
     e = bk.loss_batched(torch.zeros((0, 40, 60), dtype=torch.float64, device="cuda"),
                         torch.zeros((0, 40, 60), dtype=torch.int32, device="cuda"), A, B)
     assert e.shape == (0,)
+
+
+@pytest.mark.timeout(600)
+def test_kv28_fp64_batched_all_bit_exact(gpu_lib):
+    """All 28 k/v projections (1024 x 2048) in float64 through ONE batched
+    solve, each against the oracle on its own oracle factors: codes bit for
+    bit, values at rounding within 1e-10 code units."""
+    import oracle as O
+    from synth import config5
+    probs = [config5(i) for i in range(28)]
+    W = np.stack([p.W.astype(np.float64) for p in probs])
+    facs = [(O.factor(p.A), O.factor(p.B)) for p in probs]
+    LA = np.stack([f[0][0] for f in facs])
+    LB = np.stack([f[1][0] for f in facs])
+    S = np.stack([O.row_scales(W[i], 7, np.float64) for i in range(28)])
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    V, Wt = gpu_lib.solve_batched(t(W), t(LA), t(LB), (-8, 7, 0), t(S), return_wt=True)
+    V, Wt = V.cpu().numpy(), Wt.cpu().numpy()
+    for i in range(28):
+        ref = O.solve_recursive(W[i], LA[i], LB[i], (-8, 7, 0), O.SCALE_ROW, S[i])
+        assert np.array_equal(V[i], ref.V.astype(np.int32)), i
+        assert np.max(np.abs(Wt[i] - ref.Wt) / S[i][:, None]) <= 1e-10, i
