@@ -282,3 +282,37 @@ def test_timed_solve_equals_solve_and_times_every_launch(gpu_lib):
     assert all(x >= 0.0 for x in t), t
     assert sum(x > 0.0 for x in t) >= len([o for o in ops if o[0] == 0])  # every leaf has work
     assert sum(t) < 1000.0
+
+
+def test_solve_replays_bit_identically_from_a_captured_graph(gpu_lib):
+    """The solve enqueues only kernels on the caller's stream (no host
+    synchronisation, no memset, no allocation with a workspace given), so it
+    can be captured in a HIP graph: every replay, with eager work and
+    synchronisations in between, equals the eager result bit for bit."""
+    bk = gpu_lib
+    p = random_problem(333, 250, "f32", seed=12, w_std=0.02, heavy_tail=True, samples_factor=2)
+    inp = prepare(p.W, p.A, p.B, "f32", (-8, 7, 0), "row", 7)
+    W, LA, LB, s = to_dev(inp.W), to_dev(inp.LA), to_dev(inp.LB), to_dev(inp.s)
+    ws = torch.empty(bk.workspace_bytes("solve", bk.F32, 333, 250), dtype=torch.uint8, device="cuda")
+    V = torch.empty((333, 250), dtype=torch.int32, device="cuda")
+    ref = bk.solve(W, LA, LB, (-8, 7, 0), s).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        bk.solve(W, LA, LB, (-8, 7, 0), s, workspace=ws, out=V)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bk.solve(W, LA, LB, (-8, 7, 0), s, workspace=ws, out=V)
+    for r in range(3):
+        V.fill_(-99)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(V, ref), r
+        # eager work between the replays
+        other = bk.solve(W, LA, LB, (-8, 7, 0), s)
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref)
+    del g
