@@ -31,7 +31,8 @@ def test_status_strings_and_version():
     assert L.bakron_abi_version() == 1
     for st in (0, -1, -2, -3):
         assert L.bakron_status_string(st)
-    assert bk.tile_size(bk.F32) == bk.tile_size(bk.F64) == 16
+    # the edge of the super tiles (2 x 2 solver tiles of 16) the recursion runs over
+    assert bk.tile_size(bk.F32) == bk.tile_size(bk.F64) == 32
     assert bk.tile_size(7) == 0
 
 
@@ -224,27 +225,27 @@ def test_row_scales_mse_rejects_bad_arguments(bad):
     assert L.bakron_row_scales_mse(bk.F32, 0, 4, None, 4, -8, 7, 100, 0.5, None, None) == bk.OK
 
 
-def _closed_form_leaves(m, n, T=16):
+def _closed_form_leaves(m, n, T=32):
     return -(-m // T) + -(-n // T) - 1
 
 
 @pytest.mark.parametrize("m,n", [(1, 1), (16, 16), (17, 5), (64, 64), (200, 300), (512, 512),
                                  (4096, 4096), (14336, 4096), (4096, 14336), (1024, 2048)])
 def test_schedule_is_algorithm_6_over_blocks_of_tile_antidiagonals(m, n):
-    """Table 1 "Steps" for BaKron: one leaf per (tile) anti-diagonal, in
-    order; Algorithm 6's recursion over blocks of G tile anti-diagonals (G
-    read from the second block's start), each internal node splitting block
-    range [kb, lb) at floor((kb+lb)/2) and running after the last leaf left
-    of its midpoint and before the first leaf right of it; inside a block,
-    each leaf names its block start."""
+    """Table 1 "Steps" for BaKron: one leaf per anti-diagonal of 32 x 32
+    super tiles, in order; Algorithm 6's recursion over blocks of G such
+    anti-diagonals (G read from the second block's start), each internal
+    node splitting block range [kb, lb) at floor((kb+lb)/2) and running after
+    the last leaf left of its midpoint and before the first leaf right of it;
+    inside a block, each leaf names its block's start and end."""
     ops = bk.solve_schedule(bk.F32, m, n)
     R = _closed_form_leaves(m, n)
-    leaves = [(a, b) for (kind, a, b, c) in ops if kind == 0]
-    assert [a for a, _ in leaves] == list(range(R))
-    starts = sorted({b for _, b in leaves})
+    leaves = [(a, b, c) for (kind, a, b, c) in ops if kind == 0]
+    assert [a for a, _, _ in leaves] == list(range(R))
+    starts = sorted({b for _, b, _ in leaves})
     BLOCK = starts[1] if len(starts) > 1 else R + 1  # one block: any G > R
     nblocks = -(-R // BLOCK)
-    assert all(b == (a // BLOCK) * BLOCK for a, b in leaves)
+    assert all(b == (a // BLOCK) * BLOCK and c == min(b + BLOCK, R) for a, b, c in leaves)
     nodes = [(a, b, c) for (kind, a, b, c) in ops if kind == 2]
     assert len(nodes) == nblocks - 1
     assert sorted(mid for (_, mid, _) in nodes) == [BLOCK * i for i in range(1, nblocks)]
@@ -325,3 +326,31 @@ def test_antidiag_empty_is_noop_and_workspace_grows():
     assert 0 < L.bakron_solve_antidiag_workspace_bytes(bk.F32, 64, 64) < \
         L.bakron_solve_antidiag_workspace_bytes(bk.F32, 512, 512) < \
         L.bakron_solve_antidiag_workspace_bytes(bk.F64, 512, 512)
+
+
+def test_blockdiag_queries_and_argument_errors():
+    L = bk.lib()
+    # heads must divide m and be at least 1
+    for heads, m in ((0, 8), (3, 8), (-1, 8)):
+        assert L.bakron_factor_blockdiag_workspace_bytes(bk.F32, heads, m, 4) == 0
+        assert L.bakron_solve_blockdiag_workspace_bytes(bk.F32, heads, m, 4) == 0
+        assert L.bakron_loss_blockdiag_workspace_bytes(bk.F32, heads, m, 4) == 0
+    assert L.bakron_solve_blockdiag_workspace_bytes(bk.F32, 4, 64, 32) == \
+        L.bakron_solve_batched_workspace_bytes(bk.F32, 4, 16, 32)
+    bad = (bk._i64 * 3)(0, 0, 0)
+    # factor: heads not dividing m, then a block stride that overlaps the outputs
+    assert L.bakron_factor_blockdiag(bk.F32, 3, 8, 4, FAKE, 4, FAKE, 8, 64, FAKE, 4, FAKE, 8, 64,
+                                     None, None, FAKE, 1 << 40, bad, None) == bk.EINVAL
+    assert tuple(bad) == (-1, -1, -1)
+    assert L.bakron_factor_blockdiag(bk.F32, 2, 8, 4, FAKE, 4, FAKE, 4, 16, FAKE, 4, FAKE, 4, 4,
+                                     None, None, FAKE, 1 << 40, bad, None) == bk.EINVAL
+    # solve: heads not dividing m; empty problem
+    assert L.bakron_solve_blockdiag(bk.F32, 3, 8, 4, FAKE, 4, FAKE, 4, FAKE, 2, 4, -8, 7, 0, 0,
+                                    None, FAKE, 4, None, 0, FAKE, 1 << 40, None) == bk.EINVAL
+    assert L.bakron_solve_blockdiag(bk.F32, 2, 8, 0, None, 0, None, 0, None, 4, 16, -8, 7, 0, 0,
+                                    None, None, 0, None, 0, None, 0, None) == bk.OK
+    # loss: no output pointer, then a bad scale mode
+    assert L.bakron_loss_blockdiag(bk.F32, 2, 8, 4, FAKE, 4, FAKE, 4, 0, None, FAKE, 4, FAKE, 4, 16,
+                                   None, FAKE, 1 << 40, None) == bk.EINVAL
+    assert L.bakron_loss_blockdiag(bk.F32, 2, 8, 4, FAKE, 4, FAKE, 4, 7, None, FAKE, 4, FAKE, 4, 16,
+                                   FAKE, FAKE, 1 << 40, None) == bk.EINVAL
