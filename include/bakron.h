@@ -66,9 +66,7 @@ const char *bakron_status_string(int status);
 /* ABI revision of this header; bumped on any incompatible change. */
 int bakron_abi_version(void);
 
-/* Edge (32) of the square blocks of W whose anti-diagonals the solve's
- * recursion runs over (each block is 2 x 2 tiles of 16, the storage tile of
- * the kernels), for `dtype`: the unit of bakron_solve_schedule's records.
+/* Tile edge (16) of the tiling of W the solver works on, for `dtype`.
  * Returns 0 for an invalid dtype. */
 int bakron_tile_size(int dtype);
 
@@ -212,11 +210,10 @@ int bakron_solve_noalloc(int dtype, int64_t m, int64_t n,
 /* The launch schedule bakron_solve uses for (dtype, m, n), for measurement:
  * writes up to `max_ops` records of 4 int32 {kind, a, b, c} to the HOST
  * array `ops` (nullable) and returns the total number of records, or a
- * negative status. Anti-diagonals are those of the blocks of
- * bakron_tile_size. kind 0 = leaf: a = anti-diagonal S, [b, c) = its leaf
- * block (the leaf also applies the updates from anti-diagonals b..S-1);
- * kinds 2 and 3 = the two band products of an internal node, anti-diagonals
- * [a, b) -> [b, c). Host only. */
+ * negative status. kind 0 = leaf: a = tile anti-diagonal K, b = first tile
+ * anti-diagonal of its block (the leaf also applies the updates from tile
+ * anti-diagonals b..K-1); kinds 2 and 3 = the two band products of an
+ * internal node, tile anti-diagonals [a, b) -> [b, c). Host only. */
 int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t *ops, int64_t max_ops);
 
 /* Measurement variant of bakron_solve: same arguments and result, and it

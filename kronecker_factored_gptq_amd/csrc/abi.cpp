@@ -38,21 +38,19 @@ struct Op {
 };
 enum { OP_LEAF = 0, OP_BAND1 = 2, OP_BAND2 = 3 };
 
-// Algorithm 6 over blocks [kb, lb) of kLeafSuperBlock super anti-diagonals
-// each (R super anti-diagonals in all); a block's leaves run in order. A
-// leaf record is {OP_LEAF, S, S0, S1}: super anti-diagonal S of the block
-// [S0, S1).
+// Algorithm 6 over blocks [kb, lb) of kLeafBlock tile anti-diagonals each
+// (R tile anti-diagonals in all); a block's leaves run in order.
 void build_schedule(int kb, int lb, int R, std::vector<Op>& ops) {
   if (lb - kb == 1) {
-    const int S0 = kb * kLeafSuperBlock;
-    const int S1 = (kb + 1) * kLeafSuperBlock < R ? (kb + 1) * kLeafSuperBlock : R;
-    for (int S = S0; S < S1; ++S) ops.push_back({OP_LEAF, S, S0, S1});
+    const int K0 = kb * kLeafBlock;
+    const int K1 = (kb + 1) * kLeafBlock < R ? (kb + 1) * kLeafBlock : R;
+    for (int K = K0; K < K1; ++K) ops.push_back({OP_LEAF, K, K0, 0});
     return;
   }
   const int midb = (kb + lb) / 2;
   build_schedule(kb, midb, R, ops);
-  const int k = kb * kLeafSuperBlock, mid = midb * kLeafSuperBlock;
-  const int l = lb * kLeafSuperBlock < R ? lb * kLeafSuperBlock : R;
+  const int k = kb * kLeafBlock, mid = midb * kLeafBlock;
+  const int l = lb * kLeafBlock < R ? lb * kLeafBlock : R;
   ops.push_back({OP_BAND1, k, mid, l});
   ops.push_back({OP_BAND2, k, mid, l});
   build_schedule(midb, lb, R, ops);
@@ -61,10 +59,8 @@ void build_schedule(int kb, int lb, int R, std::vector<Op>& ops) {
 std::vector<Op> schedule_for(int64_t m, int64_t n) {
   std::vector<Op> ops;
   if (m <= 0 || n <= 0) return ops;
-  // super tiles of kSuper x kSuper solver tiles
-  const int64_t Ms = (tiles(m) + kSuper - 1) / kSuper, Ns = (tiles(n) + kSuper - 1) / kSuper;
-  const int R = (int)(Ms + Ns - 1);
-  const int nb = (R + kLeafSuperBlock - 1) / kLeafSuperBlock;
+  const int R = (int)(tiles(m) + tiles(n) - 1);
+  const int nb = (R + kLeafBlock - 1) / kLeafBlock;
   ops.reserve(3 * (size_t)R);
   build_schedule(0, nb, R, ops);
   return ops;
@@ -155,9 +151,7 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
     const bool timed = op_ms != nullptr;
     hipEvent_t e0 = timed ? ev[evi] : nullptr, e1 = timed ? ev[evi + 1] : nullptr;
     switch (op.kind) {
-      case OP_LEAF:
-        e = launch_leaf<R>(g, op.k, op.mid, op.l, Wk, LBp, LAp, Mb, lp, s, e0, e1);
-        break;
+      case OP_LEAF: e = launch_leaf<R>(g, op.k, op.mid, Wk, LBp, LAp, Mb, lp, s, e0, e1); break;
       case OP_BAND1:
         e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, bb, s, e0, e1);
         break;
@@ -485,7 +479,7 @@ const char* bakron_status_string(int status) {
 
 int bakron_abi_version(void) { return 1; }
 
-int bakron_tile_size(int dtype) { return dtype_ok(dtype) ? kTile * kSuper : 0; }
+int bakron_tile_size(int dtype) { return dtype_ok(dtype) ? kTile : 0; }
 
 size_t bakron_factor_workspace_bytes(int dtype, int64_t m, int64_t n) {
   if (!dtype_ok(dtype) || m < 0 || n < 0) return 0;

@@ -1,14 +1,13 @@
 // Band products of a large internal node, on MFMA (gfx950).
 //
-// An internal node over super anti-diagonals [k, l) (of 2 x 2 blocks of
-// solver tiles), split at mid, applies the errors E recorded on [k, mid) to
-// the tiles on [mid, l) as the two
+// An internal node over tile anti-diagonals [k, l), split at mid, applies the
+// errors E recorded on [k, mid) to the tiles on [mid, l) as the two
 // "restricted band products" of "BaKron: Efficient Quantization with
 // Kronecker-Factored Hessians" (arXiv 2608.06291), Appendix C:
-//   stage 1: M[P,J]  = sum_I L^B[P,I] E[I,J],   I <= P, k <= s(I,J) < mid
-//   stage 2: W[P,Q] += sum_J M[P,J] L^A[Q,J]^T, J <= Q, J/2 < mid,
-//            k <= s(P,J) <= l-1, written only where mid <= s(P,Q) <= l-1.
-// (Subscripts are 16 x 16 solver tiles; s(P,Q) = P/2 + Q/2.)
+//   stage 1: M[P,J]  = sum_I L^B[P,I] E[I,J],   I <= P, k <= I+J < mid
+//   stage 2: W[P,Q] += sum_J M[P,J] L^A[Q,J]^T, J <= Q, J < mid,
+//            k <= P+J <= l-1, written only where mid <= P+Q <= l-1.
+// (Subscripts are 16 x 16 solver tiles.)
 //
 // Each workgroup owns an MB x MB block of solver tiles (a BM = 16*MB square
 // macro tile) and walks K two solver tiles (32 elements) at a time. Four
@@ -60,33 +59,28 @@ struct BandShape {
   // do little MFMA work per step, so one step does not cover the latency
   static constexpr int PD = (sizeof(R) == 4 && MB <= 4) ? 2 : 1;
   static_assert(NV >= 1 && (MB * BKT * TV) % 256 == 0, "macro tile too small for 256 threads");
-  static_assert(MB % 2 == 0, "macro tiles are whole super tiles");
 };
 
 // Geometry of the output macro tile (row block pb, column block number bx of
 // that row) of one stage: first column tile C0 and the K range [Klo, Khi] in
-// solver tiles. The recursion's anti-diagonals index SUPER tiles (2 x 2
-// solver tiles: super anti-diagonal of tile (P, Q) = P/2 + Q/2), so k, mid,
-// l are super anti-diagonals; the ranges are worked out on super tiles (MB is
-// even, so macro tiles are whole super tiles) and returned in solver tiles.
-// Shared by the kernels and the host-side launch planning.
+// solver tiles. Shared by the kernels and the host-side launch planning.
 struct BandTile {
   int P0, C0, Klo, Khi;
 };
 // Column tiles [Clo, Chi] that row block pb of a stage writes; false if none.
 __host__ __device__ inline bool band_cols(int stage, int k, int mid, int l, int Nt, int MB, int pb,
                                           int* Clo, int* Chi) {
-  const int MB2 = MB / 2, P02 = pb * MB2, Nt2 = (Nt + 1) / 2;
+  const int P0 = pb * MB;
   int lo, hi;
   if (stage == 1) {  // M[P, J] is needed where stage 2 reads it: J < mid, P + J <= l - 1
-    lo = k - (P02 + MB2 - 1); if (lo < 0) lo = 0;
-    hi = Nt2 - 1; if (mid - 1 < hi) hi = mid - 1; if (l - 1 - P02 < hi) hi = l - 1 - P02;
+    lo = k - (P0 + MB - 1); if (lo < 0) lo = 0;
+    hi = Nt - 1; if (mid - 1 < hi) hi = mid - 1; if (l - 1 - P0 < hi) hi = l - 1 - P0;
   } else {           // W[P, Q] on mid <= P + Q <= l - 1
-    lo = mid - (P02 + MB2 - 1); if (lo < 0) lo = 0;
-    hi = Nt2 - 1; if (l - 1 - P02 < hi) hi = l - 1 - P02;
+    lo = mid - (P0 + MB - 1); if (lo < 0) lo = 0;
+    hi = Nt - 1; if (l - 1 - P0 < hi) hi = l - 1 - P0;
   }
-  *Clo = 2 * lo;
-  *Chi = 2 * hi + 1 < Nt - 1 ? 2 * hi + 1 : Nt - 1;
+  *Clo = lo;
+  *Chi = hi;
   return lo <= hi;
 }
 __host__ __device__ inline bool band_tile(int stage, int k, int mid, int l, int Mt, int Nt, int MB,
@@ -97,22 +91,19 @@ __host__ __device__ inline bool band_tile(int stage, int k, int mid, int l, int 
   const int cb = Clo / MB + bx;
   if (cb > Chi / MB) return false;
   const int C0 = cb * MB;
-  const int MB2 = MB / 2, P02 = P0 / 2, C02 = C0 / 2, Mt2 = (Mt + 1) / 2, Nt2 = (Nt + 1) / 2;
-  int Klo, Khi, dim;
+  int Klo, Khi;
   if (stage == 1) {  // I <= P, k <= I + J < mid
-    Klo = k - (C02 + MB2 - 1); if (Klo < 0) Klo = 0;
-    Khi = P02 + MB2 - 1; if (mid - 1 - C02 < Khi) Khi = mid - 1 - C02; if (Mt2 - 1 < Khi) Khi = Mt2 - 1;
-    dim = Mt;
+    Klo = k - (C0 + MB - 1); if (Klo < 0) Klo = 0;
+    Khi = P0 + MB - 1; if (mid - 1 - C0 < Khi) Khi = mid - 1 - C0; if (Mt - 1 < Khi) Khi = Mt - 1;
   } else {           // J <= Q, J < mid, k <= P + J <= l - 1
-    Klo = k - (P02 + MB2 - 1); if (Klo < 0) Klo = 0;
-    Khi = C02 + MB2 - 1; if (mid - 1 < Khi) Khi = mid - 1; if (Nt2 - 1 < Khi) Khi = Nt2 - 1;
-    if (l - 1 - P02 < Khi) Khi = l - 1 - P02;
-    dim = Nt;
+    Klo = k - (P0 + MB - 1); if (Klo < 0) Klo = 0;
+    Khi = C0 + MB - 1; if (mid - 1 < Khi) Khi = mid - 1; if (Nt - 1 < Khi) Khi = Nt - 1;
+    if (l - 1 - P0 < Khi) Khi = l - 1 - P0;
   }
   t->P0 = P0;
   t->C0 = C0;
-  t->Klo = 2 * Klo;
-  t->Khi = 2 * Khi + 1 < dim - 1 ? 2 * Khi + 1 : dim - 1;
+  t->Klo = Klo;
+  t->Khi = Khi;
   return Klo <= Khi;
 }
 
@@ -210,12 +201,12 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
       if (STAGE == 1) {
         if (kk <= Khi && P < Mt && kk <= P)
           va = reinterpret_cast<const vec_t*>(LBp + tri_index(P, kk) * T * T)[vo];
-        const int sd = (kk >> 1) + (C >> 1);  // super anti-diagonal of the source tile
+        const int sd = kk + C;
         if (kk <= Khi && C < Nt && sd >= k && sd < mid)
           vb = reinterpret_cast<const vec_t*>(Wk + ((int64_t)kk * Nt + C) * T * T)[vo];
       } else {
-        const int sd = (P >> 1) + (kk >> 1);
-        if (kk <= Khi && P < Mt && (kk >> 1) <= mid - 1 && sd >= k && sd <= l - 1)
+        const int sd = P + kk;
+        if (kk <= Khi && P < Mt && kk <= mid - 1 && sd >= k && sd <= l - 1)
           va = reinterpret_cast<const vec_t*>(Mb + ((int64_t)P * Nt + kk) * T * T)[vo];
         if (kk <= Khi && C < Nt && kk <= C)
           vb = reinterpret_cast<const vec_t*>(LAp + tri_index(C, kk) * T * T)[vo];
@@ -321,7 +312,7 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
   for (int t = wave; t < MB * MB; t += 4) {
     const int P = P0 + t / MB, C = C0 + t % MB;
     if (P >= Mt || C >= Nt) continue;
-    if (STAGE == 2 && ((P >> 1) + (C >> 1) < mid || (P >> 1) + (C >> 1) > l - 1)) continue;
+    if (STAGE == 2 && (P + C < mid || P + C > l - 1)) continue;
     vec_t* dst = reinterpret_cast<vec_t*>(out + ((int64_t)P * Nt + C) * T * T);
     const vec_t* src = reinterpret_cast<const vec_t*>(Cs + t * T * T);
 #pragma unroll
@@ -337,18 +328,18 @@ __global__ __launch_bounds__(256) void band_kernel(BandArgs<R> a) {
   }
 }
 
-// Macro-tile size by node width l - k (super anti-diagonals): 2 x 2 solver
+// Macro-tile size by node width l - k (tile anti-diagonals): 2 x 2 solver
 // tiles (32 x 32) below QMIN_BIG, 4 x 4 (64 x 64) from it on. Measured on
-// the 4096 x 4096 float32 solve (then in tile anti-diagonals, leaf blocks of
-// 12): 32 x 32 for every node but the top one gives 8.05 ms for the solve
-// against 8.63 with 64 x 64 everywhere and 8.18 with 32 x 32 everywhere (more
+// the 4096 x 4096 float32 solve (leaf blocks of 12): 32 x 32 for every node
+// but the top one (widths up to 259) gives 8.05 ms for the solve against
+// 8.63 with 64 x 64 everywhere and 8.18 with 32 x 32 everywhere (more
 // workgroups and less padding on the narrow bands); 128 x 128 tiles were
 // slower still.
 template <typename R> struct BandChoice;
-template <> struct BandChoice<float> { static constexpr int BIG = 4, SMALL = 2, QMIN_BIG = 150; };
-// Float64 (measured on the 4096 x 4096 solve in float64, in tile anti-diagonals): 64 x 64
-// from width 100 gives 12.45 ms against 12.74 from width 32, 12.77 from 300 and 13.40 from 1000.
-template <> struct BandChoice<double> { static constexpr int BIG = 4, SMALL = 2, QMIN_BIG = 50; };
+template <> struct BandChoice<float> { static constexpr int BIG = 4, SMALL = 2, QMIN_BIG = 300; };
+// Float64 (measured on the 4096 x 4096 solve in float64): 64 x 64 from width 100 gives
+// 12.45 ms against 12.74 from width 32, 12.77 from 300 and 13.40 from 1000.
+template <> struct BandChoice<double> { static constexpr int BIG = 4, SMALL = 2, QMIN_BIG = 100; };
 
 template <typename R, int MB>
 static hipError_t launch_band_mb(const SolveGeom& g, int k, int mid, int l, int stage,

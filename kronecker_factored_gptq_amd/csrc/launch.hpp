@@ -47,16 +47,15 @@ struct LeafParams {
   R* Wt;
   int64_t ldwt;
 };
-// Leaf for super anti-diagonal S (of 2 x 2 blocks of solver tiles) in the
-// block [S0, S1) of super anti-diagonals. Mc (Mt x Nt tiles, the band
-// products' stage-1 buffer, idle inside a block) carries each tile row's
-// partial sums from one tile of the block to the next. ev0 / ev1 (nullable):
-// events stamped with the kernel's start and end by its dispatch (for
-// measurement).
+// Leaf for tile anti-diagonal K whose block of tile anti-diagonals starts at K0.
+// Mc (Mt x Nt tiles, the band products' stage-1 buffer, idle inside a block)
+// carries each tile row's partial sums from one leaf of the block to the next.
+// ev0 / ev1 (nullable): events stamped with the kernel's start and end by
+// its dispatch (for measurement).
 template <typename R>
-hipError_t launch_leaf(const SolveGeom& g, int S, int S0, int S1, R* Wk, const R* LBp,
-                       const R* LAp, R* Mc, const LeafParams<R>& lp, hipStream_t s,
-                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
+                       R* Mc, const LeafParams<R>& lp, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 
 // Buffers of the band products: W tiles (errors on finished tiles), packed
 // L^B and L^A tiles, and the stage-1 product M.
@@ -74,11 +73,8 @@ template <typename R>
 hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage,
                             const BandBuffers<R>& bb, hipStream_t s, hipEvent_t ev0 = nullptr,
                             hipEvent_t ev1 = nullptr);
-// The recursion runs over anti-diagonals of super tiles of kSuper x kSuper
-// solver tiles; a leaf block is kLeafSuperBlock consecutive super
-// anti-diagonals (updates inside a block are left-looking).
-constexpr int kSuper = 2;
-constexpr int kLeafSuperBlock = 6;
+// Tile anti-diagonals per leaf block (updates inside a block are left-looking).
+constexpr int kLeafBlock = 12;
 
 // ---- BaKron-antidiagonal (antidiag_kernels.hip) ----------------------------
 // Workspace of the whole-matrix anti-diagonal solver (element size es): U

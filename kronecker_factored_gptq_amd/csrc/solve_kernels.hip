@@ -232,64 +232,53 @@ __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Waves of a leaf tile: wave w of the prologue takes the block's earlier
+// Waves of a leaf workgroup: wave w of the prologue takes the block's earlier
 // tiles of columns J = Jlo + w, Jlo + w + kLeafWaves, ...
 constexpr int kLeafWaves = 4;
 
-// LDS of one leaf tile (one group of kLeafWaves waves).
 template <typename R>
-struct LeafLds {
-  static constexpr int T = 16;
+__global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, int Mt, int Nt, int64_t m,
+                                                   int64_t n, R* __restrict__ Wk,
+                                                   const R* __restrict__ LBp,
+                                                   const R* __restrict__ LAp,
+                                                   R* __restrict__ Mc, LeafParams<R> lp,
+                                                   BatchStrides bs) {
+  constexpr int T = 16;
+  {  // problem blockIdx.y of a batch: its workspace and outputs
+    const int64_t b = blockIdx.y;
+    Wk += b * bs.ws;
+    LBp += b * bs.ws;
+    LAp += b * bs.ws;
+    Mc += b * bs.ws;
+    lp.V += b * bs.v;
+    if (lp.Wt) lp.Wt += b * bs.wt;
+    if (lp.scales) lp.scales += b * bs.s;
+  }
+  typedef Mfma<R> MF;
+  typedef typename MF::acc_t acc_t;
+  __shared__ R red[kLeafWaves - 1][T][T + 1];
+  __shared__ __attribute__((aligned(16))) R fm[kLeafWaves][T * T];  // fresh-column shares
+  __shared__ R lat[T][T + 1];
   // sweep: value at rounding, one copy per lane row kg; lane (kg, c) writes
   // step t to row t - c + (T - 1) of its copy (a real entry's slot when row
   // t - c is one of its own rows, an unread one otherwise)
-  static constexpr int kOwRows = 3 * T - 2, kOwLd = T + 1 + (int)(sizeof(float) / sizeof(R));
-  R red[kLeafWaves - 1][T][T + 1];                   // the other waves' prologue sums
-  __attribute__((aligned(16))) R fm[kLeafWaves][T * T];  // fresh-column shares
-  R lat[T][T + 1];                                   // L^A[Q,Q]
-  R owv[4][kOwRows][kOwLd];
-};
+  constexpr int kOwRows = 3 * T - 2, kOwLd = T + 1 + (int)(sizeof(float) / sizeof(R));
+  __shared__ R owv[4][kOwRows][kOwLd];
 
-// One tile (P, Q) of a leaf, on one group of kLeafWaves waves (tg = thread
-// index in the group, 0 .. 255): the in-block prologue, then the 31-step
-// sweep on wave `sw` of the group, then the write-back. Every thread of the
-// workgroup calls it (absent tiles do no work), since it holds one
-// workgroup barrier.
-//
-// The block's tiles before (P, Q) with I <= P, J <= Q are the tiles of row P
-// from column Jlo on and of column Q from row Ilo on (and every tile between:
-// the block is a range of anti-diagonals). Row P's partial sums
-// M[P][J] = sum_I L^B[P,I] E[I,J] over the block's tiles (I, J) are carried
-// from tile to tile of the row in Mc (slot J of row P, MFMA lane layout: lane
-// l holds M[c][row(l, r)] at l * 4 + r): the tile before (P, Q) in its row,
-// (P, Q - 1), left M[P][J] final for J < Q - 1 and M[P][Q - 1] without its
-// I = P term; this tile adds that term (and stores it back), forms the new
-// column M[P][Q] from the tiles above it (I < P), and stores that too, when
-// keep (a later tile of row P in the block reads them). The inner sum is
-// computed transposed, M^T = E^T L^B^T, because the MFMA result layout of M^T
-// is exactly the A-operand layout of the outer product with k = its row
-// index: no data movement between the two products.
-template <typename R>
-__device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, int Ilo, bool keep,
-                                          int Nt, int64_t m, int64_t n, R* __restrict__ Wk,
-                                          const R* __restrict__ LBp, const R* __restrict__ LAp,
-                                          R* __restrict__ Mc, const LeafParams<R>& lp, int tg,
-                                          int sw, LeafLds<R>& L) {
-  constexpr int T = 16;
-  typedef Mfma<R> MF;
-  typedef typename MF::acc_t acc_t;
-  constexpr int kOwLd = LeafLds<R>::kOwLd;
-  const int lane = tg & 63, wave = tg >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, kg = lane >> 4;
+  const int P = (K - (Nt - 1) > 0 ? K - (Nt - 1) : 0) + (int)blockIdx.x;
+  const int Q = K - P;
   R* tW = Wk + ((int64_t)P * Nt + Q) * T * T;
 
   // sweep inputs, requested before the prologue so that their latency
-  // overlaps it: this thread's element of L^A[Q,Q] and, on the sweep wave,
-  // the tile and its lbK operands (lbK[s] = L^B[P,P][c][KA kg + KB s])
+  // overlaps it: this thread's element of L^A[Q,Q] and, on wave 0, the tile
+  // and its lbK operands (lbK[s] = L^B[P,P][c][KA kg + KB s])
   constexpr int KA = SweepK<R>::KA, KB = SweepK<R>::KB;
-  const R lat_v = present ? LAp[tri_index(Q, Q) * T * T + tg] : R(0);
+  const R lat_v = tid < T * T ? LAp[tri_index(Q, Q) * T * T + tid] : R(0);
   R w0[4], lbK[4];
-  if (present && wave == sw) {
+  if (wave == 0) {
     const R* lb = LBp + tri_index(P, P) * T * T + c * T + KA * kg;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -298,27 +287,36 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
     }
   }
 
-  // ---- 1. prologue: acc = sum over J of M[P][J] L^A[Q,J]^T.
-  constexpr int NJ = (2 * kLeafSuperBlock - 1 + kLeafWaves - 1) / kLeafWaves;  // cached columns per wave
-  constexpr int NI = NJ;                                                       // fresh-column terms per wave
-  // the prologue waves in a fixed order starting after the sweep wave
-  const int pw = (wave - sw + kLeafWaves) % kLeafWaves;
+  // ---- 1. prologue: acc = sum over J of M[P][J] L^A[Q,J]^T, with
+  // M[P][J] = sum_I L^B[P,I] E[I,J] over the block's earlier tiles (I, J).
+  // Row P's partial sums are kept between the leaves of a block in Mc (slot
+  // J of row P, MFMA lane layout: lane l holds M[c][row(l, r)] at l * 4 + r):
+  // from leaf K - 1 to K only column J = Q - 1 gains a term (I = P) and
+  // column J = Q is new (I < P), so a leaf adds d + 1 tile products instead
+  // of recomputing all (d + 1)(d + 2) / 2 - 1 of them (d = K - K0).
+  constexpr int NJ = (kLeafBlock - 1 + kLeafWaves - 1) / kLeafWaves;  // cached columns per wave
+  constexpr int NI = (kLeafBlock - 1 + kLeafWaves - 1) / kLeafWaves;  // fresh-column terms per wave
+  const int d = K - K0;
+  const bool keep = d + 1 < kLeafBlock;  // a later leaf of this block reads the cache
   acc_t acc = MF::zero();
   acc_t fresh = MF::zero();  // this wave's share of M[P][Q]
   R* McP = Mc + (int64_t)P * Nt * T * T;
-  if (present && (Jlo < Q || Ilo < P)) {
-    // every load first: cached columns J = Jlo + pw + kLeafWaves t < Q,
+  if (d > 0) {
+    const int Jlo = K0 - P > 0 ? K0 - P : 0;
+    const int Ilo = K0 - Q > 0 ? K0 - Q : 0;  // fresh column: Ilo <= I <= P - 1
+    // every load first: cached columns J = Jlo + wave + kLeafWaves t < Q,
     // their L^A tiles, the update term of J = Q - 1, this wave's terms of
     // the fresh column, and L^A[Q,Q]
     R la[NJ][4], mc[NJ][4], laq[4], eu[4], lu[4], ef[NI][4], lf[NI][4];
     // Float: no branch around these loads (a load under a branch made the
     // compiler wait there for every load in flight, the sweep operands
-    // included; columns J >= Q read slot Q instead and are never used):
-    // 1.8 % faster solve. Double: 3.6 % slower that way, so it keeps the guards.
+    // included; columns J >= Q read slot Q instead and are never used, and
+    // the cache is selected away before the block's third leaf): 1.8 %
+    // faster solve. Double: 3.6 % slower that way, so it keeps the guards.
     constexpr bool kFlatLoads = std::is_same<R, float>::value;
 #pragma unroll
     for (int t = 0; t < NJ; ++t) {
-      const int J = Jlo + pw + kLeafWaves * t;
+      const int J = Jlo + wave + kLeafWaves * t;
       if constexpr (kFlatLoads) {
         const int Jc = J < Q ? J : Q;
         const R* La = LAp + tri_index(Q, Jc) * T * T;
@@ -332,7 +330,7 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
           const R* La = LAp + tri_index(Q, J) * T * T;
 #pragma unroll
           for (int s = 0; s < 4; ++s) la[t][s] = La[c * T + MF::row(lane, s)];
-          EVec<R>::load4(McP + (int64_t)J * T * T + lane * 4, mc[t]);
+          if (d >= 2) EVec<R>::load4(McP + (int64_t)J * T * T + lane * 4, mc[t]);
         }
       }
     }
@@ -341,7 +339,7 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
 #pragma unroll
       for (int s = 0; s < 4; ++s) laq[s] = La[c * T + MF::row(lane, s)];
     }
-    const bool upd = Q >= 1 && Q - 1 >= Jlo && (Q - 1 - Jlo) % kLeafWaves == pw;
+    const bool upd = Q >= 1 && Q - 1 >= Jlo && (Q - 1 - Jlo) % kLeafWaves == wave;
     if (upd) {
       const R* E = Wk + ((int64_t)P * Nt + Q - 1) * T * T;
       EVec<R>::load4(LBp + tri_index(P, P) * T * T + c * T + 4 * kg, lu);
@@ -350,7 +348,7 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
     }
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      const int I = Ilo + pw + kLeafWaves * u;
+      const int I = Ilo + wave + kLeafWaves * u;
       if (I <= P - 1) {
         const R* E = Wk + ((int64_t)I * Nt + Q) * T * T;
         EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lf[u]);
@@ -364,7 +362,7 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
     // fresh column: this wave's terms, and its part of the outer product
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      if (Ilo + pw + kLeafWaves * u > P - 1) break;
+      if (Ilo + wave + kLeafWaves * u > P - 1) break;
 #pragma unroll
       for (int s = 0; s < 4; ++s) fresh = MF::mma(ef[u][s], lf[u][s], fresh);
     }
@@ -373,11 +371,11 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
     // cached columns (J = Q - 1 gains its term and is stored back)
 #pragma unroll
     for (int t = 0; t < NJ; ++t) {
-      const int J = Jlo + pw + kLeafWaves * t;
+      const int J = Jlo + wave + kLeafWaves * t;
       if (J >= Q) break;
       acc_t mt;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mt[r] = mc[t][r];
+      for (int r = 0; r < 4; ++r) mt[r] = (!kFlatLoads || d >= 2) ? mc[t][r] : R(0);
       if (J == Q - 1) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) mt = MF::mma(eu[s], lu[s], mt);
@@ -391,44 +389,44 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], la[t][s], acc);
     }
-  }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) L.fm[pw][lane * 4 + r] = fresh[r];
-  if (pw > 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) L.red[pw - 1][MF::row(lane, r)][c] = acc[r];
+    for (int r = 0; r < 4; ++r) fm[wave][lane * 4 + r] = fresh[r];
   }
-  L.lat[tg >> 4][tg & 15] = lat_v;
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave - 1][MF::row(lane, r)][c] = acc[r];
+  }
+  if (tid < T * T) lat[tid >> 4][tid & 15] = lat_v;
   __syncthreads();
-  if (present && pw == 1 && keep) {
-    // the fresh column M[P][Q] for the next tile of the row, summed over the
-    // waves in a fixed order (zero when no tile above it is in the block)
+  if (wave == 1 && d > 0 && keep) {
+    // the fresh column M[P][Q] for the next leaf of the block, summed over
+    // the waves in a fixed order
     R o[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      R v = L.fm[0][lane * 4 + r];
+      R v = fm[0][lane * 4 + r];
 #pragma unroll
-      for (int w = 1; w < kLeafWaves; ++w) v += L.fm[w][lane * 4 + r];
+      for (int w = 1; w < kLeafWaves; ++w) v += fm[w][lane * 4 + r];
       o[r] = v;
     }
     EVec<R>::store4(McP + (int64_t)Q * T * T + lane * 4, o);
   }
-  if (!present || pw != 0) return;
+  if (wave > 0) return;
 
-  // ---- 2. sweep on wave sw
+  // ---- 2. sweep on wave 0
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = MF::row(lane, r);
     R pro = w0[r];
 #pragma unroll
-    for (int w = 0; w < kLeafWaves - 1; ++w) pro += L.red[w][row][c];
+    for (int w = 0; w < kLeafWaves - 1; ++w) pro += red[w][row][c];
     acc[r] += pro;
   }
   R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - KA kg]
 #pragma unroll
   for (int j = 0; j < 2 * T - 1; ++j) {
     const int jj = j - KA * kg;
-    laK[j] = (jj >= 0 && jj < T) ? L.lat[c][jj] : R(0);
+    laK[j] = (jj >= 0 && jj < T) ? lat[c][jj] : R(0);
   }
   const R lo = lp.lo, hi = lp.hi;  // +-infinity for the unbounded alphabet
 
@@ -445,7 +443,7 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
   // between padding and real rows or columns, so neither side changes the
   // other. The value at rounding goes to the lane row's own LDS copy at a
   // constant offset per step.
-  R* owl = &L.owv[kg][T - 1 - c][c];
+  R* owl = &owv[kg][T - 1 - c][c];
   static_for<0, 2 * T - 1>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
     R x = acc[0];
@@ -479,7 +477,7 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
     const int p = idx >> 4, q = idx & 15;
     const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + q;
     const bool valid = gi < m && gjj < n;
-    const R x = L.owv[std::is_same<R, float>::value ? p >> 2 : p & 3][p + T - 1][q];
+    const R x = owv[std::is_same<R, float>::value ? p >> 2 : p & 3][p + T - 1][q];
     const R cq = quant_unit(x, lo, hi);
     tW[idx] = valid ? cq - x : R(0);
     if (valid) {
@@ -492,65 +490,6 @@ __device__ __forceinline__ void leaf_tile(bool present, int P, int Q, int Jlo, i
       }
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Leaf of super anti-diagonal S (2 x 2 blocks of 16 x 16 tiles), the
-// (S - S0)-th of the block [S0, S1) of super anti-diagonals. One workgroup
-// per super tile (P2, Q2), two groups of four waves. Its tiles a = (2P2, 2Q2),
-// b = (2P2, 2Q2 + 1), c = (2P2 + 1, 2Q2), d = (2P2 + 1, 2Q2 + 1) lie on tile
-// anti-diagonals 2S, 2S + 1, 2S + 1, 2S + 2 and depend on each other only in
-// that order (an error reaches only tiles below and to the right, §3.3), and
-// on tiles of earlier super anti-diagonals. So a single launch does a, then b
-// and c side by side (one group each), then d, handing the errors on through
-// the workgroup's own memory: half the dependent launches of one launch per
-// tile anti-diagonal, for one more sequential sweep per two tile
-// anti-diagonals.
-// ---------------------------------------------------------------------------
-template <typename R>
-__global__ __launch_bounds__(128 * kLeafWaves) void leaf2_kernel(int S, int S0, int S1, int Mt,
-                                                    int Nt, int64_t m, int64_t n,
-                                                    R* __restrict__ Wk,
-                                                    const R* __restrict__ LBp,
-                                                    const R* __restrict__ LAp,
-                                                    R* __restrict__ Mc, LeafParams<R> lp,
-                                                    BatchStrides bs) {
-  {  // problem blockIdx.y of a batch: its workspace and outputs
-    const int64_t b = blockIdx.y;
-    Wk += b * bs.ws;
-    LBp += b * bs.ws;
-    LAp += b * bs.ws;
-    Mc += b * bs.ws;
-    lp.V += b * bs.v;
-    if (lp.Wt) lp.Wt += b * bs.wt;
-    if (lp.scales) lp.scales += b * bs.s;
-  }
-  __shared__ LeafLds<R> lds[2];
-  const int tid = threadIdx.x;
-  const int grp = tid >> 8, tg = tid & 255;
-  const int Nt2 = (Nt + 1) >> 1;
-  const int P2 = (S - (Nt2 - 1) > 0 ? S - (Nt2 - 1) : 0) + (int)blockIdx.x;
-  const int Q2 = S - P2;
-  // the two groups sweep on different waves (different SIMDs) when b and c
-  // run side by side
-  const int sw = grp;
-  static_for<0, 3>([&](auto stc) {
-    constexpr int st = decltype(stc)::value;
-    // step 0: a (group 0); step 1: b (group 0) and c (group 1); step 2: d (group 0)
-    const bool on = st == 1 || grp == 0;
-    const int P = 2 * P2 + (st == 2 || (st == 1 && grp == 1) ? 1 : 0);
-    const int Q = 2 * Q2 + (st == 2 || (st == 1 && grp == 0) ? 1 : 0);
-    const bool present = on && P < Mt && Q < Nt;
-    // the block's first column in row P and first row in column Q
-    const int Jlo = S0 - (P >> 1) > 0 ? 2 * (S0 - (P >> 1)) : 0;
-    const int Ilo = S0 - (Q >> 1) > 0 ? 2 * (S0 - (Q >> 1)) : 0;
-    // a later tile of row P in the block reads the carried sums
-    const bool keep = Q + 1 < Nt && (P >> 1) + ((Q + 1) >> 1) < S1;
-    leaf_tile<R>(present, P, Q, Jlo, Ilo, keep, Nt, m, n, Wk, LBp, LAp, Mc, lp, tg, sw, lds[grp]);
-    // this step's errors and carried sums, written through memory, are read
-    // by the next step's tiles
-    __syncthreads();
-  });
 }
 
 // ---------------------------------------------------------------------------
@@ -578,28 +517,31 @@ hipError_t launch_pack_l(const SolveGeom& g, bool lb, const R* L, int64_t ld, co
   return hipGetLastError();
 }
 
+static inline void diag_range(const SolveGeom& g, int K, int* lo, int* hi) {
+  *lo = K - (g.Nt - 1) > 0 ? K - (g.Nt - 1) : 0;
+  *hi = K < g.Mt - 1 ? K : g.Mt - 1;
+}
+
 template <typename R>
-hipError_t launch_leaf(const SolveGeom& g, int S, int S0, int S1, R* Wk, const R* LBp,
-                       const R* LAp, R* Mc, const LeafParams<R>& lp, hipStream_t s,
-                       hipEvent_t ev0, hipEvent_t ev1) {
-  static_assert(kTile == 16 && kSuper == 2, "the leaf kernel works on 2 x 2 blocks of 16 x 16 tiles");
-  // super tiles (P2, S - P2) on super anti-diagonal S
-  const int Mt2 = (g.Mt + 1) / 2, Nt2 = (g.Nt + 1) / 2;
-  const int lo = S - (Nt2 - 1) > 0 ? S - (Nt2 - 1) : 0;
-  const int hi = S < Mt2 - 1 ? S : Mt2 - 1;
+hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
+                       R* Mc, const LeafParams<R>& lp, hipStream_t s, hipEvent_t ev0,
+                       hipEvent_t ev1) {
+  static_assert(kTile == 16, "the leaf kernel works on 16 x 16 tiles");
+  int lo, hi;
+  diag_range(g, K, &lo, &hi);
   if (hi < lo || g.batch <= 0) {
     // nothing to do; keep the timing events valid (zero duration)
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return hipErrorUnknown;
     if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return hipErrorUnknown;
     return hipSuccess;
   }
-  const dim3 grid(hi - lo + 1, g.batch), block(128 * kLeafWaves);
+  const dim3 grid(hi - lo + 1, g.batch), block(64 * kLeafWaves);
   if (ev0 || ev1)  // the events are stamped by the dispatch packet itself
-    hipExtLaunchKernelGGL((leaf2_kernel<R>), grid, block, 0, s, ev0, ev1, 0, S, S0, S1, g.Mt,
-                          g.Nt, g.m, g.n, Wk, LBp, LAp, Mc, lp, g.bs);
+    hipExtLaunchKernelGGL((leaf_kernel<R>), grid, block, 0, s, ev0, ev1, 0, K, K0, g.Mt, g.Nt,
+                          g.m, g.n, Wk, LBp, LAp, Mc, lp, g.bs);
   else
-    hipLaunchKernelGGL((leaf2_kernel<R>), grid, block, 0, s, S, S0, S1, g.Mt, g.Nt, g.m, g.n, Wk,
-                       LBp, LAp, Mc, lp, g.bs);
+    hipLaunchKernelGGL((leaf_kernel<R>), grid, block, 0, s, K, K0, g.Mt, g.Nt, g.m, g.n, Wk, LBp,
+                       LAp, Mc, lp, g.bs);
   return hipGetLastError();
 }
 
@@ -608,9 +550,8 @@ hipError_t launch_leaf(const SolveGeom& g, int S, int S0, int S1, R* Wk, const R
                                        hipStream_t);                                            \
   template hipError_t launch_pack_l<R>(const SolveGeom&, bool, const R*, int64_t, const R*, R*, \
                                        hipStream_t);                                            \
-  template hipError_t launch_leaf<R>(const SolveGeom&, int, int, int, R*, const R*, const R*,   \
-                                     R*, const LeafParams<R>&, hipStream_t, hipEvent_t,          \
-                                     hipEvent_t);
+  template hipError_t launch_leaf<R>(const SolveGeom&, int, int, R*, const R*, const R*, R*,    \
+                                     const LeafParams<R>&, hipStream_t, hipEvent_t, hipEvent_t);
 BK_INST(float)
 BK_INST(double)
 #undef BK_INST

@@ -31,8 +31,7 @@ def test_status_strings_and_version():
     assert L.bakron_abi_version() == 1
     for st in (0, -1, -2, -3):
         assert L.bakron_status_string(st)
-    # the edge of the super tiles (2 x 2 solver tiles of 16) the recursion runs over
-    assert bk.tile_size(bk.F32) == bk.tile_size(bk.F64) == 32
+    assert bk.tile_size(bk.F32) == bk.tile_size(bk.F64) == 16
     assert bk.tile_size(7) == 0
 
 
@@ -225,27 +224,27 @@ def test_row_scales_mse_rejects_bad_arguments(bad):
     assert L.bakron_row_scales_mse(bk.F32, 0, 4, None, 4, -8, 7, 100, 0.5, None, None) == bk.OK
 
 
-def _closed_form_leaves(m, n, T=32):
+def _closed_form_leaves(m, n, T=16):
     return -(-m // T) + -(-n // T) - 1
 
 
 @pytest.mark.parametrize("m,n", [(1, 1), (16, 16), (17, 5), (64, 64), (200, 300), (512, 512),
                                  (4096, 4096), (14336, 4096), (4096, 14336), (1024, 2048)])
 def test_schedule_is_algorithm_6_over_blocks_of_tile_antidiagonals(m, n):
-    """Table 1 "Steps" for BaKron: one leaf per anti-diagonal of 32 x 32
-    super tiles, in order; Algorithm 6's recursion over blocks of G such
-    anti-diagonals (G read from the second block's start), each internal
-    node splitting block range [kb, lb) at floor((kb+lb)/2) and running after
-    the last leaf left of its midpoint and before the first leaf right of it;
-    inside a block, each leaf names its block's start and end."""
+    """Table 1 "Steps" for BaKron: one leaf per (tile) anti-diagonal, in
+    order; Algorithm 6's recursion over blocks of G tile anti-diagonals (G
+    read from the second block's start), each internal node splitting block
+    range [kb, lb) at floor((kb+lb)/2) and running after the last leaf left
+    of its midpoint and before the first leaf right of it; inside a block,
+    each leaf names its block start."""
     ops = bk.solve_schedule(bk.F32, m, n)
     R = _closed_form_leaves(m, n)
-    leaves = [(a, b, c) for (kind, a, b, c) in ops if kind == 0]
-    assert [a for a, _, _ in leaves] == list(range(R))
-    starts = sorted({b for _, b, _ in leaves})
+    leaves = [(a, b) for (kind, a, b, c) in ops if kind == 0]
+    assert [a for a, _ in leaves] == list(range(R))
+    starts = sorted({b for _, b in leaves})
     BLOCK = starts[1] if len(starts) > 1 else R + 1  # one block: any G > R
     nblocks = -(-R // BLOCK)
-    assert all(b == (a // BLOCK) * BLOCK and c == min(b + BLOCK, R) for a, b, c in leaves)
+    assert all(b == (a // BLOCK) * BLOCK for a, b in leaves)
     nodes = [(a, b, c) for (kind, a, b, c) in ops if kind == 2]
     assert len(nodes) == nblocks - 1
     assert sorted(mid for (_, mid, _) in nodes) == [BLOCK * i for i in range(1, nblocks)]

@@ -86,12 +86,12 @@ def test_in_block_count_matches_brute_force(m, n, T, K0, K1):
 
 
 def test_total_is_of_order_mn_m_plus_n_at_4096():
-    """Sum over all nodes at 4096^2 with the schedule's 32-wide blocks:
-    ~1.8 mn(m+n) flop in total (Appendix C's O(mn(m+n))), the bulk of it in
-    the band products (the leaves' in-block updates between blocks take a few
-    per cent with 6 block anti-diagonals per leaf block)."""
+    """Sum over all nodes at 4096^2 with 16-wide tiles: ~1.8 mn(m+n) flop in
+    total (Appendix C's O(mn(m+n))), the bulk of it in the band products (the
+    leaves' in-block updates between tiles take a few per cent with 12 tile
+    anti-diagonals per leaf block)."""
     ops = bk.solve_schedule(bk.F32, 4096, 4096)
-    f = schedule_flops(4096, 4096, bk.tile_size(bk.F32), ops)
+    f = schedule_flops(4096, 4096, 16, ops)
     total = f["in_block"] + f["band"]
     assert 1.6 * 4096 ** 3 * 2 < total < 1.85 * 4096 ** 3 * 2
     assert f["band"] > 0.9 * total
