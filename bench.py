@@ -380,7 +380,9 @@ def main():
         }
         leaf_ms = float(np.mean(leaf_ms_steps))
         result["leaf"] = {
-            "kernel": "leaf_kernel (in-block updates + 31-step in-tile sweep)", "bound": "latency",
+            "kernel": "leaf_rows_kernel (one launch per leaf block of tile anti-diagonals: "
+                      "one workgroup per tile row, in-block updates + 31-step in-tile sweeps)",
+            "bound": "latency",
             "launches_per_step": len(leaf_idx), "ms_per_step": leaf_ms,
             "avg_launch_us": leaf_ms * 1e3 / max(len(leaf_idx), 1),
             "note": "kernel execution time from dispatch-stamped events; the rest of the solve "

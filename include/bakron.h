@@ -15,7 +15,9 @@
  *    column-major caller can pass (n, m, W^T, B, A) with column scales.
  *  - Every pointer except `bad_pivot` is a device pointer owned by the
  *    caller. The library allocates and frees no device memory and keeps no
- *    global state; scratch memory is the caller's `workspace` of at least
+ *    global state (but for bakron_solve_noalloc's scratch and the poll bound
+ *    of bakron_debug_set_wait_polls); scratch memory is the caller's
+ *    `workspace` of at least
  *    the size the matching *_workspace_bytes query returns (256-byte
  *    aligned). The synchronous factor calls are the one place that creates
  *    HIP objects: when m != n, or an order exceeds 8192, bakron_factor and
@@ -50,6 +52,8 @@ extern "C" {
                                mode, alphabet, or workspace too small */
 #define BAKRON_ENOTSPD (-2) /* A or B is not numerically positive definite */
 #define BAKRON_EHIP (-3)    /* a HIP runtime call or kernel launch failed */
+#define BAKRON_EWAIT (-4)   /* a solve's bounded wait inside a leaf block gave up
+                               (bakron_solve_status): its outputs are invalid */
 
 /* Element types. */
 #define BAKRON_F32 0
@@ -149,6 +153,12 @@ int bakron_factor_batched(int dtype, int64_t batch, int64_t m, int64_t n,
  *
  * Asynchronous. Deterministic: the same inputs give bit-identical outputs.
  * Non-finite inputs give unspecified codes.
+ *
+ * Inside a leaf block (a launch that solves G consecutive tile
+ * anti-diagonals, one workgroup per tile row) each row waits for the rows
+ * above it through the workspace. Every wait is for a running workgroup and
+ * is bounded (about 0.1 s); one that gives up lets the launch finish with
+ * invalid outputs and marks the workspace: bakron_solve_status reports it.
  * ------------------------------------------------------------------------ */
 size_t bakron_solve_workspace_bytes(int dtype, int64_t m, int64_t n);
 int bakron_solve(int dtype, int64_t m, int64_t n,
@@ -190,15 +200,15 @@ int bakron_solve_antidiag(int dtype, int64_t m, int64_t n,
  * that GPU until the process ends (the first call on a device looks up its
  * address; no call allocates or frees anything). A problem whose
  * bakron_solve_workspace_bytes exceeds BAKRON_NOALLOC_SCRATCH_BYTES is
- * BAKRON_EINVAL (checked before any HIP call): 64 MiB holds 2048 x 2048 in
- * float32 or 1024 x 2048 in float64.
+ * BAKRON_EINVAL (checked before any HIP call): 96 MiB holds up to 2496 x
+ * 2496 in float32, or 1024 x 2048 in float64.
  * All calls on one GPU share its scratch, and it keeps the last call's
  * contents (no part needs to start at zero: the solve writes every word
  * before reading it): calls that may overlap on one GPU (different streams,
  * or host threads) race and must be serialised by the caller. The device
  * is the current one (hipGetDevice), and `stream` must belong to it.
  * ------------------------------------------------------------------------ */
-#define BAKRON_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define BAKRON_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
 int bakron_solve_noalloc(int dtype, int64_t m, int64_t n,
                          const void *W, int64_t ldw,
                          const void *LA, int64_t ldla, const void *LB, int64_t ldlb,
@@ -210,10 +220,10 @@ int bakron_solve_noalloc(int dtype, int64_t m, int64_t n,
 /* The launch schedule bakron_solve uses for (dtype, m, n), for measurement:
  * writes up to `max_ops` records of 4 int32 {kind, a, b, c} to the HOST
  * array `ops` (nullable) and returns the total number of records, or a
- * negative status. kind 0 = leaf: a = tile anti-diagonal K, b = first tile
- * anti-diagonal of its block (the leaf also applies the updates from tile
- * anti-diagonals b..K-1); kinds 2 and 3 = the two band products of an
- * internal node, tile anti-diagonals [a, b) -> [b, c). Host only. */
+ * negative status. kind 0 = leaf block: tile anti-diagonals [a, b), solved in
+ * order with the updates between them (§3.5 Algorithm 6's leaf, one
+ * launch); kinds 2 and 3 = the two band products of an internal node, tile
+ * anti-diagonals [a, b) -> [b, c). Host only. */
 int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t *ops, int64_t max_ops);
 
 /* Measurement variant of bakron_solve: same arguments and result, and it
@@ -223,8 +233,9 @@ int64_t bakron_solve_schedule(int dtype, int64_t m, int64_t n, int32_t *ops, int
  * (hipExtLaunchKernel start/stop events; 0 for a launch with no work);
  * on an error every slot receives -1. `op_ms` is a HOST
  * array of `n_ops` doubles and n_ops must equal the schedule length.
- * SYNCHRONOUS (waits for the last event). Creates and destroys its events;
- * returns BAKRON_EHIP if that fails. */
+ * SYNCHRONOUS (waits for the last event), and also returns BAKRON_EWAIT as
+ * bakron_solve_status would. Creates and destroys its events; returns
+ * BAKRON_EHIP if that fails. */
 int bakron_solve_timed(int dtype, int64_t m, int64_t n,
                        const void *W, int64_t ldw,
                        const void *LA, int64_t ldla, const void *LB, int64_t ldlb,
@@ -234,6 +245,23 @@ int bakron_solve_timed(int dtype, int64_t m, int64_t n,
                        void *Wt, int64_t ldwt,
                        void *workspace, size_t workspace_bytes, void *stream,
                        double *op_ms, int64_t n_ops);
+
+/* Status of the last solve(s) run on `workspace`: waits for `stream`, then
+ * returns BAKRON_EWAIT if a wait inside a leaf block of any of the `batch`
+ * problems gave up (their outputs are invalid), else BAKRON_OK. The
+ * arguments are those of the solve: (dtype, 1, m, n, workspace,
+ * workspace_bytes) for bakron_solve, (dtype, batch, m, n, ...) for
+ * bakron_solve_batched, (dtype, heads, m / heads, n, ...) for
+ * bakron_solve_blockdiag; workspace = NULL reads the current device's
+ * scratch of bakron_solve_noalloc (batch 1). SYNCHRONOUS. */
+int bakron_solve_status(int dtype, int64_t batch, int64_t m, int64_t n, const void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Test hook: sets the poll bound of the leaf blocks' waits for solves
+ * enqueued from now on, process-wide (polls < 0 restores the default,
+ * 65536; 0 makes any wait that finds its data not yet written give up at
+ * once); returns the previous bound. Host only. */
+int32_t bakron_debug_set_wait_polls(int32_t polls);
 
 /* ------------------------------------------------------------------------
  * Batched solve: bakron_solve on `batch` problems of the same shape (m x n)

@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libbakron.so")
 
 F32, F64 = 0, 1
 SCALE_NONE, SCALE_ROW, SCALE_COL = 0, 1, 2
-OK, EINVAL, ENOTSPD, EHIP = 0, -1, -2, -3
+OK, EINVAL, ENOTSPD, EHIP, EWAIT = 0, -1, -2, -3, -4
 
 
 class BakronError(RuntimeError):
@@ -97,6 +97,10 @@ def lib() -> ctypes.CDLL:
     L.bakron_solve_noalloc.restype = _int
     L.bakron_solve_timed.argtypes = L.bakron_solve.argtypes + [_vp, _i64]
     L.bakron_solve_timed.restype = _int
+    L.bakron_solve_status.argtypes = [_int, _i64, _i64, _i64, _vp, _sz, _vp]
+    L.bakron_solve_status.restype = _int
+    L.bakron_debug_set_wait_polls.argtypes = [_i32]
+    L.bakron_debug_set_wait_polls.restype = _i32
     L.bakron_solve_schedule.argtypes = [_int, _i64, _i64, _vp, _i64]
     L.bakron_solve_schedule.restype = _i64
     L.bakron_factor_batched_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
@@ -308,12 +312,15 @@ def _scale_mode(scales: Optional[torch.Tensor], m: int, n: int, scale_mode: Opti
 def solve(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: AlphabetLike = (0, 0, 1),
           scales: Optional[torch.Tensor] = None, scale_mode: Optional[int] = None,
           return_wt: bool = False, workspace: Optional[torch.Tensor] = None,
-          out: Optional[torch.Tensor] = None, op_ms: Optional[ctypes.Array] = None):
+          out: Optional[torch.Tensor] = None, op_ms: Optional[ctypes.Array] = None,
+          check: bool = False):
     """BaKron solve (§3.5 Algorithm 6 on a tiling of W). Returns int32 codes V
     (m x n), and with ``return_wt`` also the value each entry had when it was
     rounded. Asynchronous on the current stream, except with ``op_ms`` (a
-    ctypes double array, one slot per schedule record): then the band-product
-    launches are timed with HIP events and the call waits for them."""
+    ctypes double array, one slot per schedule record: every leaf-block and
+    band-product launch is timed with HIP events and the call waits for
+    them) or ``check`` (waits, then raises BakronError(EWAIT) if a leaf
+    block's bounded wait gave up)."""
     dev = _check_device(W, LA, LB, scales, workspace, out)
     code = _dt(W)
     m, n = W.shape
@@ -339,6 +346,9 @@ def solve(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: Alphabe
             rc = L.bakron_solve(*args)
         else:
             rc = L.bakron_solve_timed(*args, ctypes.cast(op_ms, ctypes.c_void_p), len(op_ms))
+    if rc == OK and check:
+        rc = L.bakron_solve_status(code, 1, m, n, _p(ws), ws.numel() * ws.element_size(),
+                                   _stream(dev))
     if rc != OK:
         raise BakronError(rc, "bakron_solve")
     return (V, Wt) if return_wt else V
@@ -422,9 +432,10 @@ def factor_blockdiag(A: torch.Tensor, Bblocks: torch.Tensor, workspace: Optional
 def solve_blockdiag(W: torch.Tensor, LA: torch.Tensor, LBblocks: torch.Tensor,
                     alphabet: AlphabetLike = (0, 0, 1), scales: Optional[torch.Tensor] = None,
                     scale_mode: Optional[int] = None, return_wt: bool = False,
-                    workspace: Optional[torch.Tensor] = None):
+                    workspace: Optional[torch.Tensor] = None, check: bool = False):
     """The BaKron solve with a block-diagonal L^B given by its blocks
-    (heads, b, b), m = heads * b: all heads in the same launches."""
+    (heads, b, b), m = heads * b: all heads in the same launches. ``check``:
+    as in ``solve``."""
     dev = _check_device(W, LA, LBblocks, scales, workspace)
     code = _dt(W)
     m, n = W.shape
@@ -447,6 +458,9 @@ def solve_blockdiag(W: torch.Tensor, LA: torch.Tensor, LBblocks: torch.Tensor,
                                       plb, ldlb, slb, lo, hi, unb, mode, _p(scales), _p(V),
                                       _ld(V, "V"), _p(Wt), _ld(Wt, "Wt") if Wt is not None else 0,
                                       _p(ws), ws.numel() * ws.element_size(), _stream(dev))
+    if rc == OK and check:
+        rc = L.bakron_solve_status(code, heads, b, n, _p(ws), ws.numel() * ws.element_size(),
+                                   _stream(dev))
     if rc != OK:
         raise BakronError(rc, "bakron_solve_blockdiag")
     return (V, Wt) if return_wt else V
@@ -484,16 +498,16 @@ def loss_blockdiag(W: torch.Tensor, V: torch.Tensor, A: torch.Tensor, Bblocks: t
 
 # Largest workspace bakron_solve_noalloc takes from its in-library scratch
 # (BAKRON_NOALLOC_SCRATCH_BYTES in include/bakron.h).
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 
 def solve_noalloc(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet: AlphabetLike,
                   scales: Optional[torch.Tensor], V: torch.Tensor, Wt: Optional[torch.Tensor] = None,
-                  scale_mode: Optional[int] = None) -> torch.Tensor:
+                  scale_mode: Optional[int] = None, check: bool = False) -> torch.Tensor:
     """bakron_solve_noalloc: the solve of ``solve`` with the library's own
     per-GPU scratch instead of a workspace. The caller passes the outputs
     (V int32 m x n, optional Wt of W's dtype); nothing is allocated. Calls
-    that overlap on one GPU race on the scratch."""
+    that overlap on one GPU race on the scratch. ``check``: as in ``solve``."""
     dev = _check_device(W, LA, LB, scales, V, Wt)
     code = _dt(W)
     m, n = W.shape
@@ -511,6 +525,9 @@ def solve_noalloc(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor, alphabet:
                                         _p(LB), _ld(LB, "LB"), lo, hi, unb, mode, _p(scales),
                                         _p(V), _ld(V, "V"), _p(Wt),
                                         _ld(Wt, "Wt") if Wt is not None else 0, _stream(dev))
+    if rc == OK and check:
+        with torch.cuda.device(dev):
+            rc = lib().bakron_solve_status(code, 1, m, n, None, 0, _stream(dev))
     if rc != OK:
         raise BakronError(rc, "bakron_solve_noalloc")
     return V
@@ -534,13 +551,13 @@ def _batch_operand(t: torch.Tensor, rows: int, cols: int, batch: int, name: str)
 def solve_batched(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor,
                   alphabet: AlphabetLike = (0, 0, 1), scales: Optional[torch.Tensor] = None,
                   scale_mode: Optional[int] = None, return_wt: bool = False,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None, check: bool = False):
     """bakron_solve on a batch of problems of one shape in the same launches.
     W is (batch, m, n); LA is (batch, n, n) or one (n, n) factor shared by
     all problems, LB likewise (batch, m, m) or (m, m); scales (batch, m) /
     (batch, n) or one shared vector. Returns int32 codes (batch, m, n) and,
     with ``return_wt``, the values at rounding. Each problem's result equals
-    ``solve`` on the same inputs bit for bit."""
+    ``solve`` on the same inputs bit for bit. ``check``: as in ``solve``."""
     dev = _check_device(W, LA, LB, scales, workspace)
     code = _dt(W)
     if W.dim() != 3:
@@ -575,6 +592,9 @@ def solve_batched(W: torch.Tensor, LA: torch.Tensor, LB: torch.Tensor,
                                     _p(Wt), max(n, 1) if return_wt else 0,
                                     m * n if return_wt else 0, _p(ws),
                                     ws.numel() * ws.element_size(), _stream(dev))
+    if rc == OK and check:
+        rc = L.bakron_solve_status(code, batch, m, n, _p(ws), ws.numel() * ws.element_size(),
+                                   _stream(dev))
     if rc != OK:
         raise BakronError(rc, "bakron_solve_batched")
     return (V, Wt) if return_wt else V
@@ -727,10 +747,16 @@ def shampoo_factors(Xa: torch.Tensor, Xb: torch.Tensor, damp_rel: float = 0.0):
     return gram(Xa, sample_sqnorms(Xb), damp_rel), gram(Xb, sample_sqnorms(Xa), damp_rel)
 
 
+def debug_set_wait_polls(polls: int) -> int:
+    """Test hook: the poll bound of the leaf blocks' waits for solves enqueued
+    from now on (negative: the default); returns the previous bound."""
+    return int(lib().bakron_debug_set_wait_polls(int(polls)))
+
+
 def solve_schedule(dtype: int, m: int, n: int):
-    """The solve's launch schedule: list of (kind, a, b, c); kind 0 = leaf of
-    tile anti-diagonal a whose block starts at b, kinds 2/3 = the two band
-    products of the internal node [a, b) -> [b, c). Host only."""
+    """The solve's launch schedule: list of (kind, a, b, c); kind 0 = leaf
+    block of tile anti-diagonals [a, b), kinds 2/3 = the two band products of
+    the internal node [a, b) -> [b, c). Host only."""
     L = lib()
     cnt = int(L.bakron_solve_schedule(int(dtype), int(m), int(n), None, 0))
     if cnt < 0:

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <cstring>
@@ -39,12 +40,12 @@ struct Op {
 enum { OP_LEAF = 0, OP_BAND1 = 2, OP_BAND2 = 3 };
 
 // Algorithm 6 over blocks [kb, lb) of kLeafBlock tile anti-diagonals each
-// (R tile anti-diagonals in all); a block's leaves run in order.
+// (R tile anti-diagonals in all); a leaf is a whole block, one launch.
 void build_schedule(int kb, int lb, int R, std::vector<Op>& ops) {
   if (lb - kb == 1) {
     const int K0 = kb * kLeafBlock;
     const int K1 = (kb + 1) * kLeafBlock < R ? (kb + 1) * kLeafBlock : R;
-    for (int K = K0; K < K1; ++K) ops.push_back({OP_LEAF, K, K0, 0});
+    ops.push_back({OP_LEAF, K0, K1, 0});
     return;
   }
   const int midb = (kb + lb) / 2;
@@ -61,15 +62,22 @@ std::vector<Op> schedule_for(int64_t m, int64_t n) {
   if (m <= 0 || n <= 0) return ops;
   const int R = (int)(tiles(m) + tiles(n) - 1);
   const int nb = (R + kLeafBlock - 1) / kLeafBlock;
-  ops.reserve(3 * (size_t)R);
+  ops.reserve(3 * (size_t)nb);
   build_schedule(0, nb, R, ops);
   return ops;
 }
 
-// Solve workspace: W tiles, packed L^B and L^A tiles, and the stage-1
-// product M of the band products.
+// leaf blocks of the schedule of an m x n solve
+inline int leaf_blocks(int64_t m, int64_t n) {
+  const int64_t R = tiles(m) + tiles(n) - 1;
+  return (int)((R + kLeafBlock - 1) / kLeafBlock);
+}
+
+// Solve workspace, per problem: W tiles, packed L^B and L^A tiles, the
+// stage-1 product M of the band products, the leaf blocks' ticket counters
+// and status word, and the leaves' error copy (Mt x Nt tiles).
 struct SolveLayout {
-  size_t wk, lb, la, mb, total;
+  size_t wk, lb, la, mb, sync, eb, total;
 };
 SolveLayout solve_layout(int dtype, int64_t m, int64_t n) {
   const size_t es = esize(dtype);
@@ -80,8 +88,33 @@ SolveLayout solve_layout(int dtype, int64_t m, int64_t n) {
   L.lb = align_up((size_t)(Mt * (Mt + 1) / 2) * tt);
   L.la = align_up((size_t)(Nt * (Nt + 1) / 2) * tt);
   L.mb = L.wk;
-  L.total = L.wk + L.lb + L.la + L.mb + kAlign;
+  L.sync = align_up((size_t)(leaf_blocks(m, n) + 1) * sizeof(int));
+  L.eb = L.wk;
+  L.total = L.wk + L.lb + L.la + L.mb + L.sync + L.eb + kAlign;
   return L;
+}
+// offset of the status word in a problem's workspace
+inline size_t status_offset(const SolveLayout& L, int64_t m, int64_t n) {
+  return L.wk + L.lb + L.la + L.mb + (size_t)leaf_blocks(m, n) * sizeof(int);
+}
+
+// Poll bound of the leaves' waits (bakron_debug_set_wait_polls).
+std::atomic<int> g_wait_polls{kLeafWaitPolls};
+
+// The status words of `batch` solves whose workspaces start at ws, lay.total
+// bytes apart, once the work on `s` has finished: BAKRON_EWAIT if a leaf of any
+// of them gave up waiting.
+int read_wait_status(const void* ws, const SolveLayout& lay, int64_t m, int64_t n, int64_t batch,
+                     hipStream_t s) {
+  std::vector<int32_t> st((size_t)batch, 0);
+  const char* p = static_cast<const char*>(ws) + status_offset(lay, m, n);
+  if (hipMemcpy2DAsync(st.data(), sizeof(int32_t), p, lay.total, sizeof(int32_t), (size_t)batch,
+                       hipMemcpyDeviceToHost, s) != hipSuccess)
+    return BAKRON_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return BAKRON_EHIP;
+  for (int32_t v : st)
+    if (v != 0) return BAKRON_EWAIT;
+  return BAKRON_OK;
 }
 
 template <typename R>
@@ -106,6 +139,12 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   R* LBp = reinterpret_cast<R*>(base + lay.wk);
   R* LAp = reinterpret_cast<R*>(base + lay.wk + lay.lb);
   R* Mb = reinterpret_cast<R*>(base + lay.wk + lay.lb + lay.la);
+  LeafSync ls;
+  ls.sync = reinterpret_cast<int*>(base + lay.wk + lay.lb + lay.la + lay.mb);
+  ls.stride = batch > 1 ? (int64_t)(lay.total / sizeof(int)) : 0;
+  ls.nblocks = leaf_blocks(m, n);
+  ls.eb = base + lay.wk + lay.lb + lay.la + lay.mb + lay.sync;
+  ls.polls = g_wait_polls.load();
   BandBuffers<R> bb;
   bb.Wk = Wk;
   bb.LBp = LBp;
@@ -116,7 +155,7 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   // conjugated by the scales
   const R* scB = scale_mode == 1 ? scales : nullptr;
   const R* scA = scale_mode == 2 ? scales : nullptr;
-  if (launch_pack_w<R>(g, W, ldw, scales, scale_mode, Wk, s) != hipSuccess) return BAKRON_EHIP;
+  if (launch_pack_w<R>(g, W, ldw, scales, scale_mode, Wk, s, ls) != hipSuccess) return BAKRON_EHIP;
   if (launch_pack_l<R>(g, true, LB, ldlb, scB, LBp, s) != hipSuccess) return BAKRON_EHIP;
   if (launch_pack_l<R>(g, false, LA, ldla, scA, LAp, s) != hipSuccess) return BAKRON_EHIP;
 
@@ -151,7 +190,10 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
     const bool timed = op_ms != nullptr;
     hipEvent_t e0 = timed ? ev[evi] : nullptr, e1 = timed ? ev[evi + 1] : nullptr;
     switch (op.kind) {
-      case OP_LEAF: e = launch_leaf<R>(g, op.k, op.mid, Wk, LBp, LAp, Mb, lp, s, e0, e1); break;
+      case OP_LEAF:
+        e = launch_leaf_rows<R>(g, op.k, op.mid, op.k / kLeafBlock, Wk, LBp, LAp, lp, ls, s, e0,
+                                e1);
+        break;
       case OP_BAND1:
         e = launch_node_band<R>(g, op.k, op.mid, op.l, 1, bb, s, e0, e1);
         break;
@@ -165,6 +207,7 @@ int solve_impl(int64_t m, int64_t n, const R* W, int64_t ldw, const R* LA, int64
   if (op_ms) {
     if (rc == BAKRON_OK && !ev.empty() && hipEventSynchronize(ev.back()) != hipSuccess)
       rc = BAKRON_EHIP;
+    if (rc == BAKRON_OK) rc = read_wait_status(ws, lay, m, n, batch, s);
     for (size_t i = 0; i < ops.size(); ++i) {
       op_ms[i] = -1.0;
       if (rc == BAKRON_OK) {
@@ -473,6 +516,7 @@ const char* bakron_status_string(int status) {
     case BAKRON_EINVAL: return "invalid argument";
     case BAKRON_ENOTSPD: return "matrix is not numerically positive definite";
     case BAKRON_EHIP: return "HIP runtime or kernel launch error";
+    case BAKRON_EWAIT: return "a solve's dependency wait gave up (its results are invalid)";
     default: return "unknown status";
   }
 }
@@ -643,6 +687,29 @@ int bakron_solve_timed(int dtype, int64_t m, int64_t n, const void* W, int64_t l
   return solve_entry(dtype, m, n, W, ldw, LA, ldla, LB, ldlb, alpha_lo, alpha_hi, unbounded,
                      scale_mode, scales, V, ldv, Wt, ldwt, workspace, workspace_bytes, stream,
                      op_ms, n_ops);
+}
+
+int bakron_solve_status(int dtype, int64_t batch, int64_t m, int64_t n, const void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || batch < 0 || batch > kMaxBatch || m < 0 || n < 0) return BAKRON_EINVAL;
+  if (m > INT_MAX / 2 || n > INT_MAX / 2) return BAKRON_EINVAL;
+  if (batch == 0 || m == 0 || n == 0) return BAKRON_OK;
+  const SolveLayout lay = solve_layout(dtype, m, n);
+  const void* ws = workspace;
+  if (!ws) {
+    // the no-allocation solve's scratch on the current device
+    if (batch != 1 || lay.total > (size_t)BAKRON_NOALLOC_SCRATCH_BYTES) return BAKRON_EINVAL;
+    int rc = BAKRON_OK;
+    ws = device_scratch(&rc);
+    if (!ws) return rc;
+  } else if (workspace_bytes < (size_t)batch * lay.total) {
+    return BAKRON_EINVAL;
+  }
+  return read_wait_status(ws, lay, m, n, batch, static_cast<hipStream_t>(stream));
+}
+
+int32_t bakron_debug_set_wait_polls(int32_t polls) {
+  return g_wait_polls.exchange(polls < 0 ? kLeafWaitPolls : polls);
 }
 
 size_t bakron_solve_antidiag_workspace_bytes(int dtype, int64_t m, int64_t n) {

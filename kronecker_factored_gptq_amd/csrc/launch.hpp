@@ -28,9 +28,25 @@ struct SolveGeom {
 };
 
 // ---- solve (solve_kernels.hip) --------------------------------------------
+// Polls of the rows above before a leaf row gives up (each poll is a set of
+// device-coherent loads, about a microsecond, plus a short sleep: about
+// 0.1 s in all, far beyond any real wait, which is bounded by the block's own
+// tiles, tens of microseconds). A give-up sets the problem's status word.
+constexpr int kLeafWaitPolls = 1 << 16;
+// Per-problem words of the leaf blocks: one ticket counter per leaf block,
+// then the status word (nonzero: a wait gave up), `stride` ints apart, and the
+// error copy eb (Mt x Nt tiles, the same stride in elements of the dtype).
+struct LeafSync {
+  int* sync = nullptr;
+  int64_t stride = 0;
+  int nblocks = 0;
+  void* eb = nullptr;
+  int polls = kLeafWaitPolls;
+};
+// Packs W (and clears ls's words when given).
 template <typename R>
 hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, const R* scales,
-                         int scale_mode, R* Wk, hipStream_t s);
+                         int scale_mode, R* Wk, hipStream_t s, const LeafSync& ls);
 // L^B (lb = true) or L^A of every problem of g's batch.
 template <typename R>
 hipError_t launch_pack_l(const SolveGeom& g, bool lb, const R* L, int64_t ld, const R* scales,
@@ -47,15 +63,13 @@ struct LeafParams {
   R* Wt;
   int64_t ldwt;
 };
-// Leaf for tile anti-diagonal K whose block of tile anti-diagonals starts at K0.
-// Mc (Mt x Nt tiles, the band products' stage-1 buffer, idle inside a block)
-// carries each tile row's partial sums from one leaf of the block to the next.
-// ev0 / ev1 (nullable): events stamped with the kernel's start and end by
-// its dispatch (for measurement).
+// The leaf block [K0, K1) (the blk-th leaf block of the schedule) in one
+// launch, one workgroup per tile row. ev0 / ev1 (nullable): events stamped
+// with the kernel's start and end by its dispatch (for measurement).
 template <typename R>
-hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
-                       R* Mc, const LeafParams<R>& lp, hipStream_t s, hipEvent_t ev0 = nullptr,
-                       hipEvent_t ev1 = nullptr);
+hipError_t launch_leaf_rows(const SolveGeom& g, int K0, int K1, int blk, R* Wk, const R* LBp,
+                            const R* LAp, const LeafParams<R>& lp, const LeafSync& ls,
+                            hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Buffers of the band products: W tiles (errors on finished tiles), packed
 // L^B and L^A tiles, and the stage-1 product M.
@@ -74,7 +88,7 @@ hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage
                             const BandBuffers<R>& bb, hipStream_t s, hipEvent_t ev0 = nullptr,
                             hipEvent_t ev1 = nullptr);
 // Tile anti-diagonals per leaf block (updates inside a block are left-looking).
-constexpr int kLeafBlock = 12;
+constexpr int kLeafBlock = 16;
 
 // ---- BaKron-antidiagonal (antidiag_kernels.hip) ----------------------------
 // Workspace of the whole-matrix anti-diagonal solver (element size es): U

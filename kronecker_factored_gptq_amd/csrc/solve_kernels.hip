@@ -37,6 +37,29 @@
 
 namespace bk {
 
+// Sentinel of the leaf rows' error copy: a NaN bit pattern that no error
+// takes (an error that is NaN is stored as the default quiet NaN).
+template <typename R> struct Sentinel;
+template <> struct Sentinel<float> {
+  typedef uint32_t U;
+  static constexpr U bits = 0xFFFFFFFFu;
+  __device__ static inline float qnan() { return __builtin_nanf(""); }
+};
+template <> struct Sentinel<double> {
+  typedef uint64_t U;
+  static constexpr U bits = ~(uint64_t)0;
+  __device__ static inline double qnan() { return __builtin_nan(""); }
+};
+template <typename R>
+__device__ inline bool is_sentinel(R v) {
+  return __builtin_bit_cast(typename Sentinel<R>::U, v) == Sentinel<R>::bits;
+}
+template <typename R>
+__device__ inline R sentinel_value() {
+  return __builtin_bit_cast(R, Sentinel<R>::bits);
+}
+
+
 // ---------------------------------------------------------------------------
 // Pack U = W / s (row-major W, ldw) into tiles; padding is zero. mode: 0 no
 // scales, 1 per-row, 2 per-column.
@@ -45,13 +68,25 @@ template <typename R, int T>
 __global__ __launch_bounds__(256) void pack_w_kernel(int64_t m, int64_t n, int Nt,
                                                      const R* __restrict__ W, int64_t ldw,
                                                      const R* __restrict__ sc, int mode,
-                                                     R* __restrict__ Wk, BatchStrides bs) {
+                                                     R* __restrict__ Wk, BatchStrides bs,
+                                                     int* __restrict__ sync, int64_t sync_stride,
+                                                     int sync_words, R* __restrict__ Eb) {
   // problem blockIdx.y of a batch
   const int64_t b = blockIdx.y;
   W += b * bs.w;
   if (sc) sc += b * bs.s;
   Wk += b * bs.ws;
   const int64_t tile = blockIdx.x;
+  if (sync && tile == 0) {
+    // the leaf blocks' ticket counters and the status word start at zero
+    sync += b * sync_stride;
+    for (int i = threadIdx.x; i < sync_words; i += blockDim.x) sync[i] = 0;
+  }
+  if (Eb) {
+    // the leaf blocks' error copy starts as the sentinel
+    R* e = Eb + b * bs.ws + tile * T * T;
+    for (int i = threadIdx.x; i < T * T; i += blockDim.x) e[i] = sentinel_value<R>();
+  }
   const int64_t P = tile / Nt, Q = tile % Nt;
   R* dst = Wk + tile * T * T;
   for (int e = threadIdx.x; e < T * T; e += blockDim.x) {
@@ -97,20 +132,21 @@ __global__ __launch_bounds__(256) void pack_l_kernel(int64_t dim, const R* __res
 }
 
 // ---------------------------------------------------------------------------
-// Leaf: tile anti-diagonal K, the (K - K0)-th of the block [K0, K0 + G) of
-// tile anti-diagonals. One workgroup per tile (P, Q); T = 16.
+// Leaf block [K0, K1) of G = kLeafBlock tile anti-diagonals, in one launch:
+// one workgroup per tile row P of the block, walking its tiles (P, Q) from
+// left to right, one per tile anti-diagonal K = P + Q; T = 16.
 //
-// 1. Prologue (four waves): add the errors of the tiles (I, J) of the same
-//    block on earlier tile anti-diagonals, I <= P, J <= Q, as
+// 1. Prologue: add the errors of the tiles (I, J) of the same block on
+//    earlier tile anti-diagonals, I <= P, J <= Q, as
 //    sum_J (sum_I L^B[P,I] E[I,J]) L^A[Q,J]^T — the updates between tile
 //    anti-diagonals of one block are done here, left-looking, instead of by
 //    internal nodes (any grouping of the updates gives the same codes,
-//    Appendix B). The inner sums M[P][J] of row P are carried from leaf to
-//    leaf of the block (only two columns change per leaf); each wave takes
-//    every fourth J and a quarter of the new column's terms. The inner sum is
-//    computed transposed, M^T = E^T L^B^T, because the MFMA result layout of
-//    M^T is exactly the A-operand layout of the outer product with k = its
-//    row index: no data movement between the two products.
+//    Appendix B). The inner sums M[P][J] of the row are carried from tile to
+//    tile in registers: per tile, column Q - 1 gains its I = P term and
+//    column Q is new (its terms I < P come from the rows above). The inner
+//    sum is computed transposed, M^T = E^T L^B^T, because the MFMA result
+//    layout of M^T is exactly the A-operand layout of the outer product with
+//    k = its row index: no data movement between the two products.
 // 2. Sweep (wave 0): the tile lives in the MFMA accumulator. In-tile step t
 //    rounds the entries (p, t - p) (one per column, §3.3's anti-diagonal
 //    order) to c = clamp(rint(u)) and adds L^B e L^A^T for the step's errors
@@ -232,263 +268,317 @@ __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Waves of a leaf workgroup: wave w of the prologue takes the block's earlier
-// tiles of columns J = Jlo + w, Jlo + w + kLeafWaves, ...
+// Waves of a leaf workgroup: wave 0 sweeps, the others prepare the prologue.
 constexpr int kLeafWaves = 4;
 
+// Errors handed from one row workgroup to the rows below inside a launch.
+// The L2s of the eight XCDs are not coherent with each other, and an
+// agent-scope release / acquire writes back / invalidates the whole L2 at
+// every hand-off (measured: 18-21 us per tile anti-diagonal). So they move as
+// relaxed device-scope accesses instead: loads that bypass the XCD's L2 and
+// write-through stores.
 template <typename R>
-__global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, int Mt, int Nt, int64_t m,
-                                                   int64_t n, R* __restrict__ Wk,
-                                                   const R* __restrict__ LBp,
-                                                   const R* __restrict__ LAp,
-                                                   R* __restrict__ Mc, LeafParams<R> lp,
-                                                   BatchStrides bs) {
+__device__ inline R ld_dev(const R* p) {
+  return __hip_atomic_load(const_cast<R*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename R>
+__device__ inline void st_dev(R* p, R v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// The leaf block kernel. The row's carried sums M[P][J] stay in registers,
+// its own previous tile's errors in LDS; the only data from other
+// workgroups are the
+// errors E[I][Q] (I < P) of the rows above in the tile's column, read from a
+// copy Eb that starts filled with a sentinel NaN pattern no error takes: a
+// reader polls the values themselves until none is the sentinel (no flags,
+// and no writer waits for its stores to complete). Wave 0 sweeps tile k while
+// waves 1-3 prepare tile k + 1: the products over the row's finished columns,
+// and the new column's terms from the rows above (which finish their tile on
+// the same tile anti-diagonal at about the same time); after the sweep only
+// the finished tile's own column remains (its I = P term and its product).
+// Rows only wait for rows above them, which take their tickets first, so
+// every wait is for a running workgroup.
+// ---------------------------------------------------------------------------
+// worker waves of a row workgroup, and columns / new-column terms per worker
+constexpr int kRowWorkers = kLeafWaves - 1;
+constexpr int kRowCols = (kLeafBlock + kRowWorkers - 1) / kRowWorkers;
+constexpr int kRowTerms = (kLeafBlock - 1 + kRowWorkers - 1) / kRowWorkers;
+
+template <typename R>
+struct RowLds {
+  static constexpr int T = 16;
+  static constexpr int kOwRows = 3 * T - 2, kOwLd = T + 1 + (int)(sizeof(float) / sizeof(R));
+  R red[kRowWorkers][T][T + 1];                                   // workers' prologue sums
+  __attribute__((aligned(16))) R fm[2][kRowWorkers][T * T];       // new-column shares, by parity
+  R lat[T][T + 1];                                                // L^A[Q,Q] of the next tile
+  R eprev[T][T + 1];                                              // errors of the tile just swept
+  R owv[4][kOwRows][kOwLd];
+  int ticket;
+};
+
+template <typename R>
+__global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
+    int K0, int K1, int blk, int nblocks, int Mt, int Nt, int64_t m, int64_t n,
+    R* __restrict__ Wk, R* __restrict__ Eb, const R* __restrict__ LBp, const R* __restrict__ LAp,
+    LeafParams<R> lp, BatchStrides bs, int* __restrict__ sync, int64_t sync_stride, int polls) {
   constexpr int T = 16;
+  typedef Mfma<R> MF;
+  typedef typename MF::acc_t acc_t;
+  typedef RowLds<R> LT;
+  constexpr int kOwLd = LT::kOwLd;
+  constexpr int KA = SweepK<R>::KA, KB = SweepK<R>::KB;
   {  // problem blockIdx.y of a batch: its workspace and outputs
     const int64_t b = blockIdx.y;
     Wk += b * bs.ws;
+    Eb += b * bs.ws;
     LBp += b * bs.ws;
     LAp += b * bs.ws;
-    Mc += b * bs.ws;
     lp.V += b * bs.v;
     if (lp.Wt) lp.Wt += b * bs.wt;
     if (lp.scales) lp.scales += b * bs.s;
+    sync += b * sync_stride;
   }
-  typedef Mfma<R> MF;
-  typedef typename MF::acc_t acc_t;
-  __shared__ R red[kLeafWaves - 1][T][T + 1];
-  __shared__ __attribute__((aligned(16))) R fm[kLeafWaves][T * T];  // fresh-column shares
-  __shared__ R lat[T][T + 1];
-  // sweep: value at rounding, one copy per lane row kg; lane (kg, c) writes
-  // step t to row t - c + (T - 1) of its copy (a real entry's slot when row
-  // t - c is one of its own rows, an unread one otherwise)
-  constexpr int kOwRows = 3 * T - 2, kOwLd = T + 1 + (int)(sizeof(float) / sizeof(R));
-  __shared__ R owv[4][kOwRows][kOwLd];
-
+  __shared__ LT L;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, kg = lane >> 4;
-  const int P = (K - (Nt - 1) > 0 ? K - (Nt - 1) : 0) + (int)blockIdx.x;
-  const int Q = K - P;
-  R* tW = Wk + ((int64_t)P * Nt + Q) * T * T;
+  if (tid == 0)
+    L.ticket = __hip_atomic_fetch_add(sync + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int Plo = K0 - (Nt - 1) > 0 ? K0 - (Nt - 1) : 0;
+  const int P = Plo + L.ticket;
+  // the row's tiles in the block: Q = Qa .. Qb (tile anti-diagonals P + Q)
+  const int Qa = K0 - P > 0 ? K0 - P : 0;
+  const int Qb = K1 - 1 - P < Nt - 1 ? K1 - 1 - P : Nt - 1;
+  const int nt = Qb - Qa + 1;
+  const int Jlo = Qa;
+  const R lo = lp.lo, hi = lp.hi;  // +-infinity for the unbounded alphabet
+  int* status = sync + nblocks;
 
-  // sweep inputs, requested before the prologue so that their latency
-  // overlaps it: this thread's element of L^A[Q,Q] and, on wave 0, the tile
-  // and its lbK operands (lbK[s] = L^B[P,P][c][KA kg + KB s])
-  constexpr int KA = SweepK<R>::KA, KB = SweepK<R>::KB;
-  const R lat_v = tid < T * T ? LAp[tri_index(Q, Q) * T * T + tid] : R(0);
-  R w0[4], lbK[4];
   if (wave == 0) {
-    const R* lb = LBp + tri_index(P, P) * T * T + c * T + KA * kg;
+    // ---- sweeper: tile k - 1 in iteration k
+    R lbK[4];
+    {
+      const R* lb = LBp + tri_index(P, P) * T * T + c * T + KA * kg;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      w0[r] = tW[MF::row(lane, r) * T + c];
-      lbK[r] = lb[KB * r];
+      for (int r = 0; r < 4; ++r) lbK[r] = lb[KB * r];
     }
+    R w0[4];
+    {
+      const R* tW = Wk + ((int64_t)P * Nt + Qa) * T * T;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w0[r] = tW[MF::row(lane, r) * T + c];
+    }
+    __syncthreads();  // B2 of iteration 0 (nothing swept yet)
+    for (int k = 1; k <= nt; ++k) {
+      __syncthreads();  // B1: the tile's prologue sums and L^A[Q,Q] are in LDS
+      const int Q = Qa + k - 1;
+      acc_t acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = MF::row(lane, r);
+        R pro = w0[r];
+#pragma unroll
+        for (int w = 0; w < kRowWorkers; ++w) pro += L.red[w][row][c];
+        acc[r] = pro;
+      }
+      R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - KA kg]
+#pragma unroll
+      for (int j = 0; j < 2 * T - 1; ++j) {
+        const int jj = j - KA * kg;
+        laK[j] = (jj >= 0 && jj < T) ? L.lat[c][jj] : R(0);
+      }
+      // the next tile's W, requested before the sweep
+      if (k < nt) {
+        const R* tW = Wk + ((int64_t)P * Nt + Q + 1) * T * T;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w0[r] = tW[MF::row(lane, r) * T + c];
+      }
+      // the sweep of leaf_tile, unchanged
+      R* owl = &L.owv[kg][T - 1 - c][c];
+      static_for<0, 2 * T - 1>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        R x = acc[0];
+        static_for<1, 4>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          constexpr uint64_t msk = entry_lanes<R>(t, r);
+          if constexpr (msk != 0) x = __builtin_amdgcn_inverse_ballot_w64(msk) ? acc[r] : x;
+        });
+        owl[t * kOwLd] = x;
+        if constexpr (t < 2 * T - 2) {
+          const R es = row_skew(round_clamp(x, lo, hi) - x);
+          static_for<0, 4>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            if constexpr (t - KB * s >= 0 && KA * 3 + KB * s >= t - (T - 1)) {
+              const R ev = row_bcast<(t - KB * s) & 15>(es);
+              acc = MF::mma(lbK[s] * ev, laK[t - KB * s], acc);
+            }
+          });
+        }
+      });
+      wave_sync_lds();
+      // write back: errors into the workspace (for the band products), the
+      // rows below (Eb) and this row's next tile (LDS); codes and values
+      R* tW = Wk + ((int64_t)P * Nt + Q) * T * T;
+      R* tE = Eb + ((int64_t)P * Nt + Q) * T * T;
+      R xv[4], cqv[4], ev[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = lane + 64 * u;
+        const int p = idx >> 4, q = idx & 15;
+        const bool valid = (int64_t)P * T + p < m && (int64_t)Q * T + q < n;
+        xv[u] = L.owv[std::is_same<R, float>::value ? p >> 2 : p & 3][p + T - 1][q];
+        cqv[u] = quant_unit(xv[u], lo, hi);
+        ev[u] = valid ? cqv[u] - xv[u] : R(0);
+        // the rows below wait for these stores: issued first
+        st_dev(tE + idx, ev[u] != ev[u] ? Sentinel<R>::qnan() : ev[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = lane + 64 * u;
+        const int p = idx >> 4, q = idx & 15;
+        const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + q;
+        const bool valid = gi < m && gjj < n;
+        const R x = xv[u], cq = cqv[u], e = ev[u];
+        tW[idx] = e;
+        L.eprev[p][q] = e;
+        if (valid) {
+          lp.V[gi * lp.ldv + gjj] = (int32_t)cq;
+          if (lp.Wt) {
+            R sv = R(1);
+            if (lp.scale_mode == 1) sv = lp.scales[gi];
+            else if (lp.scale_mode == 2) sv = lp.scales[gjj];
+            lp.Wt[gi * lp.ldwt + gjj] = lp.scale_mode ? sv * x : x;
+          }
+        }
+      }
+      __syncthreads();  // B2: the tile's errors are in LDS
+    }
+    return;
   }
 
-  // ---- 1. prologue: acc = sum over J of M[P][J] L^A[Q,J]^T, with
-  // M[P][J] = sum_I L^B[P,I] E[I,J] over the block's earlier tiles (I, J).
-  // Row P's partial sums are kept between the leaves of a block in Mc (slot
-  // J of row P, MFMA lane layout: lane l holds M[c][row(l, r)] at l * 4 + r):
-  // from leaf K - 1 to K only column J = Q - 1 gains a term (I = P) and
-  // column J = Q is new (I < P), so a leaf adds d + 1 tile products instead
-  // of recomputing all (d + 1)(d + 2) / 2 - 1 of them (d = K - K0).
-  constexpr int NJ = (kLeafBlock - 1 + kLeafWaves - 1) / kLeafWaves;  // cached columns per wave
-  constexpr int NI = (kLeafBlock - 1 + kLeafWaves - 1) / kLeafWaves;  // fresh-column terms per wave
-  const int d = K - K0;
-  const bool keep = d + 1 < kLeafBlock;  // a later leaf of this block reads the cache
-  acc_t acc = MF::zero();
-  acc_t fresh = MF::zero();  // this wave's share of M[P][Q]
-  R* McP = Mc + (int64_t)P * Nt * T * T;
-  if (d > 0) {
-    const int Jlo = K0 - P > 0 ? K0 - P : 0;
-    const int Ilo = K0 - Q > 0 ? K0 - Q : 0;  // fresh column: Ilo <= I <= P - 1
-    // every load first: cached columns J = Jlo + wave + kLeafWaves t < Q,
-    // their L^A tiles, the update term of J = Q - 1, this wave's terms of
-    // the fresh column, and L^A[Q,Q]
-    R la[NJ][4], mc[NJ][4], laq[4], eu[4], lu[4], ef[NI][4], lf[NI][4];
-    // Float: no branch around these loads (a load under a branch made the
-    // compiler wait there for every load in flight, the sweep operands
-    // included; columns J >= Q read slot Q instead and are never used, and
-    // the cache is selected away before the block's third leaf): 1.8 %
-    // faster solve. Double: 3.6 % slower that way, so it keeps the guards.
-    constexpr bool kFlatLoads = std::is_same<R, float>::value;
+  // ---- workers: wave 1 + wid owns columns J = Jlo + wid + kRowWorkers t and
+  // the new column's terms I = Ilo + wid + kRowWorkers u
+  const int wid = wave - 1;
+  acc_t mreg[kRowCols];  // M[P][J] (MFMA result layout of M^T), owned columns
 #pragma unroll
-    for (int t = 0; t < NJ; ++t) {
-      const int J = Jlo + wave + kLeafWaves * t;
-      if constexpr (kFlatLoads) {
-        const int Jc = J < Q ? J : Q;
+  for (int t = 0; t < kRowCols; ++t) mreg[t] = MF::zero();
+  R lu[4];  // L^B[P,P] rows for the I = P term of a finished column
+  EVec<R>::load4(LBp + tri_index(P, P) * T * T + c * T + 4 * kg, lu);
+  for (int k = 0; k <= nt; ++k) {
+    // (a) while tile k - 1 is swept: tile k's sums over the finished columns
+    // J <= Q - 2 and its new column's terms from the rows above; the factor
+    // tiles that step (b) needs are loaded here too
+    const int Q = Qa + k;
+    acc_t acc = MF::zero();
+    acc_t fresh = MF::zero();
+    R la1[4], latv[4];
+    if (k < nt) {
+      {
+        // L^A[Q,Q-1] for column Q - 1's product, L^A[Q,Q] for the sweep
+        const R* La = LAp + tri_index(Q, k >= 1 ? Q - 1 : Q) * T * T;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) la1[s] = La[c * T + MF::row(lane, s)];
+        const R* Lq = LAp + tri_index(Q, Q) * T * T;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) latv[u] = Lq[lane + 64 * u];
+      }
+      R la[kRowCols][4], laq[4], lf[kRowTerms][4], ef[kRowTerms][4];
+#pragma unroll
+      for (int t = 0; t < kRowCols; ++t) {
+        const int J = Jlo + wid + kRowWorkers * t;
+        const int Jc = J <= Q - 2 ? J : Q;
         const R* La = LAp + tri_index(Q, Jc) * T * T;
 #pragma unroll
         for (int s = 0; s < 4; ++s) la[t][s] = La[c * T + MF::row(lane, s)];
-        EVec<R>::load4(McP + (int64_t)Jc * T * T + lane * 4, mc[t]);
-      } else {
+      }
+      {
+        const R* La = LAp + tri_index(Q, Q) * T * T;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) { la[t][s] = R(0); mc[t][s] = R(0); }
-        if (J < Q) {
-          const R* La = LAp + tri_index(Q, J) * T * T;
+        for (int s = 0; s < 4; ++s) laq[s] = La[c * T + MF::row(lane, s)];
+      }
+      const int Ilo = K0 - Q > 0 ? K0 - Q : 0;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) la[t][s] = La[c * T + MF::row(lane, s)];
-          if (d >= 2) EVec<R>::load4(McP + (int64_t)J * T * T + lane * 4, mc[t]);
+      for (int u = 0; u < kRowTerms; ++u) {
+        const int I = Ilo + wid + kRowWorkers * u;
+        if (I <= P - 1) {
+          EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lf[u]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) lf[u][s] = R(0);
         }
       }
-    }
-    {
-      const R* La = LAp + tri_index(Q, Q) * T * T;
+      // the rows above: poll the values until none is the sentinel
+      bool ok = false;
+      for (int it = 0; it <= polls && !ok; ++it) {
+        bool mine = true;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) laq[s] = La[c * T + MF::row(lane, s)];
-    }
-    const bool upd = Q >= 1 && Q - 1 >= Jlo && (Q - 1 - Jlo) % kLeafWaves == wave;
-    if (upd) {
-      const R* E = Wk + ((int64_t)P * Nt + Q - 1) * T * T;
-      EVec<R>::load4(LBp + tri_index(P, P) * T * T + c * T + 4 * kg, lu);
+        for (int u = 0; u < kRowTerms; ++u) {
+          const int I = Ilo + wid + kRowWorkers * u;
+          const R* E = Eb + ((int64_t)I * Nt + Q) * T * T;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) eu[s] = E[(4 * kg + s) * T + c];
-    }
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      const int I = Ilo + wave + kLeafWaves * u;
-      if (I <= P - 1) {
-        const R* E = Wk + ((int64_t)I * Nt + Q) * T * T;
-        EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lf[u]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ef[u][s] = E[(4 * kg + s) * T + c];
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) { ef[u][s] = R(0); lf[u][s] = R(0); }
+          for (int s = 0; s < 4; ++s) {
+            ef[u][s] = I <= P - 1 ? ld_dev(E + (4 * kg + s) * T + c) : R(0);
+            mine = mine && !is_sentinel(ef[u][s]);
+          }
+        }
+        ok = __builtin_amdgcn_ballot_w64(!mine) == 0;
+        if (!ok && it < polls) __builtin_amdgcn_s_sleep(1);
       }
+      if (!ok && lane == 0)
+        __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int u = 0; u < kRowTerms; ++u) {
+        if (Ilo + wid + kRowWorkers * u > P - 1) break;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) fresh = MF::mma(ef[u][s], lf[u][s], fresh);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = MF::mma(fresh[s], laq[s], acc);
+#pragma unroll
+      for (int t = 0; t < kRowCols; ++t) {
+        const int J = Jlo + wid + kRowWorkers * t;
+        if (J > Q - 2) break;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = MF::mma(mreg[t][s], la[t][s], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) L.fm[k & 1][wid][lane * 4 + r] = fresh[r];
     }
-    // fresh column: this wave's terms, and its part of the outer product
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      if (Ilo + wave + kLeafWaves * u > P - 1) break;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) fresh = MF::mma(ef[u][s], lf[u][s], fresh);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = MF::mma(fresh[s], laq[s], acc);
-    // cached columns (J = Q - 1 gains its term and is stored back)
-#pragma unroll
-    for (int t = 0; t < NJ; ++t) {
-      const int J = Jlo + wave + kLeafWaves * t;
-      if (J >= Q) break;
+    __syncthreads();  // B2: tile k - 1 swept (its errors in LDS); tile k's shares in LDS
+    if (k == nt) break;
+    // (b) column J = Q - 1 is finished: its new-column sum plus its I = P
+    // term, kept for the row's later tiles, and its product for tile k
+    if (k >= 1 && (Q - 1 - Jlo) % kRowWorkers == wid) {
+      const int t = (Q - 1 - Jlo) / kRowWorkers;
       acc_t mt;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mt[r] = (!kFlatLoads || d >= 2) ? mc[t][r] : R(0);
-      if (J == Q - 1) {
+      for (int r = 0; r < 4; ++r) {
+        R v = L.fm[(k - 1) & 1][0][lane * 4 + r];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) mt = MF::mma(eu[s], lu[s], mt);
-        if (keep) {
-          R o[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = mt[r];
-          EVec<R>::store4(McP + (int64_t)J * T * T + lane * 4, o);
-        }
+        for (int w = 1; w < kRowWorkers; ++w) v += L.fm[(k - 1) & 1][w][lane * 4 + r];
+        mt[r] = v;
       }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], la[t][s], acc);
+      for (int s = 0; s < 4; ++s) mt = MF::mma(L.eprev[4 * kg + s][c], lu[s], mt);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], la1[s], acc);
+#pragma unroll
+      for (int u = 0; u < kRowCols; ++u)
+        if (u == t) mreg[u] = mt;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) fm[wave][lane * 4 + r] = fresh[r];
-  }
-  if (wave > 0) {
+    for (int r = 0; r < 4; ++r) L.red[wid][MF::row(lane, r)][c] = acc[r];
+    if (wid == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave - 1][MF::row(lane, r)][c] = acc[r];
-  }
-  if (tid < T * T) lat[tid >> 4][tid & 15] = lat_v;
-  __syncthreads();
-  if (wave == 1 && d > 0 && keep) {
-    // the fresh column M[P][Q] for the next leaf of the block, summed over
-    // the waves in a fixed order
-    R o[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      R v = fm[0][lane * 4 + r];
-#pragma unroll
-      for (int w = 1; w < kLeafWaves; ++w) v += fm[w][lane * 4 + r];
-      o[r] = v;
-    }
-    EVec<R>::store4(McP + (int64_t)Q * T * T + lane * 4, o);
-  }
-  if (wave > 0) return;
-
-  // ---- 2. sweep on wave 0
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = MF::row(lane, r);
-    R pro = w0[r];
-#pragma unroll
-    for (int w = 0; w < kLeafWaves - 1; ++w) pro += red[w][row][c];
-    acc[r] += pro;
-  }
-  R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - KA kg]
-#pragma unroll
-  for (int j = 0; j < 2 * T - 1; ++j) {
-    const int jj = j - KA * kg;
-    laK[j] = (jj >= 0 && jj < T) ? lat[c][jj] : R(0);
-  }
-  const R lo = lp.lo, hi = lp.hi;  // +-infinity for the unbounded alphabet
-
-  // One wave's vector instructions do not overlap its own MFMA chain on
-  // gfx950 (measured: each independent fma adds its ~6 cycles to a chain of
-  // four dependent 16x16x4 MFMAs), so the step is kept to the fewest vector
-  // instructions. Which lanes hold their entry r on step t is fixed by the
-  // lane layout, so the select masks are compile-time wave masks (scalar
-  // moves, no compares). A lane with no entry on the step keeps acc[0], any
-  // finite value: the broadcasts read only lanes at columns t - k inside the
-  // tile, which do have an entry, and the other broadcast values meet exact
-  // zeros of laK. Padding entries may be selected: they start at exact zero,
-  // and an error reaches an entry only through factors that are exact zeros
-  // between padding and real rows or columns, so neither side changes the
-  // other. The value at rounding goes to the lane row's own LDS copy at a
-  // constant offset per step.
-  R* owl = &owv[kg][T - 1 - c][c];
-  static_for<0, 2 * T - 1>([&](auto tc) {
-    constexpr int t = decltype(tc)::value;
-    R x = acc[0];
-    static_for<1, 4>([&](auto rc) {
-      constexpr int r = decltype(rc)::value;
-      constexpr uint64_t msk = entry_lanes<R>(t, r);
-      if constexpr (msk != 0) x = __builtin_amdgcn_inverse_ballot_w64(msk) ? acc[r] : x;
-    });
-    owl[t * kOwLd] = x;
-    if constexpr (t < 2 * T - 2) {
-      const R es = row_skew(round_clamp(x, lo, hi) - x);
-      static_for<0, 4>([&](auto sc) {
-        constexpr int s = decltype(sc)::value;
-        // MFMA s takes the rows k = KA kg + KB s: it contributes only if some
-        // such k has its column t - k inside the tile (k >= t - (T - 1)) and
-        // k <= t; the last step's update reaches no later anti-diagonal. The
-        // skipped products add exact zeros or are never read.
-        if constexpr (t - KB * s >= 0 && KA * 3 + KB * s >= t - (T - 1)) {
-          const R ev = row_bcast<(t - KB * s) & 15>(es);
-          acc = MF::mma(lbK[s] * ev, laK[t - KB * s], acc);
-        }
-      });
-    }
-  });
-  wave_sync_lds();
-  // write back: errors (code units) into the workspace, codes and the values
-  // at rounding (back in the units of W) to the outputs
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = lane + 64 * u;
-    const int p = idx >> 4, q = idx & 15;
-    const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + q;
-    const bool valid = gi < m && gjj < n;
-    const R x = owv[std::is_same<R, float>::value ? p >> 2 : p & 3][p + T - 1][q];
-    const R cq = quant_unit(x, lo, hi);
-    tW[idx] = valid ? cq - x : R(0);
-    if (valid) {
-      lp.V[gi * lp.ldv + gjj] = (int32_t)cq;
-      if (lp.Wt) {
-        R sv = R(1);
-        if (lp.scale_mode == 1) sv = lp.scales[gi];
-        else if (lp.scale_mode == 2) sv = lp.scales[gjj];
-        lp.Wt[gi * lp.ldwt + gjj] = lp.scale_mode ? sv * x : x;
+      for (int u = 0; u < 4; ++u) {
+        const int idx = lane + 64 * u;
+        L.lat[idx >> 4][idx & 15] = latv[u];
       }
     }
+    __syncthreads();  // B1
   }
 }
 
@@ -497,11 +587,12 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_kernel(int K, int K0, in
 // ---------------------------------------------------------------------------
 template <typename R>
 hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, const R* scales,
-                         int scale_mode, R* Wk, hipStream_t s) {
+                         int scale_mode, R* Wk, hipStream_t s, const LeafSync& ls) {
   const int64_t nt = (int64_t)g.Mt * g.Nt;
   if (nt == 0 || g.batch <= 0) return hipSuccess;
   hipLaunchKernelGGL((pack_w_kernel<R, kTile>), dim3((unsigned)nt, (unsigned)g.batch), dim3(256),
-                     0, s, g.m, g.n, g.Nt, W, ldw, scales, scale_mode, Wk, g.bs);
+                     0, s, g.m, g.n, g.Nt, W, ldw, scales, scale_mode, Wk, g.bs, ls.sync,
+                     ls.stride, ls.nblocks + 1, static_cast<R*>(ls.eb));
   return hipGetLastError();
 }
 
@@ -517,41 +608,42 @@ hipError_t launch_pack_l(const SolveGeom& g, bool lb, const R* L, int64_t ld, co
   return hipGetLastError();
 }
 
-static inline void diag_range(const SolveGeom& g, int K, int* lo, int* hi) {
-  *lo = K - (g.Nt - 1) > 0 ? K - (g.Nt - 1) : 0;
-  *hi = K < g.Mt - 1 ? K : g.Mt - 1;
-}
-
 template <typename R>
-hipError_t launch_leaf(const SolveGeom& g, int K, int K0, R* Wk, const R* LBp, const R* LAp,
-                       R* Mc, const LeafParams<R>& lp, hipStream_t s, hipEvent_t ev0,
-                       hipEvent_t ev1) {
+hipError_t launch_leaf_rows(const SolveGeom& g, int K0, int K1, int blk, R* Wk, const R* LBp,
+                            const R* LAp, const LeafParams<R>& lp, const LeafSync& ls,
+                            hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   static_assert(kTile == 16, "the leaf kernel works on 16 x 16 tiles");
-  int lo, hi;
-  diag_range(g, K, &lo, &hi);
-  if (hi < lo || g.batch <= 0) {
-    // nothing to do; keep the timing events valid (zero duration)
+  const int Plo = K0 - (g.Nt - 1) > 0 ? K0 - (g.Nt - 1) : 0;
+  const int Phi = K1 - 1 < g.Mt - 1 ? K1 - 1 : g.Mt - 1;
+  if (Phi < Plo || K1 <= K0 || g.batch <= 0) {
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return hipErrorUnknown;
     if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return hipErrorUnknown;
     return hipSuccess;
   }
-  const dim3 grid(hi - lo + 1, g.batch), block(64 * kLeafWaves);
-  if (ev0 || ev1)  // the events are stamped by the dispatch packet itself
-    hipExtLaunchKernelGGL((leaf_kernel<R>), grid, block, 0, s, ev0, ev1, 0, K, K0, g.Mt, g.Nt,
-                          g.m, g.n, Wk, LBp, LAp, Mc, lp, g.bs);
+  if (!ls.sync || !ls.eb || blk < 0 || blk >= ls.nblocks || K1 - K0 > kLeafBlock)
+    return hipErrorInvalidValue;
+  int* counters = ls.sync;
+  R* Eb = static_cast<R*>(ls.eb);
+  const dim3 grid((unsigned)(Phi - Plo + 1), g.batch), block(64 * kLeafWaves);
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL((leaf_rows_kernel<R>), grid, block, 0, s, ev0, ev1, 0, K0, K1, blk,
+                          ls.nblocks, g.Mt, g.Nt, g.m, g.n, Wk, Eb, LBp, LAp, lp, g.bs, counters,
+                          ls.stride, ls.polls);
   else
-    hipLaunchKernelGGL((leaf_kernel<R>), grid, block, 0, s, K, K0, g.Mt, g.Nt, g.m, g.n, Wk, LBp,
-                       LAp, Mc, lp, g.bs);
+    hipLaunchKernelGGL((leaf_rows_kernel<R>), grid, block, 0, s, K0, K1, blk, ls.nblocks, g.Mt,
+                       g.Nt, g.m, g.n, Wk, Eb, LBp, LAp, lp, g.bs, counters, ls.stride,
+                       ls.polls);
   return hipGetLastError();
 }
 
 #define BK_INST(R)                                                                              \
   template hipError_t launch_pack_w<R>(const SolveGeom&, const R*, int64_t, const R*, int, R*,  \
-                                       hipStream_t);                                            \
+                                       hipStream_t, const LeafSync&);                           \
   template hipError_t launch_pack_l<R>(const SolveGeom&, bool, const R*, int64_t, const R*, R*, \
                                        hipStream_t);                                            \
-  template hipError_t launch_leaf<R>(const SolveGeom&, int, int, R*, const R*, const R*, R*,    \
-                                     const LeafParams<R>&, hipStream_t, hipEvent_t, hipEvent_t);
+  template hipError_t launch_leaf_rows<R>(const SolveGeom&, int, int, int, R*, const R*,         \
+                                          const R*, const LeafParams<R>&, const LeafSync&,       \
+                                          hipStream_t, hipEvent_t, hipEvent_t);
 BK_INST(float)
 BK_INST(double)
 #undef BK_INST

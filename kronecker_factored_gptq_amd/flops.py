@@ -77,13 +77,13 @@ def node_useful_flops(m: int, n: int, T: int, k: int, mid: int, l: int) -> Tuple
 
 def in_block_useful_flops(m: int, n: int, T: int, K0: int, K1: int) -> Tuple[int, int]:
     """(stage-1 flops, stage-2 flops) of the updates between the tiles of one
-    leaf block, tile anti-diagonals [K0, K1), as the leaves compute them
-    (left-looking, with each row's inner sums carried from leaf to leaf):
+    leaf block, tile anti-diagonals [K0, K1), as the leaf block computes them
+    (left-looking, with each tile row's inner sums carried from tile to tile):
         M[P, J]  = sum_I L^B[P, I] E[I, J]     over block tiles (I, J), I <= P
         W[P, Q] += sum_J M[P, J] L^A[Q, J]^T   for every block tile (P, Q),
     where target (P, Q) takes only errors of the tiles before it
     ((I, J) != (P, Q), I <= P, J <= Q). Every inner-sum term (P, I, J) is
-    counted ONCE, whatever number of later leaves reads the carried sum,
+    counted ONCE, whatever number of later tiles reads the carried sum,
     and only if some target reads it; triangular zeros of the diagonal
     tiles and tile padding are not counted (entry granularity)."""
     Mt, Nt = -(-m // T), -(-n // T)
@@ -120,19 +120,13 @@ def in_block_useful_flops(m: int, n: int, T: int, K0: int, K1: int) -> Tuple[int
 def schedule_flops(m: int, n: int, T: int, ops: Iterable[Tuple[int, int, int, int]]
                    ) -> Dict[str, int]:
     """Useful flops of the updates between tiles in a solve schedule: kinds
-    2 and 3 are the two band products of an internal node; the leaves
-    (kind 0) of one block of tile anti-diagonals [K0, K1) together apply the
-    block's in-block updates (``in_block_useful_flops``), reported as
-    "in_block" and attributed to the block's first leaf in ``per_op``."""
-    ops = list(ops)
+    2 and 3 are the two band products of an internal node; a leaf block
+    (kind 0, tile anti-diagonals [K0, K1)) applies the block's in-block
+    updates (``in_block_useful_flops``), reported as "in_block"."""
     out = {"in_block": 0, "band": 0, "band_stage1": 0, "band_stage2": 0, "per_op": []}
-    block_end: Dict[int, int] = {}
     for (kind, k, mid, l) in ops:
         if kind == 0:
-            block_end[mid] = max(block_end.get(mid, mid), k + 1)
-    for (kind, k, mid, l) in ops:
-        if kind == 0:
-            f = sum(in_block_useful_flops(m, n, T, mid, block_end[mid])) if k == mid else 0
+            f = sum(in_block_useful_flops(m, n, T, k, mid))
             out["in_block"] += f
             out["per_op"].append(f)
             continue

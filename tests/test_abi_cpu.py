@@ -29,8 +29,8 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     L = bk.lib()
     assert L.bakron_abi_version() == 1
-    for st in (0, -1, -2, -3):
-        assert L.bakron_status_string(st)
+    for st in (0, -1, -2, -3, -4):
+        assert L.bakron_status_string(st) != L.bakron_status_string(99)
     assert bk.tile_size(bk.F32) == bk.tile_size(bk.F64) == 16
     assert bk.tile_size(7) == 0
 
@@ -231,20 +231,17 @@ def _closed_form_leaves(m, n, T=16):
 @pytest.mark.parametrize("m,n", [(1, 1), (16, 16), (17, 5), (64, 64), (200, 300), (512, 512),
                                  (4096, 4096), (14336, 4096), (4096, 14336), (1024, 2048)])
 def test_schedule_is_algorithm_6_over_blocks_of_tile_antidiagonals(m, n):
-    """Table 1 "Steps" for BaKron: one leaf per (tile) anti-diagonal, in
-    order; Algorithm 6's recursion over blocks of G tile anti-diagonals (G
-    read from the second block's start), each internal node splitting block
-    range [kb, lb) at floor((kb+lb)/2) and running after the last leaf left
-    of its midpoint and before the first leaf right of it; inside a block,
-    each leaf names its block start."""
+    """Table 1 "Steps" for BaKron: the tile anti-diagonals 0 .. R-1 in order,
+    in leaf blocks of G (G read from the first block); Algorithm 6's
+    recursion over the blocks, each internal node splitting block range
+    [kb, lb) at floor((kb+lb)/2) and running after the leaf block left of
+    its midpoint and before the one right of it."""
     ops = bk.solve_schedule(bk.F32, m, n)
     R = _closed_form_leaves(m, n)
     leaves = [(a, b) for (kind, a, b, c) in ops if kind == 0]
-    assert [a for a, _ in leaves] == list(range(R))
-    starts = sorted({b for _, b in leaves})
-    BLOCK = starts[1] if len(starts) > 1 else R + 1  # one block: any G > R
+    BLOCK = leaves[0][1] - leaves[0][0] if len(leaves) > 1 else R + 1  # one block: any G >= R
     nblocks = -(-R // BLOCK)
-    assert all(b == (a // BLOCK) * BLOCK for a, b in leaves)
+    assert leaves == [(i * BLOCK, min((i + 1) * BLOCK, R)) for i in range(nblocks)]
     nodes = [(a, b, c) for (kind, a, b, c) in ops if kind == 2]
     assert len(nodes) == nblocks - 1
     assert sorted(mid for (_, mid, _) in nodes) == [BLOCK * i for i in range(1, nblocks)]
@@ -257,9 +254,10 @@ def test_schedule_is_algorithm_6_over_blocks_of_tile_antidiagonals(m, n):
         if kd == 2:
             assert kinds[i + 1] == 3 and ops[i][1:] == ops[i + 1][1:]
     pos = {a: i for i, (kind, a, _, _) in enumerate(ops) if kind == 0}
+    end = {b: i for i, (kind, _, b, _) in enumerate(ops) if kind == 0}
     for i, (kind, k, mid, l) in enumerate(ops):
         if kind in (2, 3):
-            assert pos[mid - 1] < i < pos[mid]
+            assert end[mid] < i < pos[mid]
 
 
 def _noalloc(**kw):
@@ -273,7 +271,7 @@ def _noalloc(**kw):
 
 
 @pytest.mark.parametrize("dtype,m,n", [
-    (bk.F32, 2400, 2400),   # a float32 square just over 64 MiB of workspace
+    (bk.F32, 2600, 2600),   # a float32 square just over 96 MiB of workspace
     (bk.F32, 4096, 4096),
     (bk.F64, 2048, 2048),
     (bk.F64, 1 << 20, 1),
@@ -353,3 +351,24 @@ def test_blockdiag_queries_and_argument_errors():
                                    None, FAKE, 1 << 40, None) == bk.EINVAL
     assert L.bakron_loss_blockdiag(bk.F32, 2, 8, 4, FAKE, 4, FAKE, 4, 7, None, FAKE, 4, FAKE, 4, 16,
                                    FAKE, FAKE, 1 << 40, None) == bk.EINVAL
+
+
+def test_solve_status_arguments_and_wait_hook():
+    L = bk.lib()
+    # bad arguments are refused before any HIP call; empty problems are OK
+    assert L.bakron_solve_status(7, 1, 4, 4, FAKE, 1 << 20, None) == bk.EINVAL
+    assert L.bakron_solve_status(bk.F32, -1, 4, 4, FAKE, 1 << 20, None) == bk.EINVAL
+    assert L.bakron_solve_status(bk.F32, 1, -4, 4, FAKE, 1 << 20, None) == bk.EINVAL
+    assert L.bakron_solve_status(bk.F32, 0, 4, 4, FAKE, 0, None) == bk.OK
+    assert L.bakron_solve_status(bk.F32, 1, 0, 4, FAKE, 0, None) == bk.OK
+    # a workspace smaller than the batch's solve workspace
+    need = L.bakron_solve_batched_workspace_bytes(bk.F32, 3, 40, 50)
+    assert L.bakron_solve_status(bk.F32, 3, 40, 50, FAKE, need - 1, None) == bk.EINVAL
+    # the no-allocation scratch holds one problem of at most its size
+    assert L.bakron_solve_status(bk.F32, 2, 40, 50, None, 0, None) == bk.EINVAL
+    assert L.bakron_solve_status(bk.F32, 1, 4096, 4096, None, 0, None) == bk.EINVAL
+    # the poll bound hook: set, read back, restore the default
+    prev = bk.debug_set_wait_polls(0)
+    assert bk.debug_set_wait_polls(5) == 0
+    assert bk.debug_set_wait_polls(-1) == 5
+    assert bk.debug_set_wait_polls(prev) == prev

@@ -88,7 +88,7 @@ def test_in_block_count_matches_brute_force(m, n, T, K0, K1):
 def test_total_is_of_order_mn_m_plus_n_at_4096():
     """Sum over all nodes at 4096^2 with 16-wide tiles: ~1.8 mn(m+n) flop in
     total (Appendix C's O(mn(m+n))), the bulk of it in the band products (the
-    leaves' in-block updates between tiles take a few per cent with 12 tile
+    leaves' in-block updates between tiles take a few per cent with 16 tile
     anti-diagonals per leaf block)."""
     ops = bk.solve_schedule(bk.F32, 4096, 4096)
     f = schedule_flops(4096, 4096, 16, ops)

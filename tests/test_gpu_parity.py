@@ -316,3 +316,27 @@ def test_solve_replays_bit_identically_from_a_captured_graph(gpu_lib):
         torch.cuda.synchronize()
         assert torch.equal(other, ref)
     del g
+
+
+def test_leaf_wait_give_up_is_reported_and_recoverable(gpu_lib):
+    """The leaf blocks' waits for the rows above are bounded. With the bound
+    forced to zero from the host (every wait that finds its data not yet
+    written gives up at once; every kernel still runs to its end), the solve
+    reports BAKRON_EWAIT through bakron_solve_status; with the default bound
+    restored, the same workspace gives the normal result and status OK."""
+    bk = gpu_lib
+    p = random_problem(1024, 768, "f32", seed=21, w_std=0.02, heavy_tail=True, samples_factor=2)
+    inp = prepare(p.W, p.A, p.B, "f32", (-8, 7, 0), "row", 7)
+    W, LA, LB, s = to_dev(inp.W), to_dev(inp.LA), to_dev(inp.LB), to_dev(inp.s)
+    ws = torch.empty(bk.workspace_bytes("solve", bk.F32, 1024, 768), dtype=torch.uint8,
+                     device="cuda")
+    ref = bk.solve(W, LA, LB, (-8, 7, 0), s, workspace=ws, check=True).clone()
+    prev = bk.debug_set_wait_polls(0)
+    try:
+        with pytest.raises(bk.BakronError) as ei:
+            bk.solve(W, LA, LB, (-8, 7, 0), s, workspace=ws, check=True)
+        assert ei.value.status == bk.EWAIT
+    finally:
+        bk.debug_set_wait_polls(prev)
+    V = bk.solve(W, LA, LB, (-8, 7, 0), s, workspace=ws, check=True)
+    assert torch.equal(V, ref)

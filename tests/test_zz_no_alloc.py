@@ -59,15 +59,21 @@ def test_noalloc_matches_solve_on_shrinking_calls(gpu_lib, dtype):
 
 
 def test_noalloc_largest_float32_square(gpu_lib):
-    _compare(gpu_lib, 2048, 2048, "f32", 5, "row")
+    # 2496 x 2496 is the largest float32 square whose workspace fits
+    assert gpu_lib.workspace_bytes("solve", gpu_lib.F32, 2496, 2496) <= gpu_lib.NOALLOC_SCRATCH_BYTES
+    assert gpu_lib.workspace_bytes("solve", gpu_lib.F32, 2497, 2497) > gpu_lib.NOALLOC_SCRATCH_BYTES
+    _compare(gpu_lib, 2496, 2496, "f32", 5, "row")
     _compare(gpu_lib, 1000, 1500, "f32", 6, "row")
 
 
 def test_noalloc_rejects_oversize(gpu_lib):
-    W = torch.zeros(2400, 2400, device="cuda")
-    LA = torch.eye(2400, device="cuda")
-    LB = torch.eye(2400, device="cuda")
-    V = torch.empty(2400, 2400, dtype=torch.int32, device="cuda")
+    # a float32 square just over the scratch
+    d = 2600
+    assert gpu_lib.workspace_bytes("solve", gpu_lib.F32, d, d) > gpu_lib.NOALLOC_SCRATCH_BYTES
+    W = torch.zeros(d, d, device="cuda")
+    LA = torch.eye(d, device="cuda")
+    LB = torch.eye(d, device="cuda")
+    V = torch.empty(d, d, dtype=torch.int32, device="cuda")
     with pytest.raises(gpu_lib.BakronError) as ei:
         gpu_lib.solve_noalloc(W, LA, LB, (0, 0, 1), None, V)
     assert ei.value.status == gpu_lib.EINVAL
