@@ -88,7 +88,10 @@ hipError_t launch_node_band(const SolveGeom& g, int k, int mid, int l, int stage
                             const BandBuffers<R>& bb, hipStream_t s, hipEvent_t ev0 = nullptr,
                             hipEvent_t ev1 = nullptr);
 // Tile anti-diagonals per leaf block (updates inside a block are left-looking).
-constexpr int kLeafBlock = 16;
+#ifndef BK_LEAF_BLOCK
+#define BK_LEAF_BLOCK 24
+#endif
+constexpr int kLeafBlock = BK_LEAF_BLOCK;
 
 // ---- BaKron-antidiagonal (antidiag_kernels.hip) ----------------------------
 // Workspace of the whole-matrix anti-diagonal solver (element size es): U

@@ -510,33 +510,7 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
           for (int s = 0; s < 4; ++s) lf[u][s] = R(0);
         }
       }
-      // the rows above: poll the values until none is the sentinel
-      bool ok = false;
-      for (int it = 0; it <= polls && !ok; ++it) {
-        bool mine = true;
-#pragma unroll
-        for (int u = 0; u < kRowTerms; ++u) {
-          const int I = Ilo + wid + kRowWorkers * u;
-          const R* E = Eb + ((int64_t)I * Nt + Q) * T * T;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            ef[u][s] = I <= P - 1 ? ld_dev(E + (4 * kg + s) * T + c) : R(0);
-            mine = mine && !is_sentinel(ef[u][s]);
-          }
-        }
-        ok = __builtin_amdgcn_ballot_w64(!mine) == 0;
-        if (!ok && it < polls) __builtin_amdgcn_s_sleep(1);
-      }
-      if (!ok && lane == 0)
-        __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int u = 0; u < kRowTerms; ++u) {
-        if (Ilo + wid + kRowWorkers * u > P - 1) break;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) fresh = MF::mma(ef[u][s], lf[u][s], fresh);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc = MF::mma(fresh[s], laq[s], acc);
+      // the products over the row's finished columns (local data) first
 #pragma unroll
       for (int t = 0; t < kRowCols; ++t) {
         const int J = Jlo + wid + kRowWorkers * t;
@@ -544,6 +518,65 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc = MF::mma(mreg[t][s], la[t][s], acc);
       }
+      // then the new column's terms from the rows above, the values polled
+      // until none is the sentinel: rows I <= P - 2 (finished a tile
+      // anti-diagonal earlier, as a rule already written) together, then
+      // the row right above (I = P - 1, which sweeps its tile on the same
+      // tile anti-diagonal as this row's current one), whose term is this
+      // wave's last in the order of I
+      bool ok = true;
+      {
+        bool done = false;
+        for (int it = 0; it <= polls && !done; ++it) {
+          bool mine = true;
+#pragma unroll
+          for (int u = 0; u < kRowTerms; ++u) {
+            const int I = Ilo + wid + kRowWorkers * u;
+            const R* E = Eb + ((int64_t)I * Nt + Q) * T * T;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              ef[u][s] = I <= P - 2 ? ld_dev(E + (4 * kg + s) * T + c) : R(0);
+              mine = mine && !is_sentinel(ef[u][s]);
+            }
+          }
+          done = __builtin_amdgcn_ballot_w64(!mine) == 0;
+          if (!done && it < polls) __builtin_amdgcn_s_sleep(1);
+        }
+        ok = done;
+      }
+#pragma unroll
+      for (int u = 0; u < kRowTerms; ++u) {
+        if (Ilo + wid + kRowWorkers * u > P - 2) break;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) fresh = MF::mma(ef[u][s], lf[u][s], fresh);
+      }
+      if (P - 1 >= Ilo && (P - 1 - Ilo) % kRowWorkers == wid) {
+        const int uc = (P - 1 - Ilo) / kRowWorkers;
+        const R* E = Eb + ((int64_t)(P - 1) * Nt + Q) * T * T;
+        R e4[4];
+        bool done = false;
+        for (int it = 0; it <= polls && !done; ++it) {
+          bool mine = true;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            e4[s] = ld_dev(E + (4 * kg + s) * T + c);
+            mine = mine && !is_sentinel(e4[s]);
+          }
+          done = __builtin_amdgcn_ballot_w64(!mine) == 0;
+          if (!done && it < polls) __builtin_amdgcn_s_sleep(1);
+        }
+        ok = ok && done;
+#pragma unroll
+        for (int u = 0; u < kRowTerms; ++u)
+          if (u == uc) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) fresh = MF::mma(e4[s], lf[u][s], fresh);
+          }
+      }
+      if (!ok && lane == 0)
+        __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = MF::mma(fresh[s], laq[s], acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) L.fm[k & 1][wid][lane * 4 + r] = fresh[r];
     }
