@@ -310,10 +310,12 @@ template <typename R>
 struct RowLds {
   static constexpr int T = 16;
   static constexpr int kOwRows = 3 * T - 2, kOwLd = T + 1 + (int)(sizeof(float) / sizeof(R));
-  R red[kRowWorkers][T][T + 1];                                   // workers' prologue sums
-  __attribute__((aligned(16))) R fm[2][kRowWorkers][T * T];       // new-column shares, by parity
-  R lat[T][T + 1];                                                // L^A[Q,Q] of the next tile
-  R eprev[T][T + 1];                                              // errors of the tile just swept
+  // by tile parity: the workers' prologue sums, the new column's shares,
+  // L^A[Q,Q] of the tile, and a finished column's M[P][Q] for its owner
+  R red[2][kRowWorkers][T][T + 1];
+  __attribute__((aligned(16))) R fm[2][kRowWorkers][T * T];
+  R lat[2][T][T + 1];
+  __attribute__((aligned(16))) R ms[2][T * T];
   R owv[4][kOwRows][kOwLd];
   int ticket;
 };
@@ -358,45 +360,49 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
   int* status = sync + nblocks;
 
   if (wave == 0) {
-    // ---- sweeper: tile k - 1 in iteration k
-    R lbK[4];
+    // ---- sweeper: tile k - 1 in iteration k, then the finished column's
+    // I = P term and its product for the next tile
+    R lbK[4], lu[4], w0[4];
     {
       const R* lb = LBp + tri_index(P, P) * T * T + c * T + KA * kg;
 #pragma unroll
       for (int r = 0; r < 4; ++r) lbK[r] = lb[KB * r];
-    }
-    R w0[4];
-    {
+      EVec<R>::load4(LBp + tri_index(P, P) * T * T + c * T + 4 * kg, lu);
       const R* tW = Wk + ((int64_t)P * Nt + Qa) * T * T;
 #pragma unroll
       for (int r = 0; r < 4; ++r) w0[r] = tW[MF::row(lane, r) * T + c];
     }
-    __syncthreads();  // B2 of iteration 0 (nothing swept yet)
+    acc_t contrib = MF::zero();  // M[P][Q-1] L^A[Q,Q-1]^T for the tile about to be swept
     for (int k = 1; k <= nt; ++k) {
-      __syncthreads();  // B1: the tile's prologue sums and L^A[Q,Q] are in LDS
+      __syncthreads();  // the tile's prologue sums and L^A[Q,Q] are in LDS
       const int Q = Qa + k - 1;
+      const int pb = (k - 1) & 1;
       acc_t acc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = MF::row(lane, r);
         R pro = w0[r];
 #pragma unroll
-        for (int w = 0; w < kRowWorkers; ++w) pro += L.red[w][row][c];
-        acc[r] = pro;
+        for (int w = 0; w < kRowWorkers; ++w) pro += L.red[pb][w][row][c];
+        acc[r] = pro + contrib[r];
       }
       R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - KA kg]
 #pragma unroll
       for (int j = 0; j < 2 * T - 1; ++j) {
         const int jj = j - KA * kg;
-        laK[j] = (jj >= 0 && jj < T) ? L.lat[c][jj] : R(0);
+        laK[j] = (jj >= 0 && jj < T) ? L.lat[pb][c][jj] : R(0);
       }
-      // the next tile's W, requested before the sweep
+      // the next tile's W and L^A[Q+1,Q], requested before the sweep
+      R la1[4];
       if (k < nt) {
         const R* tW = Wk + ((int64_t)P * Nt + Q + 1) * T * T;
 #pragma unroll
         for (int r = 0; r < 4; ++r) w0[r] = tW[MF::row(lane, r) * T + c];
+        const R* La = LAp + tri_index(Q + 1, Q) * T * T;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) la1[s] = La[c * T + MF::row(lane, s)];
       }
-      // the sweep of leaf_tile, unchanged
+      // the sweep
       R* owl = &L.owv[kg][T - 1 - c][c];
       static_for<0, 2 * T - 1>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
@@ -419,199 +425,191 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
         }
       });
       wave_sync_lds();
-      // write back: errors into the workspace (for the band products), the
-      // rows below (Eb) and this row's next tile (LDS); codes and values
+      // write back, each lane the tile rows 4 kg + s of column c (the
+      // operand layout of the finished column's I = P term): errors into
+      // the copy the rows below read (first) and into the workspace (for the
+      // band products); codes and values at rounding to the outputs
       R* tW = Wk + ((int64_t)P * Nt + Q) * T * T;
       R* tE = Eb + ((int64_t)P * Nt + Q) * T * T;
       R xv[4], cqv[4], ev[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int idx = lane + 64 * u;
-        const int p = idx >> 4, q = idx & 15;
-        const bool valid = (int64_t)P * T + p < m && (int64_t)Q * T + q < n;
-        xv[u] = L.owv[std::is_same<R, float>::value ? p >> 2 : p & 3][p + T - 1][q];
-        cqv[u] = quant_unit(xv[u], lo, hi);
-        ev[u] = valid ? cqv[u] - xv[u] : R(0);
-        // the rows below wait for these stores: issued first
-        st_dev(tE + idx, ev[u] != ev[u] ? Sentinel<R>::qnan() : ev[u]);
+      for (int s = 0; s < 4; ++s) {
+        const int p = 4 * kg + s;
+        const bool valid = (int64_t)P * T + p < m && (int64_t)Q * T + c < n;
+        xv[s] = L.owv[std::is_same<R, float>::value ? kg : s][p + T - 1][c];
+        cqv[s] = quant_unit(xv[s], lo, hi);
+        ev[s] = valid ? cqv[s] - xv[s] : R(0);
+        st_dev(tE + p * T + c, ev[s] != ev[s] ? Sentinel<R>::qnan() : ev[s]);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int idx = lane + 64 * u;
-        const int p = idx >> 4, q = idx & 15;
-        const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + q;
-        const bool valid = gi < m && gjj < n;
-        const R x = xv[u], cq = cqv[u], e = ev[u];
-        tW[idx] = e;
-        L.eprev[p][q] = e;
-        if (valid) {
-          lp.V[gi * lp.ldv + gjj] = (int32_t)cq;
+      for (int s = 0; s < 4; ++s) {
+        const int p = 4 * kg + s;
+        const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + c;
+        tW[p * T + c] = ev[s];
+        if (gi < m && gjj < n) {
+          lp.V[gi * lp.ldv + gjj] = (int32_t)cqv[s];
           if (lp.Wt) {
             R sv = R(1);
             if (lp.scale_mode == 1) sv = lp.scales[gi];
             else if (lp.scale_mode == 2) sv = lp.scales[gjj];
-            lp.Wt[gi * lp.ldwt + gjj] = lp.scale_mode ? sv * x : x;
+            lp.Wt[gi * lp.ldwt + gjj] = lp.scale_mode ? sv * xv[s] : xv[s];
           }
         }
       }
-      __syncthreads();  // B2: the tile's errors are in LDS
+      if (k < nt) {
+        // column Q is finished: M[P][Q] = its new-column sum (the workers'
+        // shares, in a fixed order) plus L^B[P,P] E[P][Q], kept by the
+        // column's owner for the row's later tiles, and its product with
+        // L^A[Q+1,Q] for the next tile
+        acc_t mt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          R v = L.fm[pb][0][lane * 4 + r];
+#pragma unroll
+          for (int w = 1; w < kRowWorkers; ++w) v += L.fm[pb][w][lane * 4 + r];
+          mt[r] = v;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mt = MF::mma(ev[s], lu[s], mt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) L.ms[pb][lane * 4 + r] = mt[r];
+        contrib = MF::zero();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) contrib = MF::mma(mt[s], la1[s], contrib);
+      }
     }
     return;
   }
 
   // ---- workers: wave 1 + wid owns columns J = Jlo + wid + kRowWorkers t and
-  // the new column's terms I = Ilo + wid + kRowWorkers u
+  // the new column's terms I = Ilo + wid + kRowWorkers u; in iteration k they
+  // prepare tile k while wave 0 sweeps tile k - 1
   const int wid = wave - 1;
   acc_t mreg[kRowCols];  // M[P][J] (MFMA result layout of M^T), owned columns
 #pragma unroll
   for (int t = 0; t < kRowCols; ++t) mreg[t] = MF::zero();
-  R lu[4];  // L^B[P,P] rows for the I = P term of a finished column
-  EVec<R>::load4(LBp + tri_index(P, P) * T * T + c * T + 4 * kg, lu);
-  for (int k = 0; k <= nt; ++k) {
-    // (a) while tile k - 1 is swept: tile k's sums over the finished columns
-    // J <= Q - 2 and its new column's terms from the rows above; the factor
-    // tiles that step (b) needs are loaded here too
+  for (int k = 0; k < nt; ++k) {
     const int Q = Qa + k;
-    acc_t acc = MF::zero();
-    acc_t fresh = MF::zero();
-    R la1[4], latv[4];
-    if (k < nt) {
-      {
-        // L^A[Q,Q-1] for column Q - 1's product, L^A[Q,Q] for the sweep
-        const R* La = LAp + tri_index(Q, k >= 1 ? Q - 1 : Q) * T * T;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) la1[s] = La[c * T + MF::row(lane, s)];
-        const R* Lq = LAp + tri_index(Q, Q) * T * T;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) latv[u] = Lq[lane + 64 * u];
-      }
-      R la[kRowCols][4], laq[4], lf[kRowTerms][4], ef[kRowTerms][4];
-#pragma unroll
-      for (int t = 0; t < kRowCols; ++t) {
-        const int J = Jlo + wid + kRowWorkers * t;
-        const int Jc = J <= Q - 2 ? J : Q;
-        const R* La = LAp + tri_index(Q, Jc) * T * T;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) la[t][s] = La[c * T + MF::row(lane, s)];
-      }
-      {
-        const R* La = LAp + tri_index(Q, Q) * T * T;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) laq[s] = La[c * T + MF::row(lane, s)];
-      }
-      const int Ilo = K0 - Q > 0 ? K0 - Q : 0;
-#pragma unroll
-      for (int u = 0; u < kRowTerms; ++u) {
-        const int I = Ilo + wid + kRowWorkers * u;
-        if (I <= P - 1) {
-          EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lf[u]);
-        } else {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) lf[u][s] = R(0);
-        }
-      }
-      // the products over the row's finished columns (local data) first
-#pragma unroll
-      for (int t = 0; t < kRowCols; ++t) {
-        const int J = Jlo + wid + kRowWorkers * t;
-        if (J > Q - 2) break;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = MF::mma(mreg[t][s], la[t][s], acc);
-      }
-      // then the new column's terms from the rows above, the values polled
-      // until none is the sentinel: rows I <= P - 2 (finished a tile
-      // anti-diagonal earlier, as a rule already written) together, then
-      // the row right above (I = P - 1, which sweeps its tile on the same
-      // tile anti-diagonal as this row's current one), whose term is this
-      // wave's last in the order of I
-      bool ok = true;
-      {
-        bool done = false;
-        for (int it = 0; it <= polls && !done; ++it) {
-          bool mine = true;
-#pragma unroll
-          for (int u = 0; u < kRowTerms; ++u) {
-            const int I = Ilo + wid + kRowWorkers * u;
-            const R* E = Eb + ((int64_t)I * Nt + Q) * T * T;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              ef[u][s] = I <= P - 2 ? ld_dev(E + (4 * kg + s) * T + c) : R(0);
-              mine = mine && !is_sentinel(ef[u][s]);
-            }
-          }
-          done = __builtin_amdgcn_ballot_w64(!mine) == 0;
-          if (!done && it < polls) __builtin_amdgcn_s_sleep(1);
-        }
-        ok = done;
-      }
-#pragma unroll
-      for (int u = 0; u < kRowTerms; ++u) {
-        if (Ilo + wid + kRowWorkers * u > P - 2) break;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) fresh = MF::mma(ef[u][s], lf[u][s], fresh);
-      }
-      if (P - 1 >= Ilo && (P - 1 - Ilo) % kRowWorkers == wid) {
-        const int uc = (P - 1 - Ilo) / kRowWorkers;
-        const R* E = Eb + ((int64_t)(P - 1) * Nt + Q) * T * T;
-        R e4[4];
-        bool done = false;
-        for (int it = 0; it <= polls && !done; ++it) {
-          bool mine = true;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            e4[s] = ld_dev(E + (4 * kg + s) * T + c);
-            mine = mine && !is_sentinel(e4[s]);
-          }
-          done = __builtin_amdgcn_ballot_w64(!mine) == 0;
-          if (!done && it < polls) __builtin_amdgcn_s_sleep(1);
-        }
-        ok = ok && done;
-#pragma unroll
-        for (int u = 0; u < kRowTerms; ++u)
-          if (u == uc) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) fresh = MF::mma(e4[s], lf[u][s], fresh);
-          }
-      }
-      if (!ok && lane == 0)
-        __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc = MF::mma(fresh[s], laq[s], acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) L.fm[k & 1][wid][lane * 4 + r] = fresh[r];
-    }
-    __syncthreads();  // B2: tile k - 1 swept (its errors in LDS); tile k's shares in LDS
-    if (k == nt) break;
-    // (b) column J = Q - 1 is finished: its new-column sum plus its I = P
-    // term, kept for the row's later tiles, and its product for tile k
-    if (k >= 1 && (Q - 1 - Jlo) % kRowWorkers == wid) {
-      const int t = (Q - 1 - Jlo) / kRowWorkers;
+    // column Q - 2, finished by wave 0 one iteration ago, to its owner
+    if (k >= 2 && (Q - 2 - Jlo) % kRowWorkers == wid) {
+      const int t = (Q - 2 - Jlo) / kRowWorkers;
       acc_t mt;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        R v = L.fm[(k - 1) & 1][0][lane * 4 + r];
-#pragma unroll
-        for (int w = 1; w < kRowWorkers; ++w) v += L.fm[(k - 1) & 1][w][lane * 4 + r];
-        mt[r] = v;
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) mt = MF::mma(L.eprev[4 * kg + s][c], lu[s], mt);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc = MF::mma(mt[s], la1[s], acc);
+      for (int r = 0; r < 4; ++r) mt[r] = L.ms[k & 1][lane * 4 + r];
 #pragma unroll
       for (int u = 0; u < kRowCols; ++u)
         if (u == t) mreg[u] = mt;
     }
+    acc_t acc = MF::zero();
+    acc_t fresh = MF::zero();
+    R latv[4], la[kRowCols][4], laq[4], lf[kRowTerms][4], ef[kRowTerms][4];
+    {
+      const R* Lq = LAp + tri_index(Q, Q) * T * T;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) L.red[wid][MF::row(lane, r)][c] = acc[r];
+      for (int u = 0; u < 4; ++u) latv[u] = Lq[lane + 64 * u];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) laq[s] = Lq[c * T + MF::row(lane, s)];
+    }
+#pragma unroll
+    for (int t = 0; t < kRowCols; ++t) {
+      const int J = Jlo + wid + kRowWorkers * t;
+      const int Jc = J <= Q - 2 ? J : Q;
+      const R* La = LAp + tri_index(Q, Jc) * T * T;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) la[t][s] = La[c * T + MF::row(lane, s)];
+    }
+    const int Ilo = K0 - Q > 0 ? K0 - Q : 0;
+#pragma unroll
+    for (int u = 0; u < kRowTerms; ++u) {
+      const int I = Ilo + wid + kRowWorkers * u;
+      if (I <= P - 1) {
+        EVec<R>::load4(LBp + tri_index(P, I) * T * T + c * T + 4 * kg, lf[u]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) lf[u][s] = R(0);
+      }
+    }
+    // the products over the row's finished columns J <= Q - 2 (local data)
+#pragma unroll
+    for (int t = 0; t < kRowCols; ++t) {
+      const int J = Jlo + wid + kRowWorkers * t;
+      if (J > Q - 2) break;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = MF::mma(mreg[t][s], la[t][s], acc);
+    }
+    // then the new column's terms from the rows above, the values polled
+    // until none is the sentinel: rows I <= P - 2 (finished a tile
+    // anti-diagonal earlier, as a rule already written) together, then
+    // the row right above (I = P - 1, which sweeps its tile on the same
+    // tile anti-diagonal as this row's current one), whose term is this
+    // wave's last in the order of I
+    bool ok = true;
+    {
+      bool done = false;
+      for (int it = 0; it <= polls && !done; ++it) {
+        bool mine = true;
+#pragma unroll
+        for (int u = 0; u < kRowTerms; ++u) {
+          const int I = Ilo + wid + kRowWorkers * u;
+          const R* E = Eb + ((int64_t)I * Nt + Q) * T * T;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            ef[u][s] = I <= P - 2 ? ld_dev(E + (4 * kg + s) * T + c) : R(0);
+            mine = mine && !is_sentinel(ef[u][s]);
+          }
+        }
+        done = __builtin_amdgcn_ballot_w64(!mine) == 0;
+        if (!done && it < polls) __builtin_amdgcn_s_sleep(1);
+      }
+      ok = done;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowTerms; ++u) {
+      if (Ilo + wid + kRowWorkers * u > P - 2) break;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) fresh = MF::mma(ef[u][s], lf[u][s], fresh);
+    }
+    if (P - 1 >= Ilo && (P - 1 - Ilo) % kRowWorkers == wid) {
+      const int uc = (P - 1 - Ilo) / kRowWorkers;
+      const R* E = Eb + ((int64_t)(P - 1) * Nt + Q) * T * T + (4 * kg) * T + c;
+      R e4[4];
+      bool done = false;
+      for (int it = 0; it <= polls && !done; ++it) {
+        bool mine = true;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          e4[s] = ld_dev(E + s * T);
+          mine = mine && !is_sentinel(e4[s]);
+        }
+        done = __builtin_amdgcn_ballot_w64(!mine) == 0;
+        if (!done && it < polls) __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int u = 0; u < kRowTerms; ++u)
+        if (u == uc) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) fresh = MF::mma(e4[s], lf[u][s], fresh);
+        }
+      ok = ok && done;
+    }
+    if (!ok && lane == 0)
+      __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = MF::mma(fresh[s], laq[s], acc);
+    const int pb = k & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      L.fm[pb][wid][lane * 4 + r] = fresh[r];
+      L.red[pb][wid][MF::row(lane, r)][c] = acc[r];
+    }
     if (wid == 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int idx = lane + 64 * u;
-        L.lat[idx >> 4][idx & 15] = latv[u];
+        L.lat[pb][idx >> 4][idx & 15] = latv[u];
       }
     }
-    __syncthreads();  // B1
+    __syncthreads();  // tile k's prologue sums and L^A[Q,Q] are in LDS
   }
 }
 

@@ -119,7 +119,11 @@ def _mlp_fp32(bk, which):
     ref = oracle_solve(inp)
     rep = fp32_parity(inp, V, Wt, ref, dA=dA, dB=dB)
     if rep.mismatches:
-        rep.branch_spread, rep.branch_detail = oracle_branch_spread(inp, ref, dA, dB, ulp_seeds=(1,), noise_seeds=(1,))
+        # four branches (two of each nudge): with two, the spread of this
+        # matrix's branches (float32 loss swings of up to 2.5e-4 between
+        # nudged solves) was sampled too thinly to bound a valid solve
+        rep.branch_spread, rep.branch_detail = oracle_branch_spread(
+            inp, ref, dA, dB, ulp_seeds=(1, 2), noise_seeds=(1, 2))
     print(p.name, "fp32 whole matrix", rep.as_dict(), rep.branch_detail)
     assert_fp32_validity(rep)
     assert rep.max_dev <= 1e-4, rep
