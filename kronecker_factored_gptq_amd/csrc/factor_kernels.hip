@@ -14,7 +14,9 @@
 //       X22 -= C21 C21^T                the Schur complement,
 //       (Y22 from X22)                  recursively,
 //       Y21 = -Y22 (C21 Y11)            the off-diagonal block of the inverse;
-//                                     64 x 64 leaves in LDS, everything else
+//                                     nodes of order <= 128 in one workgroup
+//                                     (two 64 x 64 leaves and the node's four
+//                                     products in LDS), everything above on
 //                                     float64 MFMA GEMMs (gemm64)
 //   L[i][j] = Y[n-1-j][n-1-i], normalised by its diagonal  store_normalized
 #include <climits>
@@ -26,8 +28,15 @@ namespace bk {
 
 namespace {
 constexpr int NB = 64;  // Cholesky panel width
-constexpr int kLeafCols = 4;  // columns per barrier step of the leaf (8: spills, 6.90 ms factor against 6.69)
-constexpr int kLeafPatchCols = 2;  // columns of a thread's patch: 4 x 2 patches, 512 threads
+// columns per barrier step of the leaf (8: the panel wave's 8 x 8 pivot chain
+// makes each step longer than two steps of 4; factor 5.81 ms against 5.26)
+constexpr int kLeafCols = 4;
+// columns of a patch thread's patch: 4 x 2 patches, 512 threads (4 x 4 on 256
+// threads: 5.60 ms against 5.26, one wave per SIMD hides too little latency)
+constexpr int kLeafPatchCols = 2;
+// issue priority of the panel wave (its chain is every leaf step's critical
+// path; factor 5.01 -> 4.94 ms at 4096)
+constexpr int kPanelPrio = 3;
 }
 
 // X[i][j] = A[n-1-j][n-1-i] for i >= j (the lower triangle of J A J read from
@@ -58,27 +67,6 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(int64_t n, const R* 
   }
 }
 
-// Leaf of the recursion: the Cholesky factor C of the bs x bs diagonal block
-// X[off.., off..] (bs <= 64) and its inverse Y = C^-1; Y[off.., off..]
-// receives C^-1 (zeros above the diagonal). Thread (ty, tx) of a 16 x 16
-// grid keeps the 4 x 4 patch rows 4ty.., columns 4tx.. of both C and Y in
-// registers; rows and columns past bs are padded with the identity.
-// Right-looking, NC columns j .. j+NC-1 per step (whole patch columns) and
-// one barrier per step: the owners publish the raw columns j.. and the raw
-// rows j.. of Y (and the next step's pivot block as it stands); the pivot
-// factor l (NC x NC lower; reciprocal square roots by one Newton step from
-// the hardware estimate) of each step comes from one extra wave, which
-// forms it during the step before (applying that step's update to the pivot
-// block itself). After the barrier every patch thread reads l and, by
-// forward substitution, forms
-//   C[i][j+q] = (X[i][j+q] - sum_{p<q} C[i][j+p] l[q][p]) / l[q][q],
-//   Y[j+q]    = (Y[j+q]    - sum_{p<q} l[q][p] Y[j+p]) / l[q][q]   (rows),
-// then updates its patch with the rank-NC terms
-//   C[i][c] -= sum_q C[i][j+q] C[c][j+q]   (j + NC <= c <= i),
-//   Y[i][c] -= sum_q C[i][j+q] Y[j+q][c]   (i >= j + NC).
-// Published values are double-buffered by the parity of the step. A pivot
-// that is not positive and finite records off + j + q in *info (smallest
-// wins) and the factorisation continues with NaN.
 // Cholesky factor l (NC x NC, lower) of the pivot block blk and the
 // reciprocals dinv of its diagonal; bad = the first pivot that is not
 // positive and finite (-1 if none), whose dinv becomes NaN.
@@ -113,186 +101,184 @@ __device__ __forceinline__ void pivot_factor(const double (&blk)[NC][NC], double
   }
 }
 
-template <int NC, int PCW>
-__global__ __launch_bounds__(16 * (64 / PCW) + 64) void chol_inv_leaf_kernel(FactorSet set,
-                                                                            int64_t n, int64_t off,
-                                                                            int bs) {
+// Lane l's value of x (l uniform across the wave).
+__device__ __forceinline__ double lane_f64(double x, int l) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane((int)b, l);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Leaf of the recursion: the Cholesky factor C of a bs x bs diagonal block
+// (bs <= 64, padded with the identity) and its inverse Y = C^-1, in one
+// workgroup. Right-looking, NC columns per barrier step. Patch thread
+// (ty, tx) of a 16 x (64 / PCW) grid keeps rows 4 ty .., columns PCW tx .. of
+// both C and Y in registers. Step st (columns j .. j + NC - 1) needs the
+// panel C[i][j + q] of every row i and the final rows Y[j + q][c] of every
+// column c; one extra wave (lane i: row i of the panel, column i of the rows
+// of Y) forms the panel of step st + 1 during step st: it takes the columns
+// j + NC .. of C and rows j + NC .. of Y as they stand before step st
+// (published by their owners), applies step st's rank-NC update to them
+// itself (it holds step st's panel), factors the pivot block it finds on
+// rows j + NC .. (pivot_factor) and substitutes:
+//   C[i][j+q] = (X[i][j+q] - sum_{p<q} C[i][j+p] l[q][p]) / l[q][q]   (i >= j+q, else 0)
+//   Y[j+q][c] = (Y[j+q][c] - sum_{p<q} l[q][p] Y[j+p][c]) / l[q][q]
+// The patch threads only read the panel and apply the rank-NC terms
+//   C[i][c] -= sum_q C[i][j+q] C[c][j+q]   (c <= i),
+//   Y[i][c] -= sum_q C[i][j+q] Y[j+q][c]   (rows below the pivot block),
+// and the rows of the pivot block take their final rows of Y from the
+// panel. Entries of C above the diagonal stay exact zeros (masked), so the
+// upper parts of Y's rows do too. Published values are double-buffered by
+// the parity of the step. A pivot that is not positive and finite records
+// base + its index in *info (smallest wins) and the factorisation continues
+// with NaN.
+template <int NC>
+struct PanelLds {
+  double pc[2][NC][64];  // a step's panel C[i][j + q] (i = 0..63)
+  double py[2][NC][64];  // a step's final rows Y[j + q][c] (c = 0..63)
+  double rc[2][NC][64];  // the next step's columns of C before this step
+  double ry[2][NC][64];  // the next step's rows of Y before this step
+};
+
+// One 64 x 64 leaf (bs x bs, padded with the identity) by the whole
+// workgroup: 16 * (64 / PCW) patch threads and one panel wave. x(i, c)
+// returns the leaf's input for i, c < bs, c <= i. Patch thread (ty, tx)
+// returns its patch of Y = C^-1 (rows 4 ty.., columns PCW tx..) in Yr; the
+// panel wave's Yr is untouched. Every thread passes the same barriers.
+template <int NC, int PCW, typename XF>
+__device__ __forceinline__ void leaf64(int bs, const XF& x, double (&Yr)[4][PCW],
+                                       PanelLds<NC>& L, int32_t* info, int64_t base) {
   static_assert(NC % 4 == 0 && NC % PCW == 0, "whole patch rows and columns per step");
-  constexpr int PRS = NC / 4;  // patch rows per step
+  constexpr int PRS = NC / 4;   // patch rows per step
   constexpr int TX = 64 / PCW;  // thread columns; 16 thread rows of 4 rows each
-  constexpr int NCT = 16 * TX;  // patch threads; one more wave factors the pivot blocks
-  __shared__ double pnext[2][NC][NC];     // next step's pivot block before this step's update
-  __shared__ double lpub[2][NC][NC + 1];  // a step's pivot factor l, and dinv in column NC
-  __shared__ double colp[2][NC][64];
-  __shared__ double rowp[2][NC][64];
-  const FactorSide S = factor_side(set, (int)blockIdx.x);  // one matrix per workgroup
+  constexpr int NCT = 16 * TX;  // patch threads; one more wave forms the panels
   const int tid = threadIdx.x;
   const int steps = (bs + NC - 1) / NC;
+  auto input = [&](int i, int c) {
+    if (i < bs && c < bs) return c <= i ? x(i, c) : 0.0;
+    return i == c ? 1.0 : 0.0;
+  };
   if (tid >= NCT) {
-    // Pivot wave: during step st it applies step st's update to the pivot
-    // block of step st + 1 (with the same operations the patch threads use
-    // for those entries), factors it and publishes l and dinv for step
-    // st + 1, so that the patch threads never wait for a pivot factor.
-    const bool lead = tid == NCT;
-    double l[NC][NC], dinv[NC];
-    {
-      double blk[NC][NC];
+    // the panel chain is each step's critical path: its instructions go
+    // first when the patch waves on its SIMD are ready too
+    __builtin_amdgcn_s_setprio(kPanelPrio);
+    const int i = tid - NCT;  // row of the panel, column of the rows of Y
+    double cp[NC], yp[NC];    // this step's panel at row i / column i
+    // the panel of step j1 / NC from raw columns v and raw rows w (lane i),
+    // published into buffer b
+    auto panel = [&](int j1, const double (&v)[NC], const double (&w)[NC], int b) {
+      double blk[NC][NC], l[NC][NC], dinv[NC];
 #pragma unroll
       for (int q = 0; q < NC; ++q)
 #pragma unroll
-        for (int p = 0; p < NC; ++p) {
-          double v = 0.0;
-          if (q < bs && p < bs) v = p <= q ? S.X[(off + q) * n + off + p] : 0.0;
-          else if (q == p) v = 1.0;
-          blk[q][p] = v;
-        }
+        for (int p = 0; p < NC; ++p) blk[q][p] = p <= q ? lane_f64(v[p], j1 + q) : 0.0;
       int bad;
       pivot_factor<NC>(blk, l, dinv, bad);
-      if (lead && bad >= 0 && bad < bs) atomicMin(S.info, (int32_t)(off + bad));
-      if (lead) {
+      if (i == 0 && bad >= 0 && j1 + bad < bs) atomicMin(info, (int32_t)(base + j1 + bad));
 #pragma unroll
-        for (int q = 0; q < NC; ++q) {
+      for (int q = 0; q < NC; ++q) {
+        double c = v[q], y = w[q];
 #pragma unroll
-          for (int p = 0; p < NC; ++p) lpub[0][q][p] = l[q][p];
-          lpub[0][q][NC] = dinv[q];
-        }
+        for (int p = 0; p < NC; ++p)
+          if (p < q) {
+            c -= cp[p] * l[q][p];
+            y -= l[q][p] * yp[p];
+          }
+        cp[q] = i >= j1 + q ? c * dinv[q] : 0.0;
+        yp[q] = y * dinv[q];
+        L.pc[b][q][i] = cp[q];
+        L.py[b][q][i] = yp[q];
       }
+    };
+    {
+      double v[NC], w[NC];
+#pragma unroll
+      for (int a = 0; a < NC; ++a) {
+        v[a] = input(i, a);
+        w[a] = i == a ? 1.0 : 0.0;
+      }
+      panel(0, v, w, 0);
     }
     for (int st = 0; st < steps; ++st) {
       const int pb = st & 1;
       __syncthreads();
       if (st + 1 >= steps) continue;
       const int j1 = NC * (st + 1);
-      double ci[NC][NC];  // step st's panel C[j1 + a][j + q]
-#pragma unroll
-      for (int a = 0; a < NC; ++a) {
-#pragma unroll
-        for (int q = 0; q < NC; ++q) {
-          double vi = colp[pb][q][j1 + a];
-#pragma unroll
-          for (int p = 0; p < NC; ++p)
-            if (p < q) vi -= ci[a][p] * l[q][p];
-          ci[a][q] = vi * dinv[q];
-        }
-      }
-      double blk[NC][NC];
+      // step st's update of the next columns and rows:
+      //   C[i][j1+a] -= sum_q C[i][j+q] C[j1+a][j+q],  Y[j1+a][i] -= sum_q C[j1+a][j+q] Y[j+q][i]
+      double cq[NC][NC], v[NC], w[NC];
 #pragma unroll
       for (int a = 0; a < NC; ++a)
 #pragma unroll
-        for (int b = 0; b < NC; ++b) {
-          double dl = 0.0;
+        for (int q = 0; q < NC; ++q) cq[a][q] = lane_f64(cp[q], j1 + a);
 #pragma unroll
-          for (int q = 0; q < NC; ++q) dl += ci[a][q] * ci[b][q];
-          double v = pnext[pb][a][b];
-          if (b <= a) v -= dl;
-          blk[a][b] = v;
-        }
-      int bad;
-      pivot_factor<NC>(blk, l, dinv, bad);
-      if (lead && bad >= 0 && j1 + bad < bs) atomicMin(S.info, (int32_t)(off + j1 + bad));
-      if (lead) {
+      for (int a = 0; a < NC; ++a) {
+        double c = L.rc[pb][a][i], y = L.ry[pb][a][i];
 #pragma unroll
         for (int q = 0; q < NC; ++q) {
-#pragma unroll
-          for (int p = 0; p < NC; ++p) lpub[pb ^ 1][q][p] = l[q][p];
-          lpub[pb ^ 1][q][NC] = dinv[q];
+          c -= cp[q] * cq[a][q];
+          y -= cq[a][q] * yp[q];
         }
+        v[a] = i >= j1 + a ? c : 0.0;
+        w[a] = y;
       }
+      panel(j1, v, w, pb ^ 1);
     }
+    __builtin_amdgcn_s_setprio(0);
     return;
   }
   const int ty = tid / TX, tx = tid % TX;
-  double Lr[4][PCW], Yr[4][PCW];
+  double Lr[4][PCW];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < PCW; ++b) {
       const int i = 4 * ty + a, c = PCW * tx + b;
-      double v = 0.0;
-      if (i < bs && c < bs) v = c <= i ? S.X[(off + i) * n + off + c] : 0.0;
-      else if (i == c) v = 1.0;
-      Lr[a][b] = v;
+      Lr[a][b] = input(i, c);
       Yr[a][b] = (i == c) ? 1.0 : 0.0;
     }
   for (int st = 0; st < steps; ++st) {
-    const int j = NC * st, pb = st & 1;
-    // owners of columns j..j+NC-1 and of rows j..j+NC-1
-    const bool ownc = tx >= j / PCW && tx < (j + NC) / PCW;
-    const bool ownr = ty >= PRS * st && ty < PRS * (st + 1);
-    const int rq = 4 * (ty - PRS * st);  // first pivot row of this thread row
-    // publish the next step's pivot block, columns j..j+NC-1 and rows
-    // j..j+NC-1 of Y
-    if (tx >= (j + NC) / PCW && tx < (j + 2 * NC) / PCW && ty >= PRS * (st + 1) &&
-        ty < PRS * (st + 2)) {
-      const int rn = 4 * (ty - PRS * (st + 1));
+    const int j = NC * st, j1 = j + NC, pb = st & 1;
+    // publish the next step's columns of C and rows of Y as they stand
+    if (tx >= j1 / PCW && tx < (j1 + NC) / PCW) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < PCW; ++b) pnext[pb][rn + a][PCW * tx + b - j - NC] = Lr[a][b];
+        for (int b = 0; b < PCW; ++b) L.rc[pb][PCW * tx + b - j1][4 * ty + a] = Lr[a][b];
     }
-    if (ownc) {
+    if (ty >= PRS * (st + 1) && ty < PRS * (st + 2)) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < PCW; ++b) colp[pb][PCW * tx + b - j][4 * ty + a] = Lr[a][b];
-    }
-    if (ownr) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < PCW; ++b) rowp[pb][rq + a][PCW * tx + b] = Yr[a][b];
+        for (int b = 0; b < PCW; ++b)
+          L.ry[pb][4 * (ty - PRS * (st + 1)) + a][PCW * tx + b] = Yr[a][b];
     }
     __syncthreads();
-    // A thread whose rows all lie above the pivot block is done with them:
-    // its rows of Y are final and its rows of C are never read again (its
-    // entries of C in later columns are exact zeros, published as such).
+    // rows above the pivot block are final
     if (ty < PRS * st) continue;
-    // this step's pivot factor, from the pivot wave
-    double l[NC][NC], dinv[NC];
+    double ci[4][NC], cc[PCW][NC], yq[NC][PCW];
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
 #pragma unroll
-      for (int p = 0; p < NC; ++p) l[q][p] = lpub[pb][q][p];
-      dinv[q] = lpub[pb][q][NC];
-    }
-    // columns j.. of C at this thread's rows i and at its columns c taken as
-    // rows, and rows j.. of Y at its columns c (final after this step). No
-    // masks: above the pivot block these are exact zeros (C and Y keep exact
-    // zeros above their diagonals, and 0 * dinv = 0); the pivot block's own
-    // rows of C only reach entries of C in columns < j + NC, which no later
-    // step reads, and its rows of Y are overwritten with yq after the update
-    double ci[4][NC], cc[PCW][NC], yq[NC][PCW];
+      for (int a = 0; a < 4; ++a) ci[a][q] = L.pc[pb][q][4 * ty + a];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int i = 4 * ty + a;
-#pragma unroll
-      for (int q = 0; q < NC; ++q) {
-        double vi = colp[pb][q][i];
-#pragma unroll
-        for (int p = 0; p < NC; ++p)
-          if (p < q) vi -= ci[a][p] * l[q][p];
-        ci[a][q] = vi * dinv[q];
+      for (int b = 0; b < PCW; ++b) {
+        cc[b][q] = L.pc[pb][q][PCW * tx + b];
+        yq[q][b] = L.py[pb][q][PCW * tx + b];
       }
     }
+    if (ty < PRS * (st + 1)) {
+      // rows of the pivot block: their rows of Y are final now
+      const int rq = 4 * (ty - PRS * st);
 #pragma unroll
-    for (int b = 0; b < PCW; ++b) {
-      const int c = PCW * tx + b;
+      for (int pr = 0; pr < PRS; ++pr)
+        if (rq == 4 * pr) {
 #pragma unroll
-      for (int q = 0; q < NC; ++q) {
-        double vc = colp[pb][q][c];
+          for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int p = 0; p < NC; ++p)
-          if (p < q) vc -= cc[b][p] * l[q][p];
-        cc[b][q] = vc * dinv[q];
-      }
-#pragma unroll
-      for (int q = 0; q < NC; ++q) {
-        double v = rowp[pb][q][c];
-#pragma unroll
-        for (int p = 0; p < NC; ++p)
-          if (p < q) v -= l[q][p] * yq[p][b];
-        yq[q][b] = v * dinv[q];
-      }
+            for (int b = 0; b < PCW; ++b) Yr[a][b] = yq[4 * pr + a][b];
+        }
+      continue;
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -308,17 +294,21 @@ __global__ __launch_bounds__(16 * (64 / PCW) + 64) void chol_inv_leaf_kernel(Fac
         if (c <= i) Lr[a][b] -= dl;  // C keeps exact zeros above its diagonal
         Yr[a][b] -= dy;
       }
-    if (ownr) {  // rows j.. of Y are final now
-#pragma unroll
-      for (int pr = 0; pr < PRS; ++pr)
-        if (rq == 4 * pr) {
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < PCW; ++b) Yr[a][b] = yq[4 * pr + a][b];
-        }
-    }
   }
+}
+
+template <int NC, int PCW>
+__global__ __launch_bounds__(16 * (64 / PCW) + 64) void chol_inv_leaf_kernel(FactorSet set,
+                                                                                  int64_t n,
+                                                                                  int64_t off,
+                                                                                  int bs) {
+  __shared__ PanelLds<NC> L;
+  const FactorSide S = factor_side(set, (int)blockIdx.x);  // one matrix per workgroup
+  const double* X = S.X + off * n + off;
+  double Yr[4][PCW];
+  leaf64<NC, PCW>(bs, [&](int i, int c) { return X[(int64_t)i * n + c]; }, Yr, L, S.info, off);
+  if ((int)threadIdx.x >= 16 * (64 / PCW)) return;
+  const int ty = threadIdx.x / (64 / PCW), tx = threadIdx.x % (64 / PCW);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -326,6 +316,167 @@ __global__ __launch_bounds__(16 * (64 / PCW) + 64) void chol_inv_leaf_kernel(Fac
       const int i = 4 * ty + a, c = PCW * tx + b;
       if (i < bs && c < bs) S.Y[(off + i) * n + off + c] = c <= i ? Yr[a][b] : 0.0;
     }
+}
+
+// A 64 x 64 LDS matrix, padded against bank conflicts.
+constexpr int kNodeLd = 66;
+typedef double NodeMat[64][kNodeLd];
+
+// Two 16 x 16 output tiles of one wave, rows r0 .., columns c0 .. and
+// c0 + 16 ..: acc[u] += A[r0 .., k] B[k, c0 + 16 u ..] over k in [k0, k1)
+// (multiples of 16), a(r, k) and b(k, c) reading LDS; the two chains share
+// the A operand and interleave on the matrix unit.
+template <typename FA, typename FB>
+__device__ __forceinline__ void node_tiles(v4d (&acc)[2], int r0, int c0, int k0, int k1,
+                                           const FA& a, const FB& b) {
+  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  for (int k = k0; k < k1; k += 16) {
+    double av[4], b0[4], b1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      av[u] = a(r0 + r, k + 4 * u + q);
+      b0[u] = b(k + 4 * u + q, c0 + r);
+      b1[u] = b(k + 4 * u + q, c0 + 16 + r);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], b0[u], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], b1[u], acc[1], 0, 0, 0);
+    }
+  }
+}
+
+// A whole node of order len in (64, 128] (children: leaves of 64 and
+// len - 64) in one workgroup per matrix, every intermediate in LDS:
+//   Y11 = C11^-1 (leaf of X11), C21 = X21 Y11^T, X22 -= C21 C21^T,
+//   Tmp = C21 Y11, Y22 = C22^-1 (leaf of X22), Y21 = -Y22 Tmp.
+// The four products run on v_mfma_f64_16x16x4; each of the eight patch
+// waves takes two adjacent 16 x 16 output tiles (tile row ti, tile columns
+// tj0, tj0 + 1), with K ranges cut at the triangular operands' zero blocks
+// (16-granular; the extra terms are exact zeros). The wave-to-tile map
+// pairs heavy and light tile rows on each SIMD (waves w and w + 4 share
+// one). X21 and X22 are loaded into registers early, so no global load
+// latency sits between the phases.
+template <int NC, int PCW>
+__global__ __launch_bounds__(16 * (64 / PCW) + 64) void chol_inv_node_kernel(FactorSet set,
+                                                                            int64_t n,
+                                                                            int64_t off,
+                                                                            int len) {
+  constexpr int TX = 64 / PCW, NCT = 16 * TX;
+  static_assert(NCT == 512, "eight patch waves");
+  __shared__ PanelLds<NC> L;
+  __shared__ NodeMat S1, S2, S3;
+  const FactorSide S = factor_side(set, (int)blockIdx.x);
+  const int n2 = len - 64;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int ty = tid / TX, tx = tid % TX;
+  const bool patch = tid < NCT;
+  const double* X11 = S.X + off * n + off;
+  const double* X21 = S.X + (off + 64) * n + off;
+  const double* X22 = S.X + (off + 64) * n + off + 64;
+  double* Y11 = S.Y + off * n + off;
+  double* Y21 = S.Y + (off + 64) * n + off;
+  double* Y22 = S.Y + (off + 64) * n + off + 64;
+  // this thread's patch of X21 (zero rows past n2), kept until the leaf is done
+  double x21[4][PCW];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < PCW; ++b) {
+      const int i = 4 * ty + a, c = PCW * tx + b;
+      x21[a][b] = (patch && i < n2) ? X21[(int64_t)i * n + c] : 0.0;
+    }
+  double Yr[4][PCW];
+  leaf64<NC, PCW>(64, [&](int i, int c) { return X11[(int64_t)i * n + c]; }, Yr, L, S.info, off);
+  // X22's lower triangle (rows and columns below n2) for the second leaf
+  double x22[4][PCW];
+  if (patch) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < PCW; ++b) {
+        const int i = 4 * ty + a, c = PCW * tx + b;
+        x22[a][b] = (c <= i && i < n2) ? X22[(int64_t)i * n + c] : 0.0;
+        const double y = c <= i ? Yr[a][b] : 0.0;
+        Y11[(int64_t)i * n + c] = y;
+        S1[i][c] = y;
+        S2[i][c] = x21[a][b];
+      }
+  }
+  __syncthreads();
+  constexpr int kRow[8] = {1, 2, 3, 0, 0, 1, 2, 3};
+  const int ti = kRow[w & 7], tj0 = w < 4 ? 0 : 2;
+  const int lane = tid & 63, r16 = lane & 15, q4 = lane >> 4;
+  if (patch) {
+    // C21 = X21 Y11^T into S3 (Y11[c][k] = 0 for k > c)
+    v4d acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+    node_tiles(acc, 16 * ti, 16 * tj0, 0, 16 * tj0 + 32, [&](int r, int k) { return S2[r][k]; },
+               [&](int k, int c) { return S1[c][k]; });
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S3[16 * ti + q4 + 4 * r][16 * (tj0 + u) + r16] = acc[u][r];
+  }
+  __syncthreads();
+  v4d tmp[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  if (patch) {
+    // X22's update C21 C21^T on the lower tiles into S2 (X21 is done with),
+    // and Tmp = C21 Y11 (Y11[k][c] = 0 for k < c) in registers
+    if (tj0 <= ti) {
+      v4d acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+      node_tiles(acc, 16 * ti, 16 * tj0, 0, 64, [&](int r, int k) { return S3[r][k]; },
+                 [&](int k, int c) { return S3[c][k]; });
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S2[16 * ti + q4 + 4 * r][16 * (tj0 + u) + r16] = acc[u][r];
+    }
+    node_tiles(tmp, 16 * ti, 16 * tj0, 16 * tj0, 64, [&](int r, int k) { return S3[r][k]; },
+               [&](int k, int c) { return S1[k][c]; });
+  }
+  __syncthreads();
+  if (patch) {
+    // Tmp into S1 (Y11 is done with); the second leaf's input X22 - C21 C21^T
+    // into S2 (lower triangle; the leaf reads nothing else)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S1[16 * ti + q4 + 4 * r][16 * (tj0 + u) + r16] = tmp[u][r];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < PCW; ++b) {
+        const int i = 4 * ty + a, c = PCW * tx + b;
+        if (c <= i) S2[i][c] = x22[a][b] - S2[i][c];
+      }
+  }
+  __syncthreads();
+  leaf64<NC, PCW>(n2, [&](int i, int c) { return S2[i][c]; }, Yr, L, S.info, off + 64);
+  if (patch) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < PCW; ++b) {
+        const int i = 4 * ty + a, c = PCW * tx + b;
+        const double y = (c <= i && i < n2 && c < n2) ? Yr[a][b] : 0.0;
+        if (i < n2 && c < n2) Y22[(int64_t)i * n + c] = y;
+        S2[i][c] = y;
+      }
+  }
+  __syncthreads();
+  if (patch) {
+    // Y21 = -Y22 Tmp (Y22[r][k] = 0 for k > r)
+    v4d acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+    node_tiles(acc, 16 * ti, 16 * tj0, 0, 16 * ti + 16, [&](int r, int k) { return S2[r][k]; },
+               [&](int k, int c) { return S1[k][c]; });
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + q4 + 4 * r;
+        if (i < n2) Y21[(int64_t)i * n + 16 * (tj0 + u) + r16] = -acc[u][r];
+      }
+  }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {
@@ -423,7 +574,7 @@ static inline int tmp_class(int64_t len) {
 }
 
 static void tmp_need(int64_t len, int64_t* need) {
-  if (len <= NB) return;
+  if (len <= 2 * NB) return;  // nodes of order <= 128 keep Tmp in LDS
   const int64_t n1 = split_point(len), n2 = len - n1;
   const int c = tmp_class(len);
   if (n2 * n1 > need[c]) need[c] = n2 * n1;
@@ -462,6 +613,12 @@ static hipError_t chol_inv_rec(int64_t n, const FactorSet& sd, int64_t off, int6
   const int64_t zs = sd.stride;
   if (len <= NB) {
     hipLaunchKernelGGL((chol_inv_leaf_kernel<kLeafCols, kLeafPatchCols>), dim3(ns),
+                       dim3(16 * (64 / kLeafPatchCols) + 64), 0, s, sd, n, off, (int)len);
+    return hipGetLastError();
+  }
+  if (len <= 2 * NB) {
+    // split_point gives 64 here: both children are leaves
+    hipLaunchKernelGGL((chol_inv_node_kernel<kLeafCols, kLeafPatchCols>), dim3(ns),
                        dim3(16 * (64 / kLeafPatchCols) + 64), 0, s, sd, n, off, (int)len);
     return hipGetLastError();
   }

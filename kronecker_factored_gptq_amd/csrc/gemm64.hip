@@ -444,8 +444,10 @@ __device__ __forceinline__ double wg_sum(double part, double* red) {
   return t;
 }
 
+// One BM x BN output block (bmap) of one problem; nbx = column blocks of the
+// grid (indexes the dot epilogue's per-block partials).
 template <int BM, int BN, int WM, int WN, bool TRI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
+__device__ __forceinline__ void big_block(const Gemm64Args& a, const BlockMap bmap, int64_t nbx) {
   typedef BigCfg<BM, BN, WM, WN> C;
   typedef Mfma<double> MF;
   __shared__ double As[2][BM][GLD];
@@ -456,7 +458,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15;
-  const BlockMap bmap = map_block<TRI>(a);
   const int64_t bm = bmap.bm, bn = bmap.bn;
   const int z = bmap.z;
   double* Cp = a.C + z * a.sC;
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
   if (a.dot) {
     const double part = skip ? 0.0 : big_dot<BM, BN, WM, WN>(a, z, row0, col0, acc);
     const double t = wg_sum<WM * WN>(part, red);
-    if (tid == 0) a.partial[z * a.sPart + bm * gridDim.x + bn] = t;
+    if (tid == 0) a.partial[z * a.sPart + bm * nbx + bn] = t;
     return;
   }
   if (skip) return;
@@ -502,6 +503,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
           Cp[gr * a.ldc + gc] = v;
         }
       }
+}
+
+template <int BM, int BN, int WM, int WN, bool TRI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(Gemm64Args a) {
+  big_block<BM, BN, WM, WN, TRI>(a, map_block<TRI>(a), gridDim.x);
+}
+
+// Two independent products of one launch on BS x BS blocks: first the blocks
+// on or below the diagonal of a0 (a square lower-block product without a
+// triangular operand: n0 = nb (nb + 1) / 2 blocks per problem, all with the
+// same K range), then the blocks of a1 (X1 x Y1 per problem) mapped longest
+// K range first as in gemm_big_kernel. The two products share the machine,
+// so the half of the grid that a lower-block product alone leaves idle runs
+// the other product.
+template <int BS, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_big_pair_kernel(Gemm64Args a0,
+                                                                    Gemm64Args a1, int64_t n0,
+                                                                    int64_t X1, int64_t Y1) {
+  const int64_t w = blockIdx.x;
+  if (w < n0) {
+    // a0's lower blocks, problem fastest: block b of the lower triangle in
+    // row-major order is (bm, b - bm (bm + 1) / 2)
+    const int64_t b = w / a0.batch;
+    int64_t bm = (int64_t)((__builtin_sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
+    while (bm * (bm + 1) / 2 > b) --bm;
+    while ((bm + 1) * (bm + 2) / 2 <= b) ++bm;
+    const BlockMap m{bm, b - bm * (bm + 1) / 2, (int)(w % a0.batch)};
+    big_block<BS, BS, WM, WN, true>(a0, m, 0);
+  } else {
+    big_block<BS, BS, WM, WN, true>(a1, map_block_lin(a1, w - n0, X1, Y1, a1.batch), X1);
+  }
 }
 
 // Stream-K dot product over the lower blocks of a square product (the
@@ -616,7 +648,27 @@ static int small_block(const Gemm64Args& a) {
   return (!a.dot && b64 <= 512) ? 32 : 64;
 }
 
+// The pair of a square lower-block product a0 (no triangular operand) and
+// a1 on 128 x 128 blocks, when together they give at least this many blocks
+// (the factor's top node at 4096: Schur update on its lower blocks and
+// C21 Y11, 1.02 -> 0.79 ms against two launches; the order-2048 nodes' 200
+// blocks stay on the 32 x 32 pair kernel, which measured as fast)
+constexpr int64_t kBigPairMinBlocks = 256;
+
 hipError_t launch_gemm64_pair(const Gemm64Args& a0, const Gemm64Args& a1, hipStream_t s) {
+  if (a0.lower_out && !a0.a_lower && !a0.b_lower && a0.M == a0.N && !a0.dot && !a1.dot &&
+      a0.M > 0 && a1.M > 0 && a1.N > 0 && a0.batch == a1.batch && a0.batch >= 1 &&
+      a0.batch <= kMaxGemmBatch) {
+    const int64_t nb = (a0.M + 127) / 128;
+    const int64_t n0 = nb * (nb + 1) / 2 * a0.batch;
+    const int64_t X1 = (a1.N + 127) / 128, Y1 = (a1.M + 127) / 128;
+    const int64_t n1 = X1 * Y1 * a1.batch;
+    if (n0 + n1 >= kBigPairMinBlocks) {
+      hipLaunchKernelGGL((gemm_big_pair_kernel<128, 2, 4>), dim3((unsigned)(n0 + n1)), dim3(512),
+                         0, s, a0, a1, n0, X1, Y1);
+      return hipGetLastError();
+    }
+  }
   const int g0 = small_block(a0), g1 = small_block(a1);
   const bool empty0 = a0.M <= 0 || a0.N <= 0, empty1 = a1.M <= 0 || a1.N <= 0;
   if (empty0 || empty1 || g0 == 0 || g0 != g1 || a0.dot || a1.dot || a0.batch != a1.batch ||
