@@ -29,8 +29,12 @@ def _problem(m, n, dtype, seed, alpha):
 
 # ------------------------------------------------------------------ factor ---
 
+# Orders up to 128 run as one fused node (two leaves of 64 and n - 64): 127
+# and 128 give second leaves of 63 and 64 rows, 100 one of 36, 192 a node of
+# 128 next to a leaf of 64.
 @pytest.mark.parametrize("dtype", ["f64", "f32"])
-@pytest.mark.parametrize("m,n", [(1, 1), (5, 9), (16, 16), (64, 64), (65, 130), (200, 257)])
+@pytest.mark.parametrize("m,n", [(1, 1), (5, 9), (16, 16), (64, 64), (65, 130), (127, 128),
+                                 (100, 192), (200, 257)])
 def test_factor_matches_oracle(gpu_lib, dtype, m, n):
     bk = gpu_lib
     p = random_problem(m, n, dtype, seed=m + n, heavy_tail=True)
@@ -50,10 +54,14 @@ def test_factor_matches_oracle(gpu_lib, dtype, m, n):
     np.testing.assert_allclose(dB, rdB, rtol=64 * condB * 1.1e-16 * m + 4 * eps)
 
 
+# (40, 30): the bad pivot in a single leaf; (100, 110): in the second leaf of
+# a fused node (the factor runs on the reversed matrix, so entry 7 is pivot
+# n - 8 >= 64)
+@pytest.mark.parametrize("m,n", [(40, 30), (100, 110)])
 @pytest.mark.parametrize("side", ["A", "B"])
-def test_factor_rejects_non_spd(gpu_lib, side):
+def test_factor_rejects_non_spd(gpu_lib, side, m, n):
     bk = gpu_lib
-    p = random_problem(40, 30, "f64", seed=1)
+    p = random_problem(m, n, "f64", seed=1)
     A, B = p.A.copy(), p.B.copy()
     bad = A if side == "A" else B
     bad[7, 7] = -5.0  # indefinite
