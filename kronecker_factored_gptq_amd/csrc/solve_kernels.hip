@@ -372,6 +372,19 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) w0[r] = tW[MF::row(lane, r) * T + c];
     }
+    // the scales the pre-rounding outputs need: this row's four rows (row
+    // scales, the same for every tile of the row), or the tile's column
+    // (column scales, loaded for the next tile after each write-back)
+    R srow[4], scol = R(1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t gi = (int64_t)P * T + 4 * kg + s;
+      srow[s] = (lp.Wt && lp.scale_mode == 1 && gi < m) ? lp.scales[gi] : R(1);
+    }
+    if (lp.Wt && lp.scale_mode == 2) {
+      const int64_t gj = (int64_t)Qa * T + c;
+      scol = gj < n ? lp.scales[gj] : R(1);
+    }
     acc_t contrib = MF::zero();  // M[P][Q-1] L^A[Q,Q-1]^T for the tile about to be swept
     for (int k = 1; k <= nt; ++k) {
       __syncthreads();  // the tile's prologue sums and L^A[Q,Q] are in LDS
@@ -426,36 +439,26 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
       });
       wave_sync_lds();
       // write back, each lane the tile rows 4 kg + s of column c (the
-      // operand layout of the finished column's I = P term): errors into
-      // the copy the rows below read (first) and into the workspace (for the
-      // band products); codes and values at rounding to the outputs
+      // operand layout of the finished column's I = P term). In the order
+      // the next steps need them: the four values read together, the errors
+      // into the copy the rows below poll, the finished column's sum and its
+      // product for the next tile (the next sweep waits for these), and only
+      // then the workspace and the outputs
       R* tW = Wk + ((int64_t)P * Nt + Q) * T * T;
       R* tE = Eb + ((int64_t)P * Nt + Q) * T * T;
       R xv[4], cqv[4], ev[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int p = 4 * kg + s;
-        const bool valid = (int64_t)P * T + p < m && (int64_t)Q * T + c < n;
-        xv[s] = L.owv[std::is_same<R, float>::value ? kg : s][p + T - 1][c];
-        cqv[s] = quant_unit(xv[s], lo, hi);
-        ev[s] = valid ? cqv[s] - xv[s] : R(0);
-        st_dev(tE + p * T + c, ev[s] != ev[s] ? Sentinel<R>::qnan() : ev[s]);
-      }
+      for (int s = 0; s < 4; ++s) xv[s] = L.owv[std::is_same<R, float>::value ? kg : s][4 * kg + s + T - 1][c];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int p = 4 * kg + s;
-        const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + c;
-        tW[p * T + c] = ev[s];
-        if (gi < m && gjj < n) {
-          lp.V[gi * lp.ldv + gjj] = (int32_t)cqv[s];
-          if (lp.Wt) {
-            R sv = R(1);
-            if (lp.scale_mode == 1) sv = lp.scales[gi];
-            else if (lp.scale_mode == 2) sv = lp.scales[gjj];
-            lp.Wt[gi * lp.ldwt + gjj] = lp.scale_mode ? sv * xv[s] : xv[s];
-          }
-        }
+        const bool valid = (int64_t)P * T + p < m && (int64_t)Q * T + c < n;
+        cqv[s] = quant_unit(xv[s], lo, hi);
+        ev[s] = valid ? cqv[s] - xv[s] : R(0);
       }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        st_dev(tE + (4 * kg + s) * T + c, ev[s] != ev[s] ? Sentinel<R>::qnan() : ev[s]);
       if (k < nt) {
         // column Q is finished: M[P][Q] = its new-column sum (the workers'
         // shares, in a fixed order) plus L^B[P,P] E[P][Q], kept by the
@@ -476,6 +479,23 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
         contrib = MF::zero();
 #pragma unroll
         for (int s = 0; s < 4; ++s) contrib = MF::mma(mt[s], la1[s], contrib);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int p = 4 * kg + s;
+        const int64_t gi = (int64_t)P * T + p, gjj = (int64_t)Q * T + c;
+        tW[p * T + c] = ev[s];
+        if (gi < m && gjj < n) {
+          lp.V[gi * lp.ldv + gjj] = (int32_t)cqv[s];
+          if (lp.Wt) {
+            const R sv = lp.scale_mode == 1 ? srow[s] : scol;
+            lp.Wt[gi * lp.ldwt + gjj] = lp.scale_mode ? sv * xv[s] : xv[s];
+          }
+        }
+      }
+      if (lp.Wt && lp.scale_mode == 2 && k < nt) {
+        const int64_t gj1 = (int64_t)(Q + 1) * T + c;
+        scol = gj1 < n ? lp.scales[gj1] : R(1);
       }
     }
     return;
