@@ -314,7 +314,13 @@ struct RowLds {
   // L^A[Q,Q] of the tile, and a finished column's M[P][Q] for its owner
   R red[2][kRowWorkers][T][T + 1];
   __attribute__((aligned(16))) R fm[2][kRowWorkers][T * T];
-  R lat[2][T][T + 1];
+  // rows of L^A[Q,Q] stored at kLatPad .. kLatPad + T - 1 of a zero row, so
+  // that the sweep's lane-shifted window (columns j - KA kg, j = 0 .. 2T - 2)
+  // is one contiguous, unmasked read per lane (16-byte aligned for float)
+  static constexpr int kVn = 16 / (int)sizeof(R);
+  static constexpr int kLatPad = 3 * SweepK<R>::KA;
+  static constexpr int kLatLd = (kLatPad + 2 * T - 1 + kVn - 1) / kVn * kVn;
+  __attribute__((aligned(16))) R lat[2][T][kLatLd];
   __attribute__((aligned(16))) R ms[2][T * T];
   R owv[4][kOwRows][kOwLd];
   int ticket;
@@ -346,6 +352,9 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, kg = lane >> 4;
+  // the zero padding of the L^A[Q,Q] rows (the rows themselves are written
+  // per tile)
+  for (int e = tid; e < 2 * T * LT::kLatLd; e += 64 * kLeafWaves) (&L.lat[0][0][0])[e] = R(0);
   if (tid == 0)
     L.ticket = __hip_atomic_fetch_add(sync + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -399,11 +408,22 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
         for (int w = 0; w < kRowWorkers; ++w) pro += L.red[pb][w][row][c];
         acc[r] = pro + contrib[r];
       }
-      R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - KA kg]
+      R laK[2 * T - 1];  // laK[j] = L^A[Q,Q][c][j - KA kg] (zero outside the tile)
+      {
+        const R* lr = &L.lat[pb][c][LT::kLatPad - KA * kg];
+        if constexpr (sizeof(R) == 4) {
 #pragma unroll
-      for (int j = 0; j < 2 * T - 1; ++j) {
-        const int jj = j - KA * kg;
-        laK[j] = (jj >= 0 && jj < T) ? L.lat[pb][c][jj] : R(0);
+          for (int i = 0; i < (2 * T - 1 + 3) / 4; ++i) {
+            const float4 v = reinterpret_cast<const float4*>(lr)[i];
+            const R vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * i + e < 2 * T - 1) laK[4 * i + e] = vv[e];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2 * T - 1; ++j) laK[j] = lr[j];
+        }
       }
       // the next tile's W and L^A[Q+1,Q], requested before the sweep
       R la1[4];
@@ -626,7 +646,7 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int idx = lane + 64 * u;
-        L.lat[pb][idx >> 4][idx & 15] = latv[u];
+        L.lat[pb][idx >> 4][LT::kLatPad + (idx & 15)] = latv[u];
       }
     }
     __syncthreads();  // tile k's prologue sums and L^A[Q,Q] are in LDS
