@@ -61,73 +61,133 @@ __device__ inline R sentinel_value() {
 
 
 // ---------------------------------------------------------------------------
-// Pack U = W / s (row-major W, ldw) into tiles; padding is zero. mode: 0 no
-// scales, 1 per-row, 2 per-column.
+// Pack kernels. A workgroup moves a strip of kPackTiles consecutive tiles of
+// one tile row (16 rows x 64 columns): every row of the strip is one
+// contiguous run of the source, read in 16-byte vectors when the source rows
+// are 16-byte aligned, and each tile row of the destination is a contiguous
+// 16-byte-aligned run too.
 // ---------------------------------------------------------------------------
+constexpr int kPackTiles = 4;
+// 16-byte vector of R
+template <typename R> struct PackVec;
+template <> struct PackVec<float> {
+  typedef float4 T;
+  static constexpr int N = 4;
+};
+template <> struct PackVec<double> {
+  typedef double2 T;
+  static constexpr int N = 2;
+};
+
+// Pack U = W / s (row-major W, ldw) into tiles; padding is zero. mode: 0 no
+// scales, 1 per-row, 2 per-column. Also sets the leaf blocks' error copy to
+// the sentinel and their ticket counters and status word to zero. Grid:
+// (Mt * ceil(Nt / kPackTiles), batch); vec: W and ldw allow 16-byte loads.
 template <typename R, int T>
 __global__ __launch_bounds__(256) void pack_w_kernel(int64_t m, int64_t n, int Nt,
                                                      const R* __restrict__ W, int64_t ldw,
-                                                     const R* __restrict__ sc, int mode,
+                                                     const R* __restrict__ sc, int mode, int vec,
                                                      R* __restrict__ Wk, BatchStrides bs,
                                                      int* __restrict__ sync, int64_t sync_stride,
                                                      int sync_words, R* __restrict__ Eb) {
-  // problem blockIdx.y of a batch
-  const int64_t b = blockIdx.y;
+  typedef PackVec<R> V;
+  typedef typename V::T vt;
+  constexpr int VN = V::N, SW = kPackTiles * T, NV = T * SW / VN;
+  const int64_t b = blockIdx.y;  // problem of a batch
   W += b * bs.w;
   if (sc) sc += b * bs.s;
   Wk += b * bs.ws;
-  const int64_t tile = blockIdx.x;
-  if (sync && tile == 0) {
-    // the leaf blocks' ticket counters and the status word start at zero
+  const int ns = (Nt + kPackTiles - 1) / kPackTiles;
+  const int64_t P = blockIdx.x / ns;
+  const int Q0 = (int)(blockIdx.x % ns) * kPackTiles;
+  if (sync && blockIdx.x == 0) {
     sync += b * sync_stride;
     for (int i = threadIdx.x; i < sync_words; i += blockDim.x) sync[i] = 0;
   }
-  if (Eb) {
-    // the leaf blocks' error copy starts as the sentinel
-    R* e = Eb + b * bs.ws + tile * T * T;
-    for (int i = threadIdx.x; i < T * T; i += blockDim.x) e[i] = sentinel_value<R>();
-  }
-  const int64_t P = tile / Nt, Q = tile % Nt;
-  R* dst = Wk + tile * T * T;
-  for (int e = threadIdx.x; e < T * T; e += blockDim.x) {
-    const int64_t i = P * T + e / T, j = Q * T + e % T;
-    R v = R(0);
-    if (i < m && j < n) {
-      v = W[i * ldw + j];
-      if (mode == 1) v = v / sc[i];
-      else if (mode == 2) v = v / sc[j];
+  for (int f = threadIdx.x; f < NV; f += blockDim.x) {
+    const int r = f / (SW / VN), c = (f % (SW / VN)) * VN;  // strip row, first column
+    const int Q = Q0 + c / T;
+    if (Q >= Nt) continue;
+    const int64_t i = P * T + r, j0 = (int64_t)Q0 * T + c;
+    R v[VN];
+    if (i < m && vec && j0 + VN <= n) {
+      const vt x = *reinterpret_cast<const vt*>(W + i * ldw + j0);
+      __builtin_memcpy(v, &x, sizeof x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) v[e] = (i < m && j0 + e < n) ? W[i * ldw + j0 + e] : R(0);
     }
-    dst[e] = v;
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+      if (i < m && j0 + e < n) {
+        if (mode == 1) v[e] = v[e] / sc[i];
+        else if (mode == 2) v[e] = v[e] / sc[j0 + e];
+      }
+    }
+    const int64_t o = ((P * Nt + Q) * T + r) * T + c % T;
+    vt y;
+    __builtin_memcpy(&y, v, sizeof y);
+    *reinterpret_cast<vt*>(Wk + o) = y;
+    if (Eb) {
+      // the leaf blocks' error copy starts as the sentinel
+      R z[VN];
+#pragma unroll
+      for (int e = 0; e < VN; ++e) z[e] = sentinel_value<R>();
+      __builtin_memcpy(&y, z, sizeof y);
+      *reinterpret_cast<vt*>(Eb + b * bs.ws + o) = y;
+    }
   }
 }
 
 // Pack the strict lower triangle of a normalised factor into lower tiles,
 // scaled to code units when sc is given (entry (i, j) times s_j / s_i); the
-// diagonal is 1, everything above it and on padding 0.
+// diagonal is 1, everything above it and on padding 0. Grid: (ceil(Dt /
+// kPackTiles), min(Dt, 65535), batch): strip x of tile rows y, y + gridDim.y,
+// ... (strips past a row's diagonal tile are skipped); vec: L and ld allow
+// 16-byte loads.
 template <typename R, int T>
-__global__ __launch_bounds__(256) void pack_l_kernel(int64_t dim, const R* __restrict__ L,
-                                                     int64_t ld, int64_t sL,
+__global__ __launch_bounds__(256) void pack_l_kernel(int64_t dim, int64_t Dt, const R* __restrict__ L,
+                                                     int64_t ld, int64_t sL, int vec,
                                                      const R* __restrict__ sc, int64_t sS,
                                                      R* __restrict__ Lp, int64_t sLp) {
-  const int64_t b = blockIdx.y;  // problem of a batch
+  typedef PackVec<R> V;
+  typedef typename V::T vt;
+  constexpr int VN = V::N, SW = kPackTiles * T, NV = T * SW / VN;
+  const int64_t b = blockIdx.z;  // problem of a batch
   L += b * sL;
   if (sc) sc += b * sS;
   Lp += b * sLp;
-  const int64_t t = blockIdx.x;
-  int64_t P = (int64_t)((__builtin_sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-  while (P * (P + 1) / 2 > t) --P;
-  while ((P + 1) * (P + 2) / 2 <= t) ++P;
-  const int64_t I = t - P * (P + 1) / 2;
-  R* dst = Lp + t * T * T;
-  for (int e = threadIdx.x; e < T * T; e += blockDim.x) {
-    const int64_t i = P * T + e / T, j = I * T + e % T;
-    R v = R(0);
-    if (i == j) v = R(1);
-    else if (j < i && i < dim) {
-      v = L[i * ld + j];
-      if (sc) v = v * sc[j] / sc[i];
+  const int I0 = (int)blockIdx.x * kPackTiles;
+  for (int64_t P = blockIdx.y; P < Dt; P += gridDim.y) {
+  if (I0 > P) continue;
+  for (int f = threadIdx.x; f < NV; f += blockDim.x) {
+    const int r = f / (SW / VN), c = (f % (SW / VN)) * VN;
+    const int I = I0 + c / T;
+    if (I > P) continue;
+    const int64_t i = P * T + r, j0 = (int64_t)I0 * T + c;
+    R v[VN];
+    if (i < dim && vec && j0 + VN <= i) {
+      const vt x = *reinterpret_cast<const vt*>(L + i * ld + j0);
+      __builtin_memcpy(v, &x, sizeof x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) v[e] = (j0 + e < i && i < dim) ? L[i * ld + j0 + e] : R(0);
     }
-    dst[e] = v;
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+      const int64_t j = j0 + e;
+      if (i == j) v[e] = R(1);
+      else if (j < i && i < dim) {
+        if (sc) v[e] = v[e] * sc[j] / sc[i];
+      } else {
+        v[e] = R(0);
+      }
+    }
+    const int64_t o = ((P * (P + 1) / 2 + I) * T + r) * T + c % T;
+    vt y;
+    __builtin_memcpy(&y, v, sizeof y);
+    *reinterpret_cast<vt*>(Lp + o) = y;
+  }
   }
 }
 
@@ -659,10 +719,14 @@ __global__ __launch_bounds__(64 * kLeafWaves) void leaf_rows_kernel(
 template <typename R>
 hipError_t launch_pack_w(const SolveGeom& g, const R* W, int64_t ldw, const R* scales,
                          int scale_mode, R* Wk, hipStream_t s, const LeafSync& ls) {
-  const int64_t nt = (int64_t)g.Mt * g.Nt;
+  const int64_t nt = (int64_t)g.Mt * ((g.Nt + kPackTiles - 1) / kPackTiles);
   if (nt == 0 || g.batch <= 0) return hipSuccess;
+  // 16-byte loads need every row start of every problem 16-byte aligned
+  constexpr int VN = 16 / sizeof(R);
+  const int vec = reinterpret_cast<uintptr_t>(W) % 16 == 0 && ldw % VN == 0 &&
+                  (g.batch == 1 || g.bs.w % VN == 0);
   hipLaunchKernelGGL((pack_w_kernel<R, kTile>), dim3((unsigned)nt, (unsigned)g.batch), dim3(256),
-                     0, s, g.m, g.n, g.Nt, W, ldw, scales, scale_mode, Wk, g.bs, ls.sync,
+                     0, s, g.m, g.n, g.Nt, W, ldw, scales, scale_mode, vec, Wk, g.bs, ls.sync,
                      ls.stride, ls.nblocks + 1, static_cast<R*>(ls.eb));
   return hipGetLastError();
 }
@@ -672,10 +736,15 @@ hipError_t launch_pack_l(const SolveGeom& g, bool lb, const R* L, int64_t ld, co
                          R* Lp, hipStream_t s) {
   const int64_t dim = lb ? g.m : g.n;
   const int Dt = lb ? g.Mt : g.Nt;
-  const int64_t nt = (int64_t)Dt * (Dt + 1) / 2;
-  if (nt == 0 || g.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL((pack_l_kernel<R, kTile>), dim3((unsigned)nt, (unsigned)g.batch), dim3(256),
-                     0, s, dim, L, ld, lb ? g.bs.lb : g.bs.la, scales, g.bs.s, Lp, g.bs.ws);
+  if (Dt == 0 || g.batch <= 0) return hipSuccess;
+  constexpr int VN = 16 / sizeof(R);
+  const int64_t sL = lb ? g.bs.lb : g.bs.la;
+  const int vec = reinterpret_cast<uintptr_t>(L) % 16 == 0 && ld % VN == 0 &&
+                  (g.batch == 1 || sL % VN == 0);
+  const dim3 grid((unsigned)((Dt + kPackTiles - 1) / kPackTiles),
+                  (unsigned)(Dt < 65535 ? Dt : 65535), (unsigned)g.batch);
+  hipLaunchKernelGGL((pack_l_kernel<R, kTile>), grid, dim3(256), 0, s, dim, (int64_t)Dt, L, ld,
+                     sL, vec, scales, g.bs.s, Lp, g.bs.ws);
   return hipGetLastError();
 }
 
