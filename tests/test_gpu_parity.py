@@ -131,6 +131,45 @@ def test_solve_fp32_parity(gpu_lib, m, n, alpha):
     assert rep.max_dev <= 1e-3, rep
 
 
+def _strided(x: np.ndarray, ld: int, col0: int) -> torch.Tensor:
+    """x as the columns col0 .. col0 + cols - 1 of a wider device buffer whose
+    rows are ld elements apart (a leading dimension larger than the row and,
+    for odd col0, a start that is not 16-byte aligned)."""
+    rows, cols = x.shape
+    buf = np.full((rows, ld), np.nan, dtype=x.dtype)
+    buf[:, col0:col0 + cols] = x
+    return torch.from_numpy(buf).cuda()[:, col0:col0 + cols]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("alpha", ["4bit_row", "3bit_col"])
+@pytest.mark.parametrize("ld_pad,col0", [(4, 0), (4, 1), (3, 0), (2, 2)])
+def test_strided_operands_equal_contiguous(gpu_lib, dtype, alpha, ld_pad, col0):
+    """W, L^A and L^B passed as slices of wider buffers (leading dimension
+    larger than the row, aligned or not, rows starting at a misaligned
+    address) give the same codes and values bit for bit as contiguous
+    operands: the operand packing reads whole 16-byte vectors only where
+    every row start allows it and single elements elsewhere, with the same
+    per-entry arithmetic; NaN in the unused columns must not leak in."""
+    # ragged tile edges on both sides; the contiguous rows (68 and 92 elements)
+    # allow 16-byte loads, as do the strided ones with ld_pad 4 (and 2 + 2 in
+    # float64); the others start misaligned or have an odd leading dimension
+    m, n = 68, 92
+    al, rule = ALPHAS[alpha]
+    p = _problem(m, n, dtype, 3 * ld_pad + col0, alpha)
+    inp = prepare(p.W, p.A, p.B, dtype, al, rule, hi=7 if alpha != "3bit_col" else 3)
+    s = to_dev(inp.s)
+    V0, Wt0 = gpu_lib.solve(to_dev(inp.W), to_dev(inp.LA), to_dev(inp.LB), inp.alphabet, s,
+                            scale_mode=inp.mode, return_wt=True)
+    Ws = _strided(inp.W, n + col0 + ld_pad, col0)
+    LAs = _strided(inp.LA, n + col0 + ld_pad, col0)
+    LBs = _strided(inp.LB, m + col0 + ld_pad, col0)
+    V1, Wt1 = gpu_lib.solve(Ws, LAs, LBs, inp.alphabet, s, scale_mode=inp.mode, return_wt=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(V1.cpu().numpy(), V0.cpu().numpy())
+    np.testing.assert_array_equal(Wt1.cpu().numpy(), Wt0.cpu().numpy())
+
+
 def test_config2_fp32_512(gpu_lib):
     """512x512 float32, heavy-tailed input Gram, 4-bit per-row scales."""
     p = config2()
