@@ -22,3 +22,18 @@ def gpu_lib():
     import kronecker_factored_gptq_amd as bk
     bk.lib()  # raises if the extension is missing
     return bk
+
+
+@pytest.fixture
+def progress(request):
+    """say(msg): a progress line on the terminal while output is captured,
+    for tests whose oracle work runs for minutes without a result line."""
+    capman = request.config.pluginmanager.getplugin("capturemanager")
+
+    def say(msg):
+        if capman is None:
+            print(f"[progress] {msg}", flush=True)
+            return
+        with capman.global_and_fixture_disabled():
+            print(f"[progress] {msg}", flush=True)
+    return say

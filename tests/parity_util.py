@@ -138,7 +138,7 @@ def fp32_parity(inp: Inputs, V_gpu: np.ndarray, Wt_gpu: np.ndarray, ref: O.Resul
 
 
 def oracle_branch_spread(inp: Inputs, ref: O.Result, dA, dB, ulp_seeds=(1, 2, 3, 4),
-                         noise_seeds=(1, 2)):
+                         noise_seeds=(1, 2), say=None):
     """The float64 oracle's own loss spread between valid solutions. The
     oracle solves again from a nudged W and the loss of the new codes is
     compared with the loss of the reference codes (both by the error
@@ -151,7 +151,8 @@ def oracle_branch_spread(inp: Inputs, ref: O.Result, dA, dB, ulp_seeds=(1, 2, 3,
     A near-tie closer to its midpoint than the nudge flips, and the flip
     cascades into its downstream quadrant, so the spread measures how far
     two valid branches end up apart on this matrix. Returns (max relative
-    spread, [(kind, seed, agreement, relative loss change)])."""
+    spread, [(kind, seed, agreement, relative loss change)]). say(msg), if
+    given, is called after each branch."""
     l_ref = O.loss_from_errors(ref.E, dA, dB)
     W32 = np.asarray(inp.W, dtype=np.float32)
     nudged = []
@@ -168,6 +169,8 @@ def oracle_branch_spread(inp: Inputs, ref: O.Result, dA, dB, ulp_seeds=(1, 2, 3,
         r = oracle_solve(Inputs(Wp, inp.LA, inp.LB, inp.dA, inp.dB, inp.s, inp.mode, inp.alphabet))
         l = O.loss_from_errors(r.E, dA, dB)
         out.append((kind, sd, float(np.mean(r.V == ref.V)), (l - l_ref) / abs(l_ref)))
+        if say:
+            say(f"oracle branch {kind} seed {sd} solved")
     return max(abs(x[3]) for x in out), out
 
 

@@ -55,18 +55,20 @@ def _loss_identity_rel(out):
 _MLP = {}
 
 
-def _mlp(which):
+def _mlp(which, say):
     if which not in _MLP:
         _MLP.clear()
         p = config4(which)
         LA, dA = O.factor(p.A)
+        say(f"{p.name}: oracle factor of order {p.A.shape[0]} done")
         LB, dB = O.factor(p.B)
+        say(f"{p.name}: oracle factor of order {p.B.shape[0]} done")
         _MLP[which] = (p, LA, dA, LB, dB)
     return _MLP[which]
 
 
-def _mlp_fp64(bk, which):
-    p, LA, dA, LB, dB = _mlp(which)
+def _mlp_fp64(bk, which, say):
+    p, LA, dA, LB, dB = _mlp(which, say)
     m, n = p.W.shape
     W64 = p.W.astype(np.float64)
     s = O.row_scales(W64, p.scale_hi, np.float64)
@@ -74,6 +76,7 @@ def _mlp_fp64(bk, which):
     V, Wt = bk.solve(to_dev(W64), to_dev(LA), to_dev(LB), p.alphabet, to_dev(s), return_wt=True)
     V, Wt = V.cpu().numpy(), Wt.cpu().numpy()
     ref = oracle_solve(inp)
+    say(f"{p.name}: float64 oracle solve done")
     mism = int(np.count_nonzero(V != ref.V.astype(np.int32)))
     dev = float(np.max(np.abs(Wt - ref.Wt) / s[:, None]))
     print(p.name, "fp64 whole matrix: mismatches", mism, "of", m * n, "max dev", dev)
@@ -81,8 +84,8 @@ def _mlp_fp64(bk, which):
     assert dev <= 1e-9
 
 
-def _mlp_factor64(bk, which):
-    p, LA, dA, LB, dB = _mlp(which)
+def _mlp_factor64(bk, which, say):
+    p, LA, dA, LB, dB = _mlp(which, say)
     A64, B64 = p.A.astype(np.float64), p.B.astype(np.float64)
     LAg, LBg, dAg, dBg = bk.factor(to_dev(A64), to_dev(B64))
     for M, Lg, dg, R, rd in ((A64, LAg, dAg, LA, dA), (B64, LBg, dBg, LB, dB)):
@@ -91,8 +94,8 @@ def _mlp_factor64(bk, which):
         print(p.name, f"fp64 factor order {M.shape[0]}: cond <= {c:.3g}, max err {err:.3g}, tol {tol:.3g}")
 
 
-def _mlp_fp32(bk, which):
-    p, LA, dA, LB, dB = _mlp(which)
+def _mlp_fp32(bk, which, say):
+    p, LA, dA, LB, dB = _mlp(which, say)
     m, n = p.W.shape
     # the whole GPU path at full size
     out = _gpu_path(bk, p, p.scale_hi)
@@ -117,13 +120,14 @@ def _mlp_fp32(bk, which):
                      return_wt=True)
     V, Wt = V.cpu().numpy(), Wt.cpu().numpy()
     ref = oracle_solve(inp)
+    say(f"{p.name}: float64 oracle solve on the float32 factors done")
     rep = fp32_parity(inp, V, Wt, ref, dA=dA, dB=dB)
     if rep.mismatches:
         # four branches (two of each nudge): with two, the spread of this
         # matrix's branches (float32 loss swings of up to 2.5e-4 between
         # nudged solves) was sampled too thinly to bound a valid solve
         rep.branch_spread, rep.branch_detail = oracle_branch_spread(
-            inp, ref, dA, dB, ulp_seeds=(1, 2), noise_seeds=(1, 2))
+            inp, ref, dA, dB, ulp_seeds=(1, 2), noise_seeds=(1, 2), say=say)
     print(p.name, "fp32 whole matrix", rep.as_dict(), rep.branch_detail)
     assert_fp32_validity(rep)
     assert rep.max_dev <= 1e-4, rep
@@ -134,8 +138,9 @@ def _mlp_fp32(bk, which):
     ("gate_up", "fp64"), ("gate_up", "factor64"), ("gate_up", "fp32"),
     ("down", "fp64"), ("down", "factor64"), ("down", "fp32"),
 ])
-def test_mlp_full_size(gpu_lib, which, part):
-    {"fp64": _mlp_fp64, "factor64": _mlp_factor64, "fp32": _mlp_fp32}[part](gpu_lib, which)
+def test_mlp_full_size(gpu_lib, which, part, progress):
+    {"fp64": _mlp_fp64, "factor64": _mlp_factor64, "fp32": _mlp_fp32}[part](gpu_lib, which,
+                                                                          progress)
     if which == "down" and part == "fp32":
         _MLP.clear()
 

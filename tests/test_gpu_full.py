@@ -36,7 +36,7 @@ def test_attn4096_factor_matches_oracle(gpu_lib, cfg3):
 
 
 @pytest.mark.timeout(600)
-def test_attn4096_solve_parity(gpu_lib, cfg3):
+def test_attn4096_solve_parity(gpu_lib, cfg3, progress):
     """Float32 at 4096 x 4096 (the parity criteria of the hot path's
     float32 mode, replay and loss parts): every GPU decision the float64
     replay disagrees with is a near-tie within the measured float32
@@ -48,9 +48,11 @@ def test_attn4096_solve_parity(gpu_lib, cfg3):
     np.testing.assert_array_equal(s_gpu, inp.s)
     V, Wt = gpu_solve(gpu_lib, inp)
     ref = oracle_solve(inp)
+    progress("4096x4096: float64 oracle solve done")
     rep = fp32_parity(inp, V, Wt, ref, p.A, p.B)
     if rep.mismatches:
-        rep.branch_spread, rep.branch_detail = oracle_branch_spread(inp, ref, inp.dA, inp.dB)
+        rep.branch_spread, rep.branch_detail = oracle_branch_spread(inp, ref, inp.dA, inp.dB,
+                                                                    say=progress)
     print(rep.as_dict(), rep.branch_detail)
     # A float32 solve differs from the float64 one by ~1e-5 code units, so
     # among 16.7M decisions some near-ties flip and each flip cascades into its
